@@ -1,0 +1,369 @@
+#!/usr/bin/env python3
+"""Benchmark of the hybrid compressed attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Default workload: decode at 1M context of one interleaved CSA + HCA layer
+pair, batch 4 (262144 CSA entries, 8192 HCA entries, 64 heads, KV 512+64,
+MXFP4 indexer 64x128, top-k 2048, window 128, sink). One step is one pass of
+the whole hot path for one new token per sequence:
+  1. csa_compress  - the newest CSA entry (8 source tokens, two series)
+  2. csa_compress  - its indexer key, MXFP4 output
+  3. hca_compress  - the newest HCA entry (128 source tokens)
+  4. mxfp4_quantize - the indexer queries
+  5. indexer_topk  - scores over all 262144 entries, top-2048 per row
+  6. sparse_attn   - CSA attention over selected entries + window + sink
+  7. dense_compressed_attn - HCA attention over all 8192 entries + window + sink
+Each step is captured once into a HIP graph (torch.cuda.CUDAGraph) and the
+timed loop replays them. Four copies of the layer-pair state rotate between
+steps (as successive layers would), so a step never finds its 121 MB working
+set in the 256 MB Infinity Cache from the previous step.
+
+Prints one JSON line with the throughput, a roofline record of the dominant
+kernel (timed with HIP events around each of its launches inside the timed
+region) and the CPU oracle's throughput on the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "CSA+HCA decode tokens/s at 128K–1M ctx; % HBM peak; prefill % MFMA peak"
+
+
+def _log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+class DecodeWorkload:
+    """Decode-step state on the GPU for 'decode_1m_pair' (CSA + HCA) or
+    'csa_decode_128k' (CSA only), with host copies for the oracle."""
+
+    def __init__(self, name, copies=4, overrides=None, keep_host=True):
+        import torch
+
+        import compressed_sparse_kv_amd as csk
+        import synth
+
+        self.torch, self.csk = torch, csk
+        self.name = name
+        self.pair = name == "decode_1m_pair"
+        t0 = time.time()
+        d = synth.make(name, **(overrides or {}))
+        self.d = d
+        self.B, self.H, self.D, self.dv = d["B"], d["H"], d["D"], d["dv"]
+        self.N = d["kv_c"].shape[1]
+        self.HI, self.dI, self.k, self.W = d["HI"], d["dI"], d["k"], d["W"]
+        self.scale = d["scale"]
+        if not self.pair:
+            # the CSA-only workload appends its newest entry from these sources
+            g = synth.rng(1000 + d["B"])
+            for nm, dim in (("ca", self.D), ("za", self.D), ("cb", self.D), ("zb", self.D),
+                            ("ia", self.dI), ("iza", self.dI), ("ib", self.dI), ("izb", self.dI)):
+                d["src_" + nm] = synth.to_bf16(synth.normal(g, (self.B, 8, dim)))
+            d["bias_a"], d["bias_b"] = synth.normal(g, (4, self.D), 0.1), synth.normal(g, (4, self.D), 0.1)
+            d["ibias_a"], d["ibias_b"] = synth.normal(g, (4, self.dI), 0.1), synth.normal(g, (4, self.dI), 0.1)
+        _log(f"{name}: host inputs generated in {time.time() - t0:.1f}s")
+        t0 = time.time()
+        dev = torch.device("cuda:0")
+        self.dev = dev
+        T = lambda a: _to_dev(torch, a, dev)
+        # per-copy persistent state: caches and windows
+        kv_c0 = T(d["kv_c"])
+        kI = T(d["kI"])
+        kc0, ks0 = csk.mxfp4_quantize(kI)
+        del kI
+        self.copies = []
+        for c in range(copies):
+            st = {"kv_c": kv_c0 if c == 0 else kv_c0.clone(), "kc": kc0 if c == 0 else kc0.clone(),
+                  "ks": ks0 if c == 0 else ks0.clone(), "kv_w": T(d["kv_w"])}
+            if self.pair:
+                st["kv_h"] = T(d["kv_h"])
+                st["kv_w_h"] = T(d["kv_w_h"])
+            self.copies.append(st)
+        # per-step inputs (shared by the copies)
+        self.x = {k: T(d[k]) for k in ("q", "qI", "w", "q_pos", "w_pos0", "n_entries", "sink",
+                                       "src_ca", "src_za", "src_cb", "src_zb", "src_ia", "src_iza",
+                                       "src_ib", "src_izb", "bias_a", "bias_b", "ibias_a", "ibias_b")}
+        if self.pair:
+            self.Nh = d["kv_h"].shape[1]
+            for k in ("q_h", "n_entries_h", "sink_h", "src_c", "src_z", "bias_h"):
+                self.x[k] = T(d[k])
+        # outputs and workspaces, allocated once (graph capture needs fixed addresses)
+        B, H, dv, k = self.B, self.H, self.dv, self.k
+        self.qc = torch.empty((B, 1, self.HI, self.dI // 2), dtype=torch.uint8, device=dev)
+        self.qs = torch.empty((B, 1, self.HI, self.dI // 32), dtype=torch.uint8, device=dev)
+        self.idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+        self.score = torch.empty((B, 1, k), dtype=torch.float32, device=dev)
+        self.out = torch.empty((B, 1, H, dv), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B, 1, H), dtype=torch.float32, device=dev)
+        ws_i = csk.indexer_topk_workspace_size(B, 1, self.HI, self.dI, self.N, k, csk.CSK_MXFP4)
+        ws_s = csk.sparse_attn_workspace_size(B, 1, H, self.D, dv, k, self.W, csk.CSK_BF16)
+        self.ws_i = torch.empty(max(ws_i, 1), dtype=torch.uint8, device=dev)
+        self.ws_s = torch.empty(max(ws_s, 1), dtype=torch.uint8, device=dev)
+        if self.pair:
+            self.out_h = torch.empty((B, 1, H, dv), dtype=torch.bfloat16, device=dev)
+            self.lse_h = torch.empty((B, 1, H), dtype=torch.float32, device=dev)
+            ws_d = csk.dense_compressed_attn_workspace_size(B, 1, H, self.D, dv, self.Nh, 128, self.W,
+                                                            csk.CSK_BF16)
+            self.ws_d = torch.empty(max(ws_d, 1), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        if not keep_host:
+            self.d = None
+        _log(f"{name}: device state ready in {time.time() - t0:.1f}s "
+             f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
+
+    # ------------------------------------------------------------- one step
+    def step(self, c=0):
+        csk, x, st = self.csk, self.x, self.copies[c % len(self.copies)]
+        B, N, D, dI = self.B, self.N, self.D, self.dI
+        # 1-2: the newest CSA entry N-1 and its indexer key (a-block = source
+        # rows 4..7, previous block = rows 0..3 of the 8-token window)
+        csk.csa_compress(x["src_ca"][:, 4:], x["src_za"][:, 4:], x["src_cb"][:, 4:], x["src_zb"][:, 4:],
+                         x["bias_a"], x["bias_b"], 4, d_rope=64, entry0=N - 1, src_bstride=8,
+                         out=st["kv_c"][:, N - 1:], dst_bstride=N, S=4, B=B)
+        csk.csa_compress(x["src_ia"][:, 4:], x["src_iza"][:, 4:], x["src_ib"][:, 4:], x["src_izb"][:, 4:],
+                         x["ibias_a"], x["ibias_b"], 4, entry0=N - 1, src_bstride=8, out_dtype=csk.CSK_MXFP4,
+                         out=st["kc"][:, N - 1:], out_scale=st["ks"][:, N - 1:], dst_bstride=N, S=4, B=B)
+        if self.pair:
+            Nh = self.Nh
+            csk.hca_compress(x["src_c"], x["src_z"], x["bias_h"], 128, d_rope=64, entry0=Nh - 1,
+                             out=st["kv_h"][:, Nh - 1:], dst_bstride=Nh)
+        # 4-5: indexer queries to MXFP4, scores + top-k
+        csk.mxfp4_quantize(x["qI"], self.qc, self.qs)
+        csk.indexer_topk(self.qc, x["w"], st["kc"], x["q_pos"], x["n_entries"], 4, self.k, q_scale=self.qs,
+                         k_scale=st["ks"], idx=self.idx, score=self.score, workspace=self.ws_i)
+        # 6: CSA attention
+        csk.sparse_attn(x["q"], x["q_pos"], st["kv_c"], self.idx, st["kv_w"], x["w_pos0"], self.W, x["sink"],
+                        self.dv, 64, self.scale, out=self.out, lse=self.lse,
+                        workspace=self.ws_s)
+        # 7: HCA attention
+        if self.pair:
+            csk.dense_compressed_attn(x["q_h"], x["q_pos"], st["kv_h"], x["n_entries_h"], 128, st["kv_w_h"],
+                                      x["w_pos0"], self.W, x["sink_h"], self.dv, 64,
+                                      self.scale, out=self.out_h,
+                                      lse=self.lse_h, workspace=self.ws_d)
+
+    def kernels(self):
+        names = ["csa_compress", "mxfp4_quantize", "indexer_scores_fp4", "topk_threshold", "topk_filter",
+                 "topk_select", "attn_bf16_sparse", "attn_merge"]
+        if self.pair:
+            names += ["hca_compress", "attn_bf16_dense"]
+        return names
+
+    def algorithmic_bytes(self, kernel):
+        """Bytes the method must move in one launch of `kernel`."""
+        B, N, D, dI, HI, k, W, H, dv = (self.B, self.N, self.D, self.dI, self.HI, self.k, self.W,
+                                        self.H, self.dv)
+        if kernel == "indexer_scores_fp4":
+            return B * N * (dI // 2 + dI // 32) + B * HI * (dI // 2 + dI // 32 + 4)
+        if kernel == "attn_bf16_sparse":
+            return B * (k + W) * D * 2 + B * k * 4 + B * H * (D + dv) * 2
+        if kernel == "attn_bf16_dense":
+            return B * (self.Nh + W) * D * 2 + B * H * (D + dv) * 2
+        return None
+
+    def step_bytes(self):
+        b = self.algorithmic_bytes("indexer_scores_fp4") + self.algorithmic_bytes("attn_bf16_sparse")
+        if self.pair:
+            b += self.algorithmic_bytes("attn_bf16_dense")
+        return b
+
+    def config(self):
+        c = {"workload": self.name, "batch": self.B, "context": int(self.N * 4), "csa_entries": self.N,
+             "heads": self.H, "kv_dim": self.D, "value_dim": self.dv, "rope_dims": 64, "indexer_heads": self.HI,
+             "indexer_dim": self.dI, "indexer_dtype": "mxfp4", "top_k": self.k, "window": self.W, "sink": True,
+             "state_copies": len(self.copies)}
+        if self.pair:
+            c["hca_entries"] = self.Nh
+        return c
+
+    # --------------------------------------------------------- oracle step
+    def oracle_step(self, rows):
+        """The same decode step on the CPU oracle for the batch rows `rows`.
+        Returns a dict of results; the wall time is the caller's."""
+        import oracle
+
+        d = self.d
+        N = self.N
+        out = {}
+        sel = list(rows)
+        # newest entries
+        ca, za, cb, zb = (d[k][sel] for k in ("src_ca", "src_za", "src_cb", "src_zb"))
+        pos = np.array([[4 * (N - 2), 4 * (N - 1)]] * len(sel), np.int32)
+        e = oracle.csa_compress(ca, za, cb, zb, d["bias_a"], d["bias_b"], 4, d_rope=64, entry_pos=pos)[:, 1]
+        out["kv_new"] = oracle.round_bf16(e)
+        ia, iza, ib, izb = (d[k][sel] for k in ("src_ia", "src_iza", "src_ib", "src_izb"))
+        ek = oracle.csa_compress(ia, iza, ib, izb, d["ibias_a"], d["ibias_b"], 4)[:, 1]
+        kn_c, kn_s = oracle.mxfp4_encode(oracle.round_f32(ek))
+        out["key_new"] = (kn_c, kn_s)
+        kc, ks = oracle.mxfp4_encode(d["kI"][sel])
+        kc[:, N - 1], ks[:, N - 1] = kn_c, kn_s
+        out["kc"], out["ks"] = kc, ks
+        kv_c = d["kv_c"][sel].copy()
+        kv_c[:, N - 1] = out["kv_new"]
+        qc, qs = oracle.mxfp4_encode(d["qI"][sel])
+        out["qc"], out["qs"] = qc, qs
+        npos = d["q_pos"][sel]
+        idx, sc = oracle.indexer_topk(qc, d["w"][sel], kc, npos, d["n_entries"][sel], 4, self.k, q_scale=qs,
+                                      k_scale=ks)
+        out["idx"], out["score"] = idx, sc
+        o, l = oracle.sparse_attn(d["q"][sel], npos, kv_c, idx[:, None, :], d["kv_w"][sel], d["w_pos0"][sel],
+                                  self.W, d["sink"], self.dv, 64, d["scale"])
+        out["out"], out["lse"] = o, l
+        if self.pair:
+            Nh = self.Nh
+            c, z = d["src_c"][sel], d["src_z"][sel]
+            eh = oracle.hca_compress(c, z, d["bias_h"], 128, d_rope=64,
+                                     entry_pos=np.full((len(sel), 1), 128 * (Nh - 1), np.int32))[:, 0]
+            out["kvh_new"] = oracle.round_bf16(eh)
+            kv_h = d["kv_h"][sel].copy()
+            kv_h[:, Nh - 1] = out["kvh_new"]
+            oh, lh = oracle.dense_attn(d["q_h"][sel], npos, kv_h, d["n_entries_h"][sel], 128, d["kv_w_h"][sel],
+                                       d["w_pos0"][sel], self.W, d["sink_h"], self.dv, 64, d["scale"])
+            out["out_h"], out["lse_h"] = oh, lh
+        return out
+
+
+def _to_dev(torch, a, dev):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(a).to(dev)
+
+
+def run(args):
+    import torch
+
+    import compressed_sparse_kv_amd as csk
+
+    wl = DecodeWorkload(args.workload, copies=args.copies)
+    K, Wm = args.steps, args.warmup
+    # eager warm-up (first calls set kernel attributes outside any capture)
+    for i in range(max(Wm, 1)):
+        wl.step(i)
+    torch.cuda.synchronize()
+
+    # which kernel dominates: average event-timed duration per kernel
+    per = {}
+    for name in wl.kernels():
+        tm = csk.KernelTimer(name, 8)
+        for i in range(2):
+            wl.step(i)
+        torch.cuda.synchronize()
+        ds = tm.durations_ms()
+        tm.disarm()
+        if ds:
+            per[name] = (sum(ds) / len(ds), len(ds) / 2.0)
+    _log("eager per-kernel ms (avg, launches/step): " +
+         ", ".join(f"{n}={v[0]*1e3:.1f}us x{v[1]:g}" for n, v in per.items()))
+    dom = max((n for n in per if wl.algorithmic_bytes(n)), key=lambda n: per[n][0] * per[n][1])
+
+    # capture one graph per timed step, each with its own event pair around
+    # the dominant kernel
+    timer = csk.KernelTimer(dom, K)
+    graphs = []
+    cap_stream = torch.cuda.Stream()
+    for i in range(K):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            wl.step(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    if timer.count() != K:
+        raise RuntimeError(f"kernel timer recorded {timer.count()} of {K} launches")
+    timer.disarm()
+    for i in range(Wm):  # warm replays
+        graphs[i % K].replay()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(K):
+        graphs[i].replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / K
+    tokens = wl.B * K
+    value = tokens / elapsed
+    durs = timer.durations_ms()
+    avg_ms = sum(durs) / len(durs)
+    abytes = wl.algorithmic_bytes(dom)
+    achieved = abytes / (avg_ms * 1e-3) / 1e9
+    _log(f"{K} steps in {elapsed*1e3:.2f} ms -> {ms_per_step*1e3:.1f} us/step; dominant {dom} "
+         f"{avg_ms*1e3:.1f} us avg; step algorithmic bytes {wl.step_bytes()/1e6:.1f} MB -> "
+         f"{wl.step_bytes()/(ms_per_step*1e-3)/1e9:.0f} GB/s over the whole step")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16+mxfp4",
+        "data": "synthetic",
+        "config": wl.config(),
+        "roofline": {
+            "kernel": dom,
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes": abytes,
+            "avg_launch_us": round(avg_ms * 1e3, 2),
+            "step_hbm_frac": round(wl.step_bytes() / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(wl, args):
+    import oracle
+
+    rows = list(range(min(args.cpu_rows, wl.B)))
+    oracle.lib()
+    t0 = time.perf_counter()
+    wl.oracle_step(rows)
+    dt = time.perf_counter() - t0
+    threads = min(oracle.num_threads(), len(rows))
+    return {"value": round(len(rows) / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full decode step for {len(rows)} of {wl.B} sequences (compression of the newest "
+                      f"entries, MXFP4 query encoding, indexer over all {wl.N} entries, top-{wl.k}, sparse "
+                      f"attention" + (", dense HCA attention" if wl.pair else "") + f"); {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_1m_pair", choices=["decode_1m_pair", "csa_decode_128k"])
+    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--cpu-rows", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

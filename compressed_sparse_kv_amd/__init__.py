@@ -1,0 +1,251 @@
+"""Python binding of libcsk (hybrid compressed attention on MI355X / gfx950).
+
+Argument marshalling only: every function forwards torch tensors' device
+pointers, sizes and torch's current HIP stream to the C ABI declared in
+include/csk.h and raises on a non-zero return code. Outputs and workspaces
+are allocated here with torch when the caller does not pass them; all
+computation happens in the library's kernels. There is no fallback: if the
+library is missing or fails to load, every call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsk.so")
+
+CSK_F32, CSK_BF16, CSK_MXFP4 = 0, 1, 2
+_lib = None
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_i64 = ctypes.c_int64
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+
+class CskError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libcsk.so (built by compressed_sparse_kv_amd/build.py)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise CskError(f"{LIB_PATH} is not built; run compressed_sparse_kv_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        L.csk_last_error.restype = ctypes.c_char_p
+        L.csk_abi_version.restype = _i
+        L.csa_compress.argtypes = [_vp] * 6 + [_i] * 5 + [_i64, _i, _f, _vp, _i, _i, _vp, _vp, _i64, _vp]
+        L.hca_compress.argtypes = [_vp] * 3 + [_i] * 5 + [_i64, _i, _f, _vp, _i, _i, _vp, _vp, _i64, _vp]
+        L.mxfp4_quantize.argtypes = [_vp, _i, _i64, _i, _vp, _vp, _vp]
+        L.indexer_topk.argtypes = [_vp] * 7 + [_i] * 8 + [_vp, _vp, _vp, _sz, _vp]
+        L.indexer_topk_workspace_size.argtypes = [_i] * 7
+        L.indexer_topk_workspace_size.restype = _sz
+        L.sparse_attn.argtypes = ([_vp, _vp, _vp, _i, _vp, _i, _vp, _vp, _i, _i, _vp] + [_i] * 6
+                                  + [_f, _f, _i, _vp, _vp, _vp, _sz, _vp])
+        L.dense_compressed_attn.argtypes = ([_vp, _vp, _vp, _i, _vp, _i, _vp, _vp, _i, _i, _vp] + [_i] * 6
+                                            + [_f, _f, _i, _vp, _vp, _vp, _sz, _vp])
+        L.sparse_attn_workspace_size.argtypes = [_i] * 8
+        L.sparse_attn_workspace_size.restype = _sz
+        L.dense_compressed_attn_workspace_size.argtypes = [_i] * 9
+        L.dense_compressed_attn_workspace_size.restype = _sz
+        L.csk_kernel_timer_arm.argtypes = [ctypes.c_char_p, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i]
+        L.csk_kernel_timer_count.restype = _i
+        L.csk_kernel_timer_disarm.restype = None
+        _lib = L
+    return _lib
+
+
+def _check(rc, fn):
+    if rc != 0:
+        raise CskError(f"{fn} failed ({rc}): {lib().csk_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dt(t):
+    if t.dtype == torch.float32:
+        return CSK_F32
+    if t.dtype == torch.bfloat16:
+        return CSK_BF16
+    raise CskError(f"unsupported dtype {t.dtype}")
+
+
+def _torch_dt(code):
+    return {CSK_F32: torch.float32, CSK_BF16: torch.bfloat16}[code]
+
+
+def _ws(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def csa_compress(ca, za, cb, zb, bias_a, bias_b, m, d_rope=0, rope_base=10000.0, entry_pos=None,
+                 out_dtype=None, entry0=0, src_bstride=0, out=None, out_scale=None, dst_bstride=0,
+                 B=None, S=None):
+    """CSA compression of [B,S,D] series (see csa_compress in csk.h).
+
+    Returns out ([B,S//m,D] in out_dtype) or (codes, scales) for MXFP4.
+    """
+    B = ca.shape[0] if B is None else B
+    S = ca.shape[1] if S is None else S
+    D = ca.shape[-1]
+    out_dtype = _dt(ca) if out_dtype is None else out_dtype
+    out, out_scale = _alloc_compress_out(out, out_scale, B, S // m, D, out_dtype, ca.device)
+    rc = lib().csa_compress(_ptr(ca), _ptr(za), _ptr(cb), _ptr(zb), _ptr(bias_a), _ptr(bias_b), B, S, D, m,
+                            entry0, src_bstride, d_rope, rope_base, _ptr(entry_pos), _dt(ca), out_dtype,
+                            _ptr(out), _ptr(out_scale), dst_bstride, _stream())
+    _check(rc, "csa_compress")
+    return (out, out_scale) if out_dtype == CSK_MXFP4 else out
+
+
+def hca_compress(c, z, bias, m, d_rope=0, rope_base=10000.0, entry_pos=None, out_dtype=None, entry0=0,
+                 src_bstride=0, out=None, out_scale=None, dst_bstride=0, B=None, S=None):
+    B = c.shape[0] if B is None else B
+    S = c.shape[1] if S is None else S
+    D = c.shape[-1]
+    out_dtype = _dt(c) if out_dtype is None else out_dtype
+    out, out_scale = _alloc_compress_out(out, out_scale, B, S // m, D, out_dtype, c.device)
+    rc = lib().hca_compress(_ptr(c), _ptr(z), _ptr(bias), B, S, D, m, entry0, src_bstride, d_rope, rope_base,
+                            _ptr(entry_pos), _dt(c), out_dtype, _ptr(out), _ptr(out_scale), dst_bstride,
+                            _stream())
+    _check(rc, "hca_compress")
+    return (out, out_scale) if out_dtype == CSK_MXFP4 else out
+
+
+def _alloc_compress_out(out, out_scale, B, N, D, out_dtype, device):
+    if out is None:
+        if out_dtype == CSK_MXFP4:
+            out = torch.empty((B, N, D // 2), dtype=torch.uint8, device=device)
+        else:
+            out = torch.empty((B, N, D), dtype=_torch_dt(out_dtype), device=device)
+    if out_dtype == CSK_MXFP4 and out_scale is None:
+        out_scale = torch.empty((B, N, D // 32), dtype=torch.uint8, device=device)
+    return out, out_scale
+
+
+def mxfp4_quantize(x, codes=None, scales=None):
+    """x [..., cols] (fp32/bf16) -> (codes [..., cols/2], scales [..., cols/32])."""
+    cols = x.shape[-1]
+    rows = x.numel() // cols
+    if codes is None:
+        codes = torch.empty(x.shape[:-1] + (cols // 2,), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1] + (cols // 32,), dtype=torch.uint8, device=x.device)
+    rc = lib().mxfp4_quantize(_ptr(x), _dt(x), rows, cols, _ptr(codes), _ptr(scales), _stream())
+    _check(rc, "mxfp4_quantize")
+    return codes, scales
+
+
+def indexer_topk_workspace_size(B, T, HI, dI, Nmax, k, dtype):
+    return lib().indexer_topk_workspace_size(B, T, HI, dI, Nmax, k, dtype)
+
+
+def indexer_topk(q, w, kk, q_pos, n_entries, m, k, q_scale=None, k_scale=None, idx=None, score=None,
+                 workspace=None, with_score=True):
+    """Top-k compressed entries per query row (see indexer_topk in csk.h).
+
+    MXFP4: q [B,T,HI,dI/2] uint8 + q_scale, kk [B,Nmax,dI/2] uint8 + k_scale.
+    fp32:  q [B,T,HI,dI] float32, kk [B,Nmax,dI] float32.
+    Returns (idx [B,T,k] int32, score [B,T,k] float32 or None).
+    """
+    B, T, HI = w.shape
+    mx = q_scale is not None
+    dI = q.shape[-1] * 2 if mx else q.shape[-1]
+    Nmax = kk.shape[1]
+    dtype = CSK_MXFP4 if mx else CSK_F32
+    if idx is None:
+        idx = torch.empty((B, T, k), dtype=torch.int32, device=w.device)
+    if score is None and with_score:
+        score = torch.empty((B, T, k), dtype=torch.float32, device=w.device)
+    nbytes = indexer_topk_workspace_size(B, T, HI, dI, Nmax, k, dtype)
+    if workspace is None:
+        workspace = _ws(nbytes, w.device)
+    rc = lib().indexer_topk(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(kk), _ptr(k_scale), _ptr(q_pos),
+                            _ptr(n_entries), B, T, HI, dI, Nmax, m, k, dtype, _ptr(idx), _ptr(score),
+                            _ptr(workspace), workspace.numel(), _stream())
+    _check(rc, "indexer_topk")
+    return idx, score
+
+
+def sparse_attn_workspace_size(B, T, H, D, dv, k, W, dtype):
+    return lib().sparse_attn_workspace_size(B, T, H, D, dv, k, W, dtype)
+
+
+def dense_compressed_attn_workspace_size(B, T, H, D, dv, Nmax, m, W, dtype):
+    return lib().dense_compressed_attn_workspace_size(B, T, H, D, dv, Nmax, m, W, dtype)
+
+
+def _attn_io(q, kv_w, dv, out, lse, want_lse):
+    B, T, H, D = q.shape
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+    S_w = 0 if kv_w is None else kv_w.shape[1]
+    return B, T, H, D, S_w, out, lse
+
+
+def sparse_attn(q, q_pos, kv_c, idx, kv_w, w_pos0, W, sink, dv, d_rope, scale, rope_base=10000.0,
+                out=None, lse=None, workspace=None, want_lse=True):
+    """CSA attention (see sparse_attn in csk.h). Returns (out, lse)."""
+    B, T, H, D, S_w, out, lse = _attn_io(q, kv_w, dv, out, lse, want_lse)
+    k = idx.shape[-1]
+    nbytes = sparse_attn_workspace_size(B, T, H, D, dv, k, W if S_w else 0, _dt(q))
+    if workspace is None:
+        workspace = _ws(nbytes, q.device)
+    rc = lib().sparse_attn(_ptr(q), _ptr(q_pos), _ptr(kv_c), kv_c.shape[1], _ptr(idx), k, _ptr(kv_w),
+                           _ptr(w_pos0), S_w, W, _ptr(sink), B, T, H, D, dv, d_rope, rope_base, scale, _dt(q),
+                           _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream())
+    _check(rc, "sparse_attn")
+    return out, lse
+
+
+def dense_compressed_attn(q, q_pos, kv_c, n_entries, m, kv_w, w_pos0, W, sink, dv, d_rope, scale,
+                          rope_base=10000.0, out=None, lse=None, workspace=None, want_lse=True):
+    """HCA attention (see dense_compressed_attn in csk.h). Returns (out, lse)."""
+    B, T, H, D, S_w, out, lse = _attn_io(q, kv_w, dv, out, lse, want_lse)
+    Nmax = kv_c.shape[1]
+    nbytes = dense_compressed_attn_workspace_size(B, T, H, D, dv, Nmax, m, W if S_w else 0, _dt(q))
+    if workspace is None:
+        workspace = _ws(nbytes, q.device)
+    rc = lib().dense_compressed_attn(_ptr(q), _ptr(q_pos), _ptr(kv_c), Nmax, _ptr(n_entries), m, _ptr(kv_w),
+                                     _ptr(w_pos0), S_w, W, _ptr(sink), B, T, H, D, dv, d_rope, rope_base, scale,
+                                     _dt(q), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream())
+    _check(rc, "dense_compressed_attn")
+    return out, lse
+
+
+class KernelTimer:
+    """Brackets the next n launches of one library kernel with HIP events
+    recorded on the launch stream (see csk_kernel_timer_arm)."""
+
+    def __init__(self, kernel, n):
+        self.kernel = kernel
+        self.start = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        self.stop = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in self.start + self.stop:
+            e.record()  # materialise the underlying hipEvent_t
+        torch.cuda.synchronize()
+        arr = _vp * n
+        self._s = arr(*[e.cuda_event for e in self.start])
+        self._e = arr(*[e.cuda_event for e in self.stop])
+        _check(lib().csk_kernel_timer_arm(kernel.encode(), self._s, self._e, n), "csk_kernel_timer_arm")
+
+    def count(self):
+        return lib().csk_kernel_timer_count()
+
+    def disarm(self):
+        lib().csk_kernel_timer_disarm()
+
+    def durations_ms(self):
+        n = self.count()
+        return [self.start[i].elapsed_time(self.stop[i]) for i in range(n)]

@@ -1,0 +1,256 @@
+// compress.hip - CSA / HCA softmax-gated pooling with partial-RoPE and
+// MXFP4 epilogues, and the standalone MXFP4 quantiser.
+//
+// Pooling ([P1] «CSA: сжать в 4 раза и выбрать top-k», step 1; «HCA: сжать
+// в 128 раз…»): per channel, a softmax over the gate logits Z + bias of the
+// entry's source slots weights the matching C values. The work is a pure
+// stream (each source byte read once, each output written once), so it is
+// HBM-bound: one thread owns two adjacent channels of one entry, so a wave
+// reads 64 consecutive channel pairs of a source row (coalesced), loops over
+// the entry's slots with an online softmax in fp32, and finishes with the
+// RoPE rotation and the output rounding or MXFP4 encoding in registers. For
+// MXFP4, 16 consecutive lanes own one 1x32 tile; the tile maximum is a
+// 16-lane shuffle reduction.
+#include "common.h"
+
+namespace csk {
+
+enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_MXFP4 = 2 };
+
+struct CompressArgs {
+  const void* ca;
+  const void* za;
+  const void* cb;
+  const void* zb;
+  const float* bias_a;
+  const float* bias_b;
+  int B, N, D, m, entry0, d_rope;
+  int64_t src_bstride, dst_bstride;
+  double base;
+  const int32_t* entry_pos;
+  void* out;
+  uint8_t* out_scale;
+};
+
+// Online softmax over `m` slots starting at row r0 (relative to src).
+template <typename IN>
+__device__ __forceinline__ void pool_slots(const IN* c, const IN* z, const float* bias, int64_t r0,
+                                           int m, int D, int ch, float2& mx, float2& den,
+                                           float2& num) {
+  for (int r = 0; r < m; ++r) {
+    const int64_t off = (r0 + r) * (int64_t)D + ch;
+    float2 zz = io<IN>::load2(z + off);
+    float2 cc = io<IN>::load2(c + off);
+    float2 bb = *reinterpret_cast<const float2*>(bias + (int64_t)r * D + ch);
+    float l0 = zz.x + bb.x, l1 = zz.y + bb.y;
+    if (l0 > mx.x) {
+      float f = expf(mx.x - l0);
+      den.x *= f;
+      num.x *= f;
+      mx.x = l0;
+    }
+    if (l1 > mx.y) {
+      float f = expf(mx.y - l1);
+      den.y *= f;
+      num.y *= f;
+      mx.y = l1;
+    }
+    float e0 = expf(l0 - mx.x), e1 = expf(l1 - mx.y);
+    den.x += e0;
+    den.y += e1;
+    num.x = fmaf(e0, cc.x, num.x);
+    num.y = fmaf(e1, cc.y, num.y);
+  }
+}
+
+template <int OUT>
+__device__ __forceinline__ void store_pair(const CompressArgs& a, int64_t orow, int p, float v0,
+                                           float v1) {
+  if (OUT == OUT_F32) {
+    float* o = reinterpret_cast<float*>(a.out) + orow * a.D + 2 * p;
+    *reinterpret_cast<float2*>(o) = make_float2(v0, v1);
+  } else if (OUT == OUT_BF16) {
+    uint32_t* o = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.out) + orow * a.D + 2 * p);
+    *o = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+  } else {
+    // 16 consecutive lanes hold one tile of 32 channels
+    float amax = fmaxf(fabsf(v0), fabsf(v1));
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+    uint32_t byte, sc;
+    if (amax == 0.0f) {
+      byte = 0;
+      sc = 127;
+    } else {
+      int s = mx_scale_exp(amax);
+      byte = e2m1_encode(v0, s) | (e2m1_encode(v1, s) << 4);
+      sc = (uint32_t)(s + 127);
+    }
+    reinterpret_cast<uint8_t*>(a.out)[orow * (a.D / 2) + p] = (uint8_t)byte;
+    if ((p & 15) == 0) a.out_scale[orow * (a.D / 32) + p / 16] = (uint8_t)sc;
+  }
+}
+
+template <typename IN, int OUT, bool CSA>
+__global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
+  const int half = a.D / 2;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)a.B * a.N * half;
+  if (gid >= total) return;
+  const int p = (int)(gid % half);
+  const int64_t row = gid / half;
+  const int b = (int)(row / a.N);
+  const int i = (int)(row % a.N);
+  const int ch = 2 * p;
+
+  float2 mx = make_float2(-INFINITY, -INFINITY);
+  float2 den = make_float2(0.f, 0.f), num = make_float2(0.f, 0.f);
+  const int64_t src0 = (int64_t)b * a.src_bstride;
+  pool_slots<IN>(reinterpret_cast<const IN*>(a.ca) + src0 * a.D,
+                 reinterpret_cast<const IN*>(a.za) + src0 * a.D, a.bias_a, (int64_t)a.m * i, a.m,
+                 a.D, ch, mx, den, num);
+  if (CSA && (a.entry0 + i) > 0)
+    pool_slots<IN>(reinterpret_cast<const IN*>(a.cb) + src0 * a.D,
+                   reinterpret_cast<const IN*>(a.zb) + src0 * a.D, a.bias_b,
+                   (int64_t)a.m * (i - 1), a.m, a.D, ch, mx, den, num);
+  float v0 = num.x / den.x, v1 = num.y / den.y;
+
+  const int rope0 = a.D - a.d_rope;
+  if (ch >= rope0) {
+    const double pos = a.entry_pos ? (double)a.entry_pos[(int64_t)b * a.N + i]
+                                   : (double)a.m * (double)(a.entry0 + i);
+    float c, s;
+    rope_cs(pos, (ch - rope0) / 2, a.d_rope, a.base, &c, &s);
+    float r0 = v0 * c - v1 * s;
+    float r1 = v0 * s + v1 * c;
+    v0 = r0;
+    v1 = r1;
+  }
+  store_pair<OUT>(a, (int64_t)b * a.dst_bstride + i, p, v0, v1);
+}
+
+template <typename IN>
+__global__ __launch_bounds__(256) void mxfp4_quant_kernel(const IN* x, int64_t rows, int cols,
+                                                           uint8_t* codes, uint8_t* scales) {
+  const int half = cols / 2;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= rows * half) return;
+  const int p = (int)(gid % half);
+  const int64_t r = gid / half;
+  float2 v = io<IN>::load2(x + r * cols + 2 * p);
+  float amax = fmaxf(fabsf(v.x), fabsf(v.y));
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+  uint32_t byte, sc;
+  if (amax == 0.0f) {
+    byte = 0;
+    sc = 127;
+  } else {
+    int s = mx_scale_exp(amax);
+    byte = e2m1_encode(v.x, s) | (e2m1_encode(v.y, s) << 4);
+    sc = (uint32_t)(s + 127);
+  }
+  codes[r * half + p] = (uint8_t)byte;
+  if ((p & 15) == 0) scales[r * (cols / 32) + p / 16] = (uint8_t)sc;
+}
+
+template <typename IN, bool CSA>
+static int launch_compress_out(const char* name, const CompressArgs& a, int out_dtype,
+                               hipStream_t s) {
+  const int64_t total = (int64_t)a.B * a.N * (a.D / 2);
+  dim3 grid((unsigned)ceil_div(total, 256)), block(256);
+  switch (out_dtype) {
+    case CSK_F32: return launch(name, compress_kernel<IN, OUT_F32, CSA>, grid, block, 0, s, a);
+    case CSK_BF16: return launch(name, compress_kernel<IN, OUT_BF16, CSA>, grid, block, 0, s, a);
+    default: return launch(name, compress_kernel<IN, OUT_MXFP4, CSA>, grid, block, 0, s, a);
+  }
+}
+
+static int compress_common(const char* fn, bool csa, const void* ca, const void* za,
+                           const void* cb, const void* zb, const float* bias_a,
+                           const float* bias_b, int B, int S, int D, int m, int entry0,
+                           int64_t src_bstride, int d_rope, float rope_base,
+                           const int32_t* entry_pos, int in_dtype, int out_dtype, void* out,
+                           uint8_t* out_scale, int64_t dst_bstride, void* stream) {
+  clear_error();
+  std::string f(fn);
+  if (B < 0 || S < 0 || D <= 0 || (D & 1) || m <= 0 || entry0 < 0)
+    return fail(CSK_EINVAL, f + ": need B >= 0, S >= 0, even D > 0, m > 0, entry0 >= 0");
+  const bool empty = B == 0 || S / m == 0;  // nothing is read or written
+  if (!empty && (!ca || !za || !bias_a || !out || (csa && (!cb || !zb || !bias_b))))
+    return fail(CSK_EINVAL, f + ": null pointer");
+  if (d_rope < 0 || d_rope > D || (d_rope & 1))
+    return fail(CSK_EINVAL, f + ": d_rope must be even and in [0, D]");
+  if (in_dtype != CSK_F32 && in_dtype != CSK_BF16)
+    return fail(CSK_EUNSUPPORTED, f + ": in_dtype must be CSK_F32 or CSK_BF16");
+  if (out_dtype != CSK_F32 && out_dtype != CSK_BF16 && out_dtype != CSK_MXFP4)
+    return fail(CSK_EUNSUPPORTED, f + ": out_dtype must be CSK_F32, CSK_BF16 or CSK_MXFP4");
+  if (out_dtype == CSK_MXFP4 && (D % 32 || (!out_scale && !empty)))
+    return fail(CSK_EINVAL, f + ": MXFP4 output needs D % 32 == 0 and out_scale");
+  const int N = S / m;
+  if (src_bstride < 0 || (src_bstride != 0 && src_bstride < S))
+    return fail(CSK_EINVAL, f + ": src_bstride must be 0 or >= S");
+  if (dst_bstride < 0 || (dst_bstride != 0 && dst_bstride < N))
+    return fail(CSK_EINVAL, f + ": dst_bstride must be 0 or >= S/m");
+  if (B == 0 || N == 0) return CSK_OK;
+  CompressArgs a;
+  a.ca = ca; a.za = za; a.cb = cb; a.zb = zb;
+  a.bias_a = bias_a; a.bias_b = bias_b;
+  a.B = B; a.N = N; a.D = D; a.m = m; a.entry0 = entry0; a.d_rope = d_rope;
+  a.src_bstride = src_bstride ? src_bstride : S;
+  a.dst_bstride = dst_bstride ? dst_bstride : N;
+  a.base = (double)rope_base;
+  a.entry_pos = entry_pos;
+  a.out = out; a.out_scale = out_scale;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const char* name = csa ? "csa_compress" : "hca_compress";
+  if (in_dtype == CSK_F32)
+    return csa ? launch_compress_out<float, true>(name, a, out_dtype, s)
+               : launch_compress_out<float, false>(name, a, out_dtype, s);
+  return csa ? launch_compress_out<uint16_t, true>(name, a, out_dtype, s)
+             : launch_compress_out<uint16_t, false>(name, a, out_dtype, s);
+}
+
+}  // namespace csk
+
+extern "C" {
+
+int csa_compress(const void* ca, const void* za, const void* cb, const void* zb,
+                 const float* bias_a, const float* bias_b, int B, int S, int D, int m,
+                 int entry0, int64_t src_bstride, int d_rope, float rope_base,
+                 const int32_t* entry_pos, int in_dtype, int out_dtype, void* out,
+                 uint8_t* out_scale, int64_t dst_bstride, void* stream) {
+  return csk::compress_common("csa_compress", true, ca, za, cb, zb, bias_a, bias_b, B, S, D, m,
+                              entry0, src_bstride, d_rope, rope_base, entry_pos, in_dtype,
+                              out_dtype, out, out_scale, dst_bstride, stream);
+}
+
+int hca_compress(const void* c, const void* z, const float* bias, int B, int S, int D, int m,
+                 int entry0, int64_t src_bstride, int d_rope, float rope_base,
+                 const int32_t* entry_pos, int in_dtype, int out_dtype, void* out,
+                 uint8_t* out_scale, int64_t dst_bstride, void* stream) {
+  return csk::compress_common("hca_compress", false, c, z, nullptr, nullptr, bias, nullptr, B, S,
+                              D, m, entry0, src_bstride, d_rope, rope_base, entry_pos, in_dtype,
+                              out_dtype, out, out_scale, dst_bstride, stream);
+}
+
+int mxfp4_quantize(const void* x, int in_dtype, int64_t rows, int cols, uint8_t* codes,
+                   uint8_t* scales, void* stream) {
+  csk::clear_error();
+  if (!x || !codes || !scales) return csk::fail(CSK_EINVAL, "mxfp4_quantize: null pointer");
+  if (rows < 0 || cols <= 0 || cols % 32)
+    return csk::fail(CSK_EINVAL, "mxfp4_quantize: need rows >= 0 and cols % 32 == 0");
+  if (in_dtype != CSK_F32 && in_dtype != CSK_BF16)
+    return csk::fail(CSK_EUNSUPPORTED, "mxfp4_quantize: in_dtype must be CSK_F32 or CSK_BF16");
+  if (rows == 0) return CSK_OK;
+  const int64_t total = rows * (cols / 2);
+  dim3 grid((unsigned)csk::ceil_div(total, 256)), block(256);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (in_dtype == CSK_F32)
+    return csk::launch("mxfp4_quantize", csk::mxfp4_quant_kernel<float>, grid, block, 0, s,
+                       reinterpret_cast<const float*>(x), rows, cols, codes, scales);
+  return csk::launch("mxfp4_quantize", csk::mxfp4_quant_kernel<uint16_t>, grid, block, 0, s,
+                     reinterpret_cast<const uint16_t*>(x), rows, cols, codes, scales);
+}
+
+}  // extern "C"

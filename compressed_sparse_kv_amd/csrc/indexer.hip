@@ -1,0 +1,687 @@
+// indexer.hip - lightning indexer scores and top-k selection on gfx950.
+//
+// Scores ([P1] «CSA: сжать в 4 раза и выбрать top-k», step 2; [P3] FP4
+// lightning indexer with a ReLU-scored multi-head dot product):
+//   I[t,s] = sum_h w[t,h] * ReLU(q[t,h] . k[s]).
+//
+// MXFP4 path: q.k for 16 heads x 16 keys is one scaled FP4 MFMA
+// (v_mfma_scale_f32_16x16x128_f8f6f4, E2M1 operands with per-32 E8M0
+// scales). Lane l of an operand holds row l%16 and the 32 consecutive
+// elements 32*(l/16).. of the 128-wide K slice, with that tile's scale byte;
+// the result lane l holds column l%16, rows 4*(l/16)..+3. Each tile sum is
+// an integer times a power of two, so the MFMA result is the exact dot
+// product whenever the four tile exponents of a (q, k) pair lie within the
+// fp32 significand (inputs from the MXFP4 quantiser of Gaussian data do).
+//
+// The head sum must be a fp32 fma chain over h ascending, which a lane can
+// only run if it holds all heads of one key. Query heads are permuted into
+// the MFMA rows so that lane group g holds heads 4*HT*g .. 4*HT*g+4*HT-1 of
+// its key column; four key tiles (64 keys) are then transposed across lane
+// groups with v_permlane32_swap / v_permlane16_swap, after which lane l
+// holds every head of key 64*iter + l and runs the chain in registers.
+//
+// Top-k: the k highest scores (ties to the lower index) in ascending index
+// order. Rows with at most TOPK_CAP candidates are selected in LDS by an
+// 8-bit radix select on an order-preserving 32-bit key followed by an
+// index-ordered compaction. Longer rows (decode over 32K-1M entries) are
+// first filtered with a threshold L that provably keeps at least k keys:
+// the scoring kernel writes the maximum of every group of GS consecutive
+// keys, and L is the k-th largest of those group maxima (each is a distinct
+// element, so at least k elements are >= L). Filtering writes per-slice
+// candidate lists in index order, and the same radix select finishes.
+#include <mutex>
+
+#include "common.h"
+
+namespace csk {
+
+constexpr int TOPK_CAP = 16384;   // elements a row select keeps in LDS
+constexpr int TOPK_THREADS = 1024;
+constexpr int SLICE = 2048;       // keys per filter workgroup
+constexpr int IDX_KEYS_PER_WG = 256;
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+struct IdxArgs {
+  const uint8_t* qc;   // MXFP4 q codes   [R, HI, dI/2]
+  const uint8_t* qs;   // MXFP4 q scales  [R, HI, dI/32]
+  const float* qf;     // fp32 q          [R, HI, dI]
+  const float* w;      // [R, HI]
+  const uint8_t* kc;   // [B, Nmax, dI/2]
+  const uint8_t* ks;   // [B, Nmax, dI/32]
+  const float* kf;     // [B, Nmax, dI]
+  const int32_t* q_pos;
+  const int32_t* n_entries;
+  int B, T, HI, dI, Nmax, m;
+  float* scores;       // [R, Nmax]
+  float* samples;      // [R, NG] or null
+  int gs_log2, ng;
+};
+
+__device__ __forceinline__ int visible_count(const IdxArgs& a, int r) {
+  const int b = r / a.T;
+  const int64_t p = a.q_pos[r];
+  if (p < 0) return 0;
+  int64_t nv = (p + 1) / a.m;
+  nv = nv < a.n_entries[b] ? nv : a.n_entries[b];
+  nv = nv < a.Nmax ? nv : a.Nmax;
+  return nv < 0 ? 0 : (int)nv;
+}
+
+// order-preserving key: larger score -> larger key; -0 is folded onto +0
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ void swap32(float& x, float& y) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16(float& x, float& y) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+
+// Group maxima of the scores held by a wave (one per lane, key = base+lane),
+// written for groups of 2^gs_log2 keys (gs <= 64).
+__device__ __forceinline__ void write_samples(const IdxArgs& a, int r, int base, float v) {
+  const int gs = 1 << a.gs_log2;
+  float mx = v;
+  for (int o = 1; o < gs; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const int lane = threadIdx.x & 63;
+  const int key = base + lane;
+  if ((lane & (gs - 1)) == 0 && key < a.Nmax)
+    a.samples[(int64_t)r * a.ng + (key >> a.gs_log2)] = mx;
+}
+
+// ---------------------------------------------------------------- MFMA path
+// HT = HI/16 head tiles, KS = dI/128 MFMA K-steps. One workgroup = 4 waves,
+// one query row, IDX_KEYS_PER_WG consecutive keys (64 per wave).
+template <int HT, int KS>
+__global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
+  const int r = blockIdx.x;
+  const int b = r / a.T;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int base = blockIdx.y * IDX_KEYS_PER_WG + wave * 64;
+  const int nv = visible_count(a, r);
+  if (base >= nv) {
+    if (a.samples && base < a.Nmax) write_samples(a, r, base, -INFINITY);
+    return;
+  }
+  const int HI = HT * 16;
+  const int rho = lane & 15, kb = lane >> 4;
+
+  // A operands: q rows permuted so lane group g ends up with heads 4*HT*g..
+  v8i qa[HT][KS];
+  int qsc[HT][KS];
+#pragma unroll
+  for (int t = 0; t < HT; ++t) {
+    const int h = 4 * HT * (rho >> 2) + 4 * t + (rho & 3);
+    const int64_t qrow = (int64_t)r * HI + h;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint4 v = *reinterpret_cast<const uint4*>(a.qc + qrow * (a.dI / 2) + s * 64 + kb * 16);
+      qa[t][s] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      qsc[t][s] = a.qs[qrow * (a.dI / 32) + s * 4 + kb];
+    }
+  }
+
+  v4f acc[4][HT];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    int key = base + 16 * kt + rho;
+    key = key < a.Nmax ? key : a.Nmax - 1;
+    const int64_t krow = (int64_t)b * a.Nmax + key;
+#pragma unroll
+    for (int t = 0; t < HT; ++t) acc[kt][t] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint4 v = *reinterpret_cast<const uint4*>(a.kc + krow * (a.dI / 2) + s * 64 + kb * 16);
+      const v8i kbv = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      const int ksc = a.ks[krow * (a.dI / 32) + s * 4 + kb];
+#pragma unroll
+      for (int t = 0; t < HT; ++t)
+        acc[kt][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            qa[t][s], kbv, acc[kt][t], 4, 4, 0, qsc[t][s], 0, ksc);
+    }
+  }
+
+  // transpose (key tile, lane group): lane group G of register set g then
+  // holds heads 4*HT*g + 4t + j of key 16*G + (lane % 16)
+  float d[4][HT][4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int t = 0; t < HT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d[kt][t][j] = acc[kt][t][j];
+#pragma unroll
+  for (int t = 0; t < HT; ++t) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      swap32(d[0][t][j], d[2][t][j]);
+      swap32(d[1][t][j], d[3][t][j]);
+      swap16(d[0][t][j], d[1][t][j]);
+      swap16(d[2][t][j], d[3][t][j]);
+    }
+  }
+
+  const float* wr = a.w + (int64_t)r * HI;
+  float score = 0.0f;
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int t = 0; t < HT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float v = d[g][t][j];
+        score = __builtin_fmaf(wr[4 * HT * g + 4 * t + j], v > 0.0f ? v : 0.0f, score);
+      }
+
+  const int key = base + lane;
+  if (key < nv) a.scores[(int64_t)r * a.Nmax + key] = score;
+  if (a.samples) write_samples(a, r, base, key < nv ? score : -INFINITY);
+}
+
+// -------------------------------------------------------------- VALU path
+// One thread per (row, key). fp32: per-head dot is an fma chain over the
+// channels. MXFP4: per-tile integer dot products combined in fp64 (exact for
+// any tile exponents within 2^38 of each other) and rounded once to fp32.
+__device__ __forceinline__ float e2m1_twice(uint32_t c) {
+  const float tbl[8] = {0.f, 1.f, 2.f, 3.f, 4.f, 6.f, 8.f, 12.f};
+  float v = tbl[c & 7u];
+  return (c & 8u) ? -v : v;
+}
+
+template <bool MX>
+__global__ __launch_bounds__(256) void idx_valu_kernel(IdxArgs a) {
+  const int r = blockIdx.x;
+  const int b = r / a.T;
+  const int s = blockIdx.y * 256 + threadIdx.x;
+  const int nv = visible_count(a, r);
+  if (s >= nv) return;
+  const int64_t krow = (int64_t)b * a.Nmax + s;
+  float score = 0.0f;
+  for (int h = 0; h < a.HI; ++h) {
+    const int64_t qrow = (int64_t)r * a.HI + h;
+    float d;
+    if (!MX) {
+      d = 0.0f;
+      const float* q = a.qf + qrow * a.dI;
+      const float* k = a.kf + krow * a.dI;
+      for (int i = 0; i < a.dI; ++i) d = __builtin_fmaf(q[i], k[i], d);
+    } else {
+      double tot = 0.0;
+      for (int g = 0; g < a.dI / 32; ++g) {
+        float pg = 0.0f;  // integer-valued, |pg| <= 4608: exact in fp32
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t qb = a.qc[qrow * (a.dI / 2) + g * 16 + i];
+          const uint32_t kbyte = a.kc[krow * (a.dI / 2) + g * 16 + i];
+          pg += e2m1_twice(qb & 15u) * e2m1_twice(kbyte & 15u);
+          pg += e2m1_twice(qb >> 4) * e2m1_twice(kbyte >> 4);
+        }
+        const int e = (int)a.qs[qrow * (a.dI / 32) + g] + (int)a.ks[krow * (a.dI / 32) + g] - 256;
+        tot += ldexp((double)pg, e);
+      }
+      d = (float)tot;
+    }
+    score = __builtin_fmaf(a.w[qrow], d > 0.0f ? d : 0.0f, score);
+  }
+  a.scores[(int64_t)r * a.Nmax + s] = score;
+}
+
+// Group maxima for the VALU path (the MFMA path writes them itself).
+__global__ __launch_bounds__(256) void idx_samples_kernel(IdxArgs a) {
+  const int r = blockIdx.x;
+  const int g = blockIdx.y * 256 + threadIdx.x;
+  if (g >= a.ng) return;
+  const int nv = visible_count(a, r);
+  const int gs = 1 << a.gs_log2;
+  float mx = -INFINITY;
+  for (int i = 0; i < gs; ++i) {
+    const int s = g * gs + i;
+    if (s < nv) mx = fmaxf(mx, a.scores[(int64_t)r * a.Nmax + s]);
+  }
+  a.samples[(int64_t)r * a.ng + g] = mx;
+}
+
+// ------------------------------------------------------------ radix select
+// Block-wide (TOPK_THREADS) selection over n elements with keys get(e).
+// Finds (mask, prefix, take) such that the selected set is every element
+// whose masked key is > prefix, plus the first `take` elements (in element
+// order) whose masked key == prefix.
+struct SelectState {
+  uint32_t mask, prefix;
+  int take;
+};
+
+struct SelectShared {
+  int hist[256];
+  int bin_sum[64];
+  int digit, above, binc;
+  int scan[TOPK_THREADS + 1];
+  int scan2[TOPK_THREADS + 1];
+};
+
+template <typename Get>
+__device__ SelectState radix_select(Get get, int n, int k, SelectShared& sh) {
+  SelectState st{0u, 0u, k};
+  const int tid = threadIdx.x;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = tid; i < 256; i += TOPK_THREADS) sh.hist[i] = 0;
+    __syncthreads();
+    for (int e = tid; e < n; e += TOPK_THREADS) {
+      const uint32_t u = get(e);
+      if ((u & st.mask) == st.prefix) atomicAdd(&sh.hist[(u >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane L owns bins 4L..4L+3; suffix sums over lanes find the digit
+      int s4 = sh.hist[4 * tid] + sh.hist[4 * tid + 1] + sh.hist[4 * tid + 2] + sh.hist[4 * tid + 3];
+      int suf = s4;
+      for (int o = 1; o < 64; o <<= 1) {
+        int v = __shfl_down(suf, o);
+        if (tid + o < 64) suf += v;
+      }
+      // suf = sum of bins >= 4*tid; the digit lies in the highest lane with suf >= take
+      const bool ok = suf >= st.take;
+      const unsigned long long bal = __ballot(ok);
+      const int L = 63 - __clzll(bal);
+      if (tid == L) {
+        int above = suf - s4;  // bins above this lane's group
+        int d = 4 * L + 3;
+        for (; d > 4 * L; --d) {
+          if (above + sh.hist[d] >= st.take) break;
+          above += sh.hist[d];
+        }
+        sh.digit = d;
+        sh.above = above;
+        sh.binc = sh.hist[d];
+      }
+    }
+    __syncthreads();
+    st.take -= sh.above;
+    st.prefix |= (uint32_t)sh.digit << shift;
+    st.mask |= 0xffu << shift;
+    if (sh.binc == st.take) break;  // the whole bin is taken: no tie resolution needed
+    __syncthreads();
+  }
+  __syncthreads();
+  return st;
+}
+
+// Index-ordered compaction of the selected elements. Each thread owns a
+// contiguous run of elements; counts of strictly-greater and tied elements
+// are scanned across the block.
+template <typename Get, typename Emit>
+__device__ void compact_selected(Get get, Emit emit, int n, const SelectState& st,
+                                 SelectShared& sh) {
+  const int tid = threadIdx.x;
+  const int per = (n + TOPK_THREADS - 1) / TOPK_THREADS;
+  const int e0 = tid * per;
+  const int e1 = min(n, e0 + per);
+  int gt = 0, eq = 0;
+  for (int e = e0; e < e1; ++e) {
+    const uint32_t u = get(e) & st.mask;
+    gt += u > st.prefix;
+    eq += u == st.prefix;
+  }
+  sh.scan[tid] = gt;
+  sh.scan2[tid] = eq;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over TOPK_THREADS entries (both arrays)
+  for (int o = 1; o < TOPK_THREADS; o <<= 1) {
+    int a = tid >= o ? sh.scan[tid - o] : 0;
+    int b = tid >= o ? sh.scan2[tid - o] : 0;
+    __syncthreads();
+    sh.scan[tid] += a;
+    sh.scan2[tid] += b;
+    __syncthreads();
+  }
+  int gt_before = sh.scan[tid] - gt;
+  int eq_before = sh.scan2[tid] - eq;
+  for (int e = e0; e < e1; ++e) {
+    const uint32_t u = get(e) & st.mask;
+    if (u > st.prefix) {
+      emit(gt_before + min(eq_before, st.take), e);
+      ++gt_before;
+    } else if (u == st.prefix) {
+      if (eq_before < st.take) emit(gt_before + eq_before, e);
+      ++eq_before;
+    }
+  }
+}
+
+struct TopkArgs {
+  IdxArgs ia;
+  int k;
+  int n_slices;
+  const uint32_t* thresh;   // [R] key threshold (filtered mode)
+  const int* cand_cnt;      // [R, n_slices]
+  const float* cand_score;  // [R, Nmax]: slice f at [f*SLICE, f*SLICE+cnt)
+  const int* cand_idx;      // [R, Nmax]
+  uint32_t* flat_key;       // [R, Nmax] spill when a row exceeds TOPK_CAP
+  int* flat_idx;            // [R, Nmax]
+  int32_t* idx;             // [R, k]
+  float* out_score;         // [R, k] or null
+};
+
+struct TopkShared {
+  SelectShared sel;
+  uint32_t key[TOPK_CAP];
+  int eidx[TOPK_CAP];
+  int slice_off[1024 + 1];
+  int n;
+};
+
+// Threshold from the group maxima: key of the k-th largest sample (or 0 =
+// keep everything when there are too few or too many samples).
+__global__ __launch_bounds__(TOPK_THREADS) void topk_threshold_kernel(TopkArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  TopkShared& sh = *reinterpret_cast<TopkShared*>(smem);
+  const int r = blockIdx.x;
+  const int nv = visible_count(a.ia, r);
+  const int gs = 1 << a.ia.gs_log2;
+  const int ng = (nv + gs - 1) / gs;
+  if (nv <= a.k || ng < a.k || ng > TOPK_CAP) {
+    if (threadIdx.x == 0) const_cast<uint32_t*>(a.thresh)[r] = 0u;
+    return;
+  }
+  for (int e = threadIdx.x; e < ng; e += TOPK_THREADS)
+    sh.key[e] = order_key(a.ia.samples[(int64_t)r * a.ia.ng + e]);
+  __syncthreads();
+  auto get = [&](int e) { return sh.key[e]; };
+  SelectState st = radix_select(get, ng, a.k, sh.sel);
+  // the k-th largest sample key: its full key is the prefix with the low
+  // bits of that element; when the radix select stopped early, the bin's
+  // minimum is a safe (lower) threshold
+  if (threadIdx.x == 0) const_cast<uint32_t*>(a.thresh)[r] = st.prefix;
+}
+
+// Candidate filter: keys of slice blockIdx.x with key(score) >= thresh,
+// compacted in index order.
+__global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a) {
+  __shared__ int wave_cnt[4];
+  const int r = blockIdx.x, f = blockIdx.y;
+  const int nv = visible_count(a.ia, r);
+  const int s0 = f * SLICE;
+  int* cnt_out = const_cast<int*>(a.cand_cnt) + (int64_t)r * a.n_slices + f;
+  if (s0 >= nv) {
+    if (threadIdx.x == 0) *cnt_out = 0;
+    return;
+  }
+  const uint32_t thr = a.thresh[r];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* cs = const_cast<float*>(a.cand_score) + (int64_t)r * a.ia.Nmax + s0;
+  int* ci = const_cast<int*>(a.cand_idx) + (int64_t)r * a.ia.Nmax + s0;
+  const float* sc = a.ia.scores + (int64_t)r * a.ia.Nmax;
+  int written = 0;
+  // 256 keys per step: wave w takes keys [64w, 64w+64) of the step
+  for (int step = 0; step < SLICE / 256; ++step) {
+    const int s = s0 + step * 256 + wave * 64 + lane;
+    float v = 0.f;
+    bool keep = false;
+    if (s < nv) {
+      v = sc[s];
+      keep = order_key(v) >= thr;
+    }
+    const unsigned long long bal = __ballot(keep);
+    if (lane == 0) wave_cnt[wave] = __popcll(bal);
+    __syncthreads();
+    int before = written;
+    for (int w2 = 0; w2 < wave; ++w2) before += wave_cnt[w2];
+    const int rank = __popcll(bal & ((1ull << lane) - 1ull));
+    if (keep) {
+      cs[before + rank] = v;
+      ci[before + rank] = s;
+    }
+    written += wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *cnt_out = written;
+}
+
+// Final selection for one row. filtered = false: the row's scores
+// themselves (index = position); filtered = true: the slice candidates.
+template <bool FILTERED>
+__global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  TopkShared& sh = *reinterpret_cast<TopkShared*>(smem);
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int k = a.k;
+  const int nv = visible_count(a.ia, r);
+  int32_t* oidx = a.idx + (int64_t)r * k;
+  float* osc = a.out_score ? a.out_score + (int64_t)r * k : nullptr;
+
+  int n;
+  if (!FILTERED) {
+    n = nv;
+  } else {
+    if (tid == 0) {
+      int acc = 0;
+      const int ns = (nv + SLICE - 1) / SLICE;
+      for (int f = 0; f < ns; ++f) {
+        sh.slice_off[f] = acc;
+        acc += a.cand_cnt[(int64_t)r * a.n_slices + f];
+      }
+      sh.slice_off[ns] = acc;
+      sh.n = acc;
+    }
+    __syncthreads();
+    n = sh.n;
+  }
+  const bool in_lds = n <= TOPK_CAP;
+  uint32_t* gkey = a.flat_key + (int64_t)r * a.ia.Nmax;
+  int* gidx = a.flat_idx + (int64_t)r * a.ia.Nmax;
+  const float* srow = a.ia.scores + (int64_t)r * a.ia.Nmax;
+
+  // gather elements (in index order) into LDS, or into the spill buffer
+  if (!FILTERED) {
+    if (in_lds)
+      for (int e = tid; e < n; e += TOPK_THREADS) sh.key[e] = order_key(srow[e]);
+  } else {
+    const int ns = (nv + SLICE - 1) / SLICE;
+    for (int f = 0; f < ns; ++f) {
+      const int c = sh.slice_off[f + 1] - sh.slice_off[f];
+      const int o = sh.slice_off[f];
+      const float* cs = a.cand_score + (int64_t)r * a.ia.Nmax + (int64_t)f * SLICE;
+      const int* ci = a.cand_idx + (int64_t)r * a.ia.Nmax + (int64_t)f * SLICE;
+      for (int e = tid; e < c; e += TOPK_THREADS) {
+        const uint32_t u = order_key(cs[e]);
+        if (in_lds) {
+          sh.key[o + e] = u;
+          sh.eidx[o + e] = ci[e];
+        } else {
+          gkey[o + e] = u;
+          gidx[o + e] = ci[e];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  auto get = [&](int e) -> uint32_t {
+    if (in_lds) return sh.key[e];
+    if (!FILTERED) return order_key(srow[e]);
+    return gkey[e];
+  };
+  auto index_of = [&](int e) -> int {
+    if (!FILTERED) return e;
+    return in_lds ? sh.eidx[e] : gidx[e];
+  };
+  auto emit = [&](int pos, int e) {
+    oidx[pos] = index_of(e);
+    if (osc) osc[pos] = key_to_float(get(e));
+  };
+
+  int nsel;
+  if (n <= k) {
+    for (int e = tid; e < n; e += TOPK_THREADS) emit(e, e);
+    nsel = n;
+  } else {
+    SelectState st = radix_select(get, n, k, sh.sel);
+    compact_selected(get, emit, n, st, sh.sel);
+    nsel = k;
+  }
+  for (int j = nsel + tid; j < k; j += TOPK_THREADS) {
+    oidx[j] = -1;
+    if (osc) osc[j] = -INFINITY;
+  }
+}
+
+// ------------------------------------------------------------ host layout
+struct IdxPlan {
+  bool filtered;
+  int gs_log2, ng, n_slices;
+  size_t off_scores, off_samples, off_thresh, off_cnt, off_cscore, off_cidx, off_fkey, off_fidx,
+      total;
+};
+
+static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static IdxPlan plan_indexer(int B, int T, int Nmax, int k) {
+  IdxPlan p{};
+  const size_t R = (size_t)B * T;
+  p.filtered = Nmax > TOPK_CAP;
+  int gs = 1;
+  if (p.filtered) {
+    while (gs < 64 && (int64_t)Nmax / (2 * gs) >= 2 * (int64_t)k) gs *= 2;
+  }
+  p.gs_log2 = 0;
+  while ((1 << p.gs_log2) < gs) ++p.gs_log2;
+  p.ng = (int)ceil_div(Nmax, gs);
+  p.n_slices = (int)ceil_div(Nmax, SLICE);
+  size_t o = 0;
+  p.off_scores = o; o = align_up(o + R * Nmax * 4);
+  if (p.filtered) {
+    p.off_samples = o; o = align_up(o + R * p.ng * 4);
+    p.off_thresh = o; o = align_up(o + R * 4);
+    p.off_cnt = o; o = align_up(o + R * p.n_slices * 4);
+    p.off_cscore = o; o = align_up(o + R * Nmax * 4);
+    p.off_cidx = o; o = align_up(o + R * Nmax * 4);
+    p.off_fkey = o; o = align_up(o + R * Nmax * 4);
+    p.off_fidx = o; o = align_up(o + R * Nmax * 4);
+  }
+  p.total = o;
+  return p;
+}
+
+}  // namespace csk
+
+extern "C" {
+
+size_t indexer_topk_workspace_size(int B, int T, int HI, int dI, int Nmax, int k, int dtype) {
+  (void)HI; (void)dI; (void)dtype;
+  if (B <= 0 || T <= 0 || Nmax <= 0 || k <= 0) return 0;
+  return csk::plan_indexer(B, T, Nmax, k).total;
+}
+
+int indexer_topk(const void* q, const uint8_t* q_scale, const float* w, const void* kk,
+                 const uint8_t* k_scale, const int32_t* q_pos, const int32_t* n_entries, int B,
+                 int T, int HI, int dI, int Nmax, int m, int k, int dtype, int32_t* idx,
+                 float* score, void* workspace, size_t ws_bytes, void* stream) {
+  using namespace csk;
+  clear_error();
+  if (!q || !w || !kk || !q_pos || !n_entries || !idx)
+    return fail(CSK_EINVAL, "indexer_topk: null pointer");
+  if (B <= 0 || T <= 0 || HI <= 0 || dI <= 0 || Nmax <= 0 || m <= 0 || k <= 0)
+    return fail(CSK_EINVAL, "indexer_topk: sizes must be positive");
+  if (dtype != CSK_MXFP4 && dtype != CSK_F32)
+    return fail(CSK_EUNSUPPORTED, "indexer_topk: dtype must be CSK_MXFP4 or CSK_F32");
+  if (dtype == CSK_MXFP4 && (dI % 32 || !q_scale || !k_scale))
+    return fail(CSK_EINVAL, "indexer_topk: MXFP4 needs dI % 32 == 0 and both scale arrays");
+  if ((int64_t)B * T > (1LL << 30) || ceil_div(Nmax, IDX_KEYS_PER_WG) > 65535)
+    return fail(CSK_EUNSUPPORTED, "indexer_topk: B*T or Nmax too large");
+  IdxPlan p = plan_indexer(B, T, Nmax, k);
+  if (p.n_slices > 1024) return fail(CSK_EUNSUPPORTED, "indexer_topk: Nmax too large");
+  if (!workspace || ws_bytes < p.total)
+    return fail(CSK_EWORKSPACE, "indexer_topk: workspace smaller than indexer_topk_workspace_size()");
+  char* ws = reinterpret_cast<char*>(workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int R = B * T;
+
+  IdxArgs ia{};
+  ia.qc = dtype == CSK_MXFP4 ? reinterpret_cast<const uint8_t*>(q) : nullptr;
+  ia.qs = q_scale;
+  ia.qf = dtype == CSK_F32 ? reinterpret_cast<const float*>(q) : nullptr;
+  ia.w = w;
+  ia.kc = dtype == CSK_MXFP4 ? reinterpret_cast<const uint8_t*>(kk) : nullptr;
+  ia.ks = k_scale;
+  ia.kf = dtype == CSK_F32 ? reinterpret_cast<const float*>(kk) : nullptr;
+  ia.q_pos = q_pos;
+  ia.n_entries = n_entries;
+  ia.B = B; ia.T = T; ia.HI = HI; ia.dI = dI; ia.Nmax = Nmax; ia.m = m;
+  ia.scores = reinterpret_cast<float*>(ws + p.off_scores);
+  ia.samples = p.filtered ? reinterpret_cast<float*>(ws + p.off_samples) : nullptr;
+  ia.gs_log2 = p.gs_log2;
+  ia.ng = p.ng;
+
+  int rc = CSK_OK;
+  const bool mfma = dtype == CSK_MXFP4 && HI % 16 == 0 && HI <= 64 && dI % 128 == 0 && dI <= 256;
+  if (mfma) {
+    dim3 grid((unsigned)R, (unsigned)ceil_div(Nmax, IDX_KEYS_PER_WG)), block(256);
+    const int HT = HI / 16, KS = dI / 128;
+#define CSK_IDX_CASE(ht, ks)                                                                 \
+  if (HT == ht && KS == ks) rc = launch("indexer_scores_fp4", idx_fp4_kernel<ht, ks>, grid, \
+                                        block, 0, s, ia);
+    CSK_IDX_CASE(1, 1) CSK_IDX_CASE(2, 1) CSK_IDX_CASE(3, 1) CSK_IDX_CASE(4, 1)
+    CSK_IDX_CASE(1, 2) CSK_IDX_CASE(2, 2) CSK_IDX_CASE(3, 2) CSK_IDX_CASE(4, 2)
+#undef CSK_IDX_CASE
+  } else {
+    dim3 grid((unsigned)R, (unsigned)ceil_div(Nmax, 256)), block(256);
+    rc = dtype == CSK_MXFP4 ? launch("indexer_scores_valu", idx_valu_kernel<true>, grid, block, 0, s, ia)
+                            : launch("indexer_scores_valu", idx_valu_kernel<false>, grid, block, 0, s, ia);
+    if (rc == CSK_OK && p.filtered) {
+      dim3 g2((unsigned)R, (unsigned)ceil_div(p.ng, 256));
+      rc = launch("indexer_samples", idx_samples_kernel, g2, block, 0, s, ia);
+    }
+  }
+  if (rc != CSK_OK) return rc;
+
+  TopkArgs ta{};
+  ta.ia = ia;
+  ta.k = k;
+  ta.n_slices = p.n_slices;
+  ta.idx = idx;
+  ta.out_score = score;
+  const size_t lds = sizeof(TopkShared);
+  static std::once_flag attr_once;
+  std::call_once(attr_once, [&] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(topk_threshold_kernel),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(topk_select_kernel<true>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(topk_select_kernel<false>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  });
+  if (p.filtered) {
+    ta.thresh = reinterpret_cast<const uint32_t*>(ws + p.off_thresh);
+    ta.cand_cnt = reinterpret_cast<const int*>(ws + p.off_cnt);
+    ta.cand_score = reinterpret_cast<const float*>(ws + p.off_cscore);
+    ta.cand_idx = reinterpret_cast<const int*>(ws + p.off_cidx);
+    ta.flat_key = reinterpret_cast<uint32_t*>(ws + p.off_fkey);
+    ta.flat_idx = reinterpret_cast<int*>(ws + p.off_fidx);
+    rc = launch("topk_threshold", topk_threshold_kernel, dim3(R), dim3(TOPK_THREADS), lds, s, ta);
+    if (rc == CSK_OK)
+      rc = launch("topk_filter", topk_filter_kernel, dim3(R, p.n_slices), dim3(256), 0, s, ta);
+    if (rc == CSK_OK)
+      rc = launch("topk_select", topk_select_kernel<true>, dim3(R), dim3(TOPK_THREADS), lds, s, ta);
+  } else {
+    rc = launch("topk_select", topk_select_kernel<false>, dim3(R), dim3(TOPK_THREADS), lds, s, ta);
+  }
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,218 @@
+/*
+ * csk.h - C ABI of the gfx950 (MI355X) hybrid compressed attention library
+ * (libcsk.so): CSA and HCA compression, MXFP4 quantisation, the lightning
+ * indexer with top-k selection, and sparse / dense attention over
+ * compressed KV entries with a sliding window and an attention sink.
+ *
+ * Sources (web pages about the DeepSeek-V4 technical report):
+ *   [P1] "Техотчёт DeepSeek-V4 (2026): миллион токенов контекста" (ai.flicky.cc)
+ *   [P3] aixai.ru blog post on V4's million-token context,
+ *        section "Гибридный attention: CSA и HCA"
+ *   [P4] "Технический отчёт DeepSeek-V4 — часть 1/2" (aifinder.ae mirror)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers: every tensor pointer is a DEVICE pointer (hipMalloc'd or a
+ *   torch CUDA tensor's data_ptr) to a dense row-major array, 4-byte aligned
+ *   (16-byte alignment is faster). The caller owns every buffer; the library
+ *   never allocates, frees or keeps pointers after the call returns.
+ * - Streams: `stream` is a hipStream_t (NULL = the default stream). Every
+ *   call only enqueues kernels on it and returns without synchronising, so
+ *   a non-zero return code reports argument errors and launch failures, not
+ *   faults inside kernels.
+ * - Scratch: calls that need scratch memory take a caller-owned device
+ *   `workspace` of at least the size the matching *_workspace_size()
+ *   returns. Its contents on entry do not matter. Two calls that run at the
+ *   same time must not share a workspace.
+ * - Dtypes: CSK_F32 = float32, CSK_BF16 = bfloat16 (uint16 bit patterns),
+ *   CSK_MXFP4 = packed E2M1 codes (element 2j in the low nibble of byte j)
+ *   plus one E8M0 scale byte (2^(byte-127)) per 32 consecutive elements.
+ * - Errors: every call returns CSK_OK (0) or a negative code and leaves a
+ *   message for csk_last_error() (thread-local). Nothing aborts or prints.
+ * - Determinism: results are bitwise reproducible run to run (no floating-
+ *   point atomics on any result path).
+ * - Rounding: floating-point results are computed in fp32 and rounded once
+ *   to the output dtype (round to nearest even).
+ */
+#ifndef CSK_H
+#define CSK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSK_OK 0
+#define CSK_EINVAL (-1)       /* null pointer, bad size or combination of arguments */
+#define CSK_EUNSUPPORTED (-2) /* dtype/shape combination not built, or no gfx950 device */
+#define CSK_EWORKSPACE (-3)   /* workspace smaller than *_workspace_size() */
+#define CSK_EHIP (-4)         /* HIP runtime error while launching */
+
+#define CSK_F32 0
+#define CSK_BF16 1
+#define CSK_MXFP4 2
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* csk_last_error(void);
+
+/* ABI revision of this header (incremented on incompatible change). */
+int csk_abi_version(void);
+#define CSK_ABI_VERSION 1
+
+/*
+ * csa_compress - CSA compression ([P1] «CSA: сжать в 4 раза и выбрать
+ * top-k», step 1; [P4]: every 2m tokens with stride m become one entry).
+ *
+ * Two KV series (C^a, C^b) and two gate series (Z^a, Z^b) of width D are
+ * pooled m-fold along the sequence. Entry i (global index e = entry0 + i)
+ * takes, per channel c, a softmax over the logits Z^a + bias_a of its own
+ * block of m tokens together with Z^b + bias_b of the previous block, and
+ * outputs the softmax-weighted sum of the matching C values. Global entry 0
+ * has no previous block (its softmax spans its m a-slots only). After
+ * pooling, the last d_rope channels are rotated by partial RoPE at the
+ * entry's position (interleaved channel pairs; pair j turns by
+ * pos * rope_base^(-2j/d_rope), angle formed in fp64).
+ *
+ *   ca, za, cb, zb : source rows, in_dtype (CSK_F32 | CSK_BF16). Row r of
+ *                    batch b is at element offset (b*src_bstride + r)*D, for
+ *                    r in [0, S). When entry0 > 0, rows r in [-m, 0) of cb
+ *                    and zb must also be readable: they form the previous
+ *                    block of the first produced entry.
+ *   bias_a, bias_b : [m, D] fp32 learned positional biases.
+ *   B, S, D, m     : batch, source rows, channels, ratio; N = S/m entries are
+ *                    produced (a trailing partial block produces none).
+ *   entry0         : global index of the first produced entry (>= 0).
+ *   src_bstride    : rows between batches in the sources (0 means S).
+ *   d_rope         : rotated channels (even, <= D; 0 = none).
+ *   entry_pos      : [B, N] int32 entry positions, or NULL for m*(entry0+i).
+ *   out_dtype      : CSK_F32 | CSK_BF16 | CSK_MXFP4 (MXFP4 needs D % 32 == 0).
+ *   out            : entry i of batch b at (b*dst_bstride + i)*D elements
+ *                    (MXFP4: codes at byte offset (b*dst_bstride + i)*D/2).
+ *   out_scale      : MXFP4 only: scales at byte (b*dst_bstride + i)*D/32.
+ *   dst_bstride    : entries between batches in the output (0 means N).
+ */
+int csa_compress(const void* ca, const void* za, const void* cb, const void* zb,
+                 const float* bias_a, const float* bias_b, int B, int S, int D, int m,
+                 int entry0, int64_t src_bstride, int d_rope, float rope_base,
+                 const int32_t* entry_pos, int in_dtype, int out_dtype, void* out,
+                 uint8_t* out_scale, int64_t dst_bstride, void* stream);
+
+/*
+ * hca_compress - HCA compression ([P1] «HCA: сжать в 128 раз, но смотреть
+ * на всё»: ratio m' = 128, no window overlap). As csa_compress with a single
+ * series: entry i pools its own block of m rows only. entry0 only sets the
+ * default positions m*(entry0+i).
+ */
+int hca_compress(const void* c, const void* z, const float* bias, int B, int S, int D, int m,
+                 int entry0, int64_t src_bstride, int d_rope, float rope_base,
+                 const int32_t* entry_pos, int in_dtype, int out_dtype, void* out,
+                 uint8_t* out_scale, int64_t dst_bstride, void* stream);
+
+/*
+ * mxfp4_quantize - MXFP4 encoding of rows of `cols` values ([P1] «FP4 с
+ * учётом квантования»: the indexer's Q.K path is cached and multiplied in
+ * FP4; MXFP4 with E2M1 elements in 1x32 tiles). Per tile of 32: scale
+ * exponent s = floor(log2 max|x|) - 2 clamped to [-127, 127] (127 stored for
+ * an all-zero tile); each element is the E2M1 value nearest to x/2^s, ties
+ * to the even mantissa bit, saturating at 6; zero is always the +0 code.
+ *   x      : [rows, cols] in_dtype (CSK_F32 | CSK_BF16), finite values.
+ *   codes  : [rows, cols/2] bytes;  scales : [rows, cols/32] bytes.
+ */
+int mxfp4_quantize(const void* x, int in_dtype, int64_t rows, int cols, uint8_t* codes,
+                   uint8_t* scales, void* stream);
+
+/*
+ * indexer_topk - lightning indexer and top-k selection ([P1] «CSA…», step
+ * 2; [P3]: FP4 lightning indexer with a ReLU-scored multi-head dot product).
+ *
+ * For query row (b,t) at position p = q_pos[b,t], compressed entry s is a
+ * candidate when s < n_entries[b] and its last source token m*(s+1)-1 <= p.
+ * Score I[t,s] = sum_h w[b,t,h] * ReLU(q[b,t,h] . k[b,s]), where each q.k
+ * is the exact dot product rounded once to fp32 (MXFP4) or an fp32 fused
+ * multiply-add chain over channels in ascending order (CSK_F32), and the
+ * head sum is an fp32 fused multiply-add chain over h = 0..HI-1 from +0.
+ * The min(k, #candidates) highest scores are selected, ties to the lower
+ * index, and returned in ascending index order, padded with -1.
+ *
+ *   q, q_scale : MXFP4 [B,T,HI,dI/2] codes + [B,T,HI,dI/32] scales, or
+ *                CSK_F32 [B,T,HI,dI] with q_scale NULL.
+ *   w          : [B,T,HI] fp32 head weights.
+ *   kk, k_scale: MXFP4 [B,Nmax,dI/2] + [B,Nmax,dI/32], or CSK_F32 [B,Nmax,dI].
+ *   q_pos      : [B,T] int32 absolute positions;  n_entries: [B] int32.
+ *   dtype      : CSK_MXFP4 (dI % 32 == 0) or CSK_F32.
+ *   idx        : [B,T,k] int32 output;  score: [B,T,k] fp32 or NULL
+ *                (scores of the returned entries, -inf for padding).
+ *   workspace  : >= indexer_topk_workspace_size(B,T,HI,dI,Nmax,k,dtype).
+ */
+int indexer_topk(const void* q, const uint8_t* q_scale, const float* w, const void* kk,
+                 const uint8_t* k_scale, const int32_t* q_pos, const int32_t* n_entries, int B,
+                 int T, int HI, int dI, int Nmax, int m, int k, int dtype, int32_t* idx,
+                 float* score, void* workspace, size_t ws_bytes, void* stream);
+size_t indexer_topk_workspace_size(int B, int T, int HI, int dI, int Nmax, int k, int dtype);
+
+/*
+ * sparse_attn - CSA attention: MQA over the selected compressed entries, a
+ * sliding window of uncompressed tokens and an attention sink ([P1] «CSA…»,
+ * step 3: every compressed entry is both key and value for all query heads;
+ * «HCA…»: 128-token window of uncompressed entries; [P4]: SWA branch,
+ * attention sink, partial RoPE on the last 64 dims).
+ *
+ * For row (b,t,h) at position p = q_pos[b,t]: q~ = q[b,t,h] with its last
+ * d_rope channels rotated at p. Candidates: kv_c[b,i] for every i in
+ * idx[b,t,:] with 0 <= i < Nmax (other values are skipped; duplicates
+ * count twice), and kv_w[b,r] for every window row whose position
+ * w_pos0[b]+r lies in [max(0, p-W+1), p]. One softmax runs over the logits
+ * scale*(q~ . K) of all candidates plus the sink logit sink[h] (which adds
+ * to the denominator only). out = sum_j p_j * K_j[0:dv], lse = M + ln Z.
+ * With no candidate and no sink, out = 0 and lse = -inf.
+ *
+ *   q       : [B,T,H,D] dtype, unrotated;  q_pos: [B,T] int32.
+ *   kv_c    : [B,Nmax,D] dtype (entries already rotated);  idx: [B,T,k].
+ *   kv_w    : [B,S_w,D] dtype (already rotated) or NULL with S_w = 0.
+ *   w_pos0  : [B] int32 position of window row 0 (may be NULL if S_w = 0).
+ *   sink    : [H] fp32 or NULL (no sink).
+ *   dtype   : CSK_BF16 (fp32 accumulation) or CSK_F32.
+ *   out     : [B,T,H,dv] dtype;  lse: [B,T,H] fp32 or NULL.
+ *   workspace: >= sparse_attn_workspace_size(...).
+ */
+int sparse_attn(const void* q, const int32_t* q_pos, const void* kv_c, int Nmax,
+                const int32_t* idx, int k, const void* kv_w, const int32_t* w_pos0, int S_w,
+                int W, const float* sink, int B, int T, int H, int D, int dv, int d_rope,
+                float rope_base, float scale, int dtype, void* out, float* lse, void* workspace,
+                size_t ws_bytes, void* stream);
+size_t sparse_attn_workspace_size(int B, int T, int H, int D, int dv, int k, int W, int dtype);
+
+/*
+ * dense_compressed_attn - HCA attention ([P1] «HCA…»: attention over the
+ * compressed entries stays dense; [P3]: every query attends to all
+ * compressed blocks). As sparse_attn, but the compressed candidates are
+ * every entry i < n_entries[b] whose last source token m*(i+1)-1 <= p.
+ *   n_entries: [B] int32;  m: compression ratio used for visibility.
+ */
+int dense_compressed_attn(const void* q, const int32_t* q_pos, const void* kv_c, int Nmax,
+                          const int32_t* n_entries, int m, const void* kv_w,
+                          const int32_t* w_pos0, int S_w, int W, const float* sink, int B, int T,
+                          int H, int D, int dv, int d_rope, float rope_base, float scale,
+                          int dtype, void* out, float* lse, void* workspace, size_t ws_bytes,
+                          void* stream);
+size_t dense_compressed_attn_workspace_size(int B, int T, int H, int D, int dv, int Nmax, int m,
+                                            int W, int dtype);
+
+/*
+ * csk_kernel_timer_arm - measurement hook. The next n launches of the
+ * library kernel named `kernel` ("indexer_scores_fp4", "attn_bf16", ...)
+ * are each bracketed by hipEventRecord(ev_start[j]) / hipEventRecord(
+ * ev_stop[j]) on the launch stream. The events are caller-created
+ * hipEvent_t handles. csk_kernel_timer_count() returns how many launches
+ * were recorded; csk_kernel_timer_disarm() stops recording.
+ */
+int csk_kernel_timer_arm(const char* kernel, void** ev_start, void** ev_stop, int n);
+int csk_kernel_timer_count(void);
+void csk_kernel_timer_disarm(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,57 @@
+"""Host-side checks of the C ABI library (no GPU needed): it loads, exports
+every function include/csk.h declares, sizes workspaces and rejects bad
+arguments before touching a device."""
+import ctypes
+import os
+
+import pytest
+
+from util import ROOT, header_functions
+
+LIB = os.path.join(ROOT, "compressed_sparse_kv_amd", "libcsk.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libcsk.so is not built (run compressed_sparse_kv_amd/build.py)")
+    return ctypes.CDLL(LIB)
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    expected = {"csa_compress", "hca_compress", "indexer_topk", "sparse_attn", "dense_compressed_attn",
+                "mxfp4_quantize", "csk_last_error"}
+    assert expected <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"libcsk.so does not export {n}"
+
+
+def test_workspace_sizes(lib):
+    lib.indexer_topk_workspace_size.restype = ctypes.c_size_t
+    lib.sparse_attn_workspace_size.restype = ctypes.c_size_t
+    lib.dense_compressed_attn_workspace_size.restype = ctypes.c_size_t
+    # decode over 262144 entries: scores plus the filtered-selection buffers
+    ws = lib.indexer_topk_workspace_size(4, 1, 64, 128, 262144, 2048, 2)
+    assert ws >= 4 * 262144 * 4 * 5
+    # short rows need only the score buffer
+    assert lib.indexer_topk_workspace_size(1, 256, 2, 32, 64, 8, 0) >= 256 * 64 * 4
+    assert lib.indexer_topk_workspace_size(0, 1, 1, 32, 1, 1, 0) == 0
+    # prefill rows fit one chunk: no split-K partials
+    assert lib.sparse_attn_workspace_size(1, 65536, 64, 576, 512, 2048, 128, 1) == 0
+    # decode splits the candidates: partial (m, l, o) per chunk
+    assert lib.dense_compressed_attn_workspace_size(4, 1, 64, 576, 512, 8192, 128, 128, 1) > 0
+
+
+def test_argument_errors_without_device(lib):
+    lib.csk_last_error.restype = ctypes.c_char_p
+    nul = ctypes.c_void_p(0)
+    rc = lib.mxfp4_quantize(nul, 0, ctypes.c_int64(4), 32, nul, nul, nul)
+    assert rc == -1 and b"null" in lib.csk_last_error()
+    fake = ctypes.c_void_p(16)
+    rc = lib.mxfp4_quantize(fake, 0, ctypes.c_int64(4), 30, fake, fake, nul)
+    assert rc == -1 and b"cols" in lib.csk_last_error()
+    rc = lib.mxfp4_quantize(fake, 7, ctypes.c_int64(4), 32, fake, fake, nul)
+    assert rc == -2
+    lib.csk_abi_version.restype = ctypes.c_int
+    assert lib.csk_abi_version() == 1

@@ -1,0 +1,140 @@
+"""GPU parity: CSA sparse and HCA dense attention with window, sink and
+partial RoPE. bf16 bar: max-abs <= 2e-2 and relative L2 <= 1e-2; fp32 bar:
+max-abs <= 1e-5 (lse checked with the same bars)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from util import check_bf16_attention, check_f32, dev, host
+
+pytestmark = pytest.mark.gpu
+
+csk = pytest.importorskip("compressed_sparse_kv_amd")
+torch = pytest.importorskip("torch")
+
+
+def _inputs(g, B, T, H, D, N, S_w, bf16):
+    cast = synth.to_bf16 if bf16 else (lambda x: x)
+    q = cast(synth.normal(g, (B, T, H, D)))
+    kv_c = cast(synth.normal(g, (B, N, D)))
+    kv_w = cast(synth.normal(g, (B, S_w, D)))
+    return q, kv_c, kv_w
+
+
+def _check(got, ref, bf16, what):
+    if bf16:
+        check_bf16_attention(got, ref, what)
+    else:
+        check_f32(got, ref, 1e-5, what)
+
+
+def _sparse_case(seed, B, T, H, D, dv, N, k, S_w, W, bf16, d_rope, sink=True, decode=False):
+    g = synth.rng(seed)
+    q, kv_c, kv_w = _inputs(g, B, T, H, D, N, S_w, bf16)
+    if decode:
+        q_pos = np.full((B, T), 4 * N - 1, np.int32)
+        w_pos0 = np.full(B, 4 * N - S_w, np.int32)
+    else:
+        q_pos = np.sort(g.integers(0, S_w, (B, T)), axis=1).astype(np.int32)
+        w_pos0 = np.zeros(B, np.int32)
+    idx = np.full((B, T, k), -1, np.int32)
+    for b in range(B):
+        for t in range(T):
+            nsel = int(g.integers(0, k + 1))
+            idx[b, t, :nsel] = np.sort(g.choice(N, nsel, replace=False))
+    idx[0, 0, 0] = N + 5                      # out of range: skipped on both sides
+    sk = synth.normal(g, (H,)) if sink else None
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    out, lse = csk.sparse_attn(dev(q), dev(q_pos), dev(kv_c), dev(idx), dev(kv_w), dev(w_pos0), W,
+                               None if sk is None else dev(sk), dv, d_rope, scale)
+    rout, rlse = oracle.sparse_attn(q, q_pos, kv_c, idx, kv_w, w_pos0, W, sk, dv, d_rope, scale)
+    _check(host(out).reshape(-1, H, dv), rout, bf16, "out")
+    check_f32(host(lse).reshape(-1, H), rlse, 2e-2 if bf16 else 1e-5, "lse")
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_sparse_prefill_small(bf16):
+    _sparse_case(601, B=2, T=19, H=64, D=576, dv=512, N=300, k=40, S_w=300, W=16, bf16=bf16, d_rope=64)
+
+
+def test_sparse_fp32_tiny_shapes():
+    _sparse_case(602, B=1, T=256, H=4, D=64, dv=64, N=64, k=8, S_w=256, W=32, bf16=False, d_rope=32)
+
+
+@pytest.mark.parametrize("H,D,dv", [(64, 576, 512), (16, 128, 128), (32, 576, 576), (64, 64, 64), (8, 96, 80)])
+def test_sparse_decode_split(H, D, dv):
+    # decode rows: long candidate lists split across workgroups and merged
+    _sparse_case(603 + H + D, B=3, T=1, H=H, D=D, dv=dv, N=5000, k=2048, S_w=128, W=128, bf16=True,
+                 d_rope=min(64, D // 2), decode=True)
+
+
+def test_sparse_no_sink_no_window_and_empty():
+    g = synth.rng(604)
+    B, T, H, D, N = 1, 3, 64, 576, 50
+    q, kv_c, _ = _inputs(g, B, T, H, D, N, 1, True)
+    idx = np.full((B, T, 8), -1, np.int32)
+    idx[0, 1, :3] = [4, 9, 7]
+    q_pos = np.array([[10, 20, 30]], np.int32)
+    out, lse = csk.sparse_attn(dev(q), dev(q_pos), dev(kv_c), dev(idx), None, None, 0, None, 512, 64, 0.05)
+    rout, rlse = oracle.sparse_attn(q, q_pos, kv_c, idx, None, None, 0, None, 512, 64, 0.05)
+    check_bf16_attention(host(out).reshape(-1, H, 512), rout, "out")
+    o = host(out)
+    assert np.all(o[0, 0] == 0) and np.all(np.isneginf(host(lse)[0, 0]))   # no candidate, no sink
+
+
+def _dense_case(seed, B, T, H, D, dv, N, m, S_w, W, bf16, d_rope, decode):
+    g = synth.rng(seed)
+    q, kv_c, kv_w = _inputs(g, B, T, H, D, N, S_w, bf16)
+    if decode:
+        q_pos = np.full((B, T), m * N - 1, np.int32)
+        w_pos0 = np.full(B, m * N - S_w, np.int32)
+    else:
+        q_pos = np.arange(T, dtype=np.int32)[None].repeat(B, 0) + g.integers(0, 3, (B, 1)).astype(np.int32)
+        w_pos0 = np.zeros(B, np.int32)
+    ne = np.array([N] + [max(1, N - 7)] * (B - 1), np.int32)
+    sk = synth.normal(g, (H,))
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    out, lse = csk.dense_compressed_attn(dev(q), dev(q_pos), dev(kv_c), dev(ne), m, dev(kv_w), dev(w_pos0), W,
+                                         dev(sk), dv, d_rope, scale)
+    rows = None
+    if B * T > 600:
+        rows = [(b, t) for b in range(B) for t in list(range(0, T, 37)) + [T - 1]]
+    rout, rlse = oracle.dense_attn(q, q_pos, kv_c, ne, m, kv_w, w_pos0, W, sk, dv, d_rope, scale, rows=rows)
+    go, gl = host(out), host(lse)
+    if rows is not None:
+        go = np.stack([go[b, t] for b, t in rows])
+        gl = np.stack([gl[b, t] for b, t in rows])
+    _check(go.reshape(-1, H, dv), rout, bf16, "out")
+    check_f32(gl.reshape(-1, H), rlse, 2e-2 if bf16 else 1e-5, "lse")
+
+
+def test_dense_prefill_hca_shape():
+    # 16 heads x dim 128, m' = 128, window 128: the HCA prefill layer shape
+    _dense_case(701, B=1, T=2048, H=16, D=128, dv=128, N=16, m=128, S_w=2048, W=128, bf16=True, d_rope=64,
+                decode=False)
+
+
+def test_dense_decode_split():
+    _dense_case(702, B=4, T=1, H=64, D=576, dv=512, N=3000, m=128, S_w=128, W=128, bf16=True, d_rope=64,
+                decode=True)
+
+
+def test_dense_fp32():
+    _dense_case(703, B=2, T=70, H=4, D=64, dv=64, N=20, m=4, S_w=70, W=8, bf16=False, d_rope=32, decode=False)
+
+
+def test_sparse_all_visible_equals_dense():
+    # CSA with k >= #visible selects every visible entry: same as HCA attention
+    g = synth.rng(704)
+    B, T, H, D, N, m = 1, 1, 64, 576, 700, 4
+    q, kv_c, kv_w = _inputs(g, B, T, H, D, N, 128, True)
+    q_pos = np.array([[4 * N - 1]], np.int32)
+    w_pos0 = np.array([4 * N - 128], np.int32)
+    idx = np.arange(N, dtype=np.int32)[None, None]
+    sk = np.zeros(H, np.float32)
+    a, al = csk.sparse_attn(dev(q), dev(q_pos), dev(kv_c), dev(idx), dev(kv_w), dev(w_pos0), 128, dev(sk),
+                            512, 64, 1 / 24)
+    d, dl = csk.dense_compressed_attn(dev(q), dev(q_pos), dev(kv_c), dev(np.array([N], np.int32)), m, dev(kv_w),
+                                      dev(w_pos0), 128, dev(sk), 512, 64, 1 / 24)
+    check_bf16_attention(host(a), host(d), "sparse vs dense")

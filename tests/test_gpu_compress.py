@@ -1,0 +1,132 @@
+"""GPU parity: compression (CSA / HCA), partial RoPE, MXFP4 quantisation.
+
+The oracle computes in fp64 and rounds once; the GPU computes in fp32.
+fp32 outputs: max-abs <= 1e-5. bf16 outputs: within one bf16 ulp of the
+oracle's value plus the fp32 bar (the fp32 pooling and rotation error is
+about 1e-7 absolute, more than one bf16 ulp of an output near zero).
+MXFP4 quantisation of identical fp32 inputs: bit-exact. MXFP4 output of the
+compressor: the codes equal the oracle encoder applied to the GPU's own fp32
+pooled values (the decision is taken on the same fp32 value on both sides),
+and those fp32 values meet the fp32 bar.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from util import bf16_ulp, check_f32, dev, host
+
+
+def _bf16_ok(got, ref):
+    return np.all(np.abs(got - ref) <= bf16_ulp(ref) + 1e-5)
+
+pytestmark = pytest.mark.gpu
+
+csk = pytest.importorskip("compressed_sparse_kv_amd")
+torch = pytest.importorskip("torch")
+
+
+def _series(g, B, S, D, bf16):
+    xs = [synth.normal(g, (B, S, D)) for _ in range(4)]
+    return [synth.to_bf16(x) for x in xs] if bf16 else xs
+
+
+@pytest.mark.parametrize("rows,cols,seed", [(1, 32, 1), (37, 128, 2), (1000, 576, 3), (5, 64, 4)])
+def test_mxfp4_quantize_bit_exact(rows, cols, seed):
+    g = synth.rng(100 + seed)
+    x = synth.normal(g, (rows, cols)) * np.float32(2.0) ** g.integers(-20, 20, (rows, 1)).astype(np.float32)
+    x[0, :32] = 0.0                                     # all-zero tile
+    if cols >= 64:
+        x[0, 32:64] = np.float32(1.5) * np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5, 6] * 4, np.float32)
+    codes, scales = csk.mxfp4_quantize(dev(x))
+    rc, rs = oracle.mxfp4_encode(x)
+    assert np.array_equal(host(codes), rc) and np.array_equal(host(scales), rs)
+    xb = synth.to_bf16(x)                               # bf16 input path
+    codes, scales = csk.mxfp4_quantize(dev(xb))
+    rc, rs = oracle.mxfp4_encode(oracle.bf16_to_f32(xb))
+    assert np.array_equal(host(codes), rc) and np.array_equal(host(scales), rs)
+
+
+@pytest.mark.parametrize("bf16_in", [False, True])
+@pytest.mark.parametrize("B,S,D,m,d_rope", [(1, 64, 64, 4, 32), (3, 203, 576, 4, 64), (2, 40, 128, 8, 0)])
+def test_csa_compress(bf16_in, B, S, D, m, d_rope):
+    g = synth.rng(200 + S + D)
+    ca, za, cb, zb = _series(g, B, S, D, bf16_in)
+    ba, bb = synth.normal(g, (m, D), 0.1), synth.normal(g, (m, D), 0.1)
+    ref = oracle.csa_compress(ca, za, cb, zb, ba, bb, m, d_rope=d_rope)
+    args = [dev(x) for x in (ca, za, cb, zb, ba, bb)]
+    out32 = host(csk.csa_compress(*args, m, d_rope=d_rope, out_dtype=csk.CSK_F32))
+    assert out32.shape == ref.shape
+    check_f32(out32, ref, 1e-5, "csa fp32 out")
+    outb = host(csk.csa_compress(*args, m, d_rope=d_rope, out_dtype=csk.CSK_BF16))
+    assert _bf16_ok(outb, ref), np.abs(outb - ref).max()
+    if D % 32 == 0 and d_rope == 0:
+        codes, scales = csk.csa_compress(*args, m, out_dtype=csk.CSK_MXFP4)
+        rc, rs = oracle.mxfp4_encode(out32)
+        assert np.array_equal(host(codes), rc) and np.array_equal(host(scales), rs)
+
+
+@pytest.mark.parametrize("bf16_in", [False, True])
+@pytest.mark.parametrize("B,S,D,m,d_rope", [(1, 512, 128, 128, 64), (2, 300, 576, 128, 64), (1, 64, 64, 1, 32)])
+def test_hca_compress(bf16_in, B, S, D, m, d_rope):
+    g = synth.rng(300 + S + D + m)
+    c, z, _, _ = _series(g, B, S, D, bf16_in)
+    bias = synth.normal(g, (m, D), 0.1)
+    ref = oracle.hca_compress(c, z, bias, m, d_rope=d_rope)
+    out32 = host(csk.hca_compress(dev(c), dev(z), dev(bias), m, d_rope=d_rope, out_dtype=csk.CSK_F32))
+    check_f32(out32, ref, 1e-5, "hca fp32 out")
+    outb = host(csk.hca_compress(dev(c), dev(z), dev(bias), m, d_rope=d_rope, out_dtype=csk.CSK_BF16))
+    assert _bf16_ok(outb, ref)
+
+
+def test_entry_positions_and_constant_pooling():
+    g = synth.rng(401)
+    B, S, D, m = 2, 64, 128, 4
+    ca, za, cb, zb = _series(g, B, S, D, True)
+    ba, bb = synth.normal(g, (m, D), 0.1), synth.normal(g, (m, D), 0.1)
+    pos = g.integers(0, 1 << 20, (B, S // m)).astype(np.int32)
+    ref = oracle.csa_compress(ca, za, cb, zb, ba, bb, m, d_rope=64, entry_pos=pos)
+    out = host(csk.csa_compress(*[dev(x) for x in (ca, za, cb, zb, ba, bb)], m, d_rope=64,
+                                entry_pos=dev(pos), out_dtype=csk.CSK_F32))
+    check_f32(out, ref, 1e-5, "entry_pos")
+    # a constant source pools to itself (pooling weights sum to 1)
+    v = synth.to_bf16(np.full((B, S, D), 0.8125, np.float32))
+    out = host(csk.csa_compress(*[dev(x) for x in (v, za, v, zb, ba, bb)], m, out_dtype=csk.CSK_BF16))
+    assert np.all(out == np.float32(0.8125))
+
+
+def test_incremental_equals_one_shot():
+    # Appending entries with entry0 > 0 (previous block read from the rows
+    # before the first a-block) reproduces one-shot compression, written in
+    # place into the full cache through the batch strides.
+    g = synth.rng(402)
+    B, S, D, m = 3, 96, 576, 4
+    ca, za, cb, zb = _series(g, B, S, D, True)
+    ba, bb = synth.normal(g, (m, D), 0.1), synth.normal(g, (m, D), 0.1)
+    t = [dev(x) for x in (ca, za, cb, zb, ba, bb)]
+    full = csk.csa_compress(*t, m, d_rope=64)
+    cache = torch.zeros_like(full)
+    csk.csa_compress(*t, m, d_rope=64, out=cache, S=40, src_bstride=S, dst_bstride=S // m)  # entries 0..9
+    off = 40
+    tail = [x[:, off:] for x in t[:4]]
+    csk.csa_compress(*tail, t[4], t[5], m, d_rope=64, entry0=off // m, src_bstride=S,
+                     out=cache[:, off // m:], dst_bstride=S // m, S=S - off)  # entries 10..23
+    assert torch.equal(cache.view(torch.int16), full.view(torch.int16))
+    # single newest entry (the decode-time append)
+    last = torch.zeros_like(full[:, -1:])
+    csk.csa_compress(*[x[:, S - m:] for x in t[:4]], t[4], t[5], m, d_rope=64, entry0=S // m - 1,
+                     src_bstride=S, out=last, S=m)
+    assert torch.equal(last.view(torch.int16), full[:, -1:].view(torch.int16))
+
+
+def test_ragged_and_empty():
+    g = synth.rng(403)
+    ca, za, cb, zb = _series(g, 1, 10, 64, False)
+    ba, bb = synth.normal(g, (4, 64), 0.1), synth.normal(g, (4, 64), 0.1)
+    out = csk.csa_compress(*[dev(x) for x in (ca, za, cb, zb, ba, bb)], 4, out_dtype=csk.CSK_F32)
+    assert out.shape == (1, 2, 64)
+    check_f32(host(out), oracle.csa_compress(ca, za, cb, zb, ba, bb, 4), 1e-5)
+    out = csk.csa_compress(*[dev(x[:, :3]) for x in (ca, za, cb, zb)], dev(ba), dev(bb), 4)
+    assert out.shape == (1, 0, 64)
+    with pytest.raises(csk.CskError):
+        csk.csa_compress(*[dev(x) for x in (ca, za, cb, zb, ba, bb)], 4, d_rope=3)
