@@ -9,10 +9,11 @@ MXFP4 indexer 64x128, top-k 2048, window 128, sink). One step is one pass of
 the whole hot path for one new token per sequence:
   1. csa_compress  - the newest CSA entry (8 source tokens, two series)
   2. csa_compress  - its indexer key, MXFP4 output
-  3. hca_compress  - the newest HCA entry (128 source tokens)
-  4. mxfp4_quantize - the indexer queries
-  5. indexer_topk  - scores over all 262144 entries, top-2048 per row
-  6. sparse_attn   - CSA attention over selected entries + window + sink
+  3. mxfp4_quantize - the indexer queries
+  4. indexer_topk  - scores over all 262144 entries, top-2048 per row
+  5. sparse_attn   - CSA attention over selected entries + window + sink
+and, on a second stream (it does not depend on the CSA chain),
+  6. hca_compress  - the newest HCA entry (128 source tokens)
   7. dense_compressed_attn - HCA attention over all 8192 entries + window + sink
 Each step is captured once into a HIP graph (torch.cuda.CUDAGraph) and the
 timed loop replays them. Four copies of the layer-pair state rotate between
@@ -116,6 +117,7 @@ class DecodeWorkload:
             ws_d = csk.dense_compressed_attn_workspace_size(B, 1, H, self.D, dv, self.Nh, 128, self.W,
                                                             csk.CSK_BF16)
             self.ws_d = torch.empty(max(ws_d, 1), dtype=torch.uint8, device=dev)
+        self.side = torch.cuda.Stream() if self.pair else None  # default priority
         torch.cuda.synchronize()
         if not keep_host:
             self.d = None
@@ -124,8 +126,20 @@ class DecodeWorkload:
 
     # ------------------------------------------------------------- one step
     def step(self, c=0):
-        csk, x, st = self.csk, self.x, self.copies[c % len(self.copies)]
+        """One decode step. The HCA branch (its compression and attention)
+        does not depend on the CSA chain and runs on a second stream."""
+        torch, csk, x, st = self.torch, self.csk, self.x, self.copies[c % len(self.copies)]
         B, N, D, dI = self.B, self.N, self.D, self.dI
+        main = torch.cuda.current_stream()
+        if self.pair:
+            self.side.wait_stream(main)
+            with torch.cuda.stream(self.side):
+                Nh = self.Nh
+                csk.hca_compress(x["src_c"], x["src_z"], x["bias_h"], 128, d_rope=64, entry0=Nh - 1,
+                                 out=st["kv_h"][:, Nh - 1:], dst_bstride=Nh)
+                csk.dense_compressed_attn(x["q_h"], x["q_pos"], st["kv_h"], x["n_entries_h"], 128, st["kv_w_h"],
+                                          x["w_pos0"], self.W, x["sink_h"], self.dv, 64, self.scale, out=self.out_h,
+                                          lse=self.lse_h, workspace=self.ws_d)
         # 1-2: the newest CSA entry N-1 and its indexer key (a-block = source
         # rows 4..7, previous block = rows 0..3 of the 8-token window)
         csk.csa_compress(x["src_ca"][:, 4:], x["src_za"][:, 4:], x["src_cb"][:, 4:], x["src_zb"][:, 4:],
@@ -134,10 +148,6 @@ class DecodeWorkload:
         csk.csa_compress(x["src_ia"][:, 4:], x["src_iza"][:, 4:], x["src_ib"][:, 4:], x["src_izb"][:, 4:],
                          x["ibias_a"], x["ibias_b"], 4, entry0=N - 1, src_bstride=8, out_dtype=csk.CSK_MXFP4,
                          out=st["kc"][:, N - 1:], out_scale=st["ks"][:, N - 1:], dst_bstride=N, S=4, B=B)
-        if self.pair:
-            Nh = self.Nh
-            csk.hca_compress(x["src_c"], x["src_z"], x["bias_h"], 128, d_rope=64, entry0=Nh - 1,
-                             out=st["kv_h"][:, Nh - 1:], dst_bstride=Nh)
         # 4-5: indexer queries to MXFP4, scores + top-k
         csk.mxfp4_quantize(x["qI"], self.qc, self.qs)
         csk.indexer_topk(self.qc, x["w"], st["kc"], x["q_pos"], x["n_entries"], 4, self.k, q_scale=self.qs,
@@ -146,12 +156,8 @@ class DecodeWorkload:
         csk.sparse_attn(x["q"], x["q_pos"], st["kv_c"], self.idx, st["kv_w"], x["w_pos0"], self.W, x["sink"],
                         self.dv, 64, self.scale, out=self.out, lse=self.lse,
                         workspace=self.ws_s)
-        # 7: HCA attention
         if self.pair:
-            csk.dense_compressed_attn(x["q_h"], x["q_pos"], st["kv_h"], x["n_entries_h"], 128, st["kv_w_h"],
-                                      x["w_pos0"], self.W, x["sink_h"], self.dv, 64,
-                                      self.scale, out=self.out_h,
-                                      lse=self.lse_h, workspace=self.ws_d)
+            main.wait_stream(self.side)
 
     def kernels(self):
         names = ["csa_compress", "mxfp4_quantize", "indexer_scores_fp4", "topk_threshold", "topk_filter",

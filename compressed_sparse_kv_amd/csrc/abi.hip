@@ -1,4 +1,5 @@
 // abi.hip - error state, version and the kernel-timer measurement hook.
+#include <math.h>
 #include <string.h>
 
 #include <mutex>
@@ -15,6 +16,11 @@ int fail(int code, const std::string& msg) {
   return code;
 }
 void clear_error() { g_err.clear(); }
+
+void fill_rope_table(RopeTable* t, int d_rope, double base) {
+  for (int j = 0; j < MAX_ROPE_PAIRS; ++j)
+    t->theta[j] = (2 * j < d_rope) ? pow(base, -2.0 * (double)j / (double)d_rope) : 0.0;
+}
 
 // One armed timer for the process: the named kernel's next n launches get
 // an event pair each.

@@ -32,6 +32,30 @@ namespace csk {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+// LDS transpose read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// source lane s supplies an 8-byte address (4 consecutive bf16 e[s][0..3]);
+// lane i receives e[4k + i/4][i%4] for k = 0..3.
+__device__ __forceinline__ v4s lds_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(lds_u16*)(uint16_t*)p);
+}
+
+// V^T fragment of the O^T MFMA for value rows 16*dt + col: the lane's 8
+// candidates {4g..4g+3, 16+4g..16+4g+3}, fetched with two transpose reads.
+// p0 must point at dims 16*dt + 4*(col%4) .. +3 of candidate 4*g + col/4 and
+// p1 at the same dims of candidate 16 + 4*g + col/4.
+__device__ __forceinline__ v8bf vt_fragment(const uint16_t* p0, const uint16_t* p1) {
+  // whole-vector bit casts only: element-wise short -> bf16 inserts of the
+  // transpose-read result are lowered wrongly (only the low half of each
+  // dword survives)
+  const v4s r0 = lds_tr16(p0), r1 = lds_tr16(p1);
+  const v8s both = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(v8bf, both);
+}
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -49,7 +73,7 @@ struct AttnArgs {
   int Lc;                 // compressed slots per row
   int chunk, nch;         // candidates per chunk, chunks per row
   float scale;
-  double base;
+  RopeTable rope;
   bool dense;
   void* out;              // [R, H, dv]
   float* lse;             // [R, H] or null
@@ -131,21 +155,54 @@ __device__ __forceinline__ void finish_row(float m, float l, const float* sink, 
 }
 
 // ------------------------------------------------------------- bf16 MFMA
-template <int D, int DV>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
+constexpr int MAX_CHUNK = 4096;   // candidates per workgroup (row codes kept in LDS)
+
+// Row code of candidate slot j: >= 0 compressed entry, <= -2 window row
+// (-2 - row), -1 empty.
+__device__ __forceinline__ int slot_code(const AttnArgs& a, const RowInfo& ri, int r, int j) {
+  if (j < a.Lc) {
+    if (a.dense) return j < ri.nvis ? j : -1;
+    const int e = a.idx[(int64_t)r * a.k + j];
+    return (e < 0 || e >= a.Nmax) ? -1 : e;
+  }
+  const int wrow = ri.wr0 + (j - a.Lc);
+  return wrow < ri.wr1 ? -2 - wrow : -1;
+}
+
+template <int D, int DV, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnArgs a) {
   constexpr int KS = D / 32;        // MFMA K-steps over the key dim
   constexpr int DT = DV / 16;       // 16-row tiles of the value dim
   constexpr int LD = D + 8;         // LDS row stride in bf16 (16 bytes of padding)
+  constexpr int CPR = D / 8;        // 16-byte chunks per KV row
+  constexpr int NT = 64 * NW;
+  constexpr int PT = (32 * CPR + NT - 1) / NT;  // chunks per thread per tile
   __shared__ __align__(16) uint16_t tile[32 * LD];
+  __shared__ int codes[MAX_CHUNK];
 
   const int r = blockIdx.x;
   const int chunk_id = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int nthr = blockDim.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
   const int h = wave * 16 + col;
   const RowInfo ri = row_info(a, r);
+  const uint16_t* kvc = reinterpret_cast<const uint16_t*>(a.kv_c) + (int64_t)ri.b * a.Nmax * D;
+  const uint16_t* kvw = reinterpret_cast<const uint16_t*>(a.kv_w) + (int64_t)ri.b * a.S_w * D;
+
+  const int total = a.Lc + a.W;
+  const int c0 = chunk_id * a.chunk;
+  const int nc = min(a.chunk, total - c0);
+  for (int j = tid; j < nc; j += NT) codes[j] = slot_code(a, ri, r, c0 + j);
+  // cos/sin of the query position, one rotated pair per thread
+  __shared__ float2 rtab[MAX_ROPE_PAIRS];
+  if (tid < a.d_rope / 2) {
+    float cs, sn;
+    rope_cs((double)ri.p, a.rope.theta[tid], &cs, &sn);
+    rtab[tid] = make_float2(cs, sn);
+  }
+  __syncthreads();
 
   // rotated query fragments (B operand of S^T): dims 32*ks + 8*g .. +7
   v8bf qf[KS];
@@ -168,8 +225,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int c = d0 + 2 * i;
           if (c >= rope0) {
-            float cs, sn;
-            rope_cs((double)ri.p, (c - rope0) / 2, a.d_rope, a.base, &cs, &sn);
+            const float2 csn = rtab[(c - rope0) / 2];
+            const float cs = csn.x, sn = csn.y;
             const float x0 = x[2 * i], x1 = x[2 * i + 1];
             x[2 * i] = x0 * cs - x1 * sn;
             x[2 * i + 1] = x0 * sn + x1 * cs;
@@ -180,6 +237,29 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
       for (int i = 0; i < 8; ++i) qf[ks][i] = __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_bits(x[i]));
     }
   }
+  __syncthreads();  // codes visible
+
+  // register prefetch of one tile: each thread owns fixed 16-byte chunks
+  // (row id/CPR, column id%CPR) of every tile
+  uint4 pref[PT];
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+      const int id = tid + q * NT;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (id < 32 * CPR) {
+        const int j = t0 + id / CPR;
+        if (j < nc) {
+          const int code = codes[j];
+          if (code != -1) {
+            const uint16_t* src = code >= 0 ? kvc + (int64_t)code * D : kvw + (int64_t)(-2 - code) * D;
+            v = *reinterpret_cast<const uint4*>(src + 8 * (id % CPR));
+          }
+        }
+      }
+      pref[q] = v;
+    }
+  };
 
   v4f acc[DT];
 #pragma unroll
@@ -187,29 +267,16 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_part = 0.f;
   const float sl2 = a.scale * LOG2E;
 
-  const int c0 = chunk_id * a.chunk;
-  int c1 = c0 + a.chunk;
-  const int total = a.Lc + a.W;
-  c1 = c1 < total ? c1 : total;
-
-  for (int t0 = c0; t0 < c1; t0 += 32) {
-    // gather 32 candidate rows into LDS (invalid rows are zero)
-    __syncthreads();
-    constexpr int CPR = D / 8;  // 16-byte chunks per row
-    for (int id = threadIdx.x; id < 32 * CPR; id += nthr) {
-      const int row = id / CPR, cc = id % CPR;
-      const int j = t0 + row;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (j < c1) {
-        bool win;
-        const int64_t off = slot_row(a, ri, r, j, &win);
-        if (off >= 0) {
-          const uint16_t* src = reinterpret_cast<const uint16_t*>(win ? a.kv_w : a.kv_c) + off;
-          v = *reinterpret_cast<const uint4*>(src + 8 * cc);
-        }
-      }
-      *reinterpret_cast<uint4*>(&tile[row * LD + 8 * cc]) = v;
+  if (nc > 0) load_tile(0);
+  for (int t0 = 0; t0 < nc; t0 += 32) {
+    __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+      const int id = tid + q * NT;
+      if (id < 32 * CPR)
+        *reinterpret_cast<uint4*>(&tile[(id / CPR) * LD + 8 * (id % CPR)]) = pref[q];
     }
+    if (t0 + 32 < nc) load_tile(t0 + 32);  // next tile's loads overlap this tile's math
     __syncthreads();
 
     // S^T for two 16-candidate tiles
@@ -232,8 +299,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = t0 + ct * 16 + 4 * g + i;
-        bool win;
-        const bool ok = j < c1 && slot_row(a, ri, r, j, &win) >= 0;
+        const bool ok = j < nc && codes[j] != -1;
         const float v = ok ? s[ct][i] * sl2 : -INFINITY;
         p[ct * 4 + i] = v;
         tmax = fmaxf(tmax, v);
@@ -254,23 +320,273 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) pf[i] = __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_bits(p[i]));
 
-    // O^T += V^T P^T; V^T fragment: dv row 16*dt+col, candidates of slot j
-    const int cand0 = 4 * g, cand1 = 16 + 4 * g;
+    // O^T += V^T P^T (rescale only when some head's running max moved)
+    if (__ballot(alpha != 1.0f) != 0ull) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+    }
+    const uint16_t* vbase = &tile[(4 * g + (col >> 2)) * LD + 4 * (col & 3)];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const int dvr = 16 * dt + col;
-      v8bf vf;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vf[i] = __builtin_bit_cast(__bf16, tile[(cand0 + i) * LD + dvr]);
-        vf[4 + i] = __builtin_bit_cast(__bf16, tile[(cand1 + i) * LD + dvr]);
-      }
-      acc[dt] *= alpha;
+      const v8bf vf = vt_fragment(vbase + 16 * dt, vbase + 16 * LD + 16 * dt);
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc[dt], 0, 0, 0);
     }
   }
 
   // per-head totals across the four lane groups
+  float l_tot = l_part;
+  l_tot += __shfl_xor(l_tot, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+
+  if (a.nch == 1) {
+    float M, inv_z, lse;
+    finish_row(m_run, l_tot, a.sink, h, &M, &inv_z, &lse);
+    const float f = (m_run == -INFINITY) ? 0.f : exp2f(m_run - M) * inv_z;
+    uint16_t* ob = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)r * a.H + h) * DV;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d0 = 16 * dt + 4 * g;
+      const uint32_t lo = f32_to_bf16_bits(acc[dt][0] * f) | (f32_to_bf16_bits(acc[dt][1] * f) << 16);
+      const uint32_t hi = f32_to_bf16_bits(acc[dt][2] * f) | (f32_to_bf16_bits(acc[dt][3] * f) << 16);
+      *reinterpret_cast<uint2*>(ob + d0) = make_uint2(lo, hi);
+    }
+    if (a.lse && g == 0) a.lse[(int64_t)r * a.H + h] = lse;
+  } else {
+    float* po = a.part_o + (((int64_t)r * a.nch + chunk_id) * a.H + h) * DV;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) =
+          make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+    if (g == 0) {
+      float* pm = a.part_ml + (((int64_t)r * a.nch + chunk_id) * a.H + h) * 2;
+      pm[0] = m_run;
+      pm[1] = l_tot;
+    }
+  }
+}
+
+// ------------------------------------------------------- bf16 MFMA, LDS DMA
+// Same math as attn_bf16_kernel, but the candidate rows are copied straight
+// from HBM into LDS with global_load_lds_dwordx4 (no register staging),
+// three tiles deep: while tile t is computed, tiles t+1 and t+2 are in
+// flight (tile t+2 is issued right after tile t's reads). Each wave-level
+// DMA instruction fills one contiguous 1 KB block;
+// a stage holds 32 rows in column-major 16-byte units (unit = chunk*32 +
+// row), so block b carries chunks 2b and 2b+1 of all 32 rows. Waits on the
+// DMAs are explicit (vmcnt), and raw s_barrier is fenced against compiler
+// code motion, because a __syncthreads() would wait for every DMA in flight.
+#define CSK_VMCNT_LGKM0(n) ((((n) & 0xF) | ((((n) >> 4) & 0x3) << 14)) | (0x7 << 4))
+
+template <int D, int DV, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_bf16_dma_kernel(AttnArgs a) {
+  constexpr int KS = D / 32;
+  constexpr int DT = DV / 16;
+  constexpr int CPR = D / 8;            // 16-byte chunks per KV row
+  constexpr int NT = 64 * NW;
+  constexpr int BLK = CPR / 2;          // 1 KB DMA blocks per 32-row tile
+  constexpr int BPW = BLK / NW;         // DMA instructions per wave per tile
+  constexpr int STAGE = 32 * CPR;       // 16-byte units per stage
+  static_assert(BLK % NW == 0, "DMA blocks must split evenly over the waves");
+  // three distinct arrays (not one indexed array): the compiler can then
+  // tell a stage being read from the stages the DMAs are filling
+  __shared__ __align__(16) uint4 stg0[STAGE];
+  __shared__ __align__(16) uint4 stg1[STAGE];
+  __shared__ __align__(16) uint4 stg2[STAGE];
+  __shared__ int codes[MAX_CHUNK];
+
+  const int r = blockIdx.x;
+  const int chunk_id = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int h = wave * 16 + col;
+  const RowInfo ri = row_info(a, r);
+  const uint16_t* kvc = reinterpret_cast<const uint16_t*>(a.kv_c) + (int64_t)ri.b * a.Nmax * D;
+  const uint16_t* kvw = reinterpret_cast<const uint16_t*>(a.kv_w) + (int64_t)ri.b * a.S_w * D;
+
+  const int total = a.Lc + a.W;
+  const int c0 = chunk_id * a.chunk;
+  const int nc = min(a.chunk, total - c0);
+  const int ntiles = (nc + 31) / 32;
+  for (int j = tid; j < nc; j += NT) codes[j] = slot_code(a, ri, r, c0 + j);
+  // an ordinary store into the staging buffer: the DMA intrinsic is not seen
+  // as a writer of it, and without one the reads below could be folded away
+  stg0[tid] = make_uint4(0u, 0u, 0u, 0u);
+  stg1[tid] = make_uint4(0u, 0u, 0u, 0u);
+  stg2[tid] = make_uint4(0u, 0u, 0u, 0u);
+  __shared__ float2 rtab[MAX_ROPE_PAIRS];
+  if (tid < a.d_rope / 2) {
+    float cs, sn;
+    rope_cs((double)ri.p, a.rope.theta[tid], &cs, &sn);
+    rtab[tid] = make_float2(cs, sn);
+  }
+  __syncthreads();
+
+  v8bf qf[KS];
+  {
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + h) * D;
+    const int rope0 = D - a.d_rope;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int d0 = 32 * ks + 8 * g;
+      const uint4 raw = *reinterpret_cast<const uint4*>(qrow + d0);
+      float x[8];
+      const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16_bits_to_f32(wv[i] & 0xffffu);
+        x[2 * i + 1] = bf16_bits_to_f32(wv[i] >> 16);
+      }
+      if (d0 + 8 > rope0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = d0 + 2 * i;
+          if (c >= rope0) {
+            const float2 csn = rtab[(c - rope0) / 2];
+            const float cs = csn.x, sn = csn.y;
+            const float x0 = x[2 * i], x1 = x[2 * i + 1];
+            x[2 * i] = x0 * cs - x1 * sn;
+            x[2 * i + 1] = x0 * sn + x1 * cs;
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qf[ks][i] = __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_bits(x[i]));
+    }
+  }
+  __syncthreads();  // codes and the staging store are complete; no DMA issued yet
+
+  // DMA of tile t into stage s: lane i of block b loads chunk 2b + i/32 of
+  // row i%32. Empty slots read row 0 of the cache (finite data, weight 0).
+  auto issue = [&](int t, uint4* dst) {
+    const int row = lane & 31;
+    const int j = t * 32 + row;
+    const int code = j < nc ? codes[j] : -1;
+    const uint16_t* src = code >= 0 ? kvc + (int64_t)code * D : (code <= -2 ? kvw + (int64_t)(-2 - code) * D : kvc);
+#pragma unroll
+    for (int q = 0; q < BPW; ++q) {
+      const int blk = wave + NW * q;
+      const int cc = 2 * blk + (lane >> 5);
+      __builtin_amdgcn_global_load_lds(src + 8 * cc, dst + blk * 64, 16, 0, 0);
+    }
+  };
+
+  v4f acc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
+  const float sl2 = a.scale * LOG2E;
+
+  // compute of one tile from a staged buffer
+  auto process = [&](const uint4* sb, int t) {
+    const uint16_t* sb16 = reinterpret_cast<const uint16_t*>(sb);
+    v4f sc[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      sc[ct] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const v8bf kfrag = *reinterpret_cast<const v8bf*>(&sb[(4 * ks + g) * 32 + ct * 16 + col]);
+        sc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qf[ks], sc[ct], 0, 0, 0);
+      }
+    }
+    float p[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = t * 32 + ct * 16 + 4 * g + i;
+        const bool ok = j < nc && codes[j] != -1;
+        const float v = ok ? sc[ct][i] * sl2 : -INFINITY;
+        p[ct * 4 + i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = (m_new == -INFINITY) ? 0.f : exp2f(p[i] - m_new);
+      psum += p[i];
+    }
+    l_part = l_part * alpha + psum;
+    m_run = m_new;
+    v8bf pf;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pf[i] = __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_bits(p[i]));
+
+    // rescale only when some head's running max moved
+    if (__ballot(alpha != 1.0f) != 0ull) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+    }
+    // stage units are 16-byte (8-dim) chunks, unit = chunk*32 + candidate
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int dvb = 16 * dt + 4 * (col & 3);
+      const uint16_t* p0 = sb16 + ((dvb >> 3) * 32 + 4 * g + (col >> 2)) * 8 + (dvb & 7);
+      const v8bf vf = vt_fragment(p0, p0 + 16 * 8);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc[dt], 0, 0, 0);
+    }
+  };
+  // wait until this wave's DMAs for the tile about to be read are done (at
+  // most `pending` newer ones may remain), then barrier so every wave's part
+  // has landed; the fences keep the compiler from moving memory accesses
+  // across the raw barrier
+#define CSK_STAGE_SYNC(pending)                                            \
+  do {                                                                     \
+    asm volatile("" ::: "memory");                                         \
+    if (pending) __builtin_amdgcn_s_waitcnt(CSK_VMCNT_LGKM0(BPW));         \
+    else __builtin_amdgcn_s_waitcnt(CSK_VMCNT_LGKM0(0));                   \
+    __builtin_amdgcn_s_barrier();                                          \
+    asm volatile("" ::: "memory");                                         \
+  } while (0)
+  // tile t+2 is issued right after tile t's reads: its stage was last read
+  // in tile t-1, which every wave finished before tile t's barrier
+#define CSK_STAGE_ISSUE(tt, dst)              \
+  do {                                        \
+    asm volatile("" ::: "memory");            \
+    if ((tt) < ntiles) issue((tt), (dst));    \
+  } while (0)
+
+  // the first two tiles go through registers and ordinary LDS stores, so
+  // that each stage has a single DMA issue site in the loop (the compiler's
+  // DMA tracking then keeps the stages apart and adds no waits of its own)
+  auto fill = [&](int t, uint4* dst) {
+    const int row = lane & 31;
+    const int j = t * 32 + row;
+    const int code = j < nc ? codes[j] : -1;
+    const uint16_t* src = code >= 0 ? kvc + (int64_t)code * D : (code <= -2 ? kvw + (int64_t)(-2 - code) * D : kvc);
+#pragma unroll
+    for (int q = 0; q < BPW; ++q) {
+      const int blk = wave + NW * q;
+      dst[blk * 64 + lane] = *reinterpret_cast<const uint4*>(src + 8 * (2 * blk + (lane >> 5)));
+    }
+  };
+  if (ntiles > 0) fill(0, stg0);
+  if (ntiles > 1) fill(1, stg1);
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 3) {
+    CSK_STAGE_SYNC(t + 1 < ntiles);
+    process(stg0, t);
+    CSK_STAGE_ISSUE(t + 2, stg2);
+    if (t + 1 >= ntiles) break;
+    CSK_STAGE_SYNC(t + 2 < ntiles);
+    process(stg1, t + 1);
+    CSK_STAGE_ISSUE(t + 3, stg0);
+    if (t + 2 >= ntiles) break;
+    CSK_STAGE_SYNC(t + 3 < ntiles);
+    process(stg2, t + 2);
+    CSK_STAGE_ISSUE(t + 4, stg1);
+  }
+#undef CSK_STAGE_SYNC
+#undef CSK_STAGE_ISSUE
+  asm volatile("" ::: "memory");
+
   float l_tot = l_part;
   l_tot += __shfl_xor(l_tot, 16);
   l_tot += __shfl_xor(l_tot, 32);
@@ -332,7 +648,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
     float x0 = ld(q, c), x1 = ld(q, c + 1);
     if (c >= rope0) {
       float cs, sn;
-      rope_cs((double)ri.p, (c - rope0) / 2, a.d_rope, a.base, &cs, &sn);
+      rope_cs((double)ri.p, a.rope.theta[(c - rope0) / 2], &cs, &sn);
       const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
       x0 = y0;
       x1 = y1;
@@ -417,33 +733,61 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- merge
 // One workgroup per (row, head): log-sum-exp combination of the chunks'
-// partial (m, l, o) with the sink.
+// partial (m, l, o) with the sink. Chunk weights 2^(m_c - M) are formed once
+// in LDS; the value loop then issues independent loads over the chunks.
+constexpr int MERGE_MAX_CH = 2048;
+
 template <typename T>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  __shared__ float wts[MERGE_MAX_CH];
+  __shared__ float red[8];
+  __shared__ float fin[2];
   const int r = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* ml = a.part_ml + ((int64_t)r * a.nch * a.H + h) * 2;
+  const int64_t cstride = (int64_t)a.H * 2;
   float m = -INFINITY;
-  for (int c = 0; c < a.nch; ++c)
-    m = fmaxf(m, a.part_ml[(((int64_t)r * a.nch + c) * a.H + h) * 2]);
+  for (int c = tid; c < a.nch; c += 256) m = fmaxf(m, ml[c * cstride]);
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   float l = 0.f;
-  for (int c = 0; c < a.nch; ++c) {
-    const float* pm = a.part_ml + (((int64_t)r * a.nch + c) * a.H + h) * 2;
-    if (pm[0] != -INFINITY) l += pm[1] * exp2f(pm[0] - m);
+  for (int c = tid; c < a.nch; c += 256) {
+    const float mc = ml[c * cstride];
+    const float w = (mc == -INFINITY) ? 0.f : exp2f(mc - m);
+    wts[c] = w;
+    l += w * ml[c * cstride + 1];
   }
-  float M, inv_z, lse;
-  finish_row(m, l, a.sink, h, &M, &inv_z, &lse);
-  for (int d = threadIdx.x; d < a.dv; d += blockDim.x) {
-    float o = 0.f;
-    for (int c = 0; c < a.nch; ++c) {
-      const float mc = a.part_ml[(((int64_t)r * a.nch + c) * a.H + h) * 2];
-      if (mc == -INFINITY) continue;
-      o += a.part_o[(((int64_t)r * a.nch + c) * a.H + h) * a.dv + d] * exp2f(mc - M);
+  for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+  if (lane == 0) red[4 + wave] = l;
+  __syncthreads();
+  if (tid == 0) {
+    float M, inv_z, lse;
+    finish_row(m, red[4] + red[5] + red[6] + red[7], a.sink, h, &M, &inv_z, &lse);
+    fin[0] = (m == -INFINITY) ? 0.f : exp2f(m - M) * inv_z;
+    fin[1] = lse;
+  }
+  __syncthreads();
+  const float f = fin[0];
+  const float* po = a.part_o + ((int64_t)r * a.nch * a.H + h) * a.dv;
+  const int64_t ostride = (int64_t)a.H * a.dv;
+  for (int d = tid; d < a.dv; d += 256) {
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    int c = 0;
+    for (; c + 4 <= a.nch; c += 4) {
+      o0 += po[(c + 0) * ostride + d] * wts[c + 0];
+      o1 += po[(c + 1) * ostride + d] * wts[c + 1];
+      o2 += po[(c + 2) * ostride + d] * wts[c + 2];
+      o3 += po[(c + 3) * ostride + d] * wts[c + 3];
     }
-    o *= inv_z;
+    for (; c < a.nch; ++c) o0 += po[c * ostride + d] * wts[c];
+    const float o = ((o0 + o1) + (o2 + o3)) * f;
     const int64_t oi = ((int64_t)r * a.H + h) * a.dv + d;
     if (sizeof(T) == 4) reinterpret_cast<float*>(a.out)[oi] = o;
     else reinterpret_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16_bits(o);
   }
-  if (a.lse && threadIdx.x == 0) a.lse[(int64_t)r * a.H + h] = lse;
+  if (a.lse && tid == 0) a.lse[(int64_t)r * a.H + h] = fin[1];
 }
 
 // ------------------------------------------------------------ host side
@@ -468,6 +812,7 @@ static AttnPlan plan_attn(int B, int T, int H, int D, int dv, int Lc, int W, int
   int64_t want = ceil_div(R * (int64_t)total, 256);  // aim at ~256 workgroups
   int64_t ch = ceil_div(want < 128 ? 128 : want, gran) * gran;
   if (ch >= total) ch = ceil_div(total > 0 ? total : 1, gran) * gran;
+  if (p.mfma && ch > MAX_CHUNK) ch = MAX_CHUNK;
   p.chunk = (int)ch;
   p.nch = (int)ceil_div(total > 0 ? total : 1, ch);
   size_t o = 0;
@@ -497,6 +842,8 @@ static int attn_common(const char* fn, bool dense, const void* q, const int32_t*
   if (B <= 0 || T <= 0 || H <= 0 || D <= 0 || (D & 1) || dv <= 0 || dv > D || Nmax <= 0)
     return fail(CSK_EINVAL, f + ": need positive B, T, H, Nmax, even D and 0 < dv <= D");
   if (d_rope < 0 || d_rope > D || (d_rope & 1)) return fail(CSK_EINVAL, f + ": bad d_rope");
+  if (d_rope > 2 * MAX_ROPE_PAIRS)
+    return fail(CSK_EUNSUPPORTED, f + ": at most 128 rotated channels are built");
   if (W < 0 || S_w < 0 || (S_w > 0 && (!kv_w || !w_pos0)))
     return fail(CSK_EINVAL, f + ": bad window arguments");
   if (!dense && k < 0) return fail(CSK_EINVAL, f + ": k must be >= 0");
@@ -507,7 +854,7 @@ static int attn_common(const char* fn, bool dense, const void* q, const int32_t*
   const int Wslots = S_w > 0 ? W : 0;
   const int Lc = dense ? Nmax : k;
   AttnPlan p = plan_attn(B, T, H, D, dv, Lc, Wslots, dtype);
-  if (p.nch > 65535 || (int64_t)p.nch * H > 65535 || (int64_t)B * T > (1LL << 30))
+  if (p.nch > MERGE_MAX_CH || (int64_t)p.nch * H > 65535 || (int64_t)B * T > (1LL << 30))
     return fail(CSK_EUNSUPPORTED, f + ": problem too large");
   if (p.total > 0 && (!workspace || ws_bytes < p.total))
     return fail(CSK_EWORKSPACE, f + ": workspace smaller than the *_workspace_size() value");
@@ -516,7 +863,8 @@ static int attn_common(const char* fn, bool dense, const void* q, const int32_t*
   a.kv_w = kv_w; a.w_pos0 = w_pos0; a.sink = sink;
   a.B = B; a.T = T; a.H = H; a.D = D; a.dv = dv; a.d_rope = d_rope; a.Nmax = Nmax; a.k = k;
   a.m = m; a.S_w = S_w; a.W = Wslots; a.Lc = Lc; a.chunk = p.chunk; a.nch = p.nch;
-  a.scale = scale; a.base = (double)rope_base; a.dense = dense;
+  a.scale = scale; a.dense = dense;
+  fill_rope_table(&a.rope, d_rope, (double)rope_base);
   a.out = out; a.lse = lse;
   char* ws = reinterpret_cast<char*>(workspace);
   a.part_o = p.nch > 1 ? reinterpret_cast<float*>(ws + p.off_o) : nullptr;
@@ -526,12 +874,20 @@ static int attn_common(const char* fn, bool dense, const void* q, const int32_t*
   int rc;
   if (p.mfma) {
     dim3 grid(R, p.nch), block(64 * (H / 16));
-#define CSK_ATT_CASE(d, v) \
-  if (D == d && dv == v)     \
-    rc = launch(dense ? "attn_bf16_dense" : "attn_bf16_sparse", attn_bf16_kernel<d, v>, grid, block, 0, s, a);
+const int NW = H / 16;
+    const char* kname = dense ? "attn_bf16_dense" : "attn_bf16_sparse";
+#define CSK_ATT_CASE(d, v, nw)                                                         \
+  if (D == d && dv == v && NW == nw) {                                                 \
+    if ((d / 16) % nw == 0)                                                            \
+      rc = launch(kname, attn_bf16_dma_kernel<d, v, (d / 16) % nw == 0 ? nw : 1>, grid, \
+                  block, 0, s, a);                                                     \
+    else                                                                               \
+      rc = launch(kname, attn_bf16_kernel<d, v, nw>, grid, block, 0, s, a);            \
+  }
+#define CSK_ATT_NW(d, v) CSK_ATT_CASE(d, v, 1) CSK_ATT_CASE(d, v, 2) CSK_ATT_CASE(d, v, 3) CSK_ATT_CASE(d, v, 4)
     rc = CSK_EUNSUPPORTED;
-    CSK_ATT_CASE(576, 512) CSK_ATT_CASE(576, 576) CSK_ATT_CASE(128, 128) CSK_ATT_CASE(64, 64)
-    CSK_ATT_CASE(256, 256)
+    CSK_ATT_NW(576, 512) CSK_ATT_NW(576, 576) CSK_ATT_NW(128, 128) CSK_ATT_NW(64, 64) CSK_ATT_NW(256, 256)
+#undef CSK_ATT_NW
 #undef CSK_ATT_CASE
   } else {
     dim3 grid(R, p.nch * H), block(64);

@@ -83,14 +83,18 @@ __device__ __forceinline__ uint32_t e2m1_encode(float x, int s) {
   return (c != 0u && x < 0.0f) ? (c | 8u) : c;
 }
 
-// RoPE angle of pair j: pos * base^(-2j/d_rope), formed in fp64; cos/sin
-// returned in fp32.
-__device__ __forceinline__ void rope_cs(double pos, int j, int d_rope, double base, float* c,
-                                        float* s) {
-  double theta = pow(base, -2.0 * (double)j / (double)d_rope);
-  double a = pos * theta;
+// Partial RoPE frequencies theta_j = base^(-2j/d_rope), formed once per call
+// on the host in fp64 and passed by value with the kernel arguments.
+constexpr int MAX_ROPE_PAIRS = 64;
+struct RopeTable {
+  double theta[MAX_ROPE_PAIRS];
+};
+void fill_rope_table(RopeTable* t, int d_rope, double base);
+
+// cos/sin of the angle pos * theta, formed in fp64, returned in fp32.
+__device__ __forceinline__ void rope_cs(double pos, double theta, float* c, float* s) {
   double sd, cd;
-  sincos(a, &sd, &cd);
+  sincos(pos * theta, &sd, &cd);
   *c = (float)cd;
   *s = (float)sd;
 }

@@ -26,7 +26,7 @@ struct CompressArgs {
   const float* bias_b;
   int B, N, D, m, entry0, d_rope;
   int64_t src_bstride, dst_bstride;
-  double base;
+  RopeTable rope;
   const int32_t* entry_pos;
   void* out;
   uint8_t* out_scale;
@@ -37,6 +37,7 @@ template <typename IN>
 __device__ __forceinline__ void pool_slots(const IN* c, const IN* z, const float* bias, int64_t r0,
                                            int m, int D, int ch, float2& mx, float2& den,
                                            float2& num) {
+#pragma unroll 4
   for (int r = 0; r < m; ++r) {
     const int64_t off = (r0 + r) * (int64_t)D + ch;
     float2 zz = io<IN>::load2(z + off);
@@ -120,9 +121,64 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
     const double pos = a.entry_pos ? (double)a.entry_pos[(int64_t)b * a.N + i]
                                    : (double)a.m * (double)(a.entry0 + i);
     float c, s;
-    rope_cs(pos, (ch - rope0) / 2, a.d_rope, a.base, &c, &s);
+    rope_cs(pos, a.rope.theta[(ch - rope0) / 2], &c, &s);
     float r0 = v0 * c - v1 * s;
     float r1 = v0 * s + v1 * c;
+    v0 = r0;
+    v1 = r1;
+  }
+  store_pair<OUT>(a, (int64_t)b * a.dst_bstride + i, p, v0, v1);
+}
+
+// Wide blocks (HCA, m >= 32): the m slots of a channel pair are split over
+// 8 slot groups so that a wave keeps many independent loads in flight; the
+// 8 partial softmax states (max, denominator, numerator) are merged in LDS.
+// Block = 32 channel pairs x 8 slot groups; grid = (pair blocks, entries).
+template <typename IN, int OUT, bool CSA>
+__global__ __launch_bounds__(256) void compress_wide_kernel(CompressArgs a) {
+  __shared__ float part[8][32][6];
+  const int half = a.D / 2;
+  const int cpl = threadIdx.x & 31, sg = threadIdx.x >> 5;
+  const int p = blockIdx.x * 32 + cpl;
+  const int64_t row = blockIdx.y;
+  const int b = (int)(row / a.N);
+  const int i = (int)(row % a.N);
+  float2 mx = make_float2(-INFINITY, -INFINITY);
+  float2 den = make_float2(0.f, 0.f), num = make_float2(0.f, 0.f);
+  if (p < half) {
+    const int per = a.m / 8;
+    const int64_t src0 = (int64_t)b * a.src_bstride;
+    pool_slots<IN>(reinterpret_cast<const IN*>(a.ca) + src0 * a.D + (int64_t)sg * per * a.D,
+                   reinterpret_cast<const IN*>(a.za) + src0 * a.D + (int64_t)sg * per * a.D,
+                   a.bias_a + (int64_t)sg * per * a.D, (int64_t)a.m * i, per, a.D, 2 * p, mx, den, num);
+  }
+  part[sg][cpl][0] = mx.x; part[sg][cpl][1] = mx.y;
+  part[sg][cpl][2] = den.x; part[sg][cpl][3] = den.y;
+  part[sg][cpl][4] = num.x; part[sg][cpl][5] = num.y;
+  __syncthreads();
+  if (sg != 0 || p >= half) return;
+  float M0 = -INFINITY, M1 = -INFINITY;
+  for (int q = 0; q < 8; ++q) {
+    M0 = fmaxf(M0, part[q][cpl][0]);
+    M1 = fmaxf(M1, part[q][cpl][1]);
+  }
+  float d0 = 0.f, d1 = 0.f, n0 = 0.f, n1 = 0.f;
+  for (int q = 0; q < 8; ++q) {
+    const float f0 = expf(part[q][cpl][0] - M0), f1 = expf(part[q][cpl][1] - M1);
+    d0 += part[q][cpl][2] * f0;
+    d1 += part[q][cpl][3] * f1;
+    n0 += part[q][cpl][4] * f0;
+    n1 += part[q][cpl][5] * f1;
+  }
+  float v0 = n0 / d0, v1 = n1 / d1;
+  const int ch = 2 * p;
+  const int rope0 = a.D - a.d_rope;
+  if (ch >= rope0) {
+    const double pos = a.entry_pos ? (double)a.entry_pos[(int64_t)b * a.N + i]
+                                   : (double)a.m * (double)(a.entry0 + i);
+    float c, sn;
+    rope_cs(pos, a.rope.theta[(ch - rope0) / 2], &c, &sn);
+    const float r0 = v0 * c - v1 * sn, r1 = v0 * sn + v1 * c;
     v0 = r0;
     v1 = r1;
   }
@@ -157,6 +213,14 @@ __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const IN* x, int64_t r
 template <typename IN, bool CSA>
 static int launch_compress_out(const char* name, const CompressArgs& a, int out_dtype,
                                hipStream_t s) {
+  if (!CSA && a.m >= 32 && a.m % 8 == 0 && (int64_t)a.B * a.N <= 65535) {
+    dim3 grid((unsigned)ceil_div(a.D / 2, 32), (unsigned)((int64_t)a.B * a.N)), block(256);
+    switch (out_dtype) {
+      case CSK_F32: return launch(name, compress_wide_kernel<IN, OUT_F32, CSA>, grid, block, 0, s, a);
+      case CSK_BF16: return launch(name, compress_wide_kernel<IN, OUT_BF16, CSA>, grid, block, 0, s, a);
+      default: return launch(name, compress_wide_kernel<IN, OUT_MXFP4, CSA>, grid, block, 0, s, a);
+    }
+  }
   const int64_t total = (int64_t)a.B * a.N * (a.D / 2);
   dim3 grid((unsigned)ceil_div(total, 256)), block(256);
   switch (out_dtype) {
@@ -181,6 +245,8 @@ static int compress_common(const char* fn, bool csa, const void* ca, const void*
     return fail(CSK_EINVAL, f + ": null pointer");
   if (d_rope < 0 || d_rope > D || (d_rope & 1))
     return fail(CSK_EINVAL, f + ": d_rope must be even and in [0, D]");
+  if (d_rope > 2 * MAX_ROPE_PAIRS)
+    return fail(CSK_EUNSUPPORTED, f + ": at most 128 rotated channels are built");
   if (in_dtype != CSK_F32 && in_dtype != CSK_BF16)
     return fail(CSK_EUNSUPPORTED, f + ": in_dtype must be CSK_F32 or CSK_BF16");
   if (out_dtype != CSK_F32 && out_dtype != CSK_BF16 && out_dtype != CSK_MXFP4)
@@ -199,7 +265,7 @@ static int compress_common(const char* fn, bool csa, const void* ca, const void*
   a.B = B; a.N = N; a.D = D; a.m = m; a.entry0 = entry0; a.d_rope = d_rope;
   a.src_bstride = src_bstride ? src_bstride : S;
   a.dst_bstride = dst_bstride ? dst_bstride : N;
-  a.base = (double)rope_base;
+  fill_rope_table(&a.rope, d_rope, (double)rope_base);
   a.entry_pos = entry_pos;
   a.out = out; a.out_scale = out_scale;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

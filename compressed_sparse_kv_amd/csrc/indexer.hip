@@ -38,7 +38,8 @@ namespace csk {
 constexpr int TOPK_CAP = 16384;   // elements a row select keeps in LDS
 constexpr int TOPK_THREADS = 1024;
 constexpr int SLICE = 2048;       // keys per filter workgroup
-constexpr int IDX_KEYS_PER_WG = 256;
+constexpr int IDX_ITERS = 4;                        // 64-key groups per wave
+constexpr int IDX_KEYS_PER_WG = 4 * 64 * IDX_ITERS;  // 4 waves
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -104,20 +105,23 @@ __device__ __forceinline__ void write_samples(const IdxArgs& a, int r, int base,
 }
 
 // ---------------------------------------------------------------- MFMA path
-// HT = HI/16 head tiles, KS = dI/128 MFMA K-steps. One workgroup = 4 waves,
-// one query row, IDX_KEYS_PER_WG consecutive keys (64 per wave).
+// HT = HI/16 head tiles, KS = dI/128 MFMA K-steps. One workgroup = 4 waves
+// and one query row. Wave w handles the 64-key groups
+// base = blockIdx.y*IDX_KEYS_PER_WG + 256*it + 64*w, it < IDX_ITERS, so the
+// four waves of a workgroup stream 256 consecutive keys per iteration; the
+// next group's key fragments are loaded into registers while the current
+// group's MFMAs, transpose and head chain run.
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
 template <int HT, int KS>
 __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
   const int r = blockIdx.x;
   const int b = r / a.T;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int base = blockIdx.y * IDX_KEYS_PER_WG + wave * 64;
+  const int wg_base = blockIdx.y * IDX_KEYS_PER_WG + wave * 64;
   const int nv = visible_count(a, r);
-  if (base >= nv) {
-    if (a.samples && base < a.Nmax) write_samples(a, r, base, -INFINITY);
-    return;
-  }
+  if (wg_base >= nv) return;
   const int HI = HT * 16;
   const int rho = lane & 15, kb = lane >> 4;
 
@@ -135,62 +139,91 @@ __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
       qsc[t][s] = a.qs[qrow * (a.dI / 32) + s * 4 + kb];
     }
   }
+  const float* wr = a.w + (int64_t)r * HI;
 
-  v4f acc[4][HT];
+  v4u kv[4][KS];
+  int ksc[4][KS];
+  auto load_keys = [&](int base) {
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    int key = base + 16 * kt + rho;
-    key = key < a.Nmax ? key : a.Nmax - 1;
-    const int64_t krow = (int64_t)b * a.Nmax + key;
+    for (int kt = 0; kt < 4; ++kt) {
+      int key = base + 16 * kt + rho;
+      key = key < a.Nmax ? key : a.Nmax - 1;
+      const int64_t krow = (int64_t)b * a.Nmax + key;
 #pragma unroll
-    for (int t = 0; t < HT; ++t) acc[kt][t] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < KS; ++s) {
+        kv[kt][s] = __builtin_nontemporal_load(
+            reinterpret_cast<const v4u*>(a.kc + krow * (a.dI / 2) + s * 64 + kb * 16));
+        ksc[kt][s] = a.ks[krow * (a.dI / 32) + s * 4 + kb];
+      }
+    }
+  };
+  load_keys(wg_base);
+
+  for (int it = 0; it < IDX_ITERS; ++it) {
+    const int base = wg_base + it * 256;
+    if (base >= nv) break;
+    v4u cv[4][KS];
+    int csc[4][KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const uint4 v = *reinterpret_cast<const uint4*>(a.kc + krow * (a.dI / 2) + s * 64 + kb * 16);
-      const v8i kbv = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-      const int ksc = a.ks[krow * (a.dI / 32) + s * 4 + kb];
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        cv[kt][s] = kv[kt][s];
+        csc[kt][s] = ksc[kt][s];
+      }
+    if (it + 1 < IDX_ITERS && base + 256 < nv) load_keys(base + 256);
+
+    v4f acc[4][HT];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+      for (int t = 0; t < HT; ++t) acc[kt][t] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const v8i kbv = v8i{(int)cv[kt][s].x, (int)cv[kt][s].y, (int)cv[kt][s].z, (int)cv[kt][s].w,
+                            0, 0, 0, 0};
+#pragma unroll
+        for (int t = 0; t < HT; ++t)
+          acc[kt][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              qa[t][s], kbv, acc[kt][t], 4, 4, 0, qsc[t][s], 0, csc[kt][s]);
+      }
+    }
+
+    // transpose (key tile, lane group): lane group G of register set g then
+    // holds heads 4*HT*g + 4t + j of key 16*G + (lane % 16)
+    float d[4][HT][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int t = 0; t < HT; ++t)
-        acc[kt][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            qa[t][s], kbv, acc[kt][t], 4, 4, 0, qsc[t][s], 0, ksc);
-    }
-  }
-
-  // transpose (key tile, lane group): lane group G of register set g then
-  // holds heads 4*HT*g + 4t + j of key 16*G + (lane % 16)
-  float d[4][HT][4];
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
+        for (int j = 0; j < 4; ++j) d[kt][t][j] = acc[kt][t][j];
 #pragma unroll
-    for (int t = 0; t < HT; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) d[kt][t][j] = acc[kt][t][j];
-#pragma unroll
-  for (int t = 0; t < HT; ++t) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      swap32(d[0][t][j], d[2][t][j]);
-      swap32(d[1][t][j], d[3][t][j]);
-      swap16(d[0][t][j], d[1][t][j]);
-      swap16(d[2][t][j], d[3][t][j]);
-    }
-  }
-
-  const float* wr = a.w + (int64_t)r * HI;
-  float score = 0.0f;
-#pragma unroll
-  for (int g = 0; g < 4; ++g)
-#pragma unroll
-    for (int t = 0; t < HT; ++t)
+    for (int t = 0; t < HT; ++t) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float v = d[g][t][j];
-        score = __builtin_fmaf(wr[4 * HT * g + 4 * t + j], v > 0.0f ? v : 0.0f, score);
+        swap32(d[0][t][j], d[2][t][j]);
+        swap32(d[1][t][j], d[3][t][j]);
+        swap16(d[0][t][j], d[1][t][j]);
+        swap16(d[2][t][j], d[3][t][j]);
       }
+    }
 
-  const int key = base + lane;
-  if (key < nv) a.scores[(int64_t)r * a.Nmax + key] = score;
-  if (a.samples) write_samples(a, r, base, key < nv ? score : -INFINITY);
+    float score = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int t = 0; t < HT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float v = d[g][t][j];
+          score = __builtin_fmaf(wr[4 * HT * g + 4 * t + j], v > 0.0f ? v : 0.0f, score);
+        }
+
+    const int key = base + lane;
+    if (key < nv) a.scores[(int64_t)r * a.Nmax + key] = score;
+    if (a.samples) write_samples(a, r, base, key < nv ? score : -INFINITY);
+  }
 }
 
 // -------------------------------------------------------------- VALU path
@@ -255,6 +288,49 @@ __global__ __launch_bounds__(256) void idx_samples_kernel(IdxArgs a) {
   a.samples[(int64_t)r * a.ng + g] = mx;
 }
 
+// ------------------------------------------------------------ block scans
+// Exclusive prefix sums of two ints over a workgroup of NT threads (NT/64
+// waves <= 64): wave shuffles, then one wave scans the wave totals.
+struct ScanShared {
+  int2 wtot[16];
+  int2 total;
+};
+
+template <int NT>
+__device__ __forceinline__ int2 block_scan2(int a, int b, ScanShared& sh, int2* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = a, y = b;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int xs = __shfl_up(x, o), ys = __shfl_up(y, o);
+    if (lane >= o) {
+      x += xs;
+      y += ys;
+    }
+  }
+  if (lane == 63) sh.wtot[wave] = make_int2(x, y);
+  __syncthreads();
+  if (wave == 0) {
+    const int2 w = lane < NT / 64 ? sh.wtot[lane] : make_int2(0, 0);
+    int wx = w.x, wy = w.y;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int xs = __shfl_up(wx, o), ys = __shfl_up(wy, o);
+      if (lane >= o) {
+        wx += xs;
+        wy += ys;
+      }
+    }
+    if (lane < NT / 64) sh.wtot[lane] = make_int2(wx - w.x, wy - w.y);
+    if (lane == NT / 64 - 1) sh.total = make_int2(wx, wy);
+  }
+  __syncthreads();
+  const int2 off = sh.wtot[wave];
+  *total = sh.total;
+  __syncthreads();  // the shared totals may be reused by the next scan
+  return make_int2(off.x + x - a, off.y + y - b);
+}
+
 // ------------------------------------------------------------ radix select
 // Block-wide (TOPK_THREADS) selection over n elements with keys get(e).
 // Finds (mask, prefix, take) such that the selected set is every element
@@ -267,10 +343,8 @@ struct SelectState {
 
 struct SelectShared {
   int hist[256];
-  int bin_sum[64];
   int digit, above, binc;
-  int scan[TOPK_THREADS + 1];
-  int scan2[TOPK_THREADS + 1];
+  ScanShared scan;
 };
 
 template <typename Get>
@@ -314,10 +388,10 @@ __device__ SelectState radix_select(Get get, int n, int k, SelectShared& sh) {
     st.take -= sh.above;
     st.prefix |= (uint32_t)sh.digit << shift;
     st.mask |= 0xffu << shift;
-    if (sh.binc == st.take) break;  // the whole bin is taken: no tie resolution needed
+    const bool whole_bin = sh.binc == st.take;  // no tie resolution needed
     __syncthreads();
+    if (whole_bin) break;
   }
-  __syncthreads();
   return st;
 }
 
@@ -337,20 +411,9 @@ __device__ void compact_selected(Get get, Emit emit, int n, const SelectState& s
     gt += u > st.prefix;
     eq += u == st.prefix;
   }
-  sh.scan[tid] = gt;
-  sh.scan2[tid] = eq;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over TOPK_THREADS entries (both arrays)
-  for (int o = 1; o < TOPK_THREADS; o <<= 1) {
-    int a = tid >= o ? sh.scan[tid - o] : 0;
-    int b = tid >= o ? sh.scan2[tid - o] : 0;
-    __syncthreads();
-    sh.scan[tid] += a;
-    sh.scan2[tid] += b;
-    __syncthreads();
-  }
-  int gt_before = sh.scan[tid] - gt;
-  int eq_before = sh.scan2[tid] - eq;
+  int2 tot;
+  const int2 before = block_scan2<TOPK_THREADS>(gt, eq, sh.scan, &tot);
+  int gt_before = before.x, eq_before = before.y;
   for (int e = e0; e < e1; ++e) {
     const uint32_t u = get(e) & st.mask;
     if (u > st.prefix) {
@@ -367,10 +430,10 @@ struct TopkArgs {
   IdxArgs ia;
   int k;
   int n_slices;
-  const uint32_t* thresh;   // [R] key threshold (filtered mode)
-  const int* cand_cnt;      // [R, n_slices]
-  const float* cand_score;  // [R, Nmax]: slice f at [f*SLICE, f*SLICE+cnt)
-  const int* cand_idx;      // [R, Nmax]
+  uint32_t* thresh;         // [R] key threshold (filtered mode)
+  int* cand_cnt;            // [R, n_slices]
+  float* cand_score;        // [R, Nmax]: slice f at [f*SLICE, f*SLICE+cnt)
+  int* cand_idx;            // [R, Nmax]
   uint32_t* flat_key;       // [R, Nmax] spill when a row exceeds TOPK_CAP
   int* flat_idx;            // [R, Nmax]
   int32_t* idx;             // [R, k]
@@ -382,78 +445,95 @@ struct TopkShared {
   uint32_t key[TOPK_CAP];
   int eidx[TOPK_CAP];
   int slice_off[1024 + 1];
-  int n;
 };
 
-// Threshold from the group maxima: key of the k-th largest sample (or 0 =
-// keep everything when there are too few or too many samples).
+// Threshold from the group maxima, in one pass: a 4096-bin histogram of
+// the top 12 key bits; the threshold is the lower edge of the bin that holds
+// the k-th largest sample, so at least k samples (and hence at least k
+// elements of the row) are >= it. 0 keeps everything when the row has at
+// most k entries or too few samples.
+constexpr int THR_BINS = 4096;
+
 __global__ __launch_bounds__(TOPK_THREADS) void topk_threshold_kernel(TopkArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  TopkShared& sh = *reinterpret_cast<TopkShared*>(smem);
+  __shared__ int hist[THR_BINS];
+  __shared__ ScanShared scan;
+  __shared__ uint32_t result;
   const int r = blockIdx.x;
+  const int tid = threadIdx.x;
   const int nv = visible_count(a.ia, r);
   const int gs = 1 << a.ia.gs_log2;
   const int ng = (nv + gs - 1) / gs;
-  if (nv <= a.k || ng < a.k || ng > TOPK_CAP) {
-    if (threadIdx.x == 0) const_cast<uint32_t*>(a.thresh)[r] = 0u;
+  if (nv <= a.k || ng < a.k) {
+    if (tid == 0) a.thresh[r] = 0u;
     return;
   }
-  for (int e = threadIdx.x; e < ng; e += TOPK_THREADS)
-    sh.key[e] = order_key(a.ia.samples[(int64_t)r * a.ia.ng + e]);
+  for (int i = tid; i < THR_BINS; i += TOPK_THREADS) hist[i] = 0;
+  if (tid == 0) result = 0u;
   __syncthreads();
-  auto get = [&](int e) { return sh.key[e]; };
-  SelectState st = radix_select(get, ng, a.k, sh.sel);
-  // the k-th largest sample key: its full key is the prefix with the low
-  // bits of that element; when the radix select stopped early, the bin's
-  // minimum is a safe (lower) threshold
-  if (threadIdx.x == 0) const_cast<uint32_t*>(a.thresh)[r] = st.prefix;
+  for (int e = tid; e < ng; e += TOPK_THREADS)
+    atomicAdd(&hist[order_key(a.ia.samples[(int64_t)r * a.ia.ng + e]) >> 20], 1);
+  __syncthreads();
+  // thread t owns bin group G = 1023 - t (4 bins); an inclusive scan in
+  // thread order is then a suffix sum over bins
+  const int G = TOPK_THREADS - 1 - tid;
+  const int s4 = hist[4 * G] + hist[4 * G + 1] + hist[4 * G + 2] + hist[4 * G + 3];
+  int2 tot;
+  const int2 ex = block_scan2<TOPK_THREADS>(s4, 0, scan, &tot);
+  const int incl = ex.x + s4;
+  if (incl >= a.k && ex.x < a.k) {
+    int above = ex.x;
+    int d = 4 * G + 3;
+    for (; d > 4 * G; --d) {
+      if (above + hist[d] >= a.k) break;
+      above += hist[d];
+    }
+    result = (uint32_t)d << 20;
+  }
+  __syncthreads();
+  if (tid == 0) a.thresh[r] = result;
 }
 
-// Candidate filter: keys of slice blockIdx.x with key(score) >= thresh,
-// compacted in index order.
+// Candidate filter: keys of slice blockIdx.y with key(score) >= thresh,
+// compacted in index order (thread t owns 8 consecutive keys).
 __global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a) {
-  __shared__ int wave_cnt[4];
+  __shared__ ScanShared scan;
   const int r = blockIdx.x, f = blockIdx.y;
   const int nv = visible_count(a.ia, r);
   const int s0 = f * SLICE;
-  int* cnt_out = const_cast<int*>(a.cand_cnt) + (int64_t)r * a.n_slices + f;
   if (s0 >= nv) {
-    if (threadIdx.x == 0) *cnt_out = 0;
+    if (threadIdx.x == 0) a.cand_cnt[(int64_t)r * a.n_slices + f] = 0;
     return;
   }
   const uint32_t thr = a.thresh[r];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float* cs = const_cast<float*>(a.cand_score) + (int64_t)r * a.ia.Nmax + s0;
-  int* ci = const_cast<int*>(a.cand_idx) + (int64_t)r * a.ia.Nmax + s0;
-  const float* sc = a.ia.scores + (int64_t)r * a.ia.Nmax;
-  int written = 0;
-  // 256 keys per step: wave w takes keys [64w, 64w+64) of the step
-  for (int step = 0; step < SLICE / 256; ++step) {
-    const int s = s0 + step * 256 + wave * 64 + lane;
-    float v = 0.f;
-    bool keep = false;
-    if (s < nv) {
-      v = sc[s];
-      keep = order_key(v) >= thr;
-    }
-    const unsigned long long bal = __ballot(keep);
-    if (lane == 0) wave_cnt[wave] = __popcll(bal);
-    __syncthreads();
-    int before = written;
-    for (int w2 = 0; w2 < wave; ++w2) before += wave_cnt[w2];
-    const int rank = __popcll(bal & ((1ull << lane) - 1ull));
-    if (keep) {
-      cs[before + rank] = v;
-      ci[before + rank] = s;
-    }
-    written += wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
-    __syncthreads();
+  const float* sc = a.ia.scores + (int64_t)r * a.ia.Nmax + s0;
+  const int lim = min(SLICE, nv - s0);
+  const int j0 = threadIdx.x * (SLICE / 256);
+  float v[SLICE / 256];
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < SLICE / 256; ++i) {
+    const int j = j0 + i;
+    v[i] = j < lim ? sc[j] : -INFINITY;
+    cnt += (j < lim && order_key(v[i]) >= thr) ? 1 : 0;
   }
-  if (threadIdx.x == 0) *cnt_out = written;
+  int2 tot;
+  int pos = block_scan2<256>(cnt, 0, scan, &tot).x;
+  float* cs = a.cand_score + (int64_t)r * a.ia.Nmax + s0;
+  int* ci = a.cand_idx + (int64_t)r * a.ia.Nmax + s0;
+#pragma unroll
+  for (int i = 0; i < SLICE / 256; ++i) {
+    const int j = j0 + i;
+    if (j < lim && order_key(v[i]) >= thr) {
+      cs[pos] = v[i];
+      ci[pos] = s0 + j;
+      ++pos;
+    }
+  }
+  if (threadIdx.x == 0) a.cand_cnt[(int64_t)r * a.n_slices + f] = tot.x;
 }
 
-// Final selection for one row. filtered = false: the row's scores
-// themselves (index = position); filtered = true: the slice candidates.
+// Final selection for one row. FILTERED = false: the row's scores
+// themselves (index = position); FILTERED = true: the slice candidates.
 template <bool FILTERED>
 __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -466,21 +546,18 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkArgs a) {
   float* osc = a.out_score ? a.out_score + (int64_t)r * k : nullptr;
 
   int n;
+  const int ns = (nv + SLICE - 1) / SLICE;
   if (!FILTERED) {
     n = nv;
   } else {
-    if (tid == 0) {
-      int acc = 0;
-      const int ns = (nv + SLICE - 1) / SLICE;
-      for (int f = 0; f < ns; ++f) {
-        sh.slice_off[f] = acc;
-        acc += a.cand_cnt[(int64_t)r * a.n_slices + f];
-      }
-      sh.slice_off[ns] = acc;
-      sh.n = acc;
-    }
+    // slice offsets: exclusive scan of the per-slice counts (ns <= 1024)
+    const int cnt = tid < ns ? a.cand_cnt[(int64_t)r * a.n_slices + tid] : 0;
+    int2 tot;
+    const int off = block_scan2<TOPK_THREADS>(cnt, 0, sh.sel.scan, &tot).x;
+    if (tid < ns) sh.slice_off[tid] = off;
+    if (tid == 0) sh.slice_off[ns] = tot.x;
     __syncthreads();
-    n = sh.n;
+    n = tot.x;
   }
   const bool in_lds = n <= TOPK_CAP;
   uint32_t* gkey = a.flat_key + (int64_t)r * a.ia.Nmax;
@@ -492,21 +569,23 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkArgs a) {
     if (in_lds)
       for (int e = tid; e < n; e += TOPK_THREADS) sh.key[e] = order_key(srow[e]);
   } else {
-    const int ns = (nv + SLICE - 1) / SLICE;
-    for (int f = 0; f < ns; ++f) {
-      const int c = sh.slice_off[f + 1] - sh.slice_off[f];
-      const int o = sh.slice_off[f];
-      const float* cs = a.cand_score + (int64_t)r * a.ia.Nmax + (int64_t)f * SLICE;
-      const int* ci = a.cand_idx + (int64_t)r * a.ia.Nmax + (int64_t)f * SLICE;
-      for (int e = tid; e < c; e += TOPK_THREADS) {
-        const uint32_t u = order_key(cs[e]);
-        if (in_lds) {
-          sh.key[o + e] = u;
-          sh.eidx[o + e] = ci[e];
-        } else {
-          gkey[o + e] = u;
-          gidx[o + e] = ci[e];
-        }
+    // element e lives in slice f with slice_off[f] <= e < slice_off[f+1]
+    for (int e = tid; e < n; e += TOPK_THREADS) {
+      int lo = 0, hi = ns - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sh.slice_off[mid] <= e) lo = mid;
+        else hi = mid - 1;
+      }
+      const int64_t src = (int64_t)r * a.ia.Nmax + (int64_t)lo * SLICE + (e - sh.slice_off[lo]);
+      const uint32_t u = order_key(a.cand_score[src]);
+      const int ix = a.cand_idx[src];
+      if (in_lds) {
+        sh.key[e] = u;
+        sh.eidx[e] = ix;
+      } else {
+        gkey[e] = u;
+        gidx[e] = ix;
       }
     }
   }
@@ -659,21 +738,19 @@ int indexer_topk(const void* q, const uint8_t* q_scale, const float* w, const vo
   const size_t lds = sizeof(TopkShared);
   static std::once_flag attr_once;
   std::call_once(attr_once, [&] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(topk_threshold_kernel),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(topk_select_kernel<true>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(topk_select_kernel<false>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   });
   if (p.filtered) {
-    ta.thresh = reinterpret_cast<const uint32_t*>(ws + p.off_thresh);
-    ta.cand_cnt = reinterpret_cast<const int*>(ws + p.off_cnt);
-    ta.cand_score = reinterpret_cast<const float*>(ws + p.off_cscore);
-    ta.cand_idx = reinterpret_cast<const int*>(ws + p.off_cidx);
+    ta.thresh = reinterpret_cast<uint32_t*>(ws + p.off_thresh);
+    ta.cand_cnt = reinterpret_cast<int*>(ws + p.off_cnt);
+    ta.cand_score = reinterpret_cast<float*>(ws + p.off_cscore);
+    ta.cand_idx = reinterpret_cast<int*>(ws + p.off_cidx);
     ta.flat_key = reinterpret_cast<uint32_t*>(ws + p.off_fkey);
     ta.flat_idx = reinterpret_cast<int*>(ws + p.off_fidx);
-    rc = launch("topk_threshold", topk_threshold_kernel, dim3(R), dim3(TOPK_THREADS), lds, s, ta);
+    rc = launch("topk_threshold", topk_threshold_kernel, dim3(R), dim3(TOPK_THREADS), 0, s, ta);
     if (rc == CSK_OK)
       rc = launch("topk_filter", topk_filter_kernel, dim3(R, p.n_slices), dim3(256), 0, s, ta);
     if (rc == CSK_OK)
