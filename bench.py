@@ -12,11 +12,12 @@ the whole hot path for one new token per sequence:
   3. mxfp4_quantize - the indexer queries
   4. indexer_topk  - scores over all 262144 entries, top-2048 per row
   5. sparse_attn   - CSA attention over selected entries + window + sink
-and, on a second stream (it does not depend on the CSA chain),
   6. hca_compress  - the newest HCA entry (128 source tokens)
   7. dense_compressed_attn - HCA attention over all 8192 entries + window + sink
-Each step is captured once into a HIP graph (torch.cuda.CUDAGraph) and the
-timed loop replays them. Four copies of the layer-pair state rotate between
+The calls run on three streams as the data flow allows (1, 6, 7 on one; 3
+on another; 2, 4, 5 on the main stream after the entries they read). The
+timed steps are eager launches by default (--mode graph replays one
+captured HIP graph per step instead). Four copies of the layer-pair state rotate between
 steps (as successive layers would), so a step never finds its 121 MB working
 set in the 256 MB Infinity Cache from the previous step.
 
@@ -117,7 +118,11 @@ class DecodeWorkload:
             ws_d = csk.dense_compressed_attn_workspace_size(B, 1, H, self.D, dv, self.Nh, 128, self.W,
                                                             csk.CSK_BF16)
             self.ws_d = torch.empty(max(ws_d, 1), dtype=torch.uint8, device=dev)
-        self.side = torch.cuda.Stream() if self.pair else None  # default priority
+        # extra streams (default priority) and the event that hands the
+        # newest KV entry from the side stream to the sparse attention
+        self.side = torch.cuda.Stream()
+        self.qstream = torch.cuda.Stream()
+        self.ev_kv = torch.cuda.Event()
         torch.cuda.synchronize()
         if not keep_host:
             self.d = None
@@ -126,41 +131,48 @@ class DecodeWorkload:
 
     # ------------------------------------------------------------- one step
     def step(self, c=0):
-        """One decode step. The HCA branch (its compression and attention)
-        does not depend on the CSA chain and runs on a second stream."""
+        """One decode step over three streams, following the data flow:
+        the side stream computes the newest CSA KV entry (needed only by the
+        sparse attention) and then the whole HCA branch; a second stream
+        encodes the indexer queries; the main stream computes the newest
+        indexer key, scores and selects, and runs the sparse attention."""
         torch, csk, x, st = self.torch, self.csk, self.x, self.copies[c % len(self.copies)]
         B, N, D, dI = self.B, self.N, self.D, self.dI
         main = torch.cuda.current_stream()
-        if self.pair:
-            self.side.wait_stream(main)
-            with torch.cuda.stream(self.side):
+        side, qs = self.side, self.qstream
+        side.wait_stream(main)
+        qs.wait_stream(main)
+        with torch.cuda.stream(side):
+            # the newest CSA entry N-1 (a-block = source rows 4..7, previous
+            # block = rows 0..3 of the 8-token window)
+            csk.csa_compress(x["src_ca"][:, 4:], x["src_za"][:, 4:], x["src_cb"][:, 4:], x["src_zb"][:, 4:],
+                             x["bias_a"], x["bias_b"], 4, d_rope=64, entry0=N - 1, src_bstride=8,
+                             out=st["kv_c"][:, N - 1:], dst_bstride=N, S=4, B=B)
+            self.ev_kv.record(side)
+            if self.pair:
                 Nh = self.Nh
                 csk.hca_compress(x["src_c"], x["src_z"], x["bias_h"], 128, d_rope=64, entry0=Nh - 1,
                                  out=st["kv_h"][:, Nh - 1:], dst_bstride=Nh)
                 csk.dense_compressed_attn(x["q_h"], x["q_pos"], st["kv_h"], x["n_entries_h"], 128, st["kv_w_h"],
                                           x["w_pos0"], self.W, x["sink_h"], self.dv, 64, self.scale, out=self.out_h,
                                           lse=self.lse_h, workspace=self.ws_d)
-        # 1-2: the newest CSA entry N-1 and its indexer key (a-block = source
-        # rows 4..7, previous block = rows 0..3 of the 8-token window)
-        csk.csa_compress(x["src_ca"][:, 4:], x["src_za"][:, 4:], x["src_cb"][:, 4:], x["src_zb"][:, 4:],
-                         x["bias_a"], x["bias_b"], 4, d_rope=64, entry0=N - 1, src_bstride=8,
-                         out=st["kv_c"][:, N - 1:], dst_bstride=N, S=4, B=B)
+        with torch.cuda.stream(qs):
+            csk.mxfp4_quantize(x["qI"], self.qc, self.qs)
+        # the newest indexer key, MXFP4
         csk.csa_compress(x["src_ia"][:, 4:], x["src_iza"][:, 4:], x["src_ib"][:, 4:], x["src_izb"][:, 4:],
                          x["ibias_a"], x["ibias_b"], 4, entry0=N - 1, src_bstride=8, out_dtype=csk.CSK_MXFP4,
                          out=st["kc"][:, N - 1:], out_scale=st["ks"][:, N - 1:], dst_bstride=N, S=4, B=B)
-        # 4-5: indexer queries to MXFP4, scores + top-k
-        csk.mxfp4_quantize(x["qI"], self.qc, self.qs)
+        main.wait_stream(qs)
         csk.indexer_topk(self.qc, x["w"], st["kc"], x["q_pos"], x["n_entries"], 4, self.k, q_scale=self.qs,
                          k_scale=st["ks"], idx=self.idx, score=self.score, workspace=self.ws_i)
-        # 6: CSA attention
+        main.wait_event(self.ev_kv)
         csk.sparse_attn(x["q"], x["q_pos"], st["kv_c"], self.idx, st["kv_w"], x["w_pos0"], self.W, x["sink"],
                         self.dv, 64, self.scale, out=self.out, lse=self.lse,
                         workspace=self.ws_s)
-        if self.pair:
-            main.wait_stream(self.side)
+        main.wait_stream(side)
 
     def kernels(self):
-        names = ["csa_compress", "mxfp4_quantize", "indexer_scores_fp4", "topk_threshold", "topk_filter",
+        names = ["csa_compress", "mxfp4_quantize", "indexer_scores_fp4", "topk_filter",
                  "topk_select", "attn_bf16_sparse", "attn_merge"]
         if self.pair:
             names += ["hca_compress", "attn_bf16_dense"]
@@ -274,29 +286,43 @@ def run(args):
          ", ".join(f"{n}={v[0]*1e3:.1f}us x{v[1]:g}" for n, v in per.items()))
     dom = max((n for n in per if wl.algorithmic_bytes(n)), key=lambda n: per[n][0] * per[n][1])
 
-    # capture one graph per timed step, each with its own event pair around
-    # the dominant kernel
     timer = csk.KernelTimer(dom, K)
-    graphs = []
-    cap_stream = torch.cuda.Stream()
-    for i in range(K):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap_stream):
+    if args.mode == "graph":
+        # one graph per timed step, each with its own event pair around the
+        # dominant kernel
+        graphs = []
+        cap_stream = torch.cuda.Stream()
+        for i in range(K):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap_stream):
+                wl.step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        if timer.count() != K:
+            raise RuntimeError(f"kernel timer recorded {timer.count()} of {K} launches")
+        timer.disarm()
+        for i in range(Wm):  # warm replays
+            graphs[i % K].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            graphs[i].replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    else:
+        # eager launches: the host runs ahead of the GPU, and the event pair
+        # around each launch of the dominant kernel sits on its own stream
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
             wl.step(i)
-        graphs.append(g)
-    torch.cuda.synchronize()
-    if timer.count() != K:
-        raise RuntimeError(f"kernel timer recorded {timer.count()} of {K} launches")
-    timer.disarm()
-    for i in range(Wm):  # warm replays
-        graphs[i % K].replay()
-    torch.cuda.synchronize()
-
-    t0 = time.perf_counter()
-    for i in range(K):
-        graphs[i].replay()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+        t_host = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        _log(f"host enqueue {t_host * 1e6 / K:.1f} us/step")
+        if timer.count() != K:
+            raise RuntimeError(f"kernel timer recorded {timer.count()} of {K} launches")
+        timer.disarm()
     ms_per_step = elapsed * 1e3 / K
     tokens = wl.B * K
     value = tokens / elapsed
@@ -320,7 +346,7 @@ def run(args):
         "vs_baseline": None,
         "dtype": "bf16+mxfp4",
         "data": "synthetic",
-        "config": wl.config(),
+        "config": dict(wl.config(), launch=args.mode),
         "roofline": {
             "kernel": dom,
             "bound": "hbm",
@@ -361,6 +387,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_1m_pair", choices=["decode_1m_pair", "csa_decode_128k"])
     ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--mode", default="eager", choices=["eager", "graph"],
+                    help="timed steps as eager launches or as HIP graph replays")
     ap.add_argument("--cpu-rows", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()

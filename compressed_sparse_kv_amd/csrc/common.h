@@ -91,12 +91,90 @@ struct RopeTable {
 };
 void fill_rope_table(RopeTable* t, int d_rope, double base);
 
-// cos/sin of the angle pos * theta, formed in fp64, returned in fp32.
+// cos/sin of the angle pos * theta, returned in fp32. The angle is formed
+// in fp64 and reduced to r in [-pi/4, pi/4] plus a quadrant q (angle =
+// q*pi/2 + r; pi/2 as a two-part constant, products folded with fma, so r
+// keeps about 1e-10 absolute accuracy for angles up to 2^31 rad). sin r and
+// cos r are Taylor polynomials in fp64 through the r^9 and r^10 terms
+// (truncation below 2e-9 on |r| <= pi/4); the quadrant swaps and negates
+// them. The fp32 results are within one ulp of the correctly rounded ones.
 __device__ __forceinline__ void rope_cs(double pos, double theta, float* c, float* s) {
-  double sd, cd;
-  sincos(pos * theta, &sd, &cd);
-  *c = (float)cd;
-  *s = (float)sd;
+  constexpr double PI_2_HI = 1.5707963267948965580;     // nearest double to pi/2
+  constexpr double PI_2_LO = 6.123233995736766036e-17;  // pi/2 - PI_2_HI
+  constexpr double TWO_OVER_PI = 0.63661977236758134308;
+  const double ang = pos * theta;
+  const double q = rint(ang * TWO_OVER_PI);
+  double r = fma(-q, PI_2_HI, ang);
+  r = fma(-q, PI_2_LO, r);
+  const double r2 = r * r;
+  const double sp =
+      r * (1.0 + r2 * (-1.0 / 6.0 + r2 * (1.0 / 120.0 + r2 * (-1.0 / 5040.0 + r2 * (1.0 / 362880.0)))));
+  const double cp =
+      1.0 + r2 * (-0.5 + r2 * (1.0 / 24.0 + r2 * (-1.0 / 720.0 + r2 * (1.0 / 40320.0 + r2 * (-1.0 / 3628800.0)))));
+  const int iq = (int)((long long)q & 3);
+  const double sv = iq == 0 ? sp : iq == 1 ? cp : iq == 2 ? -sp : -cp;
+  const double cv = iq == 0 ? cp : iq == 1 ? -sp : iq == 2 ? -cp : sp;
+  *s = (float)sv;
+  *c = (float)cv;
+}
+
+// ------------------------------------------------------------ cross-lane
+// Cross-lane steps built from DPP and permlane swaps (VALU operations).
+// __shfl* compiles to ds_bpermute, an LDS round trip whose result must be
+// waited for; chains of those dominate short reductions and scans.
+
+// Inclusive prefix sum over a wave of 64 lanes: shifts within rows of 16
+// lanes, then the row totals are carried by row broadcasts.
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
+// Lane l and lane l^32, then l and l^16: with both operands equal, the
+// permlane swaps return the two halves that each lane combines.
+__device__ __forceinline__ float group4_max(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group4_sum(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Reductions over all 64 lanes: within quads (quad_perm), across the quads
+// of a row (row rotations), then across the four rows (group4_*).
+#define CSK_DPP_F(x, ctrl) \
+  __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xf, 0xf, false))
+// Maximum over each row of 16 lanes (quads, then rotations within the row).
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, CSK_DPP_F(x, 0xB1));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, CSK_DPP_F(x, 0x4E));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, CSK_DPP_F(x, 0x124));  // row_ror:4
+  x = fmaxf(x, CSK_DPP_F(x, 0x128));  // row_ror:8
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, CSK_DPP_F(x, 0xB1));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, CSK_DPP_F(x, 0x4E));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, CSK_DPP_F(x, 0x124));  // row_ror:4
+  x = fmaxf(x, CSK_DPP_F(x, 0x128));  // row_ror:8
+  return group4_max(x);
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x += CSK_DPP_F(x, 0xB1);
+  x += CSK_DPP_F(x, 0x4E);
+  x += CSK_DPP_F(x, 0x124);
+  x += CSK_DPP_F(x, 0x128);
+  return group4_sum(x);
 }
 
 template <typename T>

@@ -32,35 +32,69 @@ struct CompressArgs {
   uint8_t* out_scale;
 };
 
-// Online softmax over `m` slots starting at row r0 (relative to src).
+// Gate logit Z + bias and value C of one source slot for a channel pair;
+// an absent slot (ok false) has logit -inf and contributes nothing. The loads
+// are unconditional (an absent slot reads the valid row `safe_row` instead)
+// so that a batch of them stays in flight together: a load under a branch
+// would have to complete before the branch's other side could write the
+// same registers.
 template <typename IN>
+__device__ __forceinline__ void load_slot(const IN* c, const IN* z, const float* bias, int64_t row,
+                                          int brow, int D, int ch, bool ok, int64_t safe_row,
+                                          float2& l, float2& v) {
+  const int64_t off = (ok ? row : safe_row) * (int64_t)D + ch;
+  const float2 zz = io<IN>::load2(z + off);
+  const float2 cc = io<IN>::load2(c + off);
+  const float2 bb = *reinterpret_cast<const float2*>(bias + (int64_t)(ok ? brow : 0) * D + ch);
+  // the masks are applied arithmetically: a select whose operand is a load
+  // would let the compiler sink that load back under a branch
+  const float pen = ok ? 0.f : -INFINITY, keep = ok ? 1.f : 0.f;
+  l = make_float2(zz.x + bb.x + pen, zz.y + bb.y + pen);
+  v = make_float2(cc.x * keep, cc.y * keep);
+}
+
+// Folds a batch of NB slots into the running softmax state (max,
+// denominator, numerator) of a channel pair, rescaling once per batch.
+template <int NB>
+__device__ __forceinline__ void fold(const float2* l, const float2* v, float2& mx, float2& den,
+                                     float2& num) {
+  float2 bm = mx;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    bm.x = fmaxf(bm.x, l[j].x);
+    bm.y = fmaxf(bm.y, l[j].y);
+  }
+  const float f0 = mx.x == -INFINITY ? 0.f : expf(mx.x - bm.x);
+  const float f1 = mx.y == -INFINITY ? 0.f : expf(mx.y - bm.y);
+  den.x *= f0;
+  num.x *= f0;
+  den.y *= f1;
+  num.y *= f1;
+  mx = bm;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const float e0 = l[j].x == -INFINITY ? 0.f : expf(l[j].x - bm.x);
+    const float e1 = l[j].y == -INFINITY ? 0.f : expf(l[j].y - bm.y);
+    den.x += e0;
+    den.y += e1;
+    num.x = fmaf(e0, v[j].x, num.x);
+    num.y = fmaf(e1, v[j].y, num.y);
+  }
+}
+
+// Softmax over `m` slots starting at row r0 (relative to src), in batches of
+// NB slots: all loads of a batch are issued before any arithmetic depends on
+// them (no branch between them, so they are in flight together).
+template <int NB, typename IN>
 __device__ __forceinline__ void pool_slots(const IN* c, const IN* z, const float* bias, int64_t r0,
                                            int m, int D, int ch, float2& mx, float2& den,
                                            float2& num) {
-#pragma unroll 4
-  for (int r = 0; r < m; ++r) {
-    const int64_t off = (r0 + r) * (int64_t)D + ch;
-    float2 zz = io<IN>::load2(z + off);
-    float2 cc = io<IN>::load2(c + off);
-    float2 bb = *reinterpret_cast<const float2*>(bias + (int64_t)r * D + ch);
-    float l0 = zz.x + bb.x, l1 = zz.y + bb.y;
-    if (l0 > mx.x) {
-      float f = expf(mx.x - l0);
-      den.x *= f;
-      num.x *= f;
-      mx.x = l0;
-    }
-    if (l1 > mx.y) {
-      float f = expf(mx.y - l1);
-      den.y *= f;
-      num.y *= f;
-      mx.y = l1;
-    }
-    float e0 = expf(l0 - mx.x), e1 = expf(l1 - mx.y);
-    den.x += e0;
-    den.y += e1;
-    num.x = fmaf(e0, cc.x, num.x);
-    num.y = fmaf(e1, cc.y, num.y);
+  for (int rb = 0; rb < m; rb += NB) {
+    float2 l[NB], v[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      load_slot(c, z, bias, r0 + rb + j, rb + j, D, ch, rb + j < m, r0, l[j], v[j]);
+    fold<NB>(l, v, mx, den, num);
   }
 }
 
@@ -76,8 +110,7 @@ __device__ __forceinline__ void store_pair(const CompressArgs& a, int64_t orow, 
   } else {
     // 16 consecutive lanes hold one tile of 32 channels
     float amax = fmaxf(fabsf(v0), fabsf(v1));
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+    amax = row16_max(amax);
     uint32_t byte, sc;
     if (amax == 0.0f) {
       byte = 0;
@@ -93,27 +126,43 @@ __device__ __forceinline__ void store_pair(const CompressArgs& a, int64_t orow, 
 }
 
 template <typename IN, int OUT, bool CSA>
-__global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
+__global__ __launch_bounds__(64) void compress_kernel(CompressArgs a) {
   const int half = a.D / 2;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)a.B * a.N * half;
-  if (gid >= total) return;
-  const int p = (int)(gid % half);
-  const int64_t row = gid / half;
+  // grid: x = channel-pair blocks of one row, y = rows (b, i) in two levels
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= half) return;
+  const int64_t row = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
+  if (row >= (int64_t)a.B * a.N) return;
   const int b = (int)(row / a.N);
-  const int i = (int)(row % a.N);
+  const int i = (int)(row - (int64_t)b * a.N);
   const int ch = 2 * p;
 
   float2 mx = make_float2(-INFINITY, -INFINITY);
   float2 den = make_float2(0.f, 0.f), num = make_float2(0.f, 0.f);
   const int64_t src0 = (int64_t)b * a.src_bstride;
-  pool_slots<IN>(reinterpret_cast<const IN*>(a.ca) + src0 * a.D,
-                 reinterpret_cast<const IN*>(a.za) + src0 * a.D, a.bias_a, (int64_t)a.m * i, a.m,
-                 a.D, ch, mx, den, num);
-  if (CSA && (a.entry0 + i) > 0)
-    pool_slots<IN>(reinterpret_cast<const IN*>(a.cb) + src0 * a.D,
-                   reinterpret_cast<const IN*>(a.zb) + src0 * a.D, a.bias_b,
-                   (int64_t)a.m * (i - 1), a.m, a.D, ch, mx, den, num);
+  const IN* ca = reinterpret_cast<const IN*>(a.ca) + src0 * a.D;
+  const IN* za = reinterpret_cast<const IN*>(a.za) + src0 * a.D;
+  const bool has_b = CSA && (a.entry0 + i) > 0;
+  if (CSA && a.m <= 8) {
+    // both series of the entry in one batch: 2m loads in flight together
+    const IN* cb = reinterpret_cast<const IN*>(a.cb) + src0 * a.D;
+    const IN* zb = reinterpret_cast<const IN*>(a.zb) + src0 * a.D;
+    float2 l[16], v[16];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      load_slot(ca, za, a.bias_a, (int64_t)a.m * i + j, j, a.D, ch, j < a.m, (int64_t)a.m * i, l[j],
+                v[j]);
+      load_slot(cb, zb, a.bias_b, (int64_t)a.m * (i - 1) + j, j, a.D, ch, has_b && j < a.m,
+                (int64_t)a.m * i, l[8 + j], v[8 + j]);
+    }
+    fold<16>(l, v, mx, den, num);
+  } else {
+    pool_slots<8, IN>(ca, za, a.bias_a, (int64_t)a.m * i, a.m, a.D, ch, mx, den, num);
+    if (has_b)
+      pool_slots<8, IN>(reinterpret_cast<const IN*>(a.cb) + src0 * a.D,
+                        reinterpret_cast<const IN*>(a.zb) + src0 * a.D, a.bias_b, (int64_t)a.m * (i - 1),
+                        a.m, a.D, ch, mx, den, num);
+  }
   float v0 = num.x / den.x, v1 = num.y / den.y;
 
   const int rope0 = a.D - a.d_rope;
@@ -148,7 +197,7 @@ __global__ __launch_bounds__(256) void compress_wide_kernel(CompressArgs a) {
   if (p < half) {
     const int per = a.m / 8;
     const int64_t src0 = (int64_t)b * a.src_bstride;
-    pool_slots<IN>(reinterpret_cast<const IN*>(a.ca) + src0 * a.D + (int64_t)sg * per * a.D,
+    pool_slots<16, IN>(reinterpret_cast<const IN*>(a.ca) + src0 * a.D + (int64_t)sg * per * a.D,
                    reinterpret_cast<const IN*>(a.za) + src0 * a.D + (int64_t)sg * per * a.D,
                    a.bias_a + (int64_t)sg * per * a.D, (int64_t)a.m * i, per, a.D, 2 * p, mx, den, num);
   }
@@ -195,8 +244,7 @@ __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const IN* x, int64_t r
   const int64_t r = gid / half;
   float2 v = io<IN>::load2(x + r * cols + 2 * p);
   float amax = fmaxf(fabsf(v.x), fabsf(v.y));
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+  amax = row16_max(amax);
   uint32_t byte, sc;
   if (amax == 0.0f) {
     byte = 0;
@@ -221,8 +269,12 @@ static int launch_compress_out(const char* name, const CompressArgs& a, int out_
       default: return launch(name, compress_wide_kernel<IN, OUT_MXFP4, CSA>, grid, block, 0, s, a);
     }
   }
-  const int64_t total = (int64_t)a.B * a.N * (a.D / 2);
-  dim3 grid((unsigned)ceil_div(total, 256)), block(256);
+  // one wave per 64 channel pairs of a row; rows over grid.y (and grid.z
+  // past 65535 rows)
+  const int64_t rows = (int64_t)a.B * a.N;
+  if (rows <= 0) return CSK_OK;
+  const unsigned gy = (unsigned)(rows < 65535 ? rows : 65535);
+  dim3 grid((unsigned)ceil_div(a.D / 2, 64), gy, (unsigned)ceil_div(rows, gy)), block(64);
   switch (out_dtype) {
     case CSK_F32: return launch(name, compress_kernel<IN, OUT_F32, CSA>, grid, block, 0, s, a);
     case CSK_BF16: return launch(name, compress_kernel<IN, OUT_BF16, CSA>, grid, block, 0, s, a);

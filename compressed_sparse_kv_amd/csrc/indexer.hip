@@ -29,6 +29,7 @@
 // keys, and L is the k-th largest of those group maxima (each is a distinct
 // element, so at least k elements are >= L). Filtering writes per-slice
 // candidate lists in index order, and the same radix select finishes.
+#include <algorithm>
 #include <mutex>
 
 #include "common.h"
@@ -38,8 +39,8 @@ namespace csk {
 constexpr int TOPK_CAP = 16384;   // elements a row select keeps in LDS
 constexpr int TOPK_THREADS = 1024;
 constexpr int SLICE = 2048;       // keys per filter workgroup
-constexpr int IDX_ITERS = 4;                        // 64-key groups per wave
-constexpr int IDX_KEYS_PER_WG = 4 * 64 * IDX_ITERS;  // 4 waves
+constexpr int IDX_MIN_ITERS = 4;      // 64-key groups per wave, at least
+constexpr int IDX_TARGET_WGS = 512;   // two resident 4-wave workgroups per CU
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -58,6 +59,7 @@ struct IdxArgs {
   float* scores;       // [R, Nmax]
   float* samples;      // [R, NG] or null
   int gs_log2, ng;
+  int iters;           // 64-key groups per wave (MFMA path; also a template value)
 };
 
 __device__ __forceinline__ int visible_count(const IdxArgs& a, int r) {
@@ -97,7 +99,9 @@ __device__ __forceinline__ void swap16(float& x, float& y) {
 __device__ __forceinline__ void write_samples(const IdxArgs& a, int r, int base, float v) {
   const int gs = 1 << a.gs_log2;
   float mx = v;
-  for (int o = 1; o < gs; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1)
+    if (o < gs) mx = fmaxf(mx, __shfl_xor(mx, o));
   const int lane = threadIdx.x & 63;
   const int key = base + lane;
   if ((lane & (gs - 1)) == 0 && key < a.Nmax)
@@ -107,19 +111,21 @@ __device__ __forceinline__ void write_samples(const IdxArgs& a, int r, int base,
 // ---------------------------------------------------------------- MFMA path
 // HT = HI/16 head tiles, KS = dI/128 MFMA K-steps. One workgroup = 4 waves
 // and one query row. Wave w handles the 64-key groups
-// base = blockIdx.y*IDX_KEYS_PER_WG + 256*it + 64*w, it < IDX_ITERS, so the
-// four waves of a workgroup stream 256 consecutive keys per iteration; the
-// next group's key fragments are loaded into registers while the current
-// group's MFMAs, transpose and head chain run.
+// base = blockIdx.y*256*ITERS + 256*it + 64*w, it < ITERS, so the four waves
+// of a workgroup stream 256 consecutive keys per iteration. Key fragments
+// rotate through three register buffers: the two groups after the current
+// one are in flight while its MFMAs, transpose and head chain run. ITERS is
+// chosen on the host so that short grids (decode: a few rows over a long
+// cache) come out at about two resident workgroups per CU.
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-template <int HT, int KS>
+template <int HT, int KS, int ITERS>
 __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
   const int r = blockIdx.x;
   const int b = r / a.T;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wg_base = blockIdx.y * IDX_KEYS_PER_WG + wave * 64;
+  const int wg_base = blockIdx.y * (256 * ITERS) + wave * 64;
   const int nv = visible_count(a, r);
   if (wg_base >= nv) return;
   const int HI = HT * 16;
@@ -139,11 +145,22 @@ __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
       qsc[t][s] = a.qs[qrow * (a.dI / 32) + s * 4 + kb];
     }
   }
-  const float* wr = a.w + (int64_t)r * HI;
+  // the row's head weights, one LDS copy per wave, read back as broadcast
+  // LDS reads (a global load here would be counted with the in-flight key
+  // loads, and waiting for it would drain them)
+  __shared__ float wsh[4][64];
+  if (lane < HI) wsh[wave][lane] = a.w[(int64_t)r * HI + lane];
+  const float* wr = wsh[wave];
 
-  v4u kv[4][KS];
-  int ksc[4][KS];
-  auto load_keys = [&](int base) {
+  // key fragments of one 64-key group: lane (rho, kb) holds bytes 16*kb..
+  // of key 16*kt + rho in each of the four key tiles kt. The loads are
+  // unconditional (keys past the cache are clamped to its last row and their
+  // scores dropped), so no load sits under a branch.
+  struct Group {
+    v4u v[4][KS];
+    int sc[4][KS];
+  };
+  auto load_keys = [&](Group& gr, int base) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       int key = base + 16 * kt + rho;
@@ -151,28 +168,14 @@ __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
       const int64_t krow = (int64_t)b * a.Nmax + key;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        kv[kt][s] = __builtin_nontemporal_load(
+        gr.v[kt][s] = __builtin_nontemporal_load(
             reinterpret_cast<const v4u*>(a.kc + krow * (a.dI / 2) + s * 64 + kb * 16));
-        ksc[kt][s] = a.ks[krow * (a.dI / 32) + s * 4 + kb];
+        gr.sc[kt][s] = a.ks[krow * (a.dI / 32) + s * 4 + kb];
       }
     }
   };
-  load_keys(wg_base);
 
-  for (int it = 0; it < IDX_ITERS; ++it) {
-    const int base = wg_base + it * 256;
-    if (base >= nv) break;
-    v4u cv[4][KS];
-    int csc[4][KS];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        cv[kt][s] = kv[kt][s];
-        csc[kt][s] = ksc[kt][s];
-      }
-    if (it + 1 < IDX_ITERS && base + 256 < nv) load_keys(base + 256);
-
+  auto process = [&](const Group& gr, int base) {
     v4f acc[4][HT];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -180,12 +183,12 @@ __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
       for (int t = 0; t < HT; ++t) acc[kt][t] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const v8i kbv = v8i{(int)cv[kt][s].x, (int)cv[kt][s].y, (int)cv[kt][s].z, (int)cv[kt][s].w,
-                            0, 0, 0, 0};
+        const v8i kbv = v8i{(int)gr.v[kt][s].x, (int)gr.v[kt][s].y, (int)gr.v[kt][s].z,
+                            (int)gr.v[kt][s].w, 0, 0, 0, 0};
 #pragma unroll
         for (int t = 0; t < HT; ++t)
           acc[kt][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              qa[t][s], kbv, acc[kt][t], 4, 4, 0, qsc[t][s], 0, csc[kt][s]);
+              qa[t][s], kbv, acc[kt][t], 4, 4, 0, qsc[t][s], 0, gr.sc[kt][s]);
       }
     }
 
@@ -209,9 +212,12 @@ __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
       }
     }
 
+    // ascending head chain; the fences keep the weight reads next to their
+    // use (hoisted together they would hold 4*HI registers)
     float score = 0.0f;
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+    for (int g = 0; g < 4; ++g) {
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int t = 0; t < HT; ++t)
 #pragma unroll
@@ -219,10 +225,25 @@ __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
           const float v = d[g][t][j];
           score = __builtin_fmaf(wr[4 * HT * g + 4 * t + j], v > 0.0f ? v : 0.0f, score);
         }
+    }
 
     const int key = base + lane;
     if (key < nv) a.scores[(int64_t)r * a.Nmax + key] = score;
     if (a.samples) write_samples(a, r, base, key < nv ? score : -INFINITY);
+  };
+
+  // fully unrolled: group it is computed while groups it+1 and it+2 are in
+  // flight; all counts are compile-time, so every wait the compiler inserts
+  // is exact
+  Group buf[3];
+#pragma unroll
+  for (int j = 0; j < 3 && j < ITERS; ++j) load_keys(buf[j], wg_base + 256 * j);
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int base = wg_base + 256 * it;
+    if (base >= nv) break;
+    process(buf[it % 3], base);
+    if (it + 3 < ITERS) load_keys(buf[it % 3], base + 3 * 256);
   }
 }
 
@@ -299,28 +320,12 @@ struct ScanShared {
 template <int NT>
 __device__ __forceinline__ int2 block_scan2(int a, int b, ScanShared& sh, int2* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = a, y = b;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int xs = __shfl_up(x, o), ys = __shfl_up(y, o);
-    if (lane >= o) {
-      x += xs;
-      y += ys;
-    }
-  }
+  const int x = wave_incl_sum(a), y = wave_incl_sum(b);
   if (lane == 63) sh.wtot[wave] = make_int2(x, y);
   __syncthreads();
   if (wave == 0) {
     const int2 w = lane < NT / 64 ? sh.wtot[lane] : make_int2(0, 0);
-    int wx = w.x, wy = w.y;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int xs = __shfl_up(wx, o), ys = __shfl_up(wy, o);
-      if (lane >= o) {
-        wx += xs;
-        wy += ys;
-      }
-    }
+    const int wx = wave_incl_sum(w.x), wy = wave_incl_sum(w.y);
     if (lane < NT / 64) sh.wtot[lane] = make_int2(wx - w.x, wy - w.y);
     if (lane == NT / 64 - 1) sh.total = make_int2(wx, wy);
   }
@@ -329,6 +334,26 @@ __device__ __forceinline__ int2 block_scan2(int a, int b, ScanShared& sh, int2* 
   *total = sh.total;
   __syncthreads();  // the shared totals may be reused by the next scan
   return make_int2(off.x + x - a, off.y + y - b);
+}
+
+// ---------------------------------------------------- LDS histogram adds
+// hist[bin] += 1 for every active lane. Keys near a top-k threshold share
+// their leading digits, so many lanes of a wave hit the same bin; same-bin
+// lanes are combined into one atomic (up to four distinct bins per call),
+// and whatever is left goes through plain per-lane atomics.
+__device__ __forceinline__ void hist_add(int* hist, uint32_t bin, bool active) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long todo = __ballot(active);
+#pragma unroll
+  for (int round = 0; round < 4; ++round) {
+    if (todo == 0ull) return;
+    const int leader = __ffsll((long long)todo) - 1;
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
+    const unsigned long long same = __ballot(active && bin == b) & todo;
+    if (lane == leader) atomicAdd(&hist[b], __popcll(same));
+    todo &= ~same;
+  }
+  if ((todo >> lane) & 1ull) atomicAdd(&hist[bin], 1);
 }
 
 // ------------------------------------------------------------ radix select
@@ -355,19 +380,17 @@ __device__ SelectState radix_select(Get get, int n, int k, SelectShared& sh) {
     const int shift = 24 - 8 * pass;
     for (int i = tid; i < 256; i += TOPK_THREADS) sh.hist[i] = 0;
     __syncthreads();
-    for (int e = tid; e < n; e += TOPK_THREADS) {
-      const uint32_t u = get(e);
-      if ((u & st.mask) == st.prefix) atomicAdd(&sh.hist[(u >> shift) & 255u], 1);
+    for (int e0 = 0; e0 < n; e0 += TOPK_THREADS) {
+      const int e = e0 + tid;
+      const uint32_t u = e < n ? get(e) : 0u;
+      hist_add(sh.hist, (u >> shift) & 255u, e < n && (u & st.mask) == st.prefix);
     }
     __syncthreads();
     if (tid < 64) {
       // lane L owns bins 4L..4L+3; suffix sums over lanes find the digit
       int s4 = sh.hist[4 * tid] + sh.hist[4 * tid + 1] + sh.hist[4 * tid + 2] + sh.hist[4 * tid + 3];
-      int suf = s4;
-      for (int o = 1; o < 64; o <<= 1) {
-        int v = __shfl_down(suf, o);
-        if (tid + o < 64) suf += v;
-      }
+      const int incl = wave_incl_sum(s4);
+      const int suf = __builtin_amdgcn_readlane(incl, 63) - incl + s4;  // sum of lanes >= tid
       // suf = sum of bins >= 4*tid; the digit lies in the highest lane with suf >= take
       const bool ok = suf >= st.take;
       const unsigned long long bal = __ballot(ok);
@@ -430,7 +453,6 @@ struct TopkArgs {
   IdxArgs ia;
   int k;
   int n_slices;
-  uint32_t* thresh;         // [R] key threshold (filtered mode)
   int* cand_cnt;            // [R, n_slices]
   float* cand_score;        // [R, Nmax]: slice f at [f*SLICE, f*SLICE+cnt)
   int* cand_idx;            // [R, Nmax]
@@ -447,75 +469,85 @@ struct TopkShared {
   int slice_off[1024 + 1];
 };
 
-// Threshold from the group maxima, in one pass: a 4096-bin histogram of
-// the top 12 key bits; the threshold is the lower edge of the bin that holds
-// the k-th largest sample, so at least k samples (and hence at least k
-// elements of the row) are >= it. 0 keeps everything when the row has at
-// most k entries or too few samples.
+// Threshold from the group maxima: a 4096-bin histogram of the top 12 key
+// bits of the samples; the threshold is the lower edge of the bin that
+// holds the k-th largest sample, so at least k samples (and hence at least
+// k elements of the row) are >= it. 0 keeps everything when the row has at
+// most k entries or too few samples. Each filter workgroup forms it for its
+// own row (the samples are a few KB, read from L2), which saves a launch.
 constexpr int THR_BINS = 4096;
+constexpr int THR_BATCH = 32;  // samples per thread per load batch
 
-__global__ __launch_bounds__(TOPK_THREADS) void topk_threshold_kernel(TopkArgs a) {
+// Candidate filter: keys of slice blockIdx.y with key(score) >= the row's
+// threshold, compacted in index order (thread t owns 8 consecutive keys).
+// Order of work: the histogram is cleared first, so that the barrier after
+// it has no loads to wait for; then the slice's scores and the row's samples
+// are loaded together (a barrier waits for every load in flight, so each
+// barrier is placed after loads that are needed anyway).
+__global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a) {
   __shared__ int hist[THR_BINS];
   __shared__ ScanShared scan;
-  __shared__ uint32_t result;
-  const int r = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int nv = visible_count(a.ia, r);
-  const int gs = 1 << a.ia.gs_log2;
-  const int ng = (nv + gs - 1) / gs;
-  if (nv <= a.k || ng < a.k) {
-    if (tid == 0) a.thresh[r] = 0u;
-    return;
-  }
-  for (int i = tid; i < THR_BINS; i += TOPK_THREADS) hist[i] = 0;
-  if (tid == 0) result = 0u;
-  __syncthreads();
-  for (int e = tid; e < ng; e += TOPK_THREADS)
-    atomicAdd(&hist[order_key(a.ia.samples[(int64_t)r * a.ia.ng + e]) >> 20], 1);
-  __syncthreads();
-  // thread t owns bin group G = 1023 - t (4 bins); an inclusive scan in
-  // thread order is then a suffix sum over bins
-  const int G = TOPK_THREADS - 1 - tid;
-  const int s4 = hist[4 * G] + hist[4 * G + 1] + hist[4 * G + 2] + hist[4 * G + 3];
-  int2 tot;
-  const int2 ex = block_scan2<TOPK_THREADS>(s4, 0, scan, &tot);
-  const int incl = ex.x + s4;
-  if (incl >= a.k && ex.x < a.k) {
-    int above = ex.x;
-    int d = 4 * G + 3;
-    for (; d > 4 * G; --d) {
-      if (above + hist[d] >= a.k) break;
-      above += hist[d];
-    }
-    result = (uint32_t)d << 20;
-  }
-  __syncthreads();
-  if (tid == 0) a.thresh[r] = result;
-}
-
-// Candidate filter: keys of slice blockIdx.y with key(score) >= thresh,
-// compacted in index order (thread t owns 8 consecutive keys).
-__global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a) {
-  __shared__ ScanShared scan;
+  __shared__ uint32_t thr_sh;
   const int r = blockIdx.x, f = blockIdx.y;
+  const int tid = threadIdx.x;
   const int nv = visible_count(a.ia, r);
   const int s0 = f * SLICE;
   if (s0 >= nv) {
-    if (threadIdx.x == 0) a.cand_cnt[(int64_t)r * a.n_slices + f] = 0;
+    if (tid == 0) a.cand_cnt[(int64_t)r * a.n_slices + f] = 0;
     return;
   }
-  const uint32_t thr = a.thresh[r];
+  const int gs = 1 << a.ia.gs_log2;
+  const int ng = (nv + gs - 1) / gs;
+  const bool thresholded = nv > a.k && ng >= a.k;
+  if (thresholded) {
+    for (int i = tid; i < THR_BINS; i += 256) hist[i] = 0;
+    if (tid == 0) thr_sh = 0u;
+    __syncthreads();
+  }
   const float* sc = a.ia.scores + (int64_t)r * a.ia.Nmax + s0;
   const int lim = min(SLICE, nv - s0);
-  const int j0 = threadIdx.x * (SLICE / 256);
+  const int j0 = tid * (SLICE / 256);
   float v[SLICE / 256];
+#pragma unroll
+  for (int i = 0; i < SLICE / 256; ++i) v[i] = sc[min(j0 + i, lim - 1)];  // unconditional
+  uint32_t thr = 0u;
+  if (thresholded) {
+    // group-maximum histogram of the top 12 key bits
+    const float* smp = a.ia.samples + (int64_t)r * a.ia.ng;
+    for (int e0 = 0; e0 < ng; e0 += 256 * THR_BATCH) {
+      float x[THR_BATCH];
+#pragma unroll
+      for (int i = 0; i < THR_BATCH; ++i) x[i] = smp[min(e0 + 256 * i + tid, ng - 1)];
+      // plain LDS atomics: the maxima spread over enough bins that this is
+      // far cheaper than combining same-bin lanes first
+#pragma unroll
+      for (int i = 0; i < THR_BATCH; ++i)
+        if (e0 + 256 * i + tid < ng) atomicAdd(&hist[order_key(x[i]) >> 20], 1);
+    }
+    __syncthreads();
+    // thread t owns bins 16*G .. 16*G+15 with G = 255 - t; an inclusive scan
+    // in thread order is then a suffix sum over bins
+    const int G = 255 - tid;
+    int s16 = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s16 += hist[16 * G + i];
+    int2 tot;
+    const int ex = block_scan2<256>(s16, 0, scan, &tot).x;
+    if (ex < a.k && ex + s16 >= a.k) {
+      int above = ex;
+      int d = 16 * G + 15;
+      for (; d > 16 * G; --d) {
+        if (above + hist[d] >= a.k) break;
+        above += hist[d];
+      }
+      thr_sh = (uint32_t)d << 20;
+    }
+    __syncthreads();
+    thr = thr_sh;
+  }
   int cnt = 0;
 #pragma unroll
-  for (int i = 0; i < SLICE / 256; ++i) {
-    const int j = j0 + i;
-    v[i] = j < lim ? sc[j] : -INFINITY;
-    cnt += (j < lim && order_key(v[i]) >= thr) ? 1 : 0;
-  }
+  for (int i = 0; i < SLICE / 256; ++i) cnt += (j0 + i < lim && order_key(v[i]) >= thr) ? 1 : 0;
   int2 tot;
   int pos = block_scan2<256>(cnt, 0, scan, &tot).x;
   float* cs = a.cand_score + (int64_t)r * a.ia.Nmax + s0;
@@ -529,7 +561,7 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a) {
       ++pos;
     }
   }
-  if (threadIdx.x == 0) a.cand_cnt[(int64_t)r * a.n_slices + f] = tot.x;
+  if (tid == 0) a.cand_cnt[(int64_t)r * a.n_slices + f] = tot.x;
 }
 
 // Final selection for one row. FILTERED = false: the row's scores
@@ -569,23 +601,43 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkArgs a) {
     if (in_lds)
       for (int e = tid; e < n; e += TOPK_THREADS) sh.key[e] = order_key(srow[e]);
   } else {
-    // element e lives in slice f with slice_off[f] <= e < slice_off[f+1]
-    for (int e = tid; e < n; e += TOPK_THREADS) {
-      int lo = 0, hi = ns - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (sh.slice_off[mid] <= e) lo = mid;
-        else hi = mid - 1;
+    // element e lives in slice f with slice_off[f] <= e < slice_off[f+1];
+    // GATHER elements per thread are located first, then all their loads
+    // are issued together
+    constexpr int GATHER = 4;
+    for (int e0 = 0; e0 < n; e0 += GATHER * TOPK_THREADS) {
+      int64_t src[GATHER];
+#pragma unroll
+      for (int i = 0; i < GATHER; ++i) {
+        const int e = e0 + i * TOPK_THREADS + tid;
+        int lo = 0, hi = ns - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (sh.slice_off[mid] <= e) lo = mid;
+          else hi = mid - 1;
+        }
+        // past the end: a valid element is read and dropped below
+        src[i] = (int64_t)r * a.ia.Nmax + (e < n ? (int64_t)lo * SLICE + (e - sh.slice_off[lo]) : 0);
       }
-      const int64_t src = (int64_t)r * a.ia.Nmax + (int64_t)lo * SLICE + (e - sh.slice_off[lo]);
-      const uint32_t u = order_key(a.cand_score[src]);
-      const int ix = a.cand_idx[src];
-      if (in_lds) {
-        sh.key[e] = u;
-        sh.eidx[e] = ix;
-      } else {
-        gkey[e] = u;
-        gidx[e] = ix;
+      float sv[GATHER];
+      int iv[GATHER];
+#pragma unroll
+      for (int i = 0; i < GATHER; ++i) {
+        sv[i] = a.cand_score[src[i]];
+        iv[i] = a.cand_idx[src[i]];
+      }
+#pragma unroll
+      for (int i = 0; i < GATHER; ++i) {
+        const int e = e0 + i * TOPK_THREADS + tid;
+        if (e >= n) continue;
+        const uint32_t u = order_key(sv[i]);
+        if (in_lds) {
+          sh.key[e] = u;
+          sh.eidx[e] = iv[i];
+        } else {
+          gkey[e] = u;
+          gidx[e] = iv[i];
+        }
       }
     }
   }
@@ -624,7 +676,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkArgs a) {
 struct IdxPlan {
   bool filtered;
   int gs_log2, ng, n_slices;
-  size_t off_scores, off_samples, off_thresh, off_cnt, off_cscore, off_cidx, off_fkey, off_fidx,
+  size_t off_scores, off_samples, off_cnt, off_cscore, off_cidx, off_fkey, off_fidx,
       total;
 };
 
@@ -646,7 +698,6 @@ static IdxPlan plan_indexer(int B, int T, int Nmax, int k) {
   p.off_scores = o; o = align_up(o + R * Nmax * 4);
   if (p.filtered) {
     p.off_samples = o; o = align_up(o + R * p.ng * 4);
-    p.off_thresh = o; o = align_up(o + R * 4);
     p.off_cnt = o; o = align_up(o + R * p.n_slices * 4);
     p.off_cscore = o; o = align_up(o + R * Nmax * 4);
     p.off_cidx = o; o = align_up(o + R * Nmax * 4);
@@ -681,7 +732,7 @@ int indexer_topk(const void* q, const uint8_t* q_scale, const float* w, const vo
     return fail(CSK_EUNSUPPORTED, "indexer_topk: dtype must be CSK_MXFP4 or CSK_F32");
   if (dtype == CSK_MXFP4 && (dI % 32 || !q_scale || !k_scale))
     return fail(CSK_EINVAL, "indexer_topk: MXFP4 needs dI % 32 == 0 and both scale arrays");
-  if ((int64_t)B * T > (1LL << 30) || ceil_div(Nmax, IDX_KEYS_PER_WG) > 65535)
+  if ((int64_t)B * T > (1LL << 30) || ceil_div(Nmax, 256 * IDX_MIN_ITERS) > 65535)
     return fail(CSK_EUNSUPPORTED, "indexer_topk: B*T or Nmax too large");
   IdxPlan p = plan_indexer(B, T, Nmax, k);
   if (p.n_slices > 1024) return fail(CSK_EUNSUPPORTED, "indexer_topk: Nmax too large");
@@ -710,11 +761,17 @@ int indexer_topk(const void* q, const uint8_t* q_scale, const float* w, const vo
   int rc = CSK_OK;
   const bool mfma = dtype == CSK_MXFP4 && HI % 16 == 0 && HI <= 64 && dI % 128 == 0 && dI <= 256;
   if (mfma) {
-    dim3 grid((unsigned)R, (unsigned)ceil_div(Nmax, IDX_KEYS_PER_WG)), block(256);
+    // 64-key groups per wave: 8 when the grid is short (a few rows over a
+    // long cache: it then still has about two workgroups per CU), else 4
+    const int64_t groups = (int64_t)R * ceil_div(Nmax, 256);
+    const int iters = groups >= 8 * IDX_TARGET_WGS ? 8 : 4;
+    ia.iters = iters;
+    dim3 grid((unsigned)R, (unsigned)ceil_div(Nmax, 256 * iters)), block(256);
     const int HT = HI / 16, KS = dI / 128;
-#define CSK_IDX_CASE(ht, ks)                                                                 \
-  if (HT == ht && KS == ks) rc = launch("indexer_scores_fp4", idx_fp4_kernel<ht, ks>, grid, \
-                                        block, 0, s, ia);
+#define CSK_IDX_CASE(ht, ks)                                                                     \
+  if (HT == ht && KS == ks)                                                                      \
+    rc = iters == 8 ? launch("indexer_scores_fp4", idx_fp4_kernel<ht, ks, 8>, grid, block, 0, s, ia) \
+                    : launch("indexer_scores_fp4", idx_fp4_kernel<ht, ks, 4>, grid, block, 0, s, ia);
     CSK_IDX_CASE(1, 1) CSK_IDX_CASE(2, 1) CSK_IDX_CASE(3, 1) CSK_IDX_CASE(4, 1)
     CSK_IDX_CASE(1, 2) CSK_IDX_CASE(2, 2) CSK_IDX_CASE(3, 2) CSK_IDX_CASE(4, 2)
 #undef CSK_IDX_CASE
@@ -744,15 +801,12 @@ int indexer_topk(const void* q, const uint8_t* q_scale, const float* w, const vo
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   });
   if (p.filtered) {
-    ta.thresh = reinterpret_cast<uint32_t*>(ws + p.off_thresh);
     ta.cand_cnt = reinterpret_cast<int*>(ws + p.off_cnt);
     ta.cand_score = reinterpret_cast<float*>(ws + p.off_cscore);
     ta.cand_idx = reinterpret_cast<int*>(ws + p.off_cidx);
     ta.flat_key = reinterpret_cast<uint32_t*>(ws + p.off_fkey);
     ta.flat_idx = reinterpret_cast<int*>(ws + p.off_fidx);
-    rc = launch("topk_threshold", topk_threshold_kernel, dim3(R), dim3(TOPK_THREADS), 0, s, ta);
-    if (rc == CSK_OK)
-      rc = launch("topk_filter", topk_filter_kernel, dim3(R, p.n_slices), dim3(256), 0, s, ta);
+    rc = launch("topk_filter", topk_filter_kernel, dim3(R, p.n_slices), dim3(256), 0, s, ta);
     if (rc == CSK_OK)
       rc = launch("topk_select", topk_select_kernel<true>, dim3(R), dim3(TOPK_THREADS), lds, s, ta);
   } else {
