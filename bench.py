@@ -15,11 +15,12 @@ the whole hot path for one new token per sequence:
   6. hca_compress  - the newest HCA entry (128 source tokens)
   7. dense_compressed_attn - HCA attention over all 8192 entries + window + sink
 The calls run on three streams as the data flow allows (1, 6, 7 on one; 3
-on another; 2, 4, 5 on the main stream after the entries they read). The
-timed steps are eager launches by default (--mode graph replays one
-captured HIP graph per step instead). Four copies of the layer-pair state rotate between
-steps (as successive layers would), so a step never finds its 121 MB working
-set in the 256 MB Infinity Cache from the previous step.
+on another; 2, 4, 5 on the main stream after the entries they read;
+--streams 1 runs them in order on one stream). The timed steps are HIP graph
+replays, four steps per graph (--mode eager launches them directly). Four
+copies of the layer-pair state rotate between steps (as successive layers
+would), so a step never finds its 121 MB working set in the 256 MB Infinity
+Cache from the previous step.
 
 Prints one JSON line with the throughput, a roofline record of the dominant
 kernel (timed with HIP events around each of its launches inside the timed
@@ -50,7 +51,7 @@ class DecodeWorkload:
     """Decode-step state on the GPU for 'decode_1m_pair' (CSA + HCA) or
     'csa_decode_128k' (CSA only), with host copies for the oracle."""
 
-    def __init__(self, name, copies=4, overrides=None, keep_host=True):
+    def __init__(self, name, copies=4, overrides=None, keep_host=True, streams=1):
         import torch
 
         import compressed_sparse_kv_amd as csk
@@ -100,6 +101,16 @@ class DecodeWorkload:
             self.Nh = d["kv_h"].shape[1]
             for k in ("q_h", "n_entries_h", "sink_h", "src_c", "src_z", "bias_h"):
                 self.x[k] = T(d[k])
+        # views used by every step, formed once: the newest block of the
+        # source windows and the cache rows the step writes
+        for k in ("ca", "za", "cb", "zb", "ia", "iza", "ib", "izb"):
+            self.x[f"src_{k}4"] = self.x[f"src_{k}"][:, 4:]
+        for st in self.copies:
+            st["kv_new"] = st["kv_c"][:, self.N - 1:]
+            st["kc_new"] = st["kc"][:, self.N - 1:]
+            st["ks_new"] = st["ks"][:, self.N - 1:]
+            if self.pair:
+                st["kvh_new"] = st["kv_h"][:, self.Nh - 1:]
         # outputs and workspaces, allocated once (graph capture needs fixed addresses)
         B, H, dv, k = self.B, self.H, self.dv, self.k
         self.qc = torch.empty((B, 1, self.HI, self.dI // 2), dtype=torch.uint8, device=dev)
@@ -120,6 +131,7 @@ class DecodeWorkload:
             self.ws_d = torch.empty(max(ws_d, 1), dtype=torch.uint8, device=dev)
         # extra streams (default priority) and the event that hands the
         # newest KV entry from the side stream to the sparse attention
+        self.streams = streams
         self.side = torch.cuda.Stream()
         self.qstream = torch.cuda.Stream()
         self.ev_kv = torch.cuda.Event()
@@ -131,45 +143,58 @@ class DecodeWorkload:
 
     # ------------------------------------------------------------- one step
     def step(self, c=0):
-        """One decode step over three streams, following the data flow:
-        the side stream computes the newest CSA KV entry (needed only by the
-        sparse attention) and then the whole HCA branch; a second stream
-        encodes the indexer queries; the main stream computes the newest
-        indexer key, scores and selects, and runs the sparse attention."""
+        """One decode step. With one stream (default) the calls run in data
+        flow order on torch's current stream. With three streams the side
+        stream computes the newest CSA KV entry (needed only by the sparse
+        attention) and then the whole HCA branch, a second stream encodes the
+        indexer queries, and the main stream computes the newest indexer
+        key, scores and selects, and runs the sparse attention."""
         torch, csk, x, st = self.torch, self.csk, self.x, self.copies[c % len(self.copies)]
-        B, N, D, dI = self.B, self.N, self.D, self.dI
+        B, N = self.B, self.N
         main = torch.cuda.current_stream()
-        side, qs = self.side, self.qstream
-        side.wait_stream(main)
-        qs.wait_stream(main)
+        multi = self.streams > 1
+        side, qs = (self.side, self.qstream) if multi else (main, main)
+        if multi:
+            side.wait_stream(main)
+            qs.wait_stream(main)
         with torch.cuda.stream(side):
             # the newest CSA entry N-1 (a-block = source rows 4..7, previous
             # block = rows 0..3 of the 8-token window)
-            csk.csa_compress(x["src_ca"][:, 4:], x["src_za"][:, 4:], x["src_cb"][:, 4:], x["src_zb"][:, 4:],
+            csk.csa_compress(x["src_ca4"], x["src_za4"], x["src_cb4"], x["src_zb4"],
                              x["bias_a"], x["bias_b"], 4, d_rope=64, entry0=N - 1, src_bstride=8,
-                             out=st["kv_c"][:, N - 1:], dst_bstride=N, S=4, B=B)
-            self.ev_kv.record(side)
-            if self.pair:
-                Nh = self.Nh
-                csk.hca_compress(x["src_c"], x["src_z"], x["bias_h"], 128, d_rope=64, entry0=Nh - 1,
-                                 out=st["kv_h"][:, Nh - 1:], dst_bstride=Nh)
-                csk.dense_compressed_attn(x["q_h"], x["q_pos"], st["kv_h"], x["n_entries_h"], 128, st["kv_w_h"],
-                                          x["w_pos0"], self.W, x["sink_h"], self.dv, 64, self.scale, out=self.out_h,
-                                          lse=self.lse_h, workspace=self.ws_d)
+                             out=st["kv_new"], dst_bstride=N, S=4, B=B)
+            if multi:
+                self.ev_kv.record(side)
+            if self.pair and multi:
+                self._hca(x, st)
         with torch.cuda.stream(qs):
             csk.mxfp4_quantize(x["qI"], self.qc, self.qs)
         # the newest indexer key, MXFP4
-        csk.csa_compress(x["src_ia"][:, 4:], x["src_iza"][:, 4:], x["src_ib"][:, 4:], x["src_izb"][:, 4:],
+        csk.csa_compress(x["src_ia4"], x["src_iza4"], x["src_ib4"], x["src_izb4"],
                          x["ibias_a"], x["ibias_b"], 4, entry0=N - 1, src_bstride=8, out_dtype=csk.CSK_MXFP4,
-                         out=st["kc"][:, N - 1:], out_scale=st["ks"][:, N - 1:], dst_bstride=N, S=4, B=B)
-        main.wait_stream(qs)
+                         out=st["kc_new"], out_scale=st["ks_new"], dst_bstride=N, S=4, B=B)
+        if multi:
+            main.wait_stream(qs)
         csk.indexer_topk(self.qc, x["w"], st["kc"], x["q_pos"], x["n_entries"], 4, self.k, q_scale=self.qs,
                          k_scale=st["ks"], idx=self.idx, score=self.score, workspace=self.ws_i)
-        main.wait_event(self.ev_kv)
+        if multi:
+            main.wait_event(self.ev_kv)
         csk.sparse_attn(x["q"], x["q_pos"], st["kv_c"], self.idx, st["kv_w"], x["w_pos0"], self.W, x["sink"],
                         self.dv, 64, self.scale, out=self.out, lse=self.lse,
                         workspace=self.ws_s)
-        main.wait_stream(side)
+        if self.pair and not multi:
+            self._hca(x, st)
+        if multi:
+            main.wait_stream(side)
+
+    def _hca(self, x, st):
+        """The HCA branch: the newest HCA entry, then dense attention."""
+        csk, Nh = self.csk, self.Nh
+        csk.hca_compress(x["src_c"], x["src_z"], x["bias_h"], 128, d_rope=64, entry0=Nh - 1,
+                         out=st["kvh_new"], dst_bstride=Nh)
+        csk.dense_compressed_attn(x["q_h"], x["q_pos"], st["kv_h"], x["n_entries_h"], 128, st["kv_w_h"],
+                                  x["w_pos0"], self.W, x["sink_h"], self.dv, 64, self.scale, out=self.out_h,
+                                  lse=self.lse_h, workspace=self.ws_d)
 
     def kernels(self):
         names = ["csa_compress", "mxfp4_quantize", "indexer_scores_fp4", "topk_filter",
@@ -264,7 +289,7 @@ def run(args):
 
     import compressed_sparse_kv_amd as csk
 
-    wl = DecodeWorkload(args.workload, copies=args.copies)
+    wl = DecodeWorkload(args.workload, copies=args.copies, streams=args.streams)
     K, Wm = args.steps, args.warmup
     # eager warm-up (first calls set kernel attributes outside any capture)
     for i in range(max(Wm, 1)):
@@ -286,43 +311,46 @@ def run(args):
          ", ".join(f"{n}={v[0]*1e3:.1f}us x{v[1]:g}" for n, v in per.items()))
     dom = max((n for n in per if wl.algorithmic_bytes(n)), key=lambda n: per[n][0] * per[n][1])
 
+    # roofline timing: K eager steps with a HIP event pair around each launch
+    # of the dominant kernel on its own stream (event pairs captured inside
+    # a graph do not bracket the kernel tightly on this runtime, so they are
+    # not used)
     timer = csk.KernelTimer(dom, K)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        wl.step(i)
+    t_host = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    eager_elapsed = time.perf_counter() - t0
+    if timer.count() != K:
+        raise RuntimeError(f"kernel timer recorded {timer.count()} of {K} launches")
+    timer.disarm()
+    _log(f"eager steps: {eager_elapsed * 1e6 / K:.1f} us/step (host enqueue {t_host * 1e6 / K:.1f} us/step)")
+
     if args.mode == "graph":
-        # one graph per timed step, each with its own event pair around the
-        # dominant kernel
+        # the K timed steps captured G per graph (as a model's layers would
+        # be) and replayed
+        G = max(1, min(args.graph_steps, K))
         graphs = []
         cap_stream = torch.cuda.Stream()
-        for i in range(K):
+        for g0 in range(0, K, G):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap_stream):
-                wl.step(i)
+                for i in range(g0, min(K, g0 + G)):
+                    wl.step(i)
             graphs.append(g)
         torch.cuda.synchronize()
-        if timer.count() != K:
-            raise RuntimeError(f"kernel timer recorded {timer.count()} of {K} launches")
-        timer.disarm()
-        for i in range(Wm):  # warm replays
-            graphs[i % K].replay()
+        for i in range(max(1, -(-Wm // G))):  # warm replays
+            graphs[i % len(graphs)].replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(K):
-            graphs[i].replay()
+        for g in graphs:
+            g.replay()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
     else:
-        # eager launches: the host runs ahead of the GPU, and the event pair
-        # around each launch of the dominant kernel sits on its own stream
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(K):
-            wl.step(i)
-        t_host = time.perf_counter() - t0
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
-        _log(f"host enqueue {t_host * 1e6 / K:.1f} us/step")
-        if timer.count() != K:
-            raise RuntimeError(f"kernel timer recorded {timer.count()} of {K} launches")
-        timer.disarm()
+        elapsed = eager_elapsed
     ms_per_step = elapsed * 1e3 / K
     tokens = wl.B * K
     value = tokens / elapsed
@@ -346,7 +374,7 @@ def run(args):
         "vs_baseline": None,
         "dtype": "bf16+mxfp4",
         "data": "synthetic",
-        "config": dict(wl.config(), launch=args.mode),
+        "config": dict(wl.config(), launch=args.mode, streams=args.streams),
         "roofline": {
             "kernel": dom,
             "bound": "hbm",
@@ -357,6 +385,7 @@ def run(args):
             "traffic": None,
             "algorithmic_bytes": abytes,
             "avg_launch_us": round(avg_ms * 1e3, 2),
+            "timing": "HIP events around each launch on its stream, K eager steps",
             "step_hbm_frac": round(wl.step_bytes() / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         },
     }
@@ -387,8 +416,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_1m_pair", choices=["decode_1m_pair", "csa_decode_128k"])
     ap.add_argument("--copies", type=int, default=4)
-    ap.add_argument("--mode", default="eager", choices=["eager", "graph"],
-                    help="timed steps as eager launches or as HIP graph replays")
+    ap.add_argument("--mode", default="graph", choices=["eager", "graph"],
+                    help="timed steps as HIP graph replays (default) or as eager launches")
+    ap.add_argument("--graph-steps", type=int, default=4, help="steps captured per graph")
+    ap.add_argument("--streams", type=int, default=3, choices=[1, 3],
+                    help="1: every call on one stream; 3: the data-flow split over three streams")
     ap.add_argument("--cpu-rows", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()

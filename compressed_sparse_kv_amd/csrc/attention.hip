@@ -363,36 +363,45 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
-// ------------------------------------------------------- bf16 MFMA, LDS DMA
-// Same math as attn_bf16_kernel, but the candidate rows are copied straight
-// from HBM into LDS with global_load_lds_dwordx4 (no register staging),
-// three tiles deep: while tile t is computed, tiles t+1 and t+2 are in
-// flight (tile t+2 is issued right after tile t's reads). Each wave-level
-// DMA instruction fills one contiguous 1 KB block;
-// a stage holds 32 rows in column-major 16-byte units (unit = chunk*32 +
-// row), so block b carries chunks 2b and 2b+1 of all 32 rows. Waits on the
-// DMAs are explicit (vmcnt), and raw s_barrier is fenced against compiler
-// code motion, because a __syncthreads() would wait for every DMA in flight.
+// 16-byte LDS DMA of one lane: src -> lds_base + 16 * lane. (Kept in a
+// device function: a kernel body that names this builtin directly is
+// dropped from the host compilation pass, and its launch stub with it.)
+__device__ __forceinline__ void lds_dma16(const void* src, uint4* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+
+// s_waitcnt immediate: vmcnt(n), lgkmcnt(0), expcnt unchanged
 #define CSK_VMCNT_LGKM0(n) ((((n) & 0xF) | ((((n) >> 4) & 0x3) << 14)) | (0x7 << 4))
 
-// DENSE only separates the kernel symbols of the two entry points (so that
-// profiles tell them apart); the code paths are chosen at run time.
+// ------------------------------------------------- bf16 MFMA, whole chunk
+// One workgroup = one query row and a chunk of CHUNK_TILES*32 candidates,
+// all of which are resident in LDS at once (4 x 32 x 576 bf16 = 144 KB).
+//   1. q fragments are loaded first, the row codes and the RoPE cos/sin
+//      table next (one barrier for all of them);
+//   2. every KV row of the chunk is requested with LDS DMA in one burst, so
+//      all of the chunk's memory traffic is in flight together;
+//   3. S = q.k for all candidates stays in registers; the softmax of each
+//      head is then exact over the chunk (one maximum, no rescaling of the
+//      accumulators as tiles arrive);
+//   4. O^T += V^T P^T over the chunk, V^T fragments from transpose reads.
+// Each tile is 32 rows in column-major 16-byte units (unit = chunk*32 +
+// row); one wave-level DMA instruction fills a 1 KB block of a tile (chunks
+// 2b and 2b+1 of its 32 rows). Waves own 16 heads each (MFMA columns).
+constexpr int CHUNK_TILES = 4;
+constexpr int CHUNK_CANDS = 32 * CHUNK_TILES;
+
 template <int D, int DV, int NW, bool DENSE>
-__global__ __launch_bounds__(64 * NW) void attn_bf16_dma_kernel(AttnArgs a) {
-  constexpr int KS = D / 32;
-  constexpr int DT = DV / 16;
-  constexpr int CPR = D / 8;            // 16-byte chunks per KV row
-  constexpr int NT = 64 * NW;
-  constexpr int BLK = CPR / 2;          // 1 KB DMA blocks per 32-row tile
-  constexpr int BPW = BLK / NW;         // DMA instructions per wave per tile
-  constexpr int STAGE = 32 * CPR;       // 16-byte units per stage
-  static_assert(BLK % NW == 0, "DMA blocks must split evenly over the waves");
-  // three distinct arrays (not one indexed array): the compiler can then
-  // tell a stage being read from the stages the DMAs are filling
-  __shared__ __align__(16) uint4 stg0[STAGE];
-  __shared__ __align__(16) uint4 stg1[STAGE];
-  __shared__ __align__(16) uint4 stg2[STAGE];
-  __shared__ int codes[MAX_CHUNK];
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_bf16_chunk_kernel(AttnArgs a) {
+  constexpr int KS = D / 32;            // MFMA K-steps over the key dims
+  constexpr int DT = DV / 16;           // 16-row tiles of the value dims
+  constexpr int TU = 32 * D / 8;        // 16-byte units per tile
+  constexpr int BLK = D / 16;           // 1 KB DMA blocks per tile
+  constexpr int NB = CHUNK_TILES * BLK;
+  static_assert(NB % NW == 0, "DMA blocks must split evenly over the waves");
+  __shared__ __align__(16) uint4 kvs[CHUNK_TILES * TU];
+  __shared__ __align__(16) int codes[CHUNK_CANDS];
+  __shared__ float2 rtab[MAX_ROPE_PAIRS];
 
   const int r = blockIdx.x;
   const int chunk_id = blockIdx.y;
@@ -404,35 +413,56 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_dma_kernel(AttnArgs a) {
   const RowInfo ri = row_info(a, r);
   const uint16_t* kvc = reinterpret_cast<const uint16_t*>(a.kv_c) + (int64_t)ri.b * a.Nmax * D;
   const uint16_t* kvw = reinterpret_cast<const uint16_t*>(a.kv_w) + (int64_t)ri.b * a.S_w * D;
-
   const int total = a.Lc + a.W;
-  const int c0 = chunk_id * a.chunk;
-  const int nc = min(a.chunk, total - c0);
-  const int ntiles = (nc + 31) / 32;
-  for (int j = tid; j < nc; j += NT) codes[j] = slot_code(a, ri, r, c0 + j);
-  // an ordinary store into the staging buffer: the DMA intrinsic is not seen
-  // as a writer of it, and without one the reads below could be folded away
-  stg0[tid] = make_uint4(0u, 0u, 0u, 0u);
-  stg1[tid] = make_uint4(0u, 0u, 0u, 0u);
-  stg2[tid] = make_uint4(0u, 0u, 0u, 0u);
-  __shared__ float2 rtab[MAX_ROPE_PAIRS];
+  const int c0 = chunk_id * CHUNK_CANDS;
+  const int nc = min(CHUNK_CANDS, total - c0);
+
+  // 1. q fragments (dims 32*ks + 8*g .. +7 of head h), codes, RoPE table
+  uint4 qraw[KS];
+  {
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qraw[ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g);
+  }
+  for (int j = tid; j < CHUNK_CANDS; j += 64 * NW) codes[j] = j < nc ? slot_code(a, ri, r, c0 + j) : -1;
   if (tid < a.d_rope / 2) {
     float cs, sn;
     rope_cs((double)ri.p, a.rope.theta[tid], &cs, &sn);
     rtab[tid] = make_float2(cs, sn);
   }
+  // an ordinary store into the KV buffer: the DMA intrinsic is not seen as
+  // a writer of it, and without one the reads below could be folded away
+  kvs[tid] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
 
+  // 2. one burst of DMA for the whole chunk; empty slots read row 0 of the
+  // cache (finite data, weight 0)
+  {
+    // the lane's row in each tile, read once
+    const int row = lane & 31;
+    const uint16_t* src[CHUNK_TILES];
+#pragma unroll
+    for (int t = 0; t < CHUNK_TILES; ++t) {
+      const int code = codes[t * 32 + row];
+      src[t] = code >= 0 ? kvc + (int64_t)code * D : (code <= -2 ? kvw + (int64_t)(-2 - code) * D : kvc);
+    }
+#pragma unroll
+    for (int q = 0; q < NB / NW; ++q) {
+      const int blk = wave + NW * q;
+      const int t = blk / BLK, b = blk - t * BLK;
+      lds_dma16(src[t] + 8 * (2 * b + (lane >> 5)), kvs + t * TU + b * 64);
+    }
+  }
+
+  // rotated query fragments as bf16 (while the DMA is in flight)
   v8bf qf[KS];
   {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + h) * D;
     const int rope0 = D - a.d_rope;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int d0 = 32 * ks + 8 * g;
-      const uint4 raw = *reinterpret_cast<const uint4*>(qrow + d0);
       float x[8];
-      const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+      const uint32_t wv[4] = {qraw[ks].x, qraw[ks].y, qraw[ks].z, qraw[ks].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         x[2 * i] = bf16_bits_to_f32(wv[i] & 0xffffu);
@@ -444,10 +474,9 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_dma_kernel(AttnArgs a) {
           const int c = d0 + 2 * i;
           if (c >= rope0) {
             const float2 csn = rtab[(c - rope0) / 2];
-            const float cs = csn.x, sn = csn.y;
             const float x0 = x[2 * i], x1 = x[2 * i + 1];
-            x[2 * i] = x0 * cs - x1 * sn;
-            x[2 * i + 1] = x0 * sn + x1 * cs;
+            x[2 * i] = x0 * csn.x - x1 * csn.y;
+            x[2 * i + 1] = x0 * csn.y + x1 * csn.x;
           }
         }
       }
@@ -455,144 +484,132 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_dma_kernel(AttnArgs a) {
       for (int i = 0; i < 8; ++i) qf[ks][i] = __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_bits(x[i]));
     }
   }
-  __syncthreads();  // codes and the staging store are complete; no DMA issued yet
+  // every wave's DMA has landed (each waits for its own, then the barrier)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(CSK_VMCNT_LGKM0(0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 
-  // DMA of tile t into stage s: lane i of block b loads chunk 2b + i/32 of
-  // row i%32. Empty slots read row 0 of the cache (finite data, weight 0).
-  auto issue = [&](int t, uint4* dst) {
-    const int row = lane & 31;
-    const int j = t * 32 + row;
-    const int code = j < nc ? codes[j] : -1;
-    const uint16_t* src = code >= 0 ? kvc + (int64_t)code * D : (code <= -2 ? kvw + (int64_t)(-2 - code) * D : kvc);
-#pragma unroll
-    for (int q = 0; q < BPW; ++q) {
-      const int blk = wave + NW * q;
-      const int cc = 2 * blk + (lane >> 5);
-      __builtin_amdgcn_global_load_lds(src + 8 * cc, dst + blk * 64, 16, 0, 0);
-    }
-  };
-
-  v4f acc[DT];
-#pragma unroll
-  for (int t = 0; t < DT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_part = 0.f;
+  const int ntiles = (nc + 31) / 32;
   const float sl2 = a.scale * LOG2E;
 
-  // compute of one tile from a staged buffer
-  auto process = [&](const uint4* sb, int t) {
-    const uint16_t* sb16 = reinterpret_cast<const uint16_t*>(sb);
-    v4f sc[2];
+  // 3. scores of all candidates (lane holds candidates 32t + 16ct + 4g + i)
+  v4f sc[CHUNK_TILES][2];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      sc[ct] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < CHUNK_TILES; ++t) {
+    sc[t][0] = sc[t][1] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (t < ntiles) {
+      // fragments in blocks of QB K-steps, the next block's reads issued
+      // before the current block's MFMAs (the scheduling barriers keep that
+      // order; left alone, the scheduler keeps one read in flight)
+      const uint4* sb = kvs + t * TU;
+      constexpr int QB = 3, NQB = (KS + QB - 1) / QB;
+      v8bf kf[2][QB][2];
+      auto load_q = [&](int blk, v8bf (&dst)[QB][2]) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const v8bf kfrag = *reinterpret_cast<const v8bf*>(&sb[(4 * ks + g) * 32 + ct * 16 + col]);
-        sc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qf[ks], sc[ct], 0, 0, 0);
+        for (int u = 0; u < QB; ++u) {
+          const int ks = blk * QB + u;
+          if (ks < KS)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+              dst[u][ct] = *reinterpret_cast<const v8bf*>(&sb[(4 * ks + g) * 32 + ct * 16 + col]);
+        }
+      };
+      load_q(0, kf[0]);
+#pragma unroll
+      for (int blk = 0; blk < NQB; ++blk) {
+        if (blk + 1 < NQB) load_q(blk + 1, kf[(blk + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < QB; ++u) {
+          const int ks = blk * QB + u;
+          if (ks < KS)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+              sc[t][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[blk & 1][u][ct], qf[ks], sc[t][ct], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    float p[8];
-    float tmax = -INFINITY;
+  }
+  // the lane's 32 candidates are 4 consecutive codes per (tile, half):
+  // eight vector reads, then the mask is register arithmetic
+  int4 cd[CHUNK_TILES][2];
+#pragma unroll
+  for (int t = 0; t < CHUNK_TILES; ++t)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) cd[t][ct] = *reinterpret_cast<const int4*>(&codes[32 * t + 16 * ct + 4 * g]);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < CHUNK_TILES; ++t)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int c4[4] = {cd[t][ct].x, cd[t][ct].y, cd[t][ct].z, cd[t][ct].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // codes of slots past nc are -1 (set in the prologue)
+        const float v = c4[i] != -1 ? sc[t][ct][i] * sl2 : -INFINITY;
+        sc[t][ct][i] = v;
+        mx = fmaxf(mx, v);
+      }
+    }
+  mx = group4_max(mx);
+  float l_part = 0.f;
+  v8bf pf[CHUNK_TILES];
+#pragma unroll
+  for (int t = 0; t < CHUNK_TILES; ++t)
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = t * 32 + ct * 16 + 4 * g + i;
-        const bool ok = j < nc && codes[j] != -1;
-        const float v = ok ? sc[ct][i] * sl2 : -INFINITY;
-        p[ct * 4 + i] = v;
-        tmax = fmaxf(tmax, v);
+        const float pv = mx == -INFINITY ? 0.f : exp2f(sc[t][ct][i] - mx);
+        l_part += pv;
+        pf[t][4 * ct + i] = __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_bits(pv));
       }
-    tmax = group4_max(tmax);
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = (m_new == -INFINITY) ? 0.f : exp2f(p[i] - m_new);
-      psum += p[i];
-    }
-    l_part = l_part * alpha + psum;
-    m_run = m_new;
-    v8bf pf;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pf[i] = __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_bits(p[i]));
+  const float l_tot = group4_sum(l_part);
 
-    // rescale only when some head's running max moved
-    if (__ballot(alpha != 1.0f) != 0ull) {
+  // 4. O^T += V^T P^T over the chunk
+  v4f acc[DT];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
-    }
-    // stage units are 16-byte (8-dim) chunks, unit = chunk*32 + candidate
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int dvb = 16 * dt + 4 * (col & 3);
-      const uint16_t* p0 = sb16 + ((dvb >> 3) * 32 + 4 * g + (col >> 2)) * 8 + (dvb & 7);
-      const v8bf vf = vt_fragment(p0, p0 + 16 * 8);
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc[dt], 0, 0, 0);
-    }
-  };
-  // wait until this wave's DMAs for the tile about to be read are done (at
-  // most `pending` newer ones may remain), then barrier so every wave's part
-  // has landed; the fences keep the compiler from moving memory accesses
-  // across the raw barrier
-#define CSK_STAGE_SYNC(pending)                                            \
-  do {                                                                     \
-    asm volatile("" ::: "memory");                                         \
-    if (pending) __builtin_amdgcn_s_waitcnt(CSK_VMCNT_LGKM0(BPW));         \
-    else __builtin_amdgcn_s_waitcnt(CSK_VMCNT_LGKM0(0));                   \
-    __builtin_amdgcn_s_barrier();                                          \
-    asm volatile("" ::: "memory");                                         \
-  } while (0)
-  // tile t+2 is issued right after tile t's reads: its stage was last read
-  // in tile t-1, which every wave finished before tile t's barrier
-#define CSK_STAGE_ISSUE(tt, dst)              \
-  do {                                        \
-    asm volatile("" ::: "memory");            \
-    if ((tt) < ntiles) issue((tt), (dst));    \
-  } while (0)
-
-  // the first two tiles go through registers and ordinary LDS stores, so
-  // that each stage has a single DMA issue site in the loop (the compiler's
-  // DMA tracking then keeps the stages apart and adds no waits of its own)
-  auto fill = [&](int t, uint4* dst) {
-    const int row = lane & 31;
-    const int j = t * 32 + row;
-    const int code = j < nc ? codes[j] : -1;
-    const uint16_t* src = code >= 0 ? kvc + (int64_t)code * D : (code <= -2 ? kvw + (int64_t)(-2 - code) * D : kvc);
+  for (int t = 0; t < CHUNK_TILES; ++t) {
+    if (t < ntiles) {
+      // V^T fragments in blocks of VB value tiles, pipelined like the QK
+      // fragments
+      const uint16_t* sb16 = reinterpret_cast<const uint16_t*>(kvs + t * TU);
+      constexpr int VB = 4, NVB = (DT + VB - 1) / VB;
+      v8bf vf[2][VB];
+      auto load_v = [&](int blk, v8bf (&dst)[VB]) {
 #pragma unroll
-    for (int q = 0; q < BPW; ++q) {
-      const int blk = wave + NW * q;
-      dst[blk * 64 + lane] = *reinterpret_cast<const uint4*>(src + 8 * (2 * blk + (lane >> 5)));
+        for (int u = 0; u < VB; ++u) {
+          const int dt = blk * VB + u;
+          if (dt < DT) {
+            const int dvb = 16 * dt + 4 * (col & 3);
+            const uint16_t* p0 = sb16 + ((dvb >> 3) * 32 + 4 * g + (col >> 2)) * 8 + (dvb & 7);
+            dst[u] = vt_fragment(p0, p0 + 16 * 8);
+          }
+        }
+      };
+      load_v(0, vf[0]);
+#pragma unroll
+      for (int blk = 0; blk < NVB; ++blk) {
+        if (blk + 1 < NVB) load_v(blk + 1, vf[(blk + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < VB; ++u) {
+          const int dt = blk * VB + u;
+          if (dt < DT) acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[blk & 1][u], pf[t], acc[dt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-  };
-  if (ntiles > 0) fill(0, stg0);
-  if (ntiles > 1) fill(1, stg1);
-  __syncthreads();
-  for (int t = 0; t < ntiles; t += 3) {
-    CSK_STAGE_SYNC(t + 1 < ntiles);
-    process(stg0, t);
-    CSK_STAGE_ISSUE(t + 2, stg2);
-    if (t + 1 >= ntiles) break;
-    CSK_STAGE_SYNC(t + 2 < ntiles);
-    process(stg1, t + 1);
-    CSK_STAGE_ISSUE(t + 3, stg0);
-    if (t + 2 >= ntiles) break;
-    CSK_STAGE_SYNC(t + 3 < ntiles);
-    process(stg2, t + 2);
-    CSK_STAGE_ISSUE(t + 4, stg1);
   }
-#undef CSK_STAGE_SYNC
-#undef CSK_STAGE_ISSUE
-  asm volatile("" ::: "memory");
-
-  float l_tot = l_part;
-  l_tot = group4_sum(l_tot);
 
   if (a.nch == 1) {
     float M, inv_z, lse;
-    finish_row(m_run, l_tot, a.sink, h, &M, &inv_z, &lse);
-    const float f = (m_run == -INFINITY) ? 0.f : exp2f(m_run - M) * inv_z;
+    finish_row(mx, l_tot, a.sink, h, &M, &inv_z, &lse);
+    const float f = (mx == -INFINITY) ? 0.f : exp2f(mx - M) * inv_z;
     uint16_t* ob = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)r * a.H + h) * DV;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -610,7 +627,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_dma_kernel(AttnArgs a) {
           make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
     if (g == 0) {
       float* pm = a.part_ml + (((int64_t)r * a.nch + chunk_id) * a.H + h) * 2;
-      pm[0] = m_run;
+      pm[0] = mx;
       pm[1] = l_tot;
     }
   }
@@ -791,7 +808,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 // ------------------------------------------------------------ host side
 struct AttnPlan {
   int chunk, nch;
-  bool mfma;
+  bool mfma, whole;
   size_t off_o, off_ml, total;
 };
 
@@ -800,6 +817,10 @@ static bool mfma_shape(int H, int D, int dv, int dtype) {
   return (D == 576 && (dv == 512 || dv == 576)) || (D == 128 && dv == 128) ||
          (D == 64 && dv == 64) || (D == 256 && dv == 256);
 }
+
+// The whole-chunk kernel splits its DMA blocks (D/4 per chunk) over H/16
+// waves.
+static bool chunk_kernel_shape(int H, int D) { return (D / 4) % (H / 16) == 0; }
 
 static AttnPlan plan_attn(int B, int T, int H, int D, int dv, int Lc, int W, int dtype) {
   AttnPlan p{};
@@ -811,6 +832,10 @@ static AttnPlan plan_attn(int B, int T, int H, int D, int dv, int Lc, int W, int
   int64_t ch = ceil_div(want < 128 ? 128 : want, gran) * gran;
   if (ch >= total) ch = ceil_div(total > 0 ? total : 1, gran) * gran;
   if (p.mfma && ch > MAX_CHUNK) ch = MAX_CHUNK;
+  // rows split into chunks (few rows, long candidate lists: decode) go to
+  // the whole-chunk kernel; rows kept whole (prefill) to the streaming one
+  p.whole = p.mfma && chunk_kernel_shape(H, D) && ch < total;
+  if (p.whole) ch = CHUNK_CANDS;  // the chunk is resident in LDS as a whole
   p.chunk = (int)ch;
   p.nch = (int)ceil_div(total > 0 ? total : 1, ch);
   size_t o = 0;
@@ -876,10 +901,10 @@ const int NW = H / 16;
     const char* kname = dense ? "attn_bf16_dense" : "attn_bf16_sparse";
 #define CSK_ATT_CASE(d, v, nw)                                                         \
   if (D == d && dv == v && NW == nw) {                                                 \
-    if ((d / 16) % nw == 0)                                                            \
-      rc = dense ? launch(kname, attn_bf16_dma_kernel<d, v, (d / 16) % nw == 0 ? nw : 1, true>, \
+    if (p.whole)                                                                       \
+      rc = dense ? launch(kname, attn_bf16_chunk_kernel<d, v, (d / 4) % nw == 0 ? nw : 1, true>, \
                           grid, block, 0, s, a)                                        \
-                 : launch(kname, attn_bf16_dma_kernel<d, v, (d / 16) % nw == 0 ? nw : 1, false>, \
+                 : launch(kname, attn_bf16_chunk_kernel<d, v, (d / 4) % nw == 0 ? nw : 1, false>, \
                           grid, block, 0, s, a);                                       \
     else                                                                               \
       rc = launch(kname, attn_bf16_kernel<d, v, nw>, grid, block, 0, s, a);            \

@@ -372,15 +372,15 @@ struct SelectShared {
   ScanShared scan;
 };
 
-template <typename Get>
+template <int NT, typename Get>
 __device__ SelectState radix_select(Get get, int n, int k, SelectShared& sh) {
   SelectState st{0u, 0u, k};
   const int tid = threadIdx.x;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += TOPK_THREADS) sh.hist[i] = 0;
+    for (int i = tid; i < 256; i += NT) sh.hist[i] = 0;
     __syncthreads();
-    for (int e0 = 0; e0 < n; e0 += TOPK_THREADS) {
+    for (int e0 = 0; e0 < n; e0 += NT) {
       const int e = e0 + tid;
       const uint32_t u = e < n ? get(e) : 0u;
       hist_add(sh.hist, (u >> shift) & 255u, e < n && (u & st.mask) == st.prefix);
@@ -421,11 +421,11 @@ __device__ SelectState radix_select(Get get, int n, int k, SelectShared& sh) {
 // Index-ordered compaction of the selected elements. Each thread owns a
 // contiguous run of elements; counts of strictly-greater and tied elements
 // are scanned across the block.
-template <typename Get, typename Emit>
+template <int NT, typename Get, typename Emit>
 __device__ void compact_selected(Get get, Emit emit, int n, const SelectState& st,
                                  SelectShared& sh) {
   const int tid = threadIdx.x;
-  const int per = (n + TOPK_THREADS - 1) / TOPK_THREADS;
+  const int per = (n + NT - 1) / NT;
   const int e0 = tid * per;
   const int e1 = min(n, e0 + per);
   int gt = 0, eq = 0;
@@ -435,7 +435,7 @@ __device__ void compact_selected(Get get, Emit emit, int n, const SelectState& s
     eq += u == st.prefix;
   }
   int2 tot;
-  const int2 before = block_scan2<TOPK_THREADS>(gt, eq, sh.scan, &tot);
+  const int2 before = block_scan2<NT>(gt, eq, sh.scan, &tot);
   int gt_before = before.x, eq_before = before.y;
   for (int e = e0; e < e1; ++e) {
     const uint32_t u = get(e) & st.mask;
@@ -469,99 +469,148 @@ struct TopkShared {
   int slice_off[1024 + 1];
 };
 
-// Threshold from the group maxima: a 4096-bin histogram of the top 12 key
-// bits of the samples; the threshold is the lower edge of the bin that
-// holds the k-th largest sample, so at least k samples (and hence at least
-// k elements of the row) are >= it. 0 keeps everything when the row has at
-// most k entries or too few samples. Each filter workgroup forms it for its
-// own row (the samples are a few KB, read from L2), which saves a launch.
+// Threshold from the group maxima, to 20 bits of the order-preserving key:
+// a 4096-bin histogram of the top 12 bits finds the bin that holds the k-th
+// largest sample, a 256-bin histogram of the next 8 bits of the samples in
+// that bin refines it; the threshold is the lower edge of the sub-bin that
+// holds the k-th largest sample, so at least k samples (hence at least k
+// elements of the row) are >= it. 0 keeps everything when the row has at
+// most k entries or too few samples. Every workgroup of the row forms it
+// (the samples are a few KB, read from L2), which saves a launch.
 constexpr int THR_BINS = 4096;
-constexpr int THR_BATCH = 32;  // samples per thread per load batch
+constexpr int THR_BATCH = 32;       // samples per thread per load batch
+constexpr int FUSED_THREADS = 256;
 
-// Candidate filter: keys of slice blockIdx.y with key(score) >= the row's
-// threshold, compacted in index order (thread t owns 8 consecutive keys).
-// Order of work: the histogram is cleared first, so that the barrier after
-// it has no loads to wait for; then the slice's scores and the row's samples
-// are loaded together (a barrier waits for every load in flight, so each
-// barrier is placed after loads that are needed anyway).
-__global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a) {
-  __shared__ int hist[THR_BINS];
-  __shared__ ScanShared scan;
-  __shared__ uint32_t thr_sh;
+struct FusedShared {
+  int hist[THR_BINS];
+  ScanShared scan;
+  uint32_t thr;
+  int sub_bin;
+};
+
+// Suffix search over PER * FUSED_THREADS bins: the bin d holding the
+// element of rank `want` (1-based, from the top) and the count of elements
+// in bins above it. Exactly one thread returns true (none when fewer than
+// `want` elements exist).
+template <int PER>
+__device__ bool find_rank_bin(const int* hist, int want, ScanShared& scan, int* out_d, int* out_above) {
+  const int tid = threadIdx.x;
+  const int G = FUSED_THREADS - 1 - tid;  // thread t owns bins PER*G .. PER*G+PER-1
+  int sg = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) sg += hist[PER * G + i];
+  int2 tot;
+  const int ex = block_scan2<FUSED_THREADS>(sg, 0, scan, &tot).x;  // bins above this group
+  if (ex < want && ex + sg >= want) {
+    int above = ex;
+    int d = PER * G + PER - 1;
+    for (; d > PER * G; --d) {
+      if (above + hist[d] >= want) break;
+      above += hist[d];
+    }
+    *out_d = d;
+    *out_above = above;
+    return true;
+  }
+  return false;
+}
+
+// Candidate filter for long rows: workgroup (r, f) forms the row's
+// threshold and writes the candidates of slice f (keys >= threshold, in
+// index order) and their count. (A last-arriving-workgroup select in the
+// same kernel was measured slower: each workgroup's device-scope release
+// writes back its L2, while a kernel boundary does that once.)
+__global__ __launch_bounds__(FUSED_THREADS) void topk_filter_kernel(TopkArgs a) {
+  __shared__ FusedShared sh;
   const int r = blockIdx.x, f = blockIdx.y;
   const int tid = threadIdx.x;
   const int nv = visible_count(a.ia, r);
   const int s0 = f * SLICE;
-  if (s0 >= nv) {
-    if (tid == 0) a.cand_cnt[(int64_t)r * a.n_slices + f] = 0;
-    return;
-  }
-  const int gs = 1 << a.ia.gs_log2;
-  const int ng = (nv + gs - 1) / gs;
-  const bool thresholded = nv > a.k && ng >= a.k;
-  if (thresholded) {
-    for (int i = tid; i < THR_BINS; i += 256) hist[i] = 0;
-    if (tid == 0) thr_sh = 0u;
-    __syncthreads();
-  }
-  const float* sc = a.ia.scores + (int64_t)r * a.ia.Nmax + s0;
-  const int lim = min(SLICE, nv - s0);
-  const int j0 = tid * (SLICE / 256);
-  float v[SLICE / 256];
-#pragma unroll
-  for (int i = 0; i < SLICE / 256; ++i) v[i] = sc[min(j0 + i, lim - 1)];  // unconditional
-  uint32_t thr = 0u;
-  if (thresholded) {
-    // group-maximum histogram of the top 12 key bits
-    const float* smp = a.ia.samples + (int64_t)r * a.ia.ng;
-    for (int e0 = 0; e0 < ng; e0 += 256 * THR_BATCH) {
-      float x[THR_BATCH];
-#pragma unroll
-      for (int i = 0; i < THR_BATCH; ++i) x[i] = smp[min(e0 + 256 * i + tid, ng - 1)];
-      // plain LDS atomics: the maxima spread over enough bins that this is
-      // far cheaper than combining same-bin lanes first
-#pragma unroll
-      for (int i = 0; i < THR_BATCH; ++i)
-        if (e0 + 256 * i + tid < ng) atomicAdd(&hist[order_key(x[i]) >> 20], 1);
+  const int k = a.k;
+
+  // ---- filter
+  if (s0 < nv) {
+    const int gs = 1 << a.ia.gs_log2;
+    const int ng = (nv + gs - 1) / gs;
+    const bool thresholded = nv > k && ng >= k;
+    if (thresholded) {
+      for (int i = tid; i < THR_BINS; i += FUSED_THREADS) sh.hist[i] = 0;
+      if (tid == 0) sh.thr = 0u;
+      __syncthreads();
     }
-    __syncthreads();
-    // thread t owns bins 16*G .. 16*G+15 with G = 255 - t; an inclusive scan
-    // in thread order is then a suffix sum over bins
-    const int G = 255 - tid;
-    int s16 = 0;
+    // the slice's scores are loaded first; their latency overlaps the
+    // threshold (a barrier waits for every load in flight, so each barrier
+    // comes after loads that are needed anyway)
+    const float* sc = a.ia.scores + (int64_t)r * a.ia.Nmax + s0;
+    const int lim = min(SLICE, nv - s0);
+    const int j0 = tid * (SLICE / FUSED_THREADS);
+    float v[SLICE / FUSED_THREADS];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s16 += hist[16 * G + i];
-    int2 tot;
-    const int ex = block_scan2<256>(s16, 0, scan, &tot).x;
-    if (ex < a.k && ex + s16 >= a.k) {
-      int above = ex;
-      int d = 16 * G + 15;
-      for (; d > 16 * G; --d) {
-        if (above + hist[d] >= a.k) break;
-        above += hist[d];
+    for (int i = 0; i < SLICE / FUSED_THREADS; ++i) v[i] = sc[min(j0 + i, lim - 1)];  // unconditional
+    uint32_t thr = 0u;
+    if (thresholded) {
+      const float* smp = a.ia.samples + (int64_t)r * a.ia.ng;
+      // level 1: top 12 key bits (plain LDS atomics: the maxima spread over
+      // enough bins that combining same-bin lanes first costs more)
+      for (int e0 = 0; e0 < ng; e0 += FUSED_THREADS * THR_BATCH) {
+        float x[THR_BATCH];
+#pragma unroll
+        for (int i = 0; i < THR_BATCH; ++i) x[i] = smp[min(e0 + FUSED_THREADS * i + tid, ng - 1)];
+#pragma unroll
+        for (int i = 0; i < THR_BATCH; ++i)
+          if (e0 + FUSED_THREADS * i + tid < ng) atomicAdd(&sh.hist[order_key(x[i]) >> 20], 1);
       }
-      thr_sh = (uint32_t)d << 20;
-    }
-    __syncthreads();
-    thr = thr_sh;
-  }
-  int cnt = 0;
+      __syncthreads();
+      int d = 0, above = 0;
+      // the owner of the bin publishes it
+      if (find_rank_bin<16>(sh.hist, k, sh.scan, &d, &above)) {
+        sh.thr = (uint32_t)d;
+        sh.sub_bin = above;
+      }
+      __syncthreads();
+      const uint32_t d1 = sh.thr;
+      const int above1 = sh.sub_bin;
+      __syncthreads();
+      // level 2: bits 19..12 of the samples in bin d1
+      for (int i = tid; i < 256; i += FUSED_THREADS) sh.hist[i] = 0;
+      __syncthreads();
+      for (int e0 = 0; e0 < ng; e0 += FUSED_THREADS * THR_BATCH) {
+        float x[THR_BATCH];
 #pragma unroll
-  for (int i = 0; i < SLICE / 256; ++i) cnt += (j0 + i < lim && order_key(v[i]) >= thr) ? 1 : 0;
-  int2 tot;
-  int pos = block_scan2<256>(cnt, 0, scan, &tot).x;
-  float* cs = a.cand_score + (int64_t)r * a.ia.Nmax + s0;
-  int* ci = a.cand_idx + (int64_t)r * a.ia.Nmax + s0;
+        for (int i = 0; i < THR_BATCH; ++i) x[i] = smp[min(e0 + FUSED_THREADS * i + tid, ng - 1)];
 #pragma unroll
-  for (int i = 0; i < SLICE / 256; ++i) {
-    const int j = j0 + i;
-    if (j < lim && order_key(v[i]) >= thr) {
-      cs[pos] = v[i];
-      ci[pos] = s0 + j;
-      ++pos;
+        for (int i = 0; i < THR_BATCH; ++i) {
+          const uint32_t u = order_key(x[i]);
+          if (e0 + FUSED_THREADS * i + tid < ng && (u >> 20) == d1) atomicAdd(&sh.hist[(u >> 12) & 255u], 1);
+        }
+      }
+      __syncthreads();
+      int e = 0, above2 = 0;
+      if (find_rank_bin<1>(sh.hist, k - above1, sh.scan, &e, &above2)) sh.thr = (d1 << 20) | ((uint32_t)e << 12);
+      __syncthreads();
+      thr = sh.thr;
     }
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < SLICE / FUSED_THREADS; ++i) cnt += (j0 + i < lim && order_key(v[i]) >= thr) ? 1 : 0;
+    int2 tot;
+    int pos = block_scan2<FUSED_THREADS>(cnt, 0, sh.scan, &tot).x;
+    float* cs = a.cand_score + (int64_t)r * a.ia.Nmax + s0;
+    int* ci = a.cand_idx + (int64_t)r * a.ia.Nmax + s0;
+#pragma unroll
+    for (int i = 0; i < SLICE / FUSED_THREADS; ++i) {
+      const int j = j0 + i;
+      if (j < lim && order_key(v[i]) >= thr) {
+        cs[pos] = v[i];
+        ci[pos] = s0 + j;
+        ++pos;
+      }
+    }
+    if (tid == 0) a.cand_cnt[(int64_t)r * a.n_slices + f] = tot.x;
+  } else if (tid == 0) {
+    a.cand_cnt[(int64_t)r * a.n_slices + f] = 0;
   }
-  if (tid == 0) a.cand_cnt[(int64_t)r * a.n_slices + f] = tot.x;
+
 }
 
 // Final selection for one row. FILTERED = false: the row's scores
@@ -662,8 +711,8 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkArgs a) {
     for (int e = tid; e < n; e += TOPK_THREADS) emit(e, e);
     nsel = n;
   } else {
-    SelectState st = radix_select(get, n, k, sh.sel);
-    compact_selected(get, emit, n, st, sh.sel);
+    SelectState st = radix_select<TOPK_THREADS>(get, n, k, sh.sel);
+    compact_selected<TOPK_THREADS>(get, emit, n, st, sh.sel);
     nsel = k;
   }
   for (int j = nsel + tid; j < k; j += TOPK_THREADS) {
@@ -806,7 +855,7 @@ int indexer_topk(const void* q, const uint8_t* q_scale, const float* w, const vo
     ta.cand_idx = reinterpret_cast<int*>(ws + p.off_cidx);
     ta.flat_key = reinterpret_cast<uint32_t*>(ws + p.off_fkey);
     ta.flat_idx = reinterpret_cast<int*>(ws + p.off_fidx);
-    rc = launch("topk_filter", topk_filter_kernel, dim3(R, p.n_slices), dim3(256), 0, s, ta);
+    rc = launch("topk_filter", topk_filter_kernel, dim3(R, p.n_slices), dim3(FUSED_THREADS), 0, s, ta);
     if (rc == CSK_OK)
       rc = launch("topk_select", topk_select_kernel<true>, dim3(R), dim3(TOPK_THREADS), lds, s, ta);
   } else {
