@@ -382,7 +382,7 @@ def run(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(dom),
             "algorithmic_bytes": abytes,
             "avg_launch_us": round(avg_ms * 1e3, 2),
             "timing": "HIP events around each launch on its stream, K eager steps",
@@ -392,6 +392,51 @@ def run(args):
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args)
     print(json.dumps(line), flush=True)
+
+
+KERNEL_SOURCES = {  # sources whose text decides each kernel's code
+    "attn_bf16_dense": ["attention.hip", "common.h"],
+    "attn_bf16_sparse": ["attention.hip", "common.h"],
+    "indexer_scores_fp4": ["indexer.hip", "common.h"],
+}
+
+
+def source_hash(kernel):
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(ROOT, "compressed_sparse_kv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter record
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel calibration),
+    or None when there is none or the kernel's sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != source_hash(kernel):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_probe(mib):
+    """A plain device-to-device copy of `mib` MiB, repeated, for calibrating
+    the FETCH_SIZE / WRITE_SIZE counters against a known byte count."""
+    import torch
+
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
 
 
 def cpu_baseline(wl, args):
@@ -423,11 +468,16 @@ def main():
                     help="1: every call on one stream; 3: the data-flow split over three streams")
     ap.add_argument("--cpu-rows", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain MIB-MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     run(args)
 
 
