@@ -72,6 +72,7 @@ struct AttnArgs {
   int B, T, H, D, dv, d_rope, Nmax, k, m, S_w, W;
   int Lc;                 // compressed slots per row
   int chunk, nch;         // candidates per chunk, chunks per row
+  int extra;              // whole-chunk kernel: rows past the MFMA tiles (VALU), <= MAX_EXTRA
   float scale;
   RopeTable rope;
   bool dense;
@@ -374,33 +375,45 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint4* lds_base) {
 #define CSK_VMCNT_LGKM0(n) ((((n) & 0xF) | ((((n) >> 4) & 0x3) << 14)) | (0x7 << 4))
 
 // ------------------------------------------------- bf16 MFMA, whole chunk
-// One workgroup = one query row and a chunk of CHUNK_TILES*32 candidates,
-// all of which are resident in LDS at once (4 x 32 x 576 bf16 = 144 KB).
+// One workgroup = one query row and a chunk of CHUNK_TILES*32 candidates
+// (2 or 4 tiles), all of which are resident in LDS at once (4 x 32 x 576
+// bf16 = 144 KB; with 2 tiles two workgroups share a CU).
 //   1. q fragments are loaded first, the row codes and the RoPE cos/sin
 //      table next (one barrier for all of them);
 //   2. every KV row of the chunk is requested with LDS DMA in one burst, so
 //      all of the chunk's memory traffic is in flight together;
-//   3. S = q.k for all candidates stays in registers; the softmax of each
-//      head is then exact over the chunk (one maximum, no rescaling of the
-//      accumulators as tiles arrive);
+//   3. S = q.k of each tile as soon as that tile has landed; the scores of
+//      all candidates stay in registers, and the softmax of each head is
+//      exact over the chunk (one maximum, no rescaling of the accumulators);
 //   4. O^T += V^T P^T over the chunk, V^T fragments from transpose reads.
 // Each tile is 32 rows in column-major 16-byte units (unit = chunk*32 +
 // row); one wave-level DMA instruction fills a 1 KB block of a tile (chunks
 // 2b and 2b+1 of its 32 rows). Waves own 16 heads each (MFMA columns).
-constexpr int CHUNK_TILES = 4;
-constexpr int CHUNK_CANDS = 32 * CHUNK_TILES;
+constexpr int MAX_EXTRA = 4;  // rows a whole-chunk workgroup takes past its tiles
 
-template <int D, int DV, int NW, bool DENSE>
+template <int D, int DV, int NW, bool DENSE, int CHUNK_TILES>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bf16_chunk_kernel(AttnArgs a) {
+  constexpr int TILE_CANDS = 32 * CHUNK_TILES;
   constexpr int KS = D / 32;            // MFMA K-steps over the key dims
   constexpr int DT = DV / 16;           // 16-row tiles of the value dims
   constexpr int TU = 32 * D / 8;        // 16-byte units per tile
   constexpr int BLK = D / 16;           // 1 KB DMA blocks per tile
   constexpr int NB = CHUNK_TILES * BLK;
   static_assert(NB % NW == 0, "DMA blocks must split evenly over the waves");
-  __shared__ __align__(16) uint4 kvs[CHUNK_TILES * TU];
-  __shared__ __align__(16) int codes[CHUNK_CANDS];
+  // one array per tile (not one indexed array): the compiler then tells a
+  // tile being read from the tiles whose DMAs are still in flight, and the
+  // first tiles are computed while the later ones load
+  __shared__ __align__(16) uint4 kv0[TU];
+  __shared__ __align__(16) uint4 kv1[TU];
+  __shared__ __align__(16) uint4 kv2[CHUNK_TILES > 2 ? TU : 1];
+  __shared__ __align__(16) uint4 kv3[CHUNK_TILES > 2 ? TU : 1];
+  auto tile = [&](int t) -> uint4* { return t == 0 ? kv0 : t == 1 ? kv1 : t == 2 ? kv2 : kv3; };
+  __shared__ __align__(16) int codes[TILE_CANDS + MAX_EXTRA];
+  // up to MAX_EXTRA rows past the tiles, row-major (unit = row * D/8 + chunk),
+  // padded to whole 64-unit DMA blocks
+  constexpr int XU = (MAX_EXTRA * (D / 8) + 63) / 64 * 64;
+  __shared__ __align__(16) uint4 kvx[XU];
   __shared__ float2 rtab[MAX_ROPE_PAIRS];
 
   const int r = blockIdx.x;
@@ -414,8 +427,11 @@ void attn_bf16_chunk_kernel(AttnArgs a) {
   const uint16_t* kvc = reinterpret_cast<const uint16_t*>(a.kv_c) + (int64_t)ri.b * a.Nmax * D;
   const uint16_t* kvw = reinterpret_cast<const uint16_t*>(a.kv_w) + (int64_t)ri.b * a.S_w * D;
   const int total = a.Lc + a.W;
-  const int c0 = chunk_id * CHUNK_CANDS;
-  const int nc = min(CHUNK_CANDS, total - c0);
+  const int cands = TILE_CANDS + a.extra;
+  const int c0 = chunk_id * cands;
+  const int nall = min(cands, total - c0);      // candidates of this chunk
+  const int nc = min(nall, TILE_CANDS);          // of them in the MFMA tiles
+  const int nx = nall - nc;                      // extra rows (VALU)
 
   // 1. q fragments (dims 32*ks + 8*g .. +7 of head h), codes, RoPE table
   uint4 qraw[KS];
@@ -424,7 +440,7 @@ void attn_bf16_chunk_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qraw[ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g);
   }
-  for (int j = tid; j < CHUNK_CANDS; j += 64 * NW) codes[j] = j < nc ? slot_code(a, ri, r, c0 + j) : -1;
+  for (int j = tid; j < TILE_CANDS + MAX_EXTRA; j += 64 * NW) codes[j] = j < nall ? slot_code(a, ri, r, c0 + j) : -1;
   if (tid < a.d_rope / 2) {
     float cs, sn;
     rope_cs((double)ri.p, a.rope.theta[tid], &cs, &sn);
@@ -432,29 +448,14 @@ void attn_bf16_chunk_kernel(AttnArgs a) {
   }
   // an ordinary store into the KV buffer: the DMA intrinsic is not seen as
   // a writer of it, and without one the reads below could be folded away
-  kvs[tid] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (int t = 0; t < CHUNK_TILES; ++t) tile(t)[tid] = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < XU) kvx[tid] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
 
-  // 2. one burst of DMA for the whole chunk; empty slots read row 0 of the
-  // cache (finite data, weight 0)
-  {
-    // the lane's row in each tile, read once
-    const int row = lane & 31;
-    const uint16_t* src[CHUNK_TILES];
-#pragma unroll
-    for (int t = 0; t < CHUNK_TILES; ++t) {
-      const int code = codes[t * 32 + row];
-      src[t] = code >= 0 ? kvc + (int64_t)code * D : (code <= -2 ? kvw + (int64_t)(-2 - code) * D : kvc);
-    }
-#pragma unroll
-    for (int q = 0; q < NB / NW; ++q) {
-      const int blk = wave + NW * q;
-      const int t = blk / BLK, b = blk - t * BLK;
-      lds_dma16(src[t] + 8 * (2 * b + (lane >> 5)), kvs + t * TU + b * 64);
-    }
-  }
-
-  // rotated query fragments as bf16 (while the DMA is in flight)
+  // rotated query fragments as bf16, formed before the DMA burst: the q
+  // loads completed at the barrier, and a use of their registers after the
+  // burst would make the compiler wait for every DMA first
   v8bf qf[KS];
   {
     const int rope0 = D - a.d_rope;
@@ -484,11 +485,40 @@ void attn_bf16_chunk_kernel(AttnArgs a) {
       for (int i = 0; i < 8; ++i) qf[ks][i] = __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_bits(x[i]));
     }
   }
-  // every wave's DMA has landed (each waits for its own, then the barrier)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(CSK_VMCNT_LGKM0(0));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. one burst of DMA for the whole chunk; empty slots read row 0 of the
+  // cache (finite data, weight 0)
+  {
+    // the lane's row in each tile, read once
+    const int row = lane & 31;
+    const uint16_t* src[CHUNK_TILES];
+#pragma unroll
+    for (int t = 0; t < CHUNK_TILES; ++t) {
+      const int code = codes[t * 32 + row];
+      src[t] = code >= 0 ? kvc + (int64_t)code * D : (code <= -2 ? kvw + (int64_t)(-2 - code) * D : kvc);
+    }
+    // the extra rows first (wave 0; older than every tile's DMAs, so the
+    // tile waits below still count right), row-major 16-byte units
+    if (wave == 0 && nx > 0) {
+      const int nu = nx * (D / 8);
+      for (int u0 = 0; u0 < nu; u0 += 64) {
+        const int u = min(u0 + lane, nu - 1);  // the tail lanes repeat the last unit
+        const int xr = u / (D / 8), xc = u - xr * (D / 8);
+        const int code = codes[TILE_CANDS + xr];
+        const uint16_t* xs = code >= 0 ? kvc + (int64_t)code * D : (code <= -2 ? kvw + (int64_t)(-2 - code) * D : kvc);
+        lds_dma16(xs + 8 * xc, kvx + u0);
+      }
+    }
+    // tile by tile, so that a tile's DMAs are older than the next tile's
+#pragma unroll
+    for (int t = 0; t < CHUNK_TILES; ++t)
+#pragma unroll
+      for (int q = 0; q < BLK / NW; ++q) {
+        const int b = wave + NW * q;
+        lds_dma16(src[t] + 8 * (2 * b + (lane >> 5)), tile(t) + b * 64);
+      }
+  }
 
   const int ntiles = (nc + 31) / 32;
   const float sl2 = a.scale * LOG2E;
@@ -497,12 +527,27 @@ void attn_bf16_chunk_kernel(AttnArgs a) {
   v4f sc[CHUNK_TILES][2];
 #pragma unroll
   for (int t = 0; t < CHUNK_TILES; ++t) {
+    // tile t has landed once this wave's DMAs for it are done (the later
+    // tiles' BLK/NW each may remain) and every wave has passed the barrier;
+    // the fences keep the compiler from moving memory accesses across it
+    asm volatile("" ::: "memory");
+    {
+      // (vmcnt holds at most 63: a larger count clamps, which only waits longer)
+      constexpr int PER = BLK / NW;
+      const int rem = CHUNK_TILES - 1 - t;
+      if (rem <= 0) __builtin_amdgcn_s_waitcnt(CSK_VMCNT_LGKM0(0));
+      else if (rem == 1) __builtin_amdgcn_s_waitcnt(CSK_VMCNT_LGKM0(PER < 63 ? PER : 63));
+      else if (rem == 2) __builtin_amdgcn_s_waitcnt(CSK_VMCNT_LGKM0(2 * PER < 63 ? 2 * PER : 63));
+      else __builtin_amdgcn_s_waitcnt(CSK_VMCNT_LGKM0(3 * PER < 63 ? 3 * PER : 63));
+    }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     sc[t][0] = sc[t][1] = v4f{0.f, 0.f, 0.f, 0.f};
     if (t < ntiles) {
       // fragments in blocks of QB K-steps, the next block's reads issued
       // before the current block's MFMAs (the scheduling barriers keep that
       // order; left alone, the scheduler keeps one read in flight)
-      const uint4* sb = kvs + t * TU;
+      const uint4* sb = tile(t);
       constexpr int QB = 3, NQB = (KS + QB - 1) / QB;
       v8bf kf[2][QB][2];
       auto load_q = [&](int blk, v8bf (&dst)[QB][2]) {
@@ -532,6 +577,29 @@ void attn_bf16_chunk_kernel(AttnArgs a) {
       }
     }
   }
+  // scores of the extra rows (VALU): the lane's partial dot over its dims,
+  // summed over the four lane groups of its head
+  float sx[MAX_EXTRA];
+#pragma unroll
+  for (int x = 0; x < MAX_EXTRA; ++x) {
+    sx[x] = -INFINITY;
+    if (x < nx) {
+      const uint4* xr = kvx + x * (D / 8);
+      float dot = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 kk = xr[4 * ks + g];
+        const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dot = __builtin_fmaf((float)qf[ks][2 * i], bf16_bits_to_f32(kw[i] & 0xffffu), dot);
+          dot = __builtin_fmaf((float)qf[ks][2 * i + 1], bf16_bits_to_f32(kw[i] >> 16), dot);
+        }
+      }
+      dot = group4_sum(dot);
+      if (codes[TILE_CANDS + x] != -1) sx[x] = dot * sl2;
+    }
+  }
   // the lane's 32 candidates are 4 consecutive codes per (tile, half):
   // eight vector reads, then the mask is register arithmetic
   int4 cd[CHUNK_TILES][2];
@@ -554,7 +622,15 @@ void attn_bf16_chunk_kernel(AttnArgs a) {
       }
     }
   mx = group4_max(mx);
+#pragma unroll
+  for (int x = 0; x < MAX_EXTRA; ++x) mx = fmaxf(mx, sx[x]);  // equal in all lane groups
   float l_part = 0.f;
+  float px[MAX_EXTRA];
+#pragma unroll
+  for (int x = 0; x < MAX_EXTRA; ++x) {
+    px[x] = (mx == -INFINITY || sx[x] == -INFINITY) ? 0.f : exp2f(sx[x] - mx);
+    if (g == 0) l_part += px[x];  // counted once per head
+  }
   v8bf pf[CHUNK_TILES];
 #pragma unroll
   for (int t = 0; t < CHUNK_TILES; ++t)
@@ -577,7 +653,7 @@ void attn_bf16_chunk_kernel(AttnArgs a) {
     if (t < ntiles) {
       // V^T fragments in blocks of VB value tiles, pipelined like the QK
       // fragments
-      const uint16_t* sb16 = reinterpret_cast<const uint16_t*>(kvs + t * TU);
+      const uint16_t* sb16 = reinterpret_cast<const uint16_t*>(tile(t));
       constexpr int VB = 4, NVB = (DT + VB - 1) / VB;
       v8bf vf[2][VB];
       auto load_v = [&](int blk, v8bf (&dst)[VB]) {
@@ -602,6 +678,23 @@ void attn_bf16_chunk_kernel(AttnArgs a) {
           if (dt < DT) acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[blk & 1][u], pf[t], acc[dt], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // the extra rows' values (VALU): lane (head col, group g) holds value dims
+  // 16*dt + 4*g .. +3
+#pragma unroll
+  for (int x = 0; x < MAX_EXTRA; ++x) {
+    if (x < nx && px[x] != 0.f) {
+      const uint16_t* xr = reinterpret_cast<const uint16_t*>(kvx + x * (D / 8));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint2 vv = *reinterpret_cast<const uint2*>(xr + 16 * dt + 4 * g);
+        acc[dt][0] = __builtin_fmaf(px[x], bf16_bits_to_f32(vv.x & 0xffffu), acc[dt][0]);
+        acc[dt][1] = __builtin_fmaf(px[x], bf16_bits_to_f32(vv.x >> 16), acc[dt][1]);
+        acc[dt][2] = __builtin_fmaf(px[x], bf16_bits_to_f32(vv.y & 0xffffu), acc[dt][2]);
+        acc[dt][3] = __builtin_fmaf(px[x], bf16_bits_to_f32(vv.y >> 16), acc[dt][3]);
       }
     }
   }
@@ -807,7 +900,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------ host side
 struct AttnPlan {
-  int chunk, nch;
+  int chunk, nch, tiles, extra;
   bool mfma, whole;
   size_t off_o, off_ml, total;
 };
@@ -835,7 +928,30 @@ static AttnPlan plan_attn(int B, int T, int H, int D, int dv, int Lc, int W, int
   // rows split into chunks (few rows, long candidate lists: decode) go to
   // the whole-chunk kernel; rows kept whole (prefill) to the streaming one
   p.whole = p.mfma && chunk_kernel_shape(H, D) && ch < total;
-  if (p.whole) ch = CHUNK_CANDS;  // the chunk is resident in LDS as a whole
+  if (p.whole) {
+    // 2- or 4-tile chunks: a small cost model of one launch (workgroup
+    // waves over the CUs x per-workgroup time, plus the partials each chunk
+    // writes and the merge reads); the 4-tile workgroup holds a CU alone
+    auto cost = [&](int tiles) {
+      const int64_t wgs = R * ceil_div(total, 32 * tiles);
+      const int64_t slots = 256 * (tiles == 2 ? 2 : 1);
+      const double waves = (double)ceil_div(wgs, slots);
+      const double partial_us = (double)wgs * H * dv * 8 / 4.0e6;  // write + read at ~4 TB/s
+      return waves * (20.0 + 2.0 * tiles) + partial_us;
+    };
+    p.tiles = (D * 2 * 32 * 4 > 150 * 1024 || cost(2) < cost(4)) ? 2 : 4;
+    ch = 32 * p.tiles;  // the chunk is resident in LDS as a whole
+    // a few rows past the tiles (VALU) when that saves a wave of
+    // workgroups: 1M-context HCA has 8320 candidates, 65 x 128, 64 x 130
+    const int64_t slots = 256 * (p.tiles == 2 ? 2 : 1);
+    if (R * ceil_div(total, ch) > slots)
+      for (int e = 1; e <= MAX_EXTRA; ++e)
+        if (ceil_div(R * ceil_div(total, ch + e), slots) < ceil_div(R * ceil_div(total, ch), slots)) {
+          p.extra = e;
+          ch += e;
+          break;
+        }
+  }
   p.chunk = (int)ch;
   p.nch = (int)ceil_div(total > 0 ? total : 1, ch);
   size_t o = 0;
@@ -885,7 +1001,7 @@ static int attn_common(const char* fn, bool dense, const void* q, const int32_t*
   a.q = q; a.q_pos = q_pos; a.kv_c = kv_c; a.idx = idx; a.n_entries = n_entries;
   a.kv_w = kv_w; a.w_pos0 = w_pos0; a.sink = sink;
   a.B = B; a.T = T; a.H = H; a.D = D; a.dv = dv; a.d_rope = d_rope; a.Nmax = Nmax; a.k = k;
-  a.m = m; a.S_w = S_w; a.W = Wslots; a.Lc = Lc; a.chunk = p.chunk; a.nch = p.nch;
+  a.m = m; a.S_w = S_w; a.W = Wslots; a.Lc = Lc; a.chunk = p.chunk; a.nch = p.nch; a.extra = p.extra;
   a.scale = scale; a.dense = dense;
   fill_rope_table(&a.rope, d_rope, (double)rope_base);
   a.out = out; a.lse = lse;
@@ -901,12 +1017,15 @@ const int NW = H / 16;
     const char* kname = dense ? "attn_bf16_dense" : "attn_bf16_sparse";
 #define CSK_ATT_CASE(d, v, nw)                                                         \
   if (D == d && dv == v && NW == nw) {                                                 \
-    if (p.whole)                                                                       \
-      rc = dense ? launch(kname, attn_bf16_chunk_kernel<d, v, (d / 4) % nw == 0 ? nw : 1, true>, \
-                          grid, block, 0, s, a)                                        \
-                 : launch(kname, attn_bf16_chunk_kernel<d, v, (d / 4) % nw == 0 ? nw : 1, false>, \
-                          grid, block, 0, s, a);                                       \
-    else                                                                               \
+    if (p.whole) {                                                                     \
+      constexpr int nwc = (d / 4) % nw == 0 ? nw : 1;                                  \
+      if (p.tiles == 2)                                                                \
+        rc = dense ? launch(kname, attn_bf16_chunk_kernel<d, v, nwc, true, 2>, grid, block, 0, s, a) \
+                   : launch(kname, attn_bf16_chunk_kernel<d, v, nwc, false, 2>, grid, block, 0, s, a); \
+      else                                                                             \
+        rc = dense ? launch(kname, attn_bf16_chunk_kernel<d, v, nwc, true, 4>, grid, block, 0, s, a) \
+                   : launch(kname, attn_bf16_chunk_kernel<d, v, nwc, false, 4>, grid, block, 0, s, a); \
+    } else                                                                             \
       rc = launch(kname, attn_bf16_kernel<d, v, nw>, grid, block, 0, s, a);            \
   }
 #define CSK_ATT_NW(d, v) CSK_ATT_CASE(d, v, 1) CSK_ATT_CASE(d, v, 2) CSK_ATT_CASE(d, v, 3) CSK_ATT_CASE(d, v, 4)

@@ -120,6 +120,15 @@ def test_dense_decode_split():
                 decode=True)
 
 
+@pytest.mark.parametrize("B,N", [(2, 16384), (4, 8192)])
+def test_dense_decode_extra_rows(B, N):
+    # rows of 16512 / 8320 candidates: 128-candidate chunks would need one
+    # workgroup more than a wave of the chip, so each chunk also takes one or
+    # two rows past its MFMA tiles (scored on the VALU)
+    _dense_case(705 + B, B=B, T=1, H=64, D=576, dv=512, N=N, m=128, S_w=128, W=128, bf16=True, d_rope=64,
+                decode=True)
+
+
 def test_dense_fp32():
     _dense_case(703, B=2, T=70, H=4, D=64, dv=64, N=20, m=4, S_w=70, W=8, bf16=False, d_rope=32, decode=False)
 
