@@ -277,6 +277,196 @@ class DecodeWorkload:
         return out
 
 
+class PrefillWorkload:
+    """Prefill pass on the GPU for 'hca_prefill_16k' (HCA layer, seq 16384,
+    16 heads x 128) or 'csa_prefill_64k' (CSA layer, seq 65536, 64 heads,
+    KV 512+64, MXFP4 indexer 64x128, top-k 2048). Inputs are drawn on the
+    device from a seeded generator with the distributions of the workload
+    statement: sources, queries and window KV N(0,1) bf16, indexer queries
+    N(0,1) fp32, head weights N(0,1/64), positional biases N(0,0.1), sink 0,
+    positions 0..S-1.
+    One step is the whole layer pass: compression of every entry, then (CSA)
+    the indexer key series with MXFP4 output, the query MXFP4 encode, indexer
+    scores and top-k for every query, and attention for every query."""
+
+    BF16_PEAK_TFLOPS = 2500.0
+    FP4_PEAK_TFLOPS = 10100.0
+
+    def __init__(self, name, seed):
+        import torch
+
+        import compressed_sparse_kv_amd as csk
+
+        self.torch, self.csk, self.name = torch, csk, name
+        self.csa = name == "csa_prefill_64k"
+        dev = torch.device("cuda:0")
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+
+        def bf16(*shape):
+            return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+        def f32(*shape, var=1.0):
+            return torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * float(np.sqrt(var))
+
+        t0 = time.time()
+        if self.csa:
+            S, H, D, dv, HI, dI, m, k, W = 65536, 64, 576, 512, 64, 128, 4, 2048, 128
+        else:
+            S, H, D, dv, HI, dI, m, k, W = 16384, 16, 128, 128, 0, 0, 128, 0, 128
+        self.S, self.H, self.D, self.dv, self.HI, self.dI, self.m, self.k, self.W = S, H, D, dv, HI, dI, m, k, W
+        self.N = S // m
+        self.scale = float(np.float32(1.0 / np.sqrt(D)))
+        x = {}
+        if self.csa:
+            for n in ("ca", "za", "cb", "zb"):
+                x[n] = bf16(1, S, D)
+            for n in ("ia", "iza", "ib", "izb"):
+                x[n] = bf16(1, S, dI)
+            x["bias_a"], x["bias_b"] = f32(m, D, var=0.1), f32(m, D, var=0.1)
+            x["ibias_a"], x["ibias_b"] = f32(m, dI, var=0.1), f32(m, dI, var=0.1)
+            x["qI"] = f32(1, S, HI, dI)
+            x["w"] = f32(1, S, HI, var=1.0 / HI)
+        else:
+            x["c"], x["z"] = bf16(1, S, D), bf16(1, S, D)
+            x["bias"] = f32(m, D, var=0.1)
+        x["q"] = bf16(1, S, H, D)
+        x["kv_w"] = bf16(1, S, D)
+        x["sink"] = torch.zeros(H, dtype=torch.float32, device=dev)
+        x["q_pos"] = torch.arange(S, dtype=torch.int32, device=dev).reshape(1, S)
+        x["w_pos0"] = torch.zeros(1, dtype=torch.int32, device=dev)
+        x["n_entries"] = torch.full((1,), self.N, dtype=torch.int32, device=dev)
+        self.x = x
+        # outputs and workspaces
+        self.kv = torch.empty((1, self.N, D), dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty((1, S, H, dv), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((1, S, H), dtype=torch.float32, device=dev)
+        if self.csa:
+            self.kc = torch.empty((1, self.N, dI // 2), dtype=torch.uint8, device=dev)
+            self.ks = torch.empty((1, self.N, dI // 32), dtype=torch.uint8, device=dev)
+            self.qc = torch.empty((1, S, HI, dI // 2), dtype=torch.uint8, device=dev)
+            self.qs = torch.empty((1, S, HI, dI // 32), dtype=torch.uint8, device=dev)
+            self.idx = torch.empty((1, S, k), dtype=torch.int32, device=dev)
+            ws_i = csk.indexer_topk_workspace_size(1, S, HI, dI, self.N, k, csk.CSK_MXFP4)
+            ws_a = csk.sparse_attn_workspace_size(1, S, H, D, dv, k, W, csk.CSK_BF16)
+            self.ws_i = torch.empty(max(ws_i, 1), dtype=torch.uint8, device=dev)
+        else:
+            ws_a = csk.dense_compressed_attn_workspace_size(1, S, H, D, dv, self.N, m, W, csk.CSK_BF16)
+        self.ws_a = torch.empty(max(ws_a, 1), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        _log(f"{name}: device inputs ready in {time.time() - t0:.1f}s "
+             f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
+        # exact candidate counts per query row (positions 0..S-1, causal)
+        t = np.arange(S, dtype=np.int64)
+        vis = np.minimum((t + 1) // m, self.N)
+        win = np.minimum(W, t + 1)
+        self.attn_pairs = int((np.minimum(vis, k) if self.csa else vis).sum() + win.sum())
+        self.idx_pairs = int(vis.sum())
+
+    def step(self, c=0):
+        csk, x = self.csk, self.x
+        if self.csa:
+            csk.csa_compress(x["ca"], x["za"], x["cb"], x["zb"], x["bias_a"], x["bias_b"], self.m, d_rope=64,
+                             out=self.kv)
+            csk.csa_compress(x["ia"], x["iza"], x["ib"], x["izb"], x["ibias_a"], x["ibias_b"], self.m,
+                             out_dtype=csk.CSK_MXFP4, out=self.kc, out_scale=self.ks)
+            csk.mxfp4_quantize(x["qI"], self.qc, self.qs)
+            csk.indexer_topk(self.qc, x["w"], self.kc, x["q_pos"], x["n_entries"], self.m, self.k,
+                             q_scale=self.qs, k_scale=self.ks, idx=self.idx, workspace=self.ws_i,
+                             with_score=False)
+            csk.sparse_attn(x["q"], x["q_pos"], self.kv, self.idx, x["kv_w"], x["w_pos0"], self.W, x["sink"],
+                            self.dv, 64, self.scale, out=self.out, lse=self.lse, workspace=self.ws_a)
+        else:
+            csk.hca_compress(x["c"], x["z"], x["bias"], self.m, d_rope=64, out=self.kv)
+            csk.dense_compressed_attn(x["q"], x["q_pos"], self.kv, x["n_entries"], self.m, x["kv_w"],
+                                      x["w_pos0"], self.W, x["sink"], self.dv, 64, self.scale, out=self.out,
+                                      lse=self.lse, workspace=self.ws_a)
+
+    def kernels(self):
+        if self.csa:
+            return ["csa_compress", "mxfp4_quantize", "indexer_scores_fp4", "topk_filter", "topk_select",
+                    "attn_bf16_sparse", "attn_merge"]
+        return ["hca_compress", "attn_bf16_dense", "attn_merge"]
+
+    def algorithmic_work(self, kernel):
+        """(bound, work per launch, peak, unit): the roofline a launch of
+        `kernel` is held to. Attention: 2*(D+dv) flops per (query, head,
+        candidate); indexer: 2*HI*dI per (query, visible key); compression:
+        its source and output bytes."""
+        S, H, D, dv, N = self.S, self.H, self.D, self.dv, self.N
+        if kernel in ("attn_bf16_sparse", "attn_bf16_dense"):
+            return ("mfma", 2.0 * (D + dv) * H * self.attn_pairs, self.BF16_PEAK_TFLOPS, "TFLOP/s")
+        if kernel == "indexer_scores_fp4":
+            return ("mfma", 2.0 * self.HI * self.dI * self.idx_pairs, self.FP4_PEAK_TFLOPS, "TFLOP/s")
+        if kernel in ("csa_compress", "hca_compress"):
+            # the CSA step launches it twice (KV, then indexer keys); per
+            # launch: the KV launch's bytes (the larger)
+            n_series = 4 if self.csa else 2
+            return ("hbm", n_series * S * D * 2 + N * D * 2, HBM_PEAK_GBS, "GB/s")
+        return None
+
+    def attention_hbm_bytes(self):
+        """Bytes the attention kernel must move: q, out, window KV, the
+        compressed cache (once), idx."""
+        S, H, D, dv, N = self.S, self.H, self.D, self.dv, self.N
+        b = S * H * D * 2 + S * H * dv * 2 + S * D * 2 + N * D * 2
+        if self.csa:
+            b += S * self.k * 4
+        return b
+
+    def config(self):
+        c = {"workload": self.name, "batch": 1, "seq_len": self.S, "compressed_entries": self.N,
+             "compression": self.m, "heads": self.H, "kv_dim": self.D, "value_dim": self.dv, "rope_dims": 64,
+             "window": self.W, "sink": True}
+        if self.csa:
+            c.update(indexer_heads=self.HI, indexer_dim=self.dI, indexer_dtype="mxfp4", top_k=self.k)
+        return c
+
+    def host(self, t):
+        t = t.detach()
+        if t.dtype == self.torch.bfloat16:
+            return t.view(self.torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+
+    def oracle_sample(self, n_rows):
+        """The oracle on a bounded sample of the same pass: compression of
+        every entry, then n_rows query rows spread over the sequence.
+        Returns (seconds for the compression, seconds for the rows)."""
+        import oracle
+
+        x, h = self.x, self.host
+        S = self.S
+        ts = sorted(set(np.linspace(0, S - 1, n_rows).astype(int).tolist()))
+        sel = lambda a: np.ascontiguousarray(a[:, ts])
+        if self.csa:
+            srcs = [h(x[n]) for n in ("ca", "za", "cb", "zb", "bias_a", "bias_b")]
+            isrcs = [h(x[n]) for n in ("ia", "iza", "ib", "izb", "ibias_a", "ibias_b")]
+            q, qI, w = h(x["q"][:, ts]), h(x["qI"][:, ts]), h(x["w"][:, ts])
+            kv_w, q_pos = h(x["kv_w"]), np.arange(S, dtype=np.int32).reshape(1, S)
+            t0 = time.perf_counter()
+            kv = oracle.round_bf16(oracle.csa_compress(*srcs, self.m, d_rope=64))
+            kk = oracle.round_f32(oracle.csa_compress(*isrcs, self.m))
+            kc, ks = oracle.mxfp4_encode(kk)
+            t1 = time.perf_counter()
+            qc, qs = oracle.mxfp4_encode(qI)
+            ne = np.array([self.N], np.int32)
+            idx, _ = oracle.indexer_topk(qc, w, kc, sel(q_pos), ne, self.m, self.k, q_scale=qs, k_scale=ks)
+            oracle.sparse_attn(q, sel(q_pos), kv, idx[None], kv_w, np.zeros(1, np.int32), self.W,
+                               np.zeros(self.H, np.float32), self.dv, 64, self.scale)
+            t2 = time.perf_counter()
+        else:
+            c, z, bias = h(x["c"]), h(x["z"]), h(x["bias"])
+            q, kv_w, q_pos = h(x["q"][:, ts]), h(x["kv_w"]), np.arange(S, dtype=np.int32).reshape(1, S)
+            t0 = time.perf_counter()
+            kv = oracle.round_bf16(oracle.hca_compress(c, z, bias, self.m, d_rope=64))
+            t1 = time.perf_counter()
+            oracle.dense_attn(q, sel(q_pos), kv, np.array([self.N], np.int32), self.m, kv_w,
+                              np.zeros(1, np.int32), self.W, np.zeros(self.H, np.float32), self.dv, 64,
+                              self.scale)
+            t2 = time.perf_counter()
+        return t1 - t0, t2 - t1, len(ts)
+
+
 def _to_dev(torch, a, dev):
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
@@ -382,7 +572,7 @@ def run(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(dom),
+            "traffic": measured_traffic(dom, wl.name),
             "algorithmic_bytes": abytes,
             "avg_launch_us": round(avg_ms * 1e3, 2),
             "timing": "HIP events around each launch on its stream, K eager steps",
@@ -391,6 +581,105 @@ def run(args):
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args)
+    print(json.dumps(line), flush=True)
+
+
+def run_prefill(args):
+    import torch
+
+    import compressed_sparse_kv_amd as csk
+    import synth
+
+    wl = PrefillWorkload(args.workload, synth.WORKLOADS[args.workload]["seed"])
+    K, Wm = args.steps, args.warmup
+    for i in range(max(Wm, 1)):
+        wl.step(i)
+    torch.cuda.synchronize()
+    # per-kernel event-timed durations over two steps each
+    per = {}
+    for name in wl.kernels():
+        tm = csk.KernelTimer(name, 8)
+        for i in range(2):
+            wl.step(i)
+        torch.cuda.synchronize()
+        ds = tm.durations_ms()
+        tm.disarm()
+        if ds:
+            per[name] = (sum(ds) / len(ds), len(ds) / 2.0)
+    _log("per-kernel ms (avg, launches/step): " +
+         ", ".join(f"{n}={v[0]:.3f}ms x{v[1]:g}" for n, v in per.items()))
+    dom = max((n for n in per if wl.algorithmic_work(n)), key=lambda n: per[n][0] * per[n][1])
+    timer = csk.KernelTimer(dom, K * int(round(per[dom][1])))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        wl.step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    durs = timer.durations_ms()
+    timer.disarm()
+    if not durs:
+        raise RuntimeError("kernel timer recorded no launch")
+    ms_per_step = elapsed * 1e3 / K
+    value = wl.S * K / elapsed
+    avg_ms = sum(durs) / len(durs)
+    bound, work, peak, unit = wl.algorithmic_work(dom)
+    scale = 1e12 if unit == "TFLOP/s" else 1e9
+    achieved = work / (avg_ms * 1e-3) / scale
+    kern = {}
+    for n, (ms, cnt) in per.items():
+        rec = {"avg_launch_us": round(ms * 1e3, 1), "launches_per_step": cnt}
+        aw = wl.algorithmic_work(n)
+        if aw:
+            b, wk, pk, un = aw
+            a = wk / (ms * 1e-3) / (1e12 if un == "TFLOP/s" else 1e9)
+            rec.update(bound=b, achieved=round(a, 1), peak=pk, unit=un, frac=round(a / pk, 4))
+        kern[n] = rec
+    attn = [n for n in per if n.startswith("attn_bf16")]
+    if attn:
+        ab = wl.attention_hbm_bytes() / (per[attn[0]][0] * 1e-3) / 1e9
+        kern[attn[0]]["hbm_achieved_gbs"] = round(ab, 1)
+        kern[attn[0]]["hbm_frac"] = round(ab / HBM_PEAK_GBS, 4)
+    _log(f"{K} steps in {elapsed*1e3:.1f} ms -> {ms_per_step:.3f} ms/step; dominant {dom} {avg_ms:.3f} ms avg "
+         f"-> {achieved:.1f} {unit} ({achieved / peak:.1%})")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16+mxfp4" if wl.csa else "bf16",
+        "data": "synthetic",
+        "config": dict(wl.config(), launch="eager"),
+        "roofline": {
+            "kernel": dom,
+            "bound": bound,
+            "achieved": round(achieved, 1),
+            "peak": peak,
+            "unit": unit,
+            "frac": round(achieved / peak, 4),
+            "traffic": measured_traffic(dom, wl.name),
+            "algorithmic_work": work,
+            "avg_launch_us": round(avg_ms * 1e3, 1),
+            "timing": "HIP events around each launch on its stream, K eager steps",
+        },
+        "kernels": kern,
+    }
+    if not args.no_cpu_baseline:
+        n_rows = args.cpu_rows_prefill or (384 if wl.csa else wl.S)
+        tc, tr, n = wl.oracle_sample(n_rows)
+        import oracle
+
+        per_tok = tc / wl.S + tr / n
+        line["cpu_baseline"] = {
+            "value": round(1.0 / per_tok, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"compression of all {wl.N} entries ({tc:.1f} s) plus {n} query rows spread over the "
+                      f"sequence ({tr:.1f} s); tokens/s = 1 / (compression time per token + time per row)"}
     print(json.dumps(line), flush=True)
 
 
@@ -411,11 +700,12 @@ def source_hash(kernel):
     return h.hexdigest()
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed counter record
-    (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel calibration),
-    or None when there is none or the kernel's sources changed since."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    counter record (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel
+    calibration), or None when there is none or the kernel's sources changed
+    since."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_{kernel}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -459,14 +749,17 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode_1m_pair", choices=["decode_1m_pair", "csa_decode_128k"])
+    ap.add_argument("--workload", default="decode_1m_pair",
+                    choices=["decode_1m_pair", "csa_decode_128k", "hca_prefill_16k", "csa_prefill_64k"])
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--mode", default="graph", choices=["eager", "graph"],
                     help="timed steps as HIP graph replays (default) or as eager launches")
     ap.add_argument("--graph-steps", type=int, default=4, help="steps captured per graph")
     ap.add_argument("--streams", type=int, default=3, choices=[1, 3],
                     help="1: every call on one stream; 3: the data-flow split over three streams")
-    ap.add_argument("--cpu-rows", type=int, default=4)
+    ap.add_argument("--cpu-rows", type=int, default=4, help="decode: sequences the oracle runs")
+    ap.add_argument("--cpu-rows-prefill", type=int, default=None,
+                    help="prefill: query rows the oracle runs (default 384 for CSA, every row for HCA)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB device copy (counter calibration) and exit")
@@ -478,7 +771,10 @@ def main():
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
-    run(args)
+    if args.workload.endswith("prefill_16k") or args.workload.endswith("prefill_64k"):
+        run_prefill(args)
+    else:
+        run(args)
 
 
 if __name__ == "__main__":
