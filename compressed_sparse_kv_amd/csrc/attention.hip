@@ -32,6 +32,7 @@ namespace csk {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
@@ -390,6 +391,7 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint4* lds_base) {
 // row); one wave-level DMA instruction fills a 1 KB block of a tile (chunks
 // 2b and 2b+1 of its 32 rows). Waves own 16 heads each (MFMA columns).
 constexpr int MAX_EXTRA = 4;  // rows a whole-chunk workgroup takes past its tiles
+constexpr int QTILE_ROPE_PAIRS = 32;  // query-tile kernel: rotated pairs per row (d_rope <= 64)
 
 template <int D, int DV, int NW, bool DENSE, int CHUNK_TILES>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -726,6 +728,300 @@ void attn_bf16_chunk_kernel(AttnArgs a) {
   }
 }
 
+// ------------------------------------------- bf16 MFMA, query-row tiles
+// Dense attention over consecutive query rows of one sequence (prefill).
+// Rows that sit next to each other see the same compressed entries (each up
+// to its own visibility bound) and overlapping windows, so one workgroup
+// stages the union of its rows' candidates in LDS once, and every K or V
+// fragment read from LDS feeds the MFMAs of CT column tiles (16 heads of one
+// row each). Candidate j of the union: j < nvmax is compressed entry j,
+// otherwise window row w0 + j - nvmax; row i keeps j < nvis_i and the window
+// span of its own rows. Online softmax per head, with the running maximum
+// moved only when a tile's maximum passes it by more than 8 (log2 units), so
+// the accumulators are rarely rescaled (probabilities stay below 2^8).
+template <int D, int DV, int HG, int CT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bf16_qtile_kernel(AttnArgs a) {
+  constexpr int NW = 4;
+  constexpr int TQ = NW * CT / HG;           // query rows per workgroup
+  constexpr int KS = D / 32;                 // MFMA K-steps over the key dims
+  constexpr int DT = DV / 16;                // 16-row tiles of the value dims
+  constexpr int TU = 32 * D / 8;             // 16-byte units per 32-row tile
+  constexpr int BLK = D / 16;                // 1 KB DMA blocks per tile
+  constexpr int PER = BLK / NW;              // of them per wave
+  constexpr int TILES = 73728 / (64 * D);    // tiles staged at once (72 KB)
+  constexpr int RP = QTILE_ROPE_PAIRS;
+  static_assert(BLK % NW == 0 && TQ * HG == NW * CT && TILES >= 1, "unsupported shape");
+  __shared__ __align__(16) uint4 kv[TILES * TU];
+  __shared__ float2 rtab[TQ][RP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int tpb = (a.T + TQ - 1) / TQ;
+  const int b = blockIdx.x / tpb;
+  const int t0 = (blockIdx.x - b * tpb) * TQ;
+  const uint16_t* kvc = reinterpret_cast<const uint16_t*>(a.kv_c) + (int64_t)b * a.Nmax * D;
+  const uint16_t* kvw = reinterpret_cast<const uint16_t*>(a.kv_w) + (int64_t)b * a.S_w * D;
+
+  // 1. lane i < TQ reads row t0+i's position and derives its candidate
+  // spans (one vector load, issued before the q loads so that waiting for
+  // it leaves those in flight); readlane then makes them uniform
+  // (w_pos0 may be null without a window: the load then re-reads n_entries,
+  // unconditionally, so that both loads go out together)
+  const int ne_raw = a.n_entries[b];
+  const int wp_raw = (a.S_w > 0 ? a.w_pos0 : a.n_entries)[b];
+  const int ne = min(ne_raw, a.Nmax);
+  const int wpos0 = a.S_w > 0 ? wp_raw : 0;
+  const int mdiv = a.m;
+  const int li = min(lane, TQ - 1);
+  const int qpl = a.q_pos[(int64_t)b * a.T + min(t0 + li, a.T - 1)];
+  // q fragments of the wave's column tiles (rows past T load row T-1)
+  int qrow_i[CT], qh[CT];
+  uint4 qraw[CT][KS];
+#pragma unroll
+  for (int i = 0; i < CT; ++i) {
+    const int c = wave * CT + i;
+    qrow_i[i] = c / HG;
+    qh[i] = 16 * (c % HG) + col;
+    const int t = min(t0 + qrow_i[i], a.T - 1);
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + (((int64_t)b * a.T + t) * a.H + qh[i]) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qraw[i][ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g);
+  }
+  int pl, nvl, w0l, w1l;
+  {
+    const bool valid = t0 + li < a.T;
+    const int64_t p = valid ? qpl : -1;
+    pl = (int)p;
+    const int nvv = p >= 0 ? (int)((uint32_t)(p + 1) / (uint32_t)mdiv) : 0;
+    nvl = nvv < ne ? nvv : ne;
+    int64_t lo = p - a.W + 1;
+    lo = lo < 0 ? 0 : lo;
+    int64_t r0 = lo - wpos0, r1 = p - wpos0 + 1;
+    r0 = r0 < 0 ? 0 : r0;
+    r1 = r1 > a.S_w ? a.S_w : r1;
+    const bool win = valid && a.W > 0 && a.S_w > 0 && r1 > r0;
+    w0l = win ? (int)r0 : 0;
+    w1l = win ? (int)r1 : 0;
+  }
+  int rpos[TQ], rnv[TQ], rw0[TQ], rw1[TQ];
+  int nvmax = 0, w0 = 0x7fffffff, w1 = 0;
+#pragma unroll
+  for (int i = 0; i < TQ; ++i) {
+    rpos[i] = __builtin_amdgcn_readlane(pl, i);
+    rnv[i] = __builtin_amdgcn_readlane(nvl, i);
+    rw0[i] = __builtin_amdgcn_readlane(w0l, i);
+    rw1[i] = __builtin_amdgcn_readlane(w1l, i);
+    nvmax = max(nvmax, rnv[i]);
+    if (rw1[i] > rw0[i]) {
+      w0 = min(w0, rw0[i]);
+      w1 = max(w1, rw1[i]);
+    }
+  }
+  if (w1 == 0) w0 = 0;
+  const int Lt = nvmax + (w1 - w0);
+  // the column tiles' candidate spans: compressed [0, nv), window [wlo, whi)
+  int nv[CT], wlo[CT], whi[CT];
+#pragma unroll
+  for (int i = 0; i < CT; ++i) {
+    const int ri = qrow_i[i];
+    nv[i] = rnv[ri];
+    const bool win = rw1[ri] > rw0[ri];
+    wlo[i] = win ? nvmax + rw0[ri] - w0 : 0;
+    whi[i] = win ? nvmax + rw1[ri] - w0 : 0;
+  }
+  // an ordinary store into the KV buffer (the DMA intrinsic is not seen as
+  // a writer of it, and without one the reads below could be folded away),
+  // finished by every wave before any DMA is issued
+  kv[tid] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+
+  const int row = lane & 31;
+  auto stage = [&](int s0, int nt) {
+    // every KV row of a stage by LDS DMA; slots past Lt read row 0 of the
+    // cache (finite data, masked)
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      if (t < nt) {
+        const int j = s0 + 32 * t + row;
+        const uint16_t* src = j < nvmax ? kvc + (int64_t)j * D : (j < Lt ? kvw + (int64_t)(w0 + j - nvmax) * D : kvc);
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          const int bb = wave + NW * q;
+          lds_dma16(src + 8 * (2 * bb + (lane >> 5)), kv + t * TU + bb * 64);
+        }
+      }
+    }
+  };
+  int nt = min(TILES, (Lt + 31) / 32);
+  if (Lt > 0) stage(0, nt);
+
+  // 2. cos/sin of every row's position while the first stage lands
+  const int npairs = a.d_rope / 2;
+  for (int e = tid; e < TQ * RP; e += 64 * NW) {
+    const int i = e / RP, pr = e - i * RP;
+    if (pr < npairs) {
+      float cs, sn;
+      rope_cs((double)rpos[i], a.rope.theta[pr], &cs, &sn);
+      rtab[i][pr] = make_float2(cs, sn);
+    }
+  }
+  __syncthreads();
+
+  v8bf qf[CT][KS];
+  {
+    const int rope0 = D - a.d_rope;
+#pragma unroll
+    for (int i = 0; i < CT; ++i)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int d0 = 32 * ks + 8 * g;
+        float x[8];
+        const uint32_t wv[4] = {qraw[i][ks].x, qraw[i][ks].y, qraw[i][ks].z, qraw[i][ks].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          x[2 * u] = bf16_bits_to_f32(wv[u] & 0xffffu);
+          x[2 * u + 1] = bf16_bits_to_f32(wv[u] >> 16);
+        }
+        if (d0 + 8 > rope0) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int c = d0 + 2 * u;
+            if (c >= rope0) {
+              const float2 csn = rtab[qrow_i[i]][(c - rope0) / 2];
+              const float x0 = x[2 * u], x1 = x[2 * u + 1];
+              x[2 * u] = x0 * csn.x - x1 * csn.y;
+              x[2 * u + 1] = x0 * csn.y + x1 * csn.x;
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) qf[i][ks][u] = __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_bits(x[u]));
+      }
+  }
+
+  float m[CT], l[CT];
+  v4f acc[CT][DT];
+#pragma unroll
+  for (int i = 0; i < CT; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[i][dt] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  const float sl2 = a.scale * LOG2E;
+
+  for (int s0 = 0; s0 < Lt; s0 += 32 * TILES) {
+    if (s0 > 0) {
+      __syncthreads();  // every wave is done with the previous stage
+      nt = min(TILES, (Lt - s0 + 31) / 32);
+      stage(s0, nt);
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(CSK_VMCNT_LGKM0(0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    for (int t = 0; t < nt; ++t) {
+      const uint4* sb = kv + t * TU;
+      const int c0 = s0 + 32 * t;
+      // 3. S^T = K q~ for the tile's two 16-candidate halves, each K
+      // fragment shared by the wave's CT column tiles
+      v4f s[CT][2];
+#pragma unroll
+      for (int i = 0; i < CT; ++i) s[i][0] = s[i][1] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const v8bf kf = *reinterpret_cast<const v8bf*>(&sb[(4 * ks + g) * 32 + h2 * 16 + col]);
+#pragma unroll
+          for (int i = 0; i < CT; ++i)
+            s[i][h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[i][ks], s[i][h2], 0, 0, 0);
+        }
+      // 4. online softmax; lane holds candidates c0 + 16*h2 + 4g + e. The
+      // spans are uniform per column tile, so only tiles that straddle a
+      // span edge are masked element by element.
+      v8bf pf[CT];
+      float alpha[CT];
+      bool moved = false;
+#pragma unroll
+      for (int i = 0; i < CT; ++i) {
+        const bool full = c0 + 32 <= nv[i] || (c0 >= wlo[i] && c0 + 32 <= whi[i]);
+        float v[8];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[4 * h2 + e] = s[i][h2][e];
+        if (!full) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int j = c0 + 16 * (e >> 2) + 4 * g + (e & 3);
+            const int ok = (j < nv[i]) | ((unsigned)(j - wlo[i]) < (unsigned)(whi[i] - wlo[i]));
+            v[e] = ok ? v[e] : -INFINITY;
+          }
+        }
+        float tm = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+        tm = group4_max(tm) * sl2;  // scale > 0: the maximum of the scaled logits
+        const float mn = tm > m[i] + 8.f ? tm : m[i];
+        alpha[i] = mn == m[i] ? 1.f : __builtin_amdgcn_exp2f(m[i] - mn);
+        moved |= mn != m[i];
+        m[i] = mn;
+        // v_exp_f32 directly: arguments are <= 8, masked logits give 0, and
+        // a weight that underflows is negligible next to the row's largest
+        const float nm = mn == -INFINITY ? 0.f : -mn;
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(v[e], sl2, nm));
+          ps += p;
+          pf[i][e] = (__bf16)p;
+        }
+        l[i] = l[i] * alpha[i] + ps;
+      }
+      if (__ballot(moved) != 0ull) {
+#pragma unroll
+        for (int i = 0; i < CT; ++i)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) acc[i][dt] *= alpha[i];
+      }
+      // 5. O^T += V^T P^T, each V^T fragment shared by the CT column tiles
+      const uint16_t* sb16 = reinterpret_cast<const uint16_t*>(sb);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int dvb = 16 * dt + 4 * (col & 3);
+        const uint16_t* p0 = sb16 + ((dvb >> 3) * 32 + 4 * g + (col >> 2)) * 8 + (dvb & 7);
+        const v8bf vf = vt_fragment(p0, p0 + 16 * 8);
+#pragma unroll
+        for (int i = 0; i < CT; ++i) acc[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[i], acc[i][dt], 0, 0, 0);
+      }
+    }
+  }
+
+  // 6. normalise with the sink and write
+#pragma unroll
+  for (int i = 0; i < CT; ++i) {
+    const float lt = group4_sum(l[i]);
+    const int t = t0 + qrow_i[i];
+    if (t >= a.T) continue;
+    const int64_t r = (int64_t)b * a.T + t;
+    float M, inv_z, lse;
+    finish_row(m[i], lt, a.sink, qh[i], &M, &inv_z, &lse);
+    const float f = (m[i] == -INFINITY) ? 0.f : exp2f(m[i] - M) * inv_z;
+    uint16_t* ob = reinterpret_cast<uint16_t*>(a.out) + (r * a.H + qh[i]) * DV;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d0 = 16 * dt + 4 * g;
+      const v2bf lo = {(__bf16)(acc[i][dt][0] * f), (__bf16)(acc[i][dt][1] * f)};
+      const v2bf hi = {(__bf16)(acc[i][dt][2] * f), (__bf16)(acc[i][dt][3] * f)};
+      *reinterpret_cast<uint2*>(ob + d0) = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+    }
+    if (a.lse && g == 0) a.lse[r * a.H + qh[i]] = lse;
+  }
+}
+
 // ------------------------------------------------------------ VALU path
 // One wave per (row, head): 64 candidates at a time, each lane one
 // candidate; online softmax in fp32; lane c accumulates value channels
@@ -902,6 +1198,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 struct AttnPlan {
   int chunk, nch, tiles, extra;
   bool mfma, whole;
+  bool qtile;   // dense prefill: query-row tiles
+  int qt_ct;    // column tiles per wave of the query-tile kernel
   size_t off_o, off_ml, total;
 };
 
@@ -915,11 +1213,28 @@ static bool mfma_shape(int H, int D, int dv, int dtype) {
 // waves.
 static bool chunk_kernel_shape(int H, int D) { return (D / 4) % (H / 16) == 0; }
 
-static AttnPlan plan_attn(int B, int T, int H, int D, int dv, int Lc, int W, int dtype) {
+// The query-tile kernel keeps CT column tiles of 16 heads per wave (its q
+// and accumulator registers grow with D), and a workgroup's four waves must
+// cover whole rows.
+static int qtile_ct(int H, int D) {
+  const int ct = D <= 128 ? 2 : 1;
+  return (D <= 256 && (4 * ct) % (H / 16) == 0) ? ct : 0;
+}
+
+static AttnPlan plan_attn(bool dense, int B, int T, int H, int D, int dv, int Lc, int W, int dtype) {
   AttnPlan p{};
   const int64_t R = (int64_t)B * T;
   const int total = Lc + W;
   p.mfma = mfma_shape(H, D, dv, dtype);
+  // dense attention over many consecutive query rows: query-row tiles, rows
+  // kept whole
+  p.qt_ct = p.mfma ? qtile_ct(H, D) : 0;
+  p.qtile = dense && p.qt_ct > 0 && T >= 16;
+  if (p.qtile) {
+    p.chunk = total;
+    p.nch = 1;
+    return p;
+  }
   const int gran = p.mfma ? 32 : 64;
   int64_t want = ceil_div(R * (int64_t)total, 256);  // aim at ~256 workgroups
   int64_t ch = ceil_div(want < 128 ? 128 : want, gran) * gran;
@@ -992,7 +1307,7 @@ static int attn_common(const char* fn, bool dense, const void* q, const int32_t*
   if (dv > 576) return fail(CSK_EUNSUPPORTED, f + ": dv > 576 not built");
   const int Wslots = S_w > 0 ? W : 0;
   const int Lc = dense ? Nmax : k;
-  AttnPlan p = plan_attn(B, T, H, D, dv, Lc, Wslots, dtype);
+  AttnPlan p = plan_attn(dense, B, T, H, D, dv, Lc, Wslots, dtype);
   if (p.nch > MERGE_MAX_CH || (int64_t)p.nch * H > 65535 || (int64_t)B * T > (1LL << 30))
     return fail(CSK_EUNSUPPORTED, f + ": problem too large");
   if (p.total > 0 && (!workspace || ws_bytes < p.total))
@@ -1011,6 +1326,20 @@ static int attn_common(const char* fn, bool dense, const void* q, const int32_t*
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const unsigned R = (unsigned)(B * T);
   int rc;
+  if (p.qtile) {
+    if (d_rope > 2 * QTILE_ROPE_PAIRS)
+      return fail(CSK_EUNSUPPORTED, f + ": dense prefill with more than 64 rotated channels is not built");
+    const int HG = H / 16, CT = p.qt_ct, TQ = 4 * CT / HG;
+    dim3 grid((unsigned)(B * ceil_div(T, TQ))), block(256);
+    rc = CSK_EUNSUPPORTED;
+#define CSK_QT_CASE(d, v, hg, ct) \
+  if (D == d && dv == v && HG == hg && CT == ct) rc = launch("attn_bf16_dense", attn_bf16_qtile_kernel<d, v, hg, ct>, grid, block, 0, s, a);
+    CSK_QT_CASE(128, 128, 1, 2) CSK_QT_CASE(128, 128, 2, 2) CSK_QT_CASE(128, 128, 4, 2)
+    CSK_QT_CASE(64, 64, 1, 2) CSK_QT_CASE(64, 64, 2, 2) CSK_QT_CASE(64, 64, 4, 2)
+    CSK_QT_CASE(256, 256, 1, 1) CSK_QT_CASE(256, 256, 2, 1) CSK_QT_CASE(256, 256, 4, 1)
+#undef CSK_QT_CASE
+    return rc;
+  }
   if (p.mfma) {
     dim3 grid(R, p.nch), block(64 * (H / 16));
 const int NW = H / 16;
@@ -1051,14 +1380,14 @@ extern "C" {
 
 size_t sparse_attn_workspace_size(int B, int T, int H, int D, int dv, int k, int W, int dtype) {
   if (B <= 0 || T <= 0 || H <= 0 || D <= 0 || dv <= 0 || k < 0 || W < 0) return 0;
-  return csk::plan_attn(B, T, H, D, dv, k, W, dtype).total;
+  return csk::plan_attn(false, B, T, H, D, dv, k, W, dtype).total;
 }
 
 size_t dense_compressed_attn_workspace_size(int B, int T, int H, int D, int dv, int Nmax, int m,
                                             int W, int dtype) {
   (void)m;
   if (B <= 0 || T <= 0 || H <= 0 || D <= 0 || dv <= 0 || Nmax <= 0 || W < 0) return 0;
-  return csk::plan_attn(B, T, H, D, dv, Nmax, W, dtype).total;
+  return csk::plan_attn(true, B, T, H, D, dv, Nmax, W, dtype).total;
 }
 
 int sparse_attn(const void* q, const int32_t* q_pos, const void* kv_c, int Nmax,

@@ -83,10 +83,12 @@ def test_sparse_no_sink_no_window_and_empty():
     assert np.all(o[0, 0] == 0) and np.all(np.isneginf(host(lse)[0, 0]))   # no candidate, no sink
 
 
-def _dense_case(seed, B, T, H, D, dv, N, m, S_w, W, bf16, d_rope, decode):
+def _dense_case(seed, B, T, H, D, dv, N, m, S_w, W, bf16, d_rope, decode, q_pos=None):
     g = synth.rng(seed)
     q, kv_c, kv_w = _inputs(g, B, T, H, D, N, S_w, bf16)
-    if decode:
+    if q_pos is not None:
+        w_pos0 = np.zeros(B, np.int32)
+    elif decode:
         q_pos = np.full((B, T), m * N - 1, np.int32)
         w_pos0 = np.full(B, m * N - S_w, np.int32)
     else:
@@ -113,6 +115,26 @@ def test_dense_prefill_hca_shape():
     # 16 heads x dim 128, m' = 128, window 128: the HCA prefill layer shape
     _dense_case(701, B=1, T=2048, H=16, D=128, dv=128, N=16, m=128, S_w=2048, W=128, bf16=True, d_rope=64,
                 decode=False)
+
+
+@pytest.mark.parametrize("B,T,H,D,N,m,S_w,W", [
+    (2, 100, 32, 128, 30, 4, 100, 16),      # rows per tile not dividing T, two head groups
+    (1, 1200, 16, 128, 300, 4, 1200, 128),  # candidate union staged in LDS twice
+    (2, 40, 64, 64, 12, 4, 40, 8),          # four head groups, two rows per tile
+    (1, 70, 16, 256, 20, 4, 70, 32),        # one column tile per wave
+])
+def test_dense_prefill_query_tiles(B, T, H, D, N, m, S_w, W):
+    _dense_case(720 + T + H, B=B, T=T, H=H, D=D, dv=D, N=N, m=m, S_w=S_w, W=W, bf16=True,
+                d_rope=min(64, D // 2), decode=False)
+
+
+def test_dense_prefill_unordered_positions():
+    # query rows at scattered positions: a tile's candidate union spans
+    # several windows and its rows keep different subsets of it
+    g = synth.rng(731)
+    q_pos = np.stack([np.sort(g.permutation(400)[:48]), g.permutation(400)[:48]]).astype(np.int32)
+    _dense_case(732, B=2, T=48, H=16, D=128, dv=128, N=100, m=4, S_w=400, W=24, bf16=True, d_rope=64,
+                decode=False, q_pos=q_pos)
 
 
 def test_dense_decode_split():
