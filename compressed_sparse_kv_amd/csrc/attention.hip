@@ -31,6 +31,7 @@
 namespace csk {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -1022,6 +1023,311 @@ void attn_bf16_qtile_kernel(AttnArgs a) {
   }
 }
 
+// ------------------------------------------ bf16 32x32 MFMA, whole rows
+// Sparse attention of one query row with 64 heads (prefill: rows kept
+// whole). The row's candidates stream through LDS in 64-row tiles, two
+// buffers deep, each filled by LDS DMA. Wave w = (head group hg = w&1,
+// half ch = w>>1) scores 32 heads against tile rows [32ch, 32ch+32) with
+// 32x32x16 MFMAs (S^T = K q~^T; the q~ fragments stay in registers). The
+// two waves of a head group then agree on the running maximum (tile maxima
+// through LDS) and swap their probabilities, and each accumulates
+// O^T += V^T P^T over all 64 rows for its half of the value dims.
+// LDS tile layout: 16-byte units; chunk c (dims 8c..8c+7) of row j sits at
+// unit 64c + (j ^ 4(c&3)). The row swizzle puts the four chunks that one
+// transposed V^T read touches on distinct banks. A wave's DMA chunks all
+// have the same c&3, so each lane loads one row (lane ^ 4w) throughout.
+constexpr int R32_QB = 2;  // K fragments per pipelined block (two blocks in flight)
+constexpr int R32_VB = 2;  // V^T fragments per pipelined block
+
+template <int D, int DV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_bf16_row32_kernel(AttnArgs a) {
+  constexpr int NCH = D / 8;             // 16-byte chunks per KV row
+  constexpr int TU = NCH * 64;           // units per 64-row tile
+  constexpr int KS = D / 16;             // 32x32x16 K-steps over the key dims
+  constexpr int HDT = DV / 64;           // 32-row value tiles per wave (half of DV)
+  constexpr int CPW = NCH / 4;           // DMA instructions per wave per tile
+  static_assert(NCH % 4 == 0 && DV % 64 == 0 && DV <= D, "unsupported shape");
+  __shared__ __align__(16) uint4 buf0[TU];
+  __shared__ __align__(16) uint4 buf1[TU];
+  __shared__ __align__(16) uint4 pex[4][2][64];  // probabilities, B-operand fragments
+  __shared__ float mx[4][32];                      // tile maxima per head
+  __shared__ float xl[4][32];                      // end-of-row sums per head
+  __shared__ float2 rtab[MAX_ROPE_PAIRS];
+
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // wave-uniform (readfirstlane): everything derived from it stays scalar,
+  // the DMA destinations (M0) among them
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hg = wave & 1, ch = wave >> 1, pw = wave ^ 2;
+  const int c32 = lane & 31, hi = lane >> 5;
+  const int head = 32 * hg + c32;
+  const RowInfo ri = row_info(a, r);
+  const uint16_t* kvc = reinterpret_cast<const uint16_t*>(a.kv_c) + (int64_t)ri.b * a.Nmax * D;
+  const uint16_t* kvw = reinterpret_cast<const uint16_t*>(a.kv_w) + (int64_t)ri.b * a.S_w * D;
+  const int total = a.Lc + a.W;
+  const int ntiles = (total + 63) / 64;
+  const int32_t* idxr = a.idx + (int64_t)r * a.k;
+  const int drow = lane ^ (4 * wave);  // the tile row this lane's DMAs load
+
+  // the index read is issued unconditionally (clamped), so that every wave
+  // issues the same loads in the same order and the constant wait counts
+  // below hold
+  auto idx_load = [&](int j) -> int { return idxr[min(j, a.k - 1)]; };
+  auto code_of = [&](int j, int e) -> int {
+    if (j < a.Lc) return (e < 0 || e >= a.Nmax) ? -1 : e;
+    const int wrow = ri.wr0 + (j - a.Lc);
+    return (j < total && wrow < ri.wr1) ? -2 - wrow : -1;
+  };
+  auto dma_tile = [&](uint4* dst, int code) {
+    const uint16_t* src = code >= 0 ? kvc + (int64_t)code * D : (code <= -2 ? kvw + (int64_t)(-2 - code) * D : kvc);
+#pragma unroll
+    for (int q = 0; q < CPW; ++q) {
+      const int c = wave + 4 * q;
+      lds_dma16(src + 8 * c, dst + 64 * c);
+    }
+  };
+  // unit of (row j, chunk c)
+  auto unit = [](int j, int c) { return 64 * c + (j ^ (4 * (c & 3))); };
+
+  // 1. q loads, the first three tiles' indices, the RoPE table
+  uint4 qraw[KS];
+  {
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + head) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qraw[ks] = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hi);
+  }
+  const int e0 = idx_load(drow), e1 = idx_load(64 + drow);
+  if (tid < a.d_rope / 2) {
+    float cs, sn;
+    rope_cs((double)ri.p, a.rope.theta[tid], &cs, &sn);
+    rtab[tid] = make_float2(cs, sn);
+  }
+  // ordinary stores into the KV buffers: the DMA intrinsic is not seen as a
+  // writer of them, and without one the reads below could be folded away
+  buf0[tid] = make_uint4(0u, 0u, 0u, 0u);
+  buf1[tid] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+
+  // 2. rotated query fragments (B operand: head c32, dims 16ks + 8hi ..)
+  v8bf qf[KS];
+  {
+    const int rope0 = D - a.d_rope;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int d0 = 16 * ks + 8 * hi;
+      float x[8];
+      const uint32_t wv[4] = {qraw[ks].x, qraw[ks].y, qraw[ks].z, qraw[ks].w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        x[2 * u] = bf16_bits_to_f32(wv[u] & 0xffffu);
+        x[2 * u + 1] = bf16_bits_to_f32(wv[u] >> 16);
+      }
+      if (d0 + 8 > rope0) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = d0 + 2 * u;
+          if (c >= rope0) {
+            const float2 csn = rtab[(c - rope0) / 2];
+            const float x0 = x[2 * u], x1 = x[2 * u + 1];
+            x[2 * u] = x0 * csn.x - x1 * csn.y;
+            x[2 * u + 1] = x0 * csn.y + x1 * csn.x;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) qf[ks][u] = (__bf16)x[u];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. tiles 0 and 1 requested, then tile 2's index. Issue order per wave:
+  // DMA(0), DMA(1), idx(2) | tile 1: DMA(2), idx(3) | tile 2: DMA(3), idx(4)
+  // ... so before tile t (t >= 1) only idx(t+1) may still be in flight, and
+  // before tile 0 also DMA(1).
+  int code_cur = code_of(drow, e0);
+  int code_nxt = code_of(64 + drow, e1);
+  dma_tile(buf0, code_cur);
+  dma_tile(buf1, code_nxt);
+  int e_pend = idx_load(128 + drow);
+
+  v16f acc[HDT];
+#pragma unroll
+  for (int u = 0; u < HDT; ++u)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[u][i] = 0.f;
+  float m_run = -INFINITY, l_part = 0.f;
+  const float sl2 = a.scale * LOG2E;
+  // V^T fragment geometry: lane (16-group g16, k4 = (lane&15)>>2, j4 = lane&3)
+  const int k4 = (lane & 15) >> 2, j4 = lane & 3, g16 = c32 >> 4;
+
+  auto tile_step = [&](const uint4* sb, uint4* other, int t) {
+    asm volatile("" ::: "memory");
+    if (t == 0) __builtin_amdgcn_s_waitcnt(CSK_VMCNT_LGKM0(CPW + 1));
+    else __builtin_amdgcn_s_waitcnt(CSK_VMCNT_LGKM0(1));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // code_cur: this lane's DMA row of tile t; afterwards, of tile t+1
+    const int code_t = code_cur;
+    if (t >= 1) {
+      // every wave is past tile t-1: its buffer takes tile t+1
+      code_cur = code_of(64 * (t + 1) + drow, e_pend);
+      dma_tile(other, code_cur);
+      e_pend = idx_load(64 * (t + 2) + drow);
+    } else {
+      code_cur = code_nxt;  // tile 1, requested with tile 0
+    }
+    // bit (j ^ 4w) tells whether tile row j holds a candidate
+    const uint64_t vmask = __ballot(code_t != -1);
+
+    // S^T[row 32ch + (8(i/4) + 4hi + i%4), head c32]
+    v16f s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    {
+      // chunk 2ks + hi has chunk&3 = hi (ks even) or 2 + hi (ks odd): two
+      // lane bases, then compile-time offsets of 128 units per K-step
+      const int krow = 32 * ch + c32;
+      const uint4* kb_e = sb + 64 * hi + (krow ^ (4 * hi));
+      const uint4* kb_o = sb + 64 * hi + (krow ^ (8 + 4 * hi));
+      constexpr int QB = R32_QB, NQB = (KS + QB - 1) / QB;
+      v8bf kf[2][QB];
+      auto load_k = [&](int blk, v8bf (&dst)[QB]) {
+#pragma unroll
+        for (int u = 0; u < QB; ++u) {
+          const int ks = blk * QB + u;
+          if (ks < KS) dst[u] = *reinterpret_cast<const v8bf*>((ks & 1 ? kb_o : kb_e) + 128 * ks);
+        }
+      };
+      load_k(0, kf[0]);
+#pragma unroll
+      for (int blk = 0; blk < NQB; ++blk) {
+        if (blk + 1 < NQB) load_k(blk + 1, kf[(blk + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < QB; ++u) {
+          const int ks = blk * QB + u;
+          if (ks < KS) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[blk & 1][u], qf[ks], s, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // mask (only when the tile has empty rows); this half's maxima to LDS
+    if (vmask != ~0ull) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 32 * ch + 8 * (i >> 2) + 4 * hi + (i & 3);
+        s[i] = ((vmask >> (row ^ (4 * wave))) & 1ull) ? s[i] : -INFINITY;
+      }
+    }
+    float tm = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) tm = fmaxf(tm, s[i]);
+    tm = pair32_max(tm);
+    if (hi == 0) mx[wave][c32] = tm;
+    __syncthreads();
+    // one running maximum for the head group (both halves compute it alike)
+    tm = fmaxf(tm, mx[pw][c32]) * sl2;
+    const float mn = tm > m_run + 8.f ? tm : m_run;
+    const float alpha = mn == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
+    const bool moved = mn != m_run;
+    m_run = mn;
+    const float nm = mn == -INFINITY ? 0.f : -mn;
+    v8bf pf[2];
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      // v_exp_f32 directly: arguments are <= 8; masked rows give 0
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl2, nm));
+      ps += pv;
+      pf[i >> 3][i & 7] = (__bf16)pv;
+    }
+    l_part = l_part * alpha + ps;
+    pex[wave][0][lane] = __builtin_bit_cast(uint4, pf[0]);
+    pex[wave][1][lane] = __builtin_bit_cast(uint4, pf[1]);
+    if (__ballot(moved) != 0ull) {
+#pragma unroll
+      for (int u = 0; u < HDT; ++u) acc[u] *= alpha;
+    }
+    __syncthreads();
+    v8bf pp[2];
+    pp[0] = __builtin_bit_cast(v8bf, pex[pw][0][lane]);
+    pp[1] = __builtin_bit_cast(v8bf, pex[pw][1][lane]);
+    // O^T[dv, head] += V^T P^T over the 64 rows: K-chunk kc holds rows
+    // 32(kc/2) + 16(kc%2) + {4hi+k, 8+4hi+k}, k < 4, whose probabilities are
+    // elements 8(kc%2) .. +7 of half kc/2's lanes
+    {
+      // dims d = 32(ch*HDT + dtl) + 16g16 + 4j4: chunk 4(ch*HDT + dtl) + cl
+      // with cl = 2g16 + j4/2, so chunk&3 = cl for every value tile; rows
+      // 16kc + (4hi + k4) and +8: two lane bases, compile-time offsets
+      const uint16_t* sb16 = reinterpret_cast<const uint16_t*>(sb) + 256 * 8 * ch * HDT;
+      const int cl = 2 * g16 + (j4 >> 1);
+      const uint16_t* vb0 = sb16 + (64 * cl + ((4 * hi + k4) ^ (4 * cl))) * 8 + 4 * (j4 & 1);
+      const uint16_t* vb1 = sb16 + (64 * cl + ((8 + 4 * hi + k4) ^ (4 * cl))) * 8 + 4 * (j4 & 1);
+      constexpr int VB = R32_VB;
+      constexpr int NV = 4 * HDT, NVB = NV / VB;
+      v8bf vf[2][VB];
+      auto load_v = [&](int blk, v8bf (&dst)[VB]) {
+#pragma unroll
+        for (int u = 0; u < VB; ++u) {
+          const int v = blk * VB + u;
+          const int kc = v / HDT, dtl = v % HDT;
+          const int off = (256 * dtl + 16 * kc) * 8;
+          dst[u] = vt_fragment(vb0 + off, vb1 + off);
+        }
+      };
+      load_v(0, vf[0]);
+#pragma unroll
+      for (int blk = 0; blk < NVB; ++blk) {
+        if (blk + 1 < NVB) load_v(blk + 1, vf[(blk + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < VB; ++u) {
+          const int v = blk * VB + u;
+          const int kc = v / HDT, dtl = v % HDT;
+          const v8bf pb = (kc >> 1) == ch ? pf[kc & 1] : pp[kc & 1];
+          acc[dtl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[blk & 1][u], pb, acc[dtl], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  for (int t = 0; t < ntiles; t += 2) {
+    tile_step(buf0, buf1, t);
+    if (t + 1 < ntiles) tile_step(buf1, buf0, t + 1);
+  }
+
+  // 4. the head group's sum over both halves, the sink, the output
+  const float l_half = pair32_sum(l_part);
+  if (hi == 0) xl[wave][c32] = l_half;
+  __builtin_amdgcn_s_waitcnt(CSK_VMCNT_LGKM0(0));  // no DMA outlives the workgroup
+  __syncthreads();
+  const float l_tot = l_half + xl[pw][c32];
+  const float s2 = a.sink ? a.sink[head] * LOG2E : -INFINITY;
+  const float M = fmaxf(m_run, s2);
+  float f = 0.f, z = 0.f;
+  if (M != -INFINITY) {
+    const float fo = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
+    z = l_tot * fo + (a.sink ? exp2f(s2 - M) : 0.f);
+    f = z > 0.f ? fo / z : 0.f;
+  }
+  uint16_t* ob = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)r * a.H + head) * DV + 32 * ch * HDT;
+#pragma unroll
+  for (int u = 0; u < HDT; ++u)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const v2bf lo = {(__bf16)(acc[u][4 * q4] * f), (__bf16)(acc[u][4 * q4 + 1] * f)};
+      const v2bf hh = {(__bf16)(acc[u][4 * q4 + 2] * f), (__bf16)(acc[u][4 * q4 + 3] * f)};
+      *reinterpret_cast<uint2*>(ob + 32 * u + 8 * q4 + 4 * hi) =
+          make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hh));
+    }
+  if (a.lse && ch == 0 && hi == 0)
+    a.lse[(int64_t)r * a.H + head] = M == -INFINITY ? -INFINITY : (M + log2f(z)) * LN2;
+}
+
 // ------------------------------------------------------------ VALU path
 // One wave per (row, head): 64 candidates at a time, each lane one
 // candidate; online softmax in fp32; lane c accumulates value channels
@@ -1221,6 +1527,12 @@ static int qtile_ct(int H, int D) {
   return (D <= 256 && (4 * ct) % (H / 16) == 0) ? ct : 0;
 }
 
+// The 32x32 whole-row kernel: 64 heads, value dims split into two halves of
+// 32-row tiles, DMA chunks split over four waves.
+static bool row32_shape(int D, int dv) {
+  return (D == 576 && dv == 512) || (D == 256 && dv == 256) || (D == 128 && dv == 128) || (D == 64 && dv == 64);
+}
+
 static AttnPlan plan_attn(bool dense, int B, int T, int H, int D, int dv, int Lc, int W, int dtype) {
   AttnPlan p{};
   const int64_t R = (int64_t)B * T;
@@ -1338,6 +1650,14 @@ static int attn_common(const char* fn, bool dense, const void* q, const int32_t*
     CSK_QT_CASE(64, 64, 1, 2) CSK_QT_CASE(64, 64, 2, 2) CSK_QT_CASE(64, 64, 4, 2)
     CSK_QT_CASE(256, 256, 1, 1) CSK_QT_CASE(256, 256, 2, 1) CSK_QT_CASE(256, 256, 4, 1)
 #undef CSK_QT_CASE
+    return rc;
+  }
+  if (p.mfma && !dense && !p.whole && p.nch == 1 && H == 64 && k >= 1 && row32_shape(D, dv)) {
+    rc = CSK_EUNSUPPORTED;
+#define CSK_R32_CASE(d, v) \
+  if (D == d && dv == v) rc = launch("attn_bf16_sparse", attn_bf16_row32_kernel<d, v>, dim3(R), dim3(256), 0, s, a);
+    CSK_R32_CASE(576, 512) CSK_R32_CASE(256, 256) CSK_R32_CASE(128, 128) CSK_R32_CASE(64, 64)
+#undef CSK_R32_CASE
     return rc;
   }
   if (p.mfma) {

@@ -150,6 +150,16 @@ __device__ __forceinline__ float group4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Lane l and lane l^32 (the two row halves of a 32x32 MFMA output column).
+__device__ __forceinline__ float pair32_max(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
 // Reductions over all 64 lanes: within quads (quad_perm), across the quads
 // of a row (row rotations), then across the four rows (group4_*).
 #define CSK_DPP_F(x, ctrl) \

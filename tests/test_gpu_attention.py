@@ -69,6 +69,14 @@ def test_sparse_decode_split(H, D, dv):
                  d_rope=min(64, D // 2), decode=True)
 
 
+@pytest.mark.parametrize("D,dv", [(576, 512), (256, 256), (128, 128), (64, 64)])
+def test_sparse_prefill_whole_rows(D, dv):
+    # 320 rows of up to 150 selected entries + 40 window tokens: rows stay
+    # whole, three 64-row tiles with a ragged last one, rows with padding
+    _sparse_case(610 + D, B=2, T=160, H=64, D=D, dv=dv, N=700, k=150, S_w=200, W=40, bf16=True,
+                 d_rope=min(64, D // 2))
+
+
 def test_sparse_no_sink_no_window_and_empty():
     g = synth.rng(604)
     B, T, H, D, N = 1, 3, 64, 576, 50
