@@ -1023,6 +1023,16 @@ void attn_bf16_qtile_kernel(AttnArgs a) {
   }
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// accesses, not for its global loads (__syncthreads would also wait for
+// every LDS DMA in flight).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(CSK_VMCNT_LGKM0(63));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------ bf16 32x32 MFMA, whole rows
 // Sparse attention of one query row with 64 heads (prefill: rows kept
 // whole). The row's candidates stream through LDS in 64-row tiles, two
@@ -1032,10 +1042,15 @@ void attn_bf16_qtile_kernel(AttnArgs a) {
 // two waves of a head group then agree on the running maximum (tile maxima
 // through LDS) and swap their probabilities, and each accumulates
 // O^T += V^T P^T over all 64 rows for its half of the value dims.
-// LDS tile layout: 16-byte units; chunk c (dims 8c..8c+7) of row j sits at
-// unit 64c + (j ^ 4(c&3)). The row swizzle puts the four chunks that one
-// transposed V^T read touches on distinct banks. A wave's DMA chunks all
-// have the same c&3, so each lane loads one row (lane ^ 4w) throughout.
+// LDS tile layout (16-byte units): rows in groups of eight, G = j/8; chunk
+// c (dims 8c..8c+7) of row j sits at unit G*8*NCH + 8*(c ^ (G&1)) + j%8.
+// One DMA instruction (64 consecutive units) then reads 8 chunks of each
+// of eight rows, i.e. eight 128-byte runs (for rows gathered from a large
+// cache this spreads better than longer runs from fewer rows), and both the
+// K reads (32 rows of one chunk) and the transposed V^T reads (4 rows x 2
+// chunks per 16 lanes) find their units on distinct bank groups. The DMA
+// of the next tile is issued one instruction per K-step block of the
+// current tile's QK.
 constexpr int R32_QB = 2;  // K fragments per pipelined block (two blocks in flight)
 constexpr int R32_VB = 2;  // V^T fragments per pipelined block
 
@@ -1043,11 +1058,14 @@ template <int D, int DV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bf16_row32_kernel(AttnArgs a) {
   constexpr int NCH = D / 8;             // 16-byte chunks per KV row
-  constexpr int TU = NCH * 64;           // units per 64-row tile
+  constexpr int GU = 8 * NCH;            // units per group of eight rows
+  constexpr int TU = 8 * GU;             // units per 64-row tile
+  constexpr int IPG = NCH / 8;           // DMA instructions per row group
   constexpr int KS = D / 16;             // 32x32x16 K-steps over the key dims
   constexpr int HDT = DV / 64;           // 32-row value tiles per wave (half of DV)
   constexpr int CPW = NCH / 4;           // DMA instructions per wave per tile
-  static_assert(NCH % 4 == 0 && DV % 64 == 0 && DV <= D, "unsupported shape");
+  constexpr int QB = R32_QB, NQB = KS / QB;
+  static_assert(NCH % 8 == 0 && DV % 64 == 0 && DV <= D && KS % QB == 0 && NQB == CPW, "unsupported shape");
   __shared__ __align__(16) uint4 buf0[TU];
   __shared__ __align__(16) uint4 buf1[TU];
   __shared__ __align__(16) uint4 pex[4][2][64];  // probabilities, B-operand fragments
@@ -1058,8 +1076,7 @@ void attn_bf16_row32_kernel(AttnArgs a) {
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  // wave-uniform (readfirstlane): everything derived from it stays scalar,
-  // the DMA destinations (M0) among them
+  // wave-uniform (readfirstlane): everything derived from it stays scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hg = wave & 1, ch = wave >> 1, pw = wave ^ 2;
   const int c32 = lane & 31, hi = lane >> 5;
@@ -1070,36 +1087,54 @@ void attn_bf16_row32_kernel(AttnArgs a) {
   const int total = a.Lc + a.W;
   const int ntiles = (total + 63) / 64;
   const int32_t* idxr = a.idx + (int64_t)r * a.k;
-  const int drow = lane ^ (4 * wave);  // the tile row this lane's DMAs load
 
-  // the index read is issued unconditionally (clamped), so that every wave
-  // issues the same loads in the same order and the constant wait counts
-  // below hold
+  // index read (clamped, issued unconditionally), code (>= 0 entry, <= -2
+  // window row, -1 empty), KV row address (selects, no branches)
   auto idx_load = [&](int j) -> int { return idxr[min(j, a.k - 1)]; };
   auto code_of = [&](int j, int e) -> int {
     if (j < a.Lc) return (e < 0 || e >= a.Nmax) ? -1 : e;
     const int wrow = ri.wr0 + (j - a.Lc);
     return (j < total && wrow < ri.wr1) ? -2 - wrow : -1;
   };
-  auto dma_tile = [&](uint4* dst, int code) {
-    const uint16_t* src = code >= 0 ? kvc + (int64_t)code * D : (code <= -2 ? kvw + (int64_t)(-2 - code) * D : kvc);
-#pragma unroll
-    for (int q = 0; q < CPW; ++q) {
-      const int c = wave + 4 * q;
-      lds_dma16(src + 8 * c, dst + 64 * c);
-    }
+  auto row_addr = [&](int code) -> const uint16_t* {
+    const bool win = code <= -2;
+    const int rowi = code >= 0 ? code : (win ? -2 - code : 0);
+    return (win ? kvw : kvc) + (int64_t)rowi * D;
   };
-  // unit of (row j, chunk c)
-  auto unit = [](int j, int c) { return 64 * c + (j ^ (4 * (c & 3))); };
+  // DMA instruction q of this wave: units 64i .. 64i+63, i = CPW*wave + q,
+  // so the wave covers row groups 2w and 2w+1 and instruction q is block
+  // q%IPG of group 2w + q/IPG (compile-time but for the wave term, and
+  // G&1 = q/IPG&1); the lane loads row 16w + 8(q/IPG) + lane%8, whose
+  // address it holds itself (two per tile), at chunk 8*block + lane/8,
+  // swizzled
+  const int dma_row = 16 * wave + (lane & 7);
+  const int dma_c0 = 8 * (lane >> 3), dma_c1 = 8 * ((lane >> 3) ^ 1);  // elements
+  auto dma_one = [&](uint4* dst, const uint16_t* const (&rp)[2], int q) {
+    const int gq = q / IPG, blk = q % IPG;
+    const uint16_t* src = rp[gq] + 64 * blk + ((gq & 1) ? dma_c1 : dma_c0);
+    lds_dma16(src, dst + 64 * (CPW * wave + q));
+  };
+  // tile T's index reads of this lane: row = lane (its mask bit) and the two
+  // rows its DMAs load
+  struct TileIdx { int em, e0, e1; };
+  auto tile_idx = [&](int T) -> TileIdx {
+    return TileIdx{idx_load(64 * T + lane), idx_load(64 * T + dma_row), idx_load(64 * T + dma_row + 8)};
+  };
 
-  // 1. q loads, the first three tiles' indices, the RoPE table
+  // 1. q loads, tiles 0 and 1's row addresses, the RoPE table
   uint4 qraw[KS];
   {
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + head) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qraw[ks] = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hi);
   }
-  const int e0 = idx_load(drow), e1 = idx_load(64 + drow);
+  const TileIdx ix0 = tile_idx(0), ix1 = tile_idx(1);
+  TileIdx ixp = tile_idx(2);  // index reads of tile t+2 during tile t
+  // bit j: tile row j holds a candidate (tiles t and t+1)
+  uint64_t vm_cur = __ballot(code_of(lane, ix0.em) != -1);
+  uint64_t vm_n1 = __ballot(code_of(64 + lane, ix1.em) != -1);
+  const uint16_t* rp0[2] = {row_addr(code_of(dma_row, ix0.e0)), row_addr(code_of(dma_row + 8, ix0.e1))};
+  const uint16_t* rp1[2] = {row_addr(code_of(64 + dma_row, ix1.e0)), row_addr(code_of(64 + dma_row + 8, ix1.e1))};
   if (tid < a.d_rope / 2) {
     float cs, sn;
     rope_cs((double)ri.p, a.rope.theta[tid], &cs, &sn);
@@ -1143,15 +1178,14 @@ void attn_bf16_row32_kernel(AttnArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // 3. tiles 0 and 1 requested, then tile 2's index. Issue order per wave:
-  // DMA(0), DMA(1), idx(2) | tile 1: DMA(2), idx(3) | tile 2: DMA(3), idx(4)
-  // ... so before tile t (t >= 1) only idx(t+1) may still be in flight, and
-  // before tile 0 also DMA(1).
-  int code_cur = code_of(drow, e0);
-  int code_nxt = code_of(64 + drow, e1);
-  dma_tile(buf0, code_cur);
-  dma_tile(buf1, code_nxt);
-  int e_pend = idx_load(128 + drow);
+  // 3. tiles 0 and 1 requested
+#pragma unroll
+  for (int q = 0; q < CPW; ++q) dma_one(buf0, rp0, q);
+#pragma unroll
+  for (int q = 0; q < CPW; ++q) dma_one(buf1, rp1, q);
+  // row addresses of the tile that tile t's QK requests (t+1; set at the
+  // end of tile t-1)
+  const uint16_t* rp_nxt[2] = {kvc, kvc};
 
   v16f acc[HDT];
 #pragma unroll
@@ -1160,66 +1194,61 @@ void attn_bf16_row32_kernel(AttnArgs a) {
     for (int i = 0; i < 16; ++i) acc[u][i] = 0.f;
   float m_run = -INFINITY, l_part = 0.f;
   const float sl2 = a.scale * LOG2E;
-  // V^T fragment geometry: lane (16-group g16, k4 = (lane&15)>>2, j4 = lane&3)
+
+  // K fragment base: row 32ch + c32 (group G = 4ch + c32/8, G&1 = g1),
+  // chunk 2ks + hi: unit G*GU + 8(2ks + (hi ^ g1)) + c32%8 = kb + 16ks
+  const int kg1 = (c32 >> 3) & 1;
+  const int kb = (4 * ch + (c32 >> 3)) * GU + 8 * (hi ^ kg1) + (c32 & 7);
+  // V^T fragment bases: rows 16kc + 8s + 4hi + k4 (G = 2kc + s, G&1 = s),
+  // dims 32(ch*HDT + dtl) + 16g16 + 4j4 (chunk 4(ch*HDT + dtl) + cl with
+  // cl = 2g16 + j4/2): unit base_s + 2kc*GU + 32dtl (elements x8)
   const int k4 = (lane & 15) >> 2, j4 = lane & 3, g16 = c32 >> 4;
+  const int cl = 2 * g16 + (j4 >> 1);
+  const int vbase0 = (8 * cl + 4 * hi + k4 + 32 * ch * HDT) * 8 + 4 * (j4 & 1);
+  const int vbase1 = (GU + 8 * (cl ^ 1) + 4 * hi + k4 + 32 * ch * HDT) * 8 + 4 * (j4 & 1);
 
   auto tile_step = [&](const uint4* sb, uint4* other, int t) {
+    // tile t has landed in every wave's view
     asm volatile("" ::: "memory");
-    if (t == 0) __builtin_amdgcn_s_waitcnt(CSK_VMCNT_LGKM0(CPW + 1));
-    else __builtin_amdgcn_s_waitcnt(CSK_VMCNT_LGKM0(1));
+    __builtin_amdgcn_s_waitcnt(CSK_VMCNT_LGKM0(0));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    // code_cur: this lane's DMA row of tile t; afterwards, of tile t+1
-    const int code_t = code_cur;
-    if (t >= 1) {
-      // every wave is past tile t-1: its buffer takes tile t+1
-      code_cur = code_of(64 * (t + 1) + drow, e_pend);
-      dma_tile(other, code_cur);
-      e_pend = idx_load(64 * (t + 2) + drow);
-    } else {
-      code_cur = code_nxt;  // tile 1, requested with tile 0
-    }
-    // bit (j ^ 4w) tells whether tile row j holds a candidate
-    const uint64_t vmask = __ballot(code_t != -1);
+    const bool issue = t >= 1 && t + 1 < ntiles;  // tile t+1 (tile 1 went out with tile 0)
 
-    // S^T[row 32ch + (8(i/4) + 4hi + i%4), head c32]
+    // S^T[row 32ch + (8(i/4) + 4hi + i%4), head c32]; one DMA instruction
+    // of tile t+1 per K-step block
     v16f s;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
     {
-      // chunk 2ks + hi has chunk&3 = hi (ks even) or 2 + hi (ks odd): two
-      // lane bases, then compile-time offsets of 128 units per K-step
-      const int krow = 32 * ch + c32;
-      const uint4* kb_e = sb + 64 * hi + (krow ^ (4 * hi));
-      const uint4* kb_o = sb + 64 * hi + (krow ^ (8 + 4 * hi));
-      constexpr int QB = R32_QB, NQB = (KS + QB - 1) / QB;
       v8bf kf[2][QB];
       auto load_k = [&](int blk, v8bf (&dst)[QB]) {
 #pragma unroll
         for (int u = 0; u < QB; ++u) {
           const int ks = blk * QB + u;
-          if (ks < KS) dst[u] = *reinterpret_cast<const v8bf*>((ks & 1 ? kb_o : kb_e) + 128 * ks);
+          dst[u] = *reinterpret_cast<const v8bf*>(sb + kb + 16 * ks);
         }
       };
       load_k(0, kf[0]);
 #pragma unroll
       for (int blk = 0; blk < NQB; ++blk) {
         if (blk + 1 < NQB) load_k(blk + 1, kf[(blk + 1) & 1]);
+        if (issue) dma_one(other, rp_nxt, blk);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < QB; ++u) {
           const int ks = blk * QB + u;
-          if (ks < KS) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[blk & 1][u], qf[ks], s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[blk & 1][u], qf[ks], s, 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     // mask (only when the tile has empty rows); this half's maxima to LDS
-    if (vmask != ~0ull) {
+    if (vm_cur != ~0ull) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = 32 * ch + 8 * (i >> 2) + 4 * hi + (i & 3);
-        s[i] = ((vmask >> (row ^ (4 * wave))) & 1ull) ? s[i] : -INFINITY;
+        s[i] = ((vm_cur >> row) & 1ull) ? s[i] : -INFINITY;
       }
     }
     float tm = s[0];
@@ -1227,7 +1256,7 @@ void attn_bf16_row32_kernel(AttnArgs a) {
     for (int i = 1; i < 16; ++i) tm = fmaxf(tm, s[i]);
     tm = pair32_max(tm);
     if (hi == 0) mx[wave][c32] = tm;
-    __syncthreads();
+    lds_barrier();
     // one running maximum for the head group (both halves compute it alike)
     tm = fmaxf(tm, mx[pw][c32]) * sl2;
     const float mn = tm > m_run + 8.f ? tm : m_run;
@@ -1251,7 +1280,7 @@ void attn_bf16_row32_kernel(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < HDT; ++u) acc[u] *= alpha;
     }
-    __syncthreads();
+    lds_barrier();
     v8bf pp[2];
     pp[0] = __builtin_bit_cast(v8bf, pex[pw][0][lane]);
     pp[1] = __builtin_bit_cast(v8bf, pex[pw][1][lane]);
@@ -1259,13 +1288,7 @@ void attn_bf16_row32_kernel(AttnArgs a) {
     // 32(kc/2) + 16(kc%2) + {4hi+k, 8+4hi+k}, k < 4, whose probabilities are
     // elements 8(kc%2) .. +7 of half kc/2's lanes
     {
-      // dims d = 32(ch*HDT + dtl) + 16g16 + 4j4: chunk 4(ch*HDT + dtl) + cl
-      // with cl = 2g16 + j4/2, so chunk&3 = cl for every value tile; rows
-      // 16kc + (4hi + k4) and +8: two lane bases, compile-time offsets
-      const uint16_t* sb16 = reinterpret_cast<const uint16_t*>(sb) + 256 * 8 * ch * HDT;
-      const int cl = 2 * g16 + (j4 >> 1);
-      const uint16_t* vb0 = sb16 + (64 * cl + ((4 * hi + k4) ^ (4 * cl))) * 8 + 4 * (j4 & 1);
-      const uint16_t* vb1 = sb16 + (64 * cl + ((8 + 4 * hi + k4) ^ (4 * cl))) * 8 + 4 * (j4 & 1);
+      const uint16_t* sb16 = reinterpret_cast<const uint16_t*>(sb);
       constexpr int VB = R32_VB;
       constexpr int NV = 4 * HDT, NVB = NV / VB;
       v8bf vf[2][VB];
@@ -1274,8 +1297,8 @@ void attn_bf16_row32_kernel(AttnArgs a) {
         for (int u = 0; u < VB; ++u) {
           const int v = blk * VB + u;
           const int kc = v / HDT, dtl = v % HDT;
-          const int off = (256 * dtl + 16 * kc) * 8;
-          dst[u] = vt_fragment(vb0 + off, vb1 + off);
+          const int off = (2 * kc * GU + 32 * dtl) * 8;
+          dst[u] = vt_fragment(sb16 + vbase0 + off, sb16 + vbase1 + off);
         }
       };
       load_v(0, vf[0]);
@@ -1293,6 +1316,13 @@ void attn_bf16_row32_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // tile t+2 (index reads made a tile ago): the row addresses tile t+1's
+    // QK requests and its mask; then tile t+3's index reads
+    rp_nxt[0] = row_addr(code_of(64 * (t + 2) + dma_row, ixp.e0));
+    rp_nxt[1] = row_addr(code_of(64 * (t + 2) + dma_row + 8, ixp.e1));
+    vm_cur = vm_n1;
+    vm_n1 = __ballot(code_of(64 * (t + 2) + lane, ixp.em) != -1);
+    ixp = tile_idx(t + 3);
   };
 
   for (int t = 0; t < ntiles; t += 2) {
