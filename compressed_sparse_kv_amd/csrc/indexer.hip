@@ -160,17 +160,20 @@ __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
     v4u v[4][KS];
     int sc[4][KS];
   };
+  // (the lane's code and scale pointers for key 0 of the batch, formed once;
+  // keys are then a 32-bit offset from them)
+  const uint8_t* kc_lane = a.kc + (int64_t)b * a.Nmax * (a.dI / 2) + kb * 16;
+  const uint8_t* ks_lane = a.ks + (int64_t)b * a.Nmax * (a.dI / 32) + kb;
   auto load_keys = [&](Group& gr, int base) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       int key = base + 16 * kt + rho;
       key = key < a.Nmax ? key : a.Nmax - 1;
-      const int64_t krow = (int64_t)b * a.Nmax + key;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         gr.v[kt][s] = __builtin_nontemporal_load(
-            reinterpret_cast<const v4u*>(a.kc + krow * (a.dI / 2) + s * 64 + kb * 16));
-        gr.sc[kt][s] = a.ks[krow * (a.dI / 32) + s * 4 + kb];
+            reinterpret_cast<const v4u*>(kc_lane + (uint32_t)key * (uint32_t)(a.dI / 2) + s * 64));
+        gr.sc[kt][s] = ks_lane[(uint32_t)key * (uint32_t)(a.dI / 32) + s * 4];
       }
     }
   };
@@ -213,7 +216,10 @@ __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
     }
 
     // ascending head chain; the fences keep the weight reads next to their
-    // use (hoisted together they would hold 4*HI registers)
+    // use (hoisted together they would hold 4*HI registers). ReLU as an
+    // integer max on the bits: +0 for every negative value and for -0, the
+    // value itself otherwise (a float max would also canonicalise each
+    // value coming out of the lane swaps)
     float score = 0.0f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -222,8 +228,8 @@ __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
       for (int t = 0; t < HT; ++t)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float v = d[g][t][j];
-          score = __builtin_fmaf(wr[4 * HT * g + 4 * t + j], v > 0.0f ? v : 0.0f, score);
+          const float v = __int_as_float(max(__float_as_int(d[g][t][j]), 0));
+          score = __builtin_fmaf(wr[4 * HT * g + 4 * t + j], v, score);
         }
     }
 
