@@ -1065,7 +1065,9 @@ void attn_bf16_row32_kernel(AttnArgs a) {
   constexpr int HDT = DV / 64;           // 32-row value tiles per wave (half of DV)
   constexpr int CPW = NCH / 4;           // DMA instructions per wave per tile
   constexpr int QB = R32_QB, NQB = KS / QB;
-  static_assert(NCH % 8 == 0 && DV % 64 == 0 && DV <= D && KS % QB == 0 && NQB == CPW, "unsupported shape");
+  static_assert(NCH % 8 == 0 && DV % 64 == 0 && DV <= D && KS % QB == 0 && NQB == CPW &&
+                    CPW - (CPW + 1) / 2 <= 4 * HDT / R32_VB,
+                "unsupported shape");
   __shared__ __align__(16) uint4 buf0[TU];
   __shared__ __align__(16) uint4 buf1[TU];
   __shared__ __align__(16) uint4 pex[4][2][64];  // probabilities, B-operand fragments
@@ -1233,7 +1235,7 @@ void attn_bf16_row32_kernel(AttnArgs a) {
 #pragma unroll
       for (int blk = 0; blk < NQB; ++blk) {
         if (blk + 1 < NQB) load_k(blk + 1, kf[(blk + 1) & 1]);
-        if (issue) dma_one(other, rp_nxt, blk);
+        if (issue && (blk & 1) == 0) dma_one(other, rp_nxt, blk >> 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < QB; ++u) {
@@ -1305,6 +1307,9 @@ void attn_bf16_row32_kernel(AttnArgs a) {
 #pragma unroll
       for (int blk = 0; blk < NVB; ++blk) {
         if (blk + 1 < NVB) load_v(blk + 1, vf[(blk + 1) & 1]);
+        // the second half of tile t+1's DMA, spread over the PV blocks
+        constexpr int QD = (CPW + 1) / 2;  // issued during QK
+        if (issue && blk < CPW - QD) dma_one(other, rp_nxt, QD + blk);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < VB; ++u) {
