@@ -98,6 +98,16 @@ __device__ __forceinline__ void pool_slots(const IN* c, const IN* z, const float
   }
 }
 
+// Exactly N slots starting at row r0, all loads issued before the fold.
+template <int N, typename IN>
+__device__ __forceinline__ void pool_fixed(const IN* c, const IN* z, const float* bias, int64_t r0, int D,
+                                           int ch, float2& mx, float2& den, float2& num) {
+  float2 l[N], v[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) load_slot(c, z, bias, r0 + j, j, D, ch, true, r0, l[j], v[j]);
+  fold<N>(l, v, mx, den, num);
+}
+
 template <int OUT>
 __device__ __forceinline__ void store_pair(const CompressArgs& a, int64_t orow, int p, float v0,
                                            float v1) {
@@ -197,9 +207,13 @@ __global__ __launch_bounds__(256) void compress_wide_kernel(CompressArgs a) {
   if (p < half) {
     const int per = a.m / 8;
     const int64_t src0 = (int64_t)b * a.src_bstride;
-    pool_slots<16, IN>(reinterpret_cast<const IN*>(a.ca) + src0 * a.D + (int64_t)sg * per * a.D,
-                   reinterpret_cast<const IN*>(a.za) + src0 * a.D + (int64_t)sg * per * a.D,
-                   a.bias_a + (int64_t)sg * per * a.D, (int64_t)a.m * i, per, a.D, 2 * p, mx, den, num);
+    const IN* cs = reinterpret_cast<const IN*>(a.ca) + src0 * a.D + (int64_t)sg * per * a.D;
+    const IN* zs = reinterpret_cast<const IN*>(a.za) + src0 * a.D + (int64_t)sg * per * a.D;
+    const float* bs = a.bias_a + (int64_t)sg * per * a.D;
+    // m' = 128 (16 slots per group): a compile-time count, so that all 16
+    // slot loads are in flight together
+    if (per == 16) pool_fixed<16, IN>(cs, zs, bs, (int64_t)a.m * i, a.D, 2 * p, mx, den, num);
+    else pool_slots<16, IN>(cs, zs, bs, (int64_t)a.m * i, per, a.D, 2 * p, mx, den, num);
   }
   part[sg][cpl][0] = mx.x; part[sg][cpl][1] = mx.y;
   part[sg][cpl][2] = den.x; part[sg][cpl][3] = den.y;
