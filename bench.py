@@ -14,9 +14,9 @@ the whole hot path for one new token per sequence:
   5. sparse_attn   - CSA attention over selected entries + window + sink
   6. hca_compress  - the newest HCA entry (128 source tokens)
   7. dense_compressed_attn - HCA attention over all 8192 entries + window + sink
-The calls run on three streams as the data flow allows (1, 6, 7 on one; 3
-on another; 2, 4, 5 on the main stream after the entries they read;
---streams 1 runs them in order on one stream). The timed steps are HIP graph
+The HCA branch (6, 7) runs on a side stream next to the CSA chain (2, 3, 1,
+4, 5 in that order on the main stream); --streams 1 runs every call in order
+on one stream. The timed steps are HIP graph
 replays, four steps per graph (--mode eager launches them directly). Four
 copies of the layer-pair state rotate between steps (as successive layers
 would), so a step never finds its 121 MB working set in the 256 MB Infinity
@@ -129,12 +129,9 @@ class DecodeWorkload:
             ws_d = csk.dense_compressed_attn_workspace_size(B, 1, H, self.D, dv, self.Nh, 128, self.W,
                                                             csk.CSK_BF16)
             self.ws_d = torch.empty(max(ws_d, 1), dtype=torch.uint8, device=dev)
-        # extra streams (default priority) and the event that hands the
-        # newest KV entry from the side stream to the sparse attention
+        # the side stream of the HCA branch (default priority)
         self.streams = streams
         self.side = torch.cuda.Stream()
-        self.qstream = torch.cuda.Stream()
-        self.ev_kv = torch.cuda.Event()
         torch.cuda.synchronize()
         if not keep_host:
             self.d = None
@@ -144,48 +141,40 @@ class DecodeWorkload:
     # ------------------------------------------------------------- one step
     def step(self, c=0):
         """One decode step. With one stream (default) the calls run in data
-        flow order on torch's current stream. With three streams the side
-        stream computes the newest CSA KV entry (needed only by the sparse
-        attention) and then the whole HCA branch, a second stream encodes the
-        indexer queries, and the main stream computes the newest indexer
-        key, scores and selects, and runs the sparse attention."""
+        flow order on torch's current stream. With several streams the HCA
+        branch (its newest entry, then the dense attention) runs on a side
+        stream from the start of the step, and the CSA chain (newest indexer
+        key, query encoding, newest KV entry, scores and top-k, sparse
+        attention) stays on the main stream: every cross-stream wait inside
+        the chain costs more on this runtime than running its small kernels
+        back to back."""
         torch, csk, x, st = self.torch, self.csk, self.x, self.copies[c % len(self.copies)]
         B, N = self.B, self.N
         main = torch.cuda.current_stream()
         multi = self.streams > 1
-        side, qs = (self.side, self.qstream) if multi else (main, main)
-        if multi:
-            side.wait_stream(main)
-            qs.wait_stream(main)
-        with torch.cuda.stream(side):
-            # the newest CSA entry N-1 (a-block = source rows 4..7, previous
-            # block = rows 0..3 of the 8-token window)
-            csk.csa_compress(x["src_ca4"], x["src_za4"], x["src_cb4"], x["src_zb4"],
-                             x["bias_a"], x["bias_b"], 4, d_rope=64, entry0=N - 1, src_bstride=8,
-                             out=st["kv_new"], dst_bstride=N, S=4, B=B)
-            if multi:
-                self.ev_kv.record(side)
-            if self.pair and multi:
+        if self.pair and multi:
+            self.side.wait_stream(main)
+            with torch.cuda.stream(self.side):
                 self._hca(x, st)
-        with torch.cuda.stream(qs):
-            csk.mxfp4_quantize(x["qI"], self.qc, self.qs)
         # the newest indexer key, MXFP4
         csk.csa_compress(x["src_ia4"], x["src_iza4"], x["src_ib4"], x["src_izb4"],
                          x["ibias_a"], x["ibias_b"], 4, entry0=N - 1, src_bstride=8, out_dtype=csk.CSK_MXFP4,
                          out=st["kc_new"], out_scale=st["ks_new"], dst_bstride=N, S=4, B=B)
-        if multi:
-            main.wait_stream(qs)
+        csk.mxfp4_quantize(x["qI"], self.qc, self.qs)
+        # the newest CSA entry N-1 (a-block = source rows 4..7, previous
+        # block = rows 0..3 of the 8-token window)
+        csk.csa_compress(x["src_ca4"], x["src_za4"], x["src_cb4"], x["src_zb4"],
+                         x["bias_a"], x["bias_b"], 4, d_rope=64, entry0=N - 1, src_bstride=8,
+                         out=st["kv_new"], dst_bstride=N, S=4, B=B)
         csk.indexer_topk(self.qc, x["w"], st["kc"], x["q_pos"], x["n_entries"], 4, self.k, q_scale=self.qs,
                          k_scale=st["ks"], idx=self.idx, score=self.score, workspace=self.ws_i)
-        if multi:
-            main.wait_event(self.ev_kv)
         csk.sparse_attn(x["q"], x["q_pos"], st["kv_c"], self.idx, st["kv_w"], x["w_pos0"], self.W, x["sink"],
                         self.dv, 64, self.scale, out=self.out, lse=self.lse,
                         workspace=self.ws_s)
         if self.pair and not multi:
             self._hca(x, st)
-        if multi:
-            main.wait_stream(side)
+        if self.pair and multi:
+            main.wait_stream(self.side)
 
     def _hca(self, x, st):
         """The HCA branch: the newest HCA entry, then dense attention."""
@@ -755,8 +744,8 @@ def main():
     ap.add_argument("--mode", default="graph", choices=["eager", "graph"],
                     help="timed steps as HIP graph replays (default) or as eager launches")
     ap.add_argument("--graph-steps", type=int, default=4, help="steps captured per graph")
-    ap.add_argument("--streams", type=int, default=3, choices=[1, 3],
-                    help="1: every call on one stream; 3: the data-flow split over three streams")
+    ap.add_argument("--streams", type=int, default=2, choices=[1, 2],
+                    help="1: every call on one stream; 2: the HCA branch on a side stream")
     ap.add_argument("--cpu-rows", type=int, default=4, help="decode: sequences the oracle runs")
     ap.add_argument("--cpu-rows-prefill", type=int, default=None,
                     help="prefill: query rows the oracle runs (default 384 for CSA, every row for HCA)")

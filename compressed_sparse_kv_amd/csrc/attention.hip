@@ -80,8 +80,9 @@ struct AttnArgs {
   bool dense;
   void* out;              // [R, H, dv]
   float* lse;             // [R, H] or null
-  float* part_o;          // [R, nch, H, dv]
+  float* part_o;          // [R, nch, H, dv], fp32 (bf16 when part_bf16)
   float* part_ml;         // [R, nch, H, 2]
+  bool part_bf16;         // partial O stored as bf16 (the streamed-row kernel)
 };
 
 struct RowInfo {
@@ -93,21 +94,25 @@ struct RowInfo {
 
 __device__ __forceinline__ RowInfo row_info(const AttnArgs& a, int r) {
   RowInfo ri;
-  ri.b = r / a.T;
-  ri.p = a.q_pos[r];
+  ri.b = (int)((unsigned)r / (unsigned)a.T);
+  // the row's three loads first, so that they are in flight together
+  const int p = a.q_pos[r];
+  const int ne = a.dense ? a.n_entries[ri.b] : 0;
+  const int w0 = (a.W > 0 && a.S_w > 0) ? a.w_pos0[ri.b] : 0;
+  ri.p = p;
   ri.nvis = 0;
-  if (a.dense && ri.p >= 0) {
-    int64_t nv = (ri.p + 1) / a.m;
-    nv = nv < a.n_entries[ri.b] ? nv : a.n_entries[ri.b];
+  if (a.dense && p >= 0) {
+    // p + 1 <= 2^31 fits an unsigned 32-bit division
+    int nv = (int)(((unsigned)p + 1u) / (unsigned)a.m);
+    nv = nv < ne ? nv : ne;
     nv = nv < a.Nmax ? nv : a.Nmax;
-    ri.nvis = (int)(nv < 0 ? 0 : nv);
+    ri.nvis = nv < 0 ? 0 : nv;
   }
   ri.wr0 = ri.wr1 = 0;
   if (a.W > 0 && a.S_w > 0) {
-    int64_t lo = ri.p - a.W + 1;
+    int64_t lo = (int64_t)p - a.W + 1;
     lo = lo < 0 ? 0 : lo;
-    const int64_t w0 = a.w_pos0[ri.b];
-    int64_t r0 = lo - w0, r1 = ri.p - w0 + 1;
+    int64_t r0 = lo - w0, r1 = (int64_t)p - w0 + 1;
     r0 = r0 < 0 ? 0 : r0;
     r1 = r1 > a.S_w ? a.S_w : r1;
     if (r1 > r0) {
@@ -1033,10 +1038,25 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// ------------------------------------------ bf16 32x32 MFMA, whole rows
-// Sparse attention of one query row with 64 heads (prefill: rows kept
-// whole). The row's candidates stream through LDS in 64-row tiles, two
-// buffers deep, each filled by LDS DMA. Wave w = (head group hg = w&1,
+// The lane's index, formed again at each use: the values derived from it
+// are cheap to recompute, and holding them across a long loop takes
+// registers that the loop's own values need (the compiler spills them, and a
+// reload waits for every DMA in flight). Volatile, so that separate calls
+// are not merged into one long-lived value.
+__device__ __forceinline__ int fresh_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// ------------------------------------------ bf16 32x32 MFMA, streamed rows
+// Sparse or dense attention of one query row with 64 heads. The row's
+// candidates stream through LDS in 64-row tiles, two buffers deep, each
+// filled by LDS DMA. Rows with long candidate lists and few rows to spread
+// (decode) are split into runs of tiles, one workgroup each, that write
+// unnormalised partials (O in bf16, m and l in fp32) for the merge kernel; otherwise (prefill) a
+// workgroup keeps its row whole and writes the output. Dense rows take
+// compressed entries 0..nvis-1 in order, so they read no index list. Wave w = (head group hg = w&1,
 // half ch = w>>1) scores 32 heads against tile rows [32ch, 32ch+32) with
 // 32x32x16 MFMAs (S^T = K q~^T; the q~ fragments stay in registers). The
 // two waves of a head group then agree on the running maximum (tile maxima
@@ -1054,7 +1074,7 @@ __device__ __forceinline__ void lds_barrier() {
 constexpr int R32_QB = 2;  // K fragments per pipelined block (two blocks in flight)
 constexpr int R32_VB = 2;  // V^T fragments per pipelined block
 
-template <int D, int DV>
+template <int D, int DV, bool DENSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bf16_row32_kernel(AttnArgs a) {
   constexpr int NCH = D / 8;             // 16-byte chunks per KV row
@@ -1076,27 +1096,38 @@ void attn_bf16_row32_kernel(AttnArgs a) {
   __shared__ float2 rtab[MAX_ROPE_PAIRS];
 
   const int r = blockIdx.x;
+  const int split = blockIdx.y;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
   // wave-uniform (readfirstlane): everything derived from it stays scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hg = wave & 1, ch = wave >> 1, pw = wave ^ 2;
+  // lane terms (prologue only; the loop and the epilogue form them again)
+  const int lane = tid & 63;
   const int c32 = lane & 31, hi = lane >> 5;
-  const int head = 32 * hg + c32;
   const RowInfo ri = row_info(a, r);
   const uint16_t* kvc = reinterpret_cast<const uint16_t*>(a.kv_c) + (int64_t)ri.b * a.Nmax * D;
   const uint16_t* kvw = reinterpret_cast<const uint16_t*>(a.kv_w) + (int64_t)ri.b * a.S_w * D;
   const int total = a.Lc + a.W;
-  const int ntiles = (total + 63) / 64;
-  const int32_t* idxr = a.idx + (int64_t)r * a.k;
+  // this workgroup's 64-row tiles [t0, t1) of the row's candidate slots
+  // (a.nch workgroups share a row; the merge kernel combines them)
+  const int nt_row = (total + 63) / 64;
+  const int t0 = (int)((int64_t)split * nt_row / a.nch);
+  const int ntiles = (int)((int64_t)(split + 1) * nt_row / a.nch) - t0;
+  const int j0 = 64 * t0;
+  const int32_t* idxr = DENSE ? nullptr : a.idx + (int64_t)r * a.k;
 
-  // index read (clamped, issued unconditionally), code (>= 0 entry, <= -2
-  // window row, -1 empty), KV row address (selects, no branches)
-  auto idx_load = [&](int j) -> int { return idxr[min(j, a.k - 1)]; };
+  // index read (clamped, issued unconditionally; dense rows read none),
+  // code (>= 0 entry, <= -2 window row, -1 empty) of the workgroup's slot
+  // j0 + j, KV row address (selects, no branches)
+  auto idx_load = [&](int j) -> int { return DENSE ? 0 : idxr[min(j0 + j, a.k - 1)]; };
   auto code_of = [&](int j, int e) -> int {
-    if (j < a.Lc) return (e < 0 || e >= a.Nmax) ? -1 : e;
-    const int wrow = ri.wr0 + (j - a.Lc);
-    return (j < total && wrow < ri.wr1) ? -2 - wrow : -1;
+    const int jj = j0 + j;
+    if (jj < a.Lc) {
+      if (DENSE) return jj < ri.nvis ? jj : -1;
+      return (e < 0 || e >= a.Nmax) ? -1 : e;
+    }
+    const int wrow = ri.wr0 + (jj - a.Lc);
+    return (jj < total && wrow < ri.wr1) ? -2 - wrow : -1;
   };
   auto row_addr = [&](int code) -> const uint16_t* {
     const bool win = code <= -2;
@@ -1109,85 +1140,91 @@ void attn_bf16_row32_kernel(AttnArgs a) {
   // G&1 = q/IPG&1); the lane loads row 16w + 8(q/IPG) + lane%8, whose
   // address it holds itself (two per tile), at chunk 8*block + lane/8,
   // swizzled
-  const int dma_row = 16 * wave + (lane & 7);
-  const int dma_c0 = 8 * (lane >> 3), dma_c1 = 8 * ((lane >> 3) ^ 1);  // elements
-  auto dma_one = [&](uint4* dst, const uint16_t* const (&rp)[2], int q) {
+  auto dma_row_of = [&](int ln) { return 16 * wave + (ln & 7); };
+  auto dma_one = [&](uint4* dst, const uint16_t* const (&rp)[2], int q, int ln) {
     const int gq = q / IPG, blk = q % IPG;
-    const uint16_t* src = rp[gq] + 64 * blk + ((gq & 1) ? dma_c1 : dma_c0);
+    const uint16_t* src = rp[gq] + 64 * blk + 8 * ((ln >> 3) ^ (gq & 1));
     lds_dma16(src, dst + 64 * (CPW * wave + q));
   };
   // tile T's index reads of this lane: row = lane (its mask bit) and the two
   // rows its DMAs load
   struct TileIdx { int em, e0, e1; };
-  auto tile_idx = [&](int T) -> TileIdx {
-    return TileIdx{idx_load(64 * T + lane), idx_load(64 * T + dma_row), idx_load(64 * T + dma_row + 8)};
+  auto tile_idx = [&](int T, int ln) -> TileIdx {
+    const int dr = dma_row_of(ln);
+    return TileIdx{idx_load(64 * T + ln), idx_load(64 * T + dr), idx_load(64 * T + dr + 8)};
   };
 
-  // 1. q loads, tiles 0 and 1's row addresses, the RoPE table
-  uint4 qraw[KS];
-  {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + head) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qraw[ks] = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hi);
-  }
-  const TileIdx ix0 = tile_idx(0), ix1 = tile_idx(1);
-  TileIdx ixp = tile_idx(2);  // index reads of tile t+2 during tile t
-  // bit j: tile row j holds a candidate (tiles t and t+1)
-  uint64_t vm_cur = __ballot(code_of(lane, ix0.em) != -1);
-  uint64_t vm_n1 = __ballot(code_of(64 + lane, ix1.em) != -1);
-  const uint16_t* rp0[2] = {row_addr(code_of(dma_row, ix0.e0)), row_addr(code_of(dma_row + 8, ix0.e1))};
-  const uint16_t* rp1[2] = {row_addr(code_of(64 + dma_row, ix1.e0)), row_addr(code_of(64 + dma_row + 8, ix1.e1))};
-  if (tid < a.d_rope / 2) {
-    float cs, sn;
-    rope_cs((double)ri.p, a.rope.theta[tid], &cs, &sn);
-    rtab[tid] = make_float2(cs, sn);
-  }
-  // ordinary stores into the KV buffers: the DMA intrinsic is not seen as a
-  // writer of them, and without one the reads below could be folded away
+  // 1. the lane's RoPE frequency and the index reads of tiles 0..2;
+  // ordinary stores into the KV buffers (the DMA intrinsic is not seen as a
+  // writer of them, and without one the reads below could be folded away),
+  // complete in every wave before any DMA is issued
+  const double theta = a.rope.theta[min(tid, MAX_ROPE_PAIRS - 1)];
+  const TileIdx ix0 = tile_idx(0, lane), ix1 = tile_idx(1, lane);
+  TileIdx ixp = tile_idx(2, lane);  // index reads of tile t+2 during tile t
   buf0[tid] = make_uint4(0u, 0u, 0u, 0u);
   buf1[tid] = make_uint4(0u, 0u, 0u, 0u);
+  lds_barrier();
+
+  // 2. tile 0 requested (tile t+1 goes out during tile t's QK); bit j of
+  // the masks: tile row j holds a candidate (tiles t and t+1)
+  uint64_t vm_cur = __ballot(code_of(lane, ix0.em) != -1);
+  uint64_t vm_n1 = __ballot(code_of(64 + lane, ix1.em) != -1);
+  const int dma_row = dma_row_of(lane);
+  const uint16_t* rp0[2] = {row_addr(code_of(dma_row, ix0.e0)), row_addr(code_of(dma_row + 8, ix0.e1))};
+  const uint16_t* rp1[2] = {row_addr(code_of(64 + dma_row, ix1.e0)), row_addr(code_of(64 + dma_row + 8, ix1.e1))};
+#pragma unroll
+  for (int q = 0; q < CPW; ++q) dma_one(buf0, rp0, q, lane);
+
+  // 3. the row's q (64 heads, contiguous) into buf1 by DMA while tile 0
+  // loads, 1 KB per instruction: 16-byte piece p = NCH*h + c (head h, chunk
+  // c), instruction i = p/64; lane l of instruction i loads piece
+  // 64i + (l ^ (i%16)) into unit 64i + l, so that the fragment reads below
+  // (16 heads of one chunk per 16 lanes) spread over the bank groups
+  {
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)r * a.H * D;
+#pragma unroll
+    for (int q = 0; q < CPW; ++q) {
+      const int i = CPW * wave + q;
+      lds_dma16(qrow + 8 * (64 * i + (lane ^ (i & 15))), buf1 + 64 * i);
+    }
+  }
+  if (tid < a.d_rope / 2) {
+    float cs, sn;
+    rope_cs((double)ri.p, theta, &cs, &sn);
+    rtab[tid] = make_float2(cs, sn);
+  }
+  // every wave's DMAs (tile 0 and q) and RoPE table writes are in
   __syncthreads();
 
-  // 2. rotated query fragments (B operand: head c32, dims 16ks + 8hi ..)
+  // 4. rotated query fragments (B operand: head h = 32hg + c32, chunk
+  // c = 2ks + hi: piece p = NCH*h + c); at most 128 dims rotate (checked on
+  // the host), all within the last eight K-steps
+  constexpr int KR = KS > 8 ? KS - 8 : 0;
   v8bf qf[KS];
   {
+    const int pb = NCH * (32 * hg + c32) + hi;
     const int rope0 = D - a.d_rope;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int d0 = 16 * ks + 8 * hi;
-      float x[8];
-      const uint32_t wv[4] = {qraw[ks].x, qraw[ks].y, qraw[ks].z, qraw[ks].w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        x[2 * u] = bf16_bits_to_f32(wv[u] & 0xffffu);
-        x[2 * u + 1] = bf16_bits_to_f32(wv[u] >> 16);
-      }
-      if (d0 + 8 > rope0) {
+      const int pc = pb + 2 * ks, ic = pc >> 6;
+      qf[ks] = *reinterpret_cast<const v8bf*>(buf1 + ((pc & ~63) | ((pc & 63) ^ (ic & 15))));
+      if (ks >= KR) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int c = d0 + 2 * u;
-          if (c >= rope0) {
-            const float2 csn = rtab[(c - rope0) / 2];
-            const float x0 = x[2 * u], x1 = x[2 * u + 1];
-            x[2 * u] = x0 * csn.x - x1 * csn.y;
-            x[2 * u + 1] = x0 * csn.y + x1 * csn.x;
-          }
+          const int c = 16 * ks + 8 * hi + 2 * u;
+          const float2 csn = c >= rope0 ? rtab[(c - rope0) >> 1] : make_float2(1.f, 0.f);
+          const float x0 = (float)qf[ks][2 * u], x1 = (float)qf[ks][2 * u + 1];
+          qf[ks][2 * u] = (__bf16)(x0 * csn.x - x1 * csn.y);
+          qf[ks][2 * u + 1] = (__bf16)(x0 * csn.y + x1 * csn.x);
         }
       }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) qf[ks][u] = (__bf16)x[u];
     }
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // 3. tiles 0 and 1 requested
-#pragma unroll
-  for (int q = 0; q < CPW; ++q) dma_one(buf0, rp0, q);
-#pragma unroll
-  for (int q = 0; q < CPW; ++q) dma_one(buf1, rp1, q);
   // row addresses of the tile that tile t's QK requests (t+1; set at the
   // end of tile t-1)
-  const uint16_t* rp_nxt[2] = {kvc, kvc};
+  const uint16_t* rp_nxt[2] = {rp1[0], rp1[1]};
 
   v16f acc[HDT];
 #pragma unroll
@@ -1199,15 +1236,19 @@ void attn_bf16_row32_kernel(AttnArgs a) {
 
   // K fragment base: row 32ch + c32 (group G = 4ch + c32/8, G&1 = g1),
   // chunk 2ks + hi: unit G*GU + 8(2ks + (hi ^ g1)) + c32%8 = kb + 16ks
-  const int kg1 = (c32 >> 3) & 1;
-  const int kb = (4 * ch + (c32 >> 3)) * GU + 8 * (hi ^ kg1) + (c32 & 7);
+  auto k_base = [&](int ln) {
+    const int c = ln & 31, h = ln >> 5;
+    return (4 * ch + (c >> 3)) * GU + 8 * (h ^ ((c >> 3) & 1)) + (c & 7);
+  };
   // V^T fragment bases: rows 16kc + 8s + 4hi + k4 (G = 2kc + s, G&1 = s),
   // dims 32(ch*HDT + dtl) + 16g16 + 4j4 (chunk 4(ch*HDT + dtl) + cl with
   // cl = 2g16 + j4/2): unit base_s + 2kc*GU + 32dtl (elements x8)
-  const int k4 = (lane & 15) >> 2, j4 = lane & 3, g16 = c32 >> 4;
-  const int cl = 2 * g16 + (j4 >> 1);
-  const int vbase0 = (8 * cl + 4 * hi + k4 + 32 * ch * HDT) * 8 + 4 * (j4 & 1);
-  const int vbase1 = (GU + 8 * (cl ^ 1) + 4 * hi + k4 + 32 * ch * HDT) * 8 + 4 * (j4 & 1);
+  auto v_bases = [&](int ln, int& vb0, int& vb1) {
+    const int h = ln >> 5, k4 = (ln & 15) >> 2, j4 = ln & 3, g16 = (ln & 31) >> 4;
+    const int cl = 2 * g16 + (j4 >> 1);
+    vb0 = (8 * cl + 4 * h + k4 + 32 * ch * HDT) * 8 + 4 * (j4 & 1);
+    vb1 = (GU + 8 * (cl ^ 1) + 4 * h + k4 + 32 * ch * HDT) * 8 + 4 * (j4 & 1);
+  };
 
   auto tile_step = [&](const uint4* sb, uint4* other, int t) {
     // tile t has landed in every wave's view
@@ -1215,7 +1256,7 @@ void attn_bf16_row32_kernel(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(CSK_VMCNT_LGKM0(0));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const bool issue = t >= 1 && t + 1 < ntiles;  // tile t+1 (tile 1 went out with tile 0)
+    const bool issue = t + 1 < ntiles;  // tile t+1
 
     // S^T[row 32ch + (8(i/4) + 4hi + i%4), head c32]; one DMA instruction
     // of tile t+1 per K-step block
@@ -1223,6 +1264,8 @@ void attn_bf16_row32_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
     {
+      const int lq = fresh_lane();
+      const int kb = k_base(lq);
       v8bf kf[2][QB];
       auto load_k = [&](int blk, v8bf (&dst)[QB]) {
 #pragma unroll
@@ -1235,7 +1278,7 @@ void attn_bf16_row32_kernel(AttnArgs a) {
 #pragma unroll
       for (int blk = 0; blk < NQB; ++blk) {
         if (blk + 1 < NQB) load_k(blk + 1, kf[(blk + 1) & 1]);
-        if (issue && (blk & 1) == 0) dma_one(other, rp_nxt, blk >> 1);
+        if (issue && (blk & 1) == 0) dma_one(other, rp_nxt, blk >> 1, lq);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < QB; ++u) {
@@ -1246,21 +1289,24 @@ void attn_bf16_row32_kernel(AttnArgs a) {
       }
     }
     // mask (only when the tile has empty rows); this half's maxima to LDS
+    const int lm = fresh_lane();
     if (vm_cur != ~0ull) {
+      // this half's rows of the tile, shifted down by the lane's 4hi
+      const uint32_t vmh = (uint32_t)(vm_cur >> (32 * ch + 4 * (lm >> 5)));
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int row = 32 * ch + 8 * (i >> 2) + 4 * hi + (i & 3);
-        s[i] = ((vm_cur >> row) & 1ull) ? s[i] : -INFINITY;
+        const int row = 8 * (i >> 2) + (i & 3);
+        s[i] = ((vmh >> row) & 1u) ? s[i] : -INFINITY;
       }
     }
     float tm = s[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) tm = fmaxf(tm, s[i]);
     tm = pair32_max(tm);
-    if (hi == 0) mx[wave][c32] = tm;
+    if (lm < 32) mx[wave][lm] = tm;
     lds_barrier();
     // one running maximum for the head group (both halves compute it alike)
-    tm = fmaxf(tm, mx[pw][c32]) * sl2;
+    tm = fmaxf(tm, mx[pw][lm & 31]) * sl2;
     const float mn = tm > m_run + 8.f ? tm : m_run;
     const float alpha = mn == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
     const bool moved = mn != m_run;
@@ -1276,21 +1322,24 @@ void attn_bf16_row32_kernel(AttnArgs a) {
       pf[i >> 3][i & 7] = (__bf16)pv;
     }
     l_part = l_part * alpha + ps;
-    pex[wave][0][lane] = __builtin_bit_cast(uint4, pf[0]);
-    pex[wave][1][lane] = __builtin_bit_cast(uint4, pf[1]);
+    pex[wave][0][lm] = __builtin_bit_cast(uint4, pf[0]);
+    pex[wave][1][lm] = __builtin_bit_cast(uint4, pf[1]);
     if (__ballot(moved) != 0ull) {
 #pragma unroll
       for (int u = 0; u < HDT; ++u) acc[u] *= alpha;
     }
     lds_barrier();
     v8bf pp[2];
-    pp[0] = __builtin_bit_cast(v8bf, pex[pw][0][lane]);
-    pp[1] = __builtin_bit_cast(v8bf, pex[pw][1][lane]);
+    const int lp = fresh_lane();
+    pp[0] = __builtin_bit_cast(v8bf, pex[pw][0][lp]);
+    pp[1] = __builtin_bit_cast(v8bf, pex[pw][1][lp]);
     // O^T[dv, head] += V^T P^T over the 64 rows: K-chunk kc holds rows
     // 32(kc/2) + 16(kc%2) + {4hi+k, 8+4hi+k}, k < 4, whose probabilities are
     // elements 8(kc%2) .. +7 of half kc/2's lanes
     {
       const uint16_t* sb16 = reinterpret_cast<const uint16_t*>(sb);
+      int vbase0, vbase1;
+      v_bases(lp, vbase0, vbase1);
       constexpr int VB = R32_VB;
       constexpr int NV = 4 * HDT, NVB = NV / VB;
       v8bf vf[2][VB];
@@ -1309,7 +1358,7 @@ void attn_bf16_row32_kernel(AttnArgs a) {
         if (blk + 1 < NVB) load_v(blk + 1, vf[(blk + 1) & 1]);
         // the second half of tile t+1's DMA, spread over the PV blocks
         constexpr int QD = (CPW + 1) / 2;  // issued during QK
-        if (issue && blk < CPW - QD) dma_one(other, rp_nxt, QD + blk);
+        if (issue && blk < CPW - QD) dma_one(other, rp_nxt, QD + blk, lp);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < VB; ++u) {
@@ -1323,11 +1372,13 @@ void attn_bf16_row32_kernel(AttnArgs a) {
     }
     // tile t+2 (index reads made a tile ago): the row addresses tile t+1's
     // QK requests and its mask; then tile t+3's index reads
-    rp_nxt[0] = row_addr(code_of(64 * (t + 2) + dma_row, ixp.e0));
-    rp_nxt[1] = row_addr(code_of(64 * (t + 2) + dma_row + 8, ixp.e1));
+    const int le = fresh_lane();
+    const int dre = dma_row_of(le);
+    rp_nxt[0] = row_addr(code_of(64 * (t + 2) + dre, ixp.e0));
+    rp_nxt[1] = row_addr(code_of(64 * (t + 2) + dre + 8, ixp.e1));
     vm_cur = vm_n1;
-    vm_n1 = __ballot(code_of(64 * (t + 2) + lane, ixp.em) != -1);
-    ixp = tile_idx(t + 3);
+    vm_n1 = __ballot(code_of(64 * (t + 2) + le, ixp.em) != -1);
+    ixp = tile_idx(t + 3, le);
   };
 
   for (int t = 0; t < ntiles; t += 2) {
@@ -1336,31 +1387,79 @@ void attn_bf16_row32_kernel(AttnArgs a) {
   }
 
   // 4. the head group's sum over both halves, the sink, the output
+  const int lo_ = fresh_lane();
+  const int c32o = lo_ & 31, hio = lo_ >> 5, heado = 32 * hg + c32o;
   const float l_half = pair32_sum(l_part);
-  if (hi == 0) xl[wave][c32] = l_half;
+  if (hio == 0) xl[wave][c32o] = l_half;
   __builtin_amdgcn_s_waitcnt(CSK_VMCNT_LGKM0(0));  // no DMA outlives the workgroup
   __syncthreads();
-  const float l_tot = l_half + xl[pw][c32];
-  const float s2 = a.sink ? a.sink[head] * LOG2E : -INFINITY;
-  const float M = fmaxf(m_run, s2);
-  float f = 0.f, z = 0.f;
-  if (M != -INFINITY) {
-    const float fo = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
-    z = l_tot * fo + (a.sink ? exp2f(s2 - M) : 0.f);
-    f = z > 0.f ? fo / z : 0.f;
-  }
-  uint16_t* ob = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)r * a.H + head) * DV + 32 * ch * HDT;
-#pragma unroll
-  for (int u = 0; u < HDT; ++u)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const v2bf lo = {(__bf16)(acc[u][4 * q4] * f), (__bf16)(acc[u][4 * q4 + 1] * f)};
-      const v2bf hh = {(__bf16)(acc[u][4 * q4 + 2] * f), (__bf16)(acc[u][4 * q4 + 3] * f)};
-      *reinterpret_cast<uint2*>(ob + 32 * u + 8 * q4 + 4 * hi) =
-          make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hh));
+  const float l_tot = l_half + xl[pw][c32o];
+  // the output scale: 1 for a partial of a split row (unnormalised O, merged
+  // with the sink by the merge kernel), else the softmax normaliser with the
+  // sink
+  float f = 1.f, M = m_run, z = l_tot;
+  if (a.nch == 1) {
+    const float s2 = a.sink ? a.sink[heado] * LOG2E : -INFINITY;
+    M = fmaxf(m_run, s2);
+    f = 0.f;
+    z = 0.f;
+    if (M != -INFINITY) {
+      const float fo = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
+      z = l_tot * fo + (a.sink ? exp2f(s2 - M) : 0.f);
+      f = z > 0.f ? fo / z : 0.f;
     }
-  if (a.lse && ch == 0 && hi == 0)
-    a.lse[(int64_t)r * a.H + head] = M == -INFINITY ? -INFINITY : (M + log2f(z)) * LN2;
+  }
+  // 5. O through LDS (every wave is past its last tile: both buffers are
+  // free), so that each store instruction writes contiguous memory. Head
+  // group hg uses buffer hg; float4 unit du of head h's row sits at
+  // (h%32)*DV/4 + (du ^ h%16), which keeps the scattered writes and the
+  // row-wise reads on distinct bank groups.
+  constexpr int DU = DV / 4;
+  static_assert(DU % 16 == 0 && 32 * DV * 4 <= TU * 16, "staging layout");
+  {
+    float* st = reinterpret_cast<float*>(hg ? buf1 : buf0);
+#pragma unroll
+    for (int u = 0; u < HDT; ++u)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int du = 8 * ch * HDT + 8 * u + 2 * q4 + hio;
+        *reinterpret_cast<float4*>(st + 4 * (c32o * DU + (du ^ (c32o & 15)))) =
+            make_float4(acc[u][4 * q4] * f, acc[u][4 * q4 + 1] * f, acc[u][4 * q4 + 2] * f,
+                        acc[u][4 * q4 + 3] * f);
+      }
+  }
+  lds_barrier();
+  {
+    const int ls = fresh_lane() + 64 * wave;
+    const int64_t row0 = a.nch > 1 ? ((int64_t)r * a.nch + split) * a.H : (int64_t)r * a.H;
+#pragma unroll 4
+    for (int k = 0; k < 64 * DU / 256; ++k) {
+      const int idx = 256 * k + ls;
+      const int h = idx / DU, du = idx % DU;
+      const float* st = reinterpret_cast<const float*>(h >= 32 ? buf1 : buf0);
+      const float4 v = *reinterpret_cast<const float4*>(st + 4 * ((h & 31) * DU + (du ^ (h & 15))));
+      if (a.nch > 1) {
+        const v2bf lo = {(__bf16)v.x, (__bf16)v.y};
+        const v2bf hh = {(__bf16)v.z, (__bf16)v.w};
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.part_o) + (row0 + h) * DV + 4 * du) =
+            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hh));
+      } else {
+        const v2bf lo = {(__bf16)v.x, (__bf16)v.y};
+        const v2bf hh = {(__bf16)v.z, (__bf16)v.w};
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + (row0 + h) * DV + 4 * du) =
+            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hh));
+      }
+    }
+  }
+  if (ch == 0 && hio == 0) {
+    if (a.nch > 1) {
+      float* pm = a.part_ml + (((int64_t)r * a.nch + split) * a.H + heado) * 2;
+      pm[0] = m_run;
+      pm[1] = l_tot;
+    } else if (a.lse) {
+      a.lse[(int64_t)r * a.H + heado] = M == -INFINITY ? -INFINITY : (M + log2f(z)) * LN2;
+    }
+  }
 }
 
 // ------------------------------------------------------------ VALU path
@@ -1477,60 +1576,134 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------- merge
-// One workgroup per (row, head): log-sum-exp combination of the chunks'
-// partial (m, l, o) with the sink. Chunk weights 2^(m_c - M) are formed once
-// in LDS; the value loop then issues independent loads over the chunks.
+// One workgroup of two waves per (row, head): log-sum-exp combination of
+// the chunks' partial (m, l, o) with the sink (o in fp32, or in bf16 from the
+// streamed-row kernel, whose partials are as large as its KV reads and so
+// are written and read at half the bytes). The chunks' (m, l) pairs are
+// read once into LDS and turned into weights 2^(m_c - M); each thread then
+// sums four value dims over the chunks with MB independent 16-byte loads in
+// flight (the merge is a short, latency-bound pass over the partials).
 constexpr int MERGE_MAX_CH = 2048;
 
 template <typename T>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
   __shared__ float wts[MERGE_MAX_CH];
-  __shared__ float red[8];
+  __shared__ float lsv[MERGE_MAX_CH];
+  __shared__ float red[4];
   __shared__ float fin[2];
   const int r = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* ml = a.part_ml + ((int64_t)r * a.nch * a.H + h) * 2;
+  const int nch = a.nch;
+  const float* ml = a.part_ml + ((int64_t)r * nch * a.H + h) * 2;
   const int64_t cstride = (int64_t)a.H * 2;
   float m = -INFINITY;
-  for (int c = tid; c < a.nch; c += 256) m = fmaxf(m, ml[c * cstride]);
+  for (int c = tid; c < nch; c += 128) {
+    const float2 v = *reinterpret_cast<const float2*>(ml + c * cstride);
+    wts[c] = v.x;
+    lsv[c] = v.y;
+    m = fmaxf(m, v.x);
+  }
   m = wave_max(m);
   if (lane == 0) red[wave] = m;
   __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  m = fmaxf(red[0], red[1]);
   float l = 0.f;
-  for (int c = tid; c < a.nch; c += 256) {
-    const float mc = ml[c * cstride];
+  for (int c = tid; c < nch; c += 128) {
+    const float mc = wts[c];
     const float w = (mc == -INFINITY) ? 0.f : exp2f(mc - m);
     wts[c] = w;
-    l += w * ml[c * cstride + 1];
+    l += w * lsv[c];
   }
   l = wave_sum(l);
-  if (lane == 0) red[4 + wave] = l;
+  if (lane == 0) red[2 + wave] = l;
   __syncthreads();
   if (tid == 0) {
     float M, inv_z, lse;
-    finish_row(m, red[4] + red[5] + red[6] + red[7], a.sink, h, &M, &inv_z, &lse);
+    finish_row(m, red[2] + red[3], a.sink, h, &M, &inv_z, &lse);
     fin[0] = (m == -INFINITY) ? 0.f : exp2f(m - M) * inv_z;
     fin[1] = lse;
   }
   __syncthreads();
   const float f = fin[0];
-  const float* po = a.part_o + ((int64_t)r * a.nch * a.H + h) * a.dv;
+  const float* po = a.part_o + ((int64_t)r * nch * a.H + h) * a.dv;
   const int64_t ostride = (int64_t)a.H * a.dv;
-  for (int d = tid; d < a.dv; d += 256) {
-    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-    int c = 0;
-    for (; c + 4 <= a.nch; c += 4) {
-      o0 += po[(c + 0) * ostride + d] * wts[c + 0];
-      o1 += po[(c + 1) * ostride + d] * wts[c + 1];
-      o2 += po[(c + 2) * ostride + d] * wts[c + 2];
-      o3 += po[(c + 3) * ostride + d] * wts[c + 3];
+  const int64_t orow = ((int64_t)r * a.H + h) * a.dv;
+  auto store4 = [&](int d, float4 o) {
+    if (sizeof(T) == 4) {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + orow + d) =
+          make_float4(o.x * f, o.y * f, o.z * f, o.w * f);
+    } else {
+      const uint32_t lo = f32_to_bf16_bits(o.x * f) | (f32_to_bf16_bits(o.y * f) << 16);
+      const uint32_t hi = f32_to_bf16_bits(o.z * f) | (f32_to_bf16_bits(o.w * f) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + orow + d) = make_uint2(lo, hi);
     }
-    for (; c < a.nch; ++c) o0 += po[c * ostride + d] * wts[c];
-    const float o = ((o0 + o1) + (o2 + o3)) * f;
-    const int64_t oi = ((int64_t)r * a.H + h) * a.dv + d;
-    if (sizeof(T) == 4) reinterpret_cast<float*>(a.out)[oi] = o;
-    else reinterpret_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16_bits(o);
+  };
+  if (a.part_bf16) {
+    // bf16 partials (dv is a multiple of 64 on this path)
+    const uint16_t* pb = reinterpret_cast<const uint16_t*>(a.part_o) + ((int64_t)r * nch * a.H + h) * a.dv;
+    constexpr int MB = 16;
+    for (int d = 4 * tid; d < a.dv; d += 4 * 128) {
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+      auto acc4 = [&](uint2 v, float w) {
+        o.x += bf16_bits_to_f32(v.x & 0xffffu) * w;
+        o.y += bf16_bits_to_f32(v.x >> 16) * w;
+        o.z += bf16_bits_to_f32(v.y & 0xffffu) * w;
+        o.w += bf16_bits_to_f32(v.y >> 16) * w;
+      };
+      int c = 0;
+      for (; c + MB <= nch; c += MB) {
+        uint2 v[MB];
+#pragma unroll
+        for (int u = 0; u < MB; ++u) v[u] = *reinterpret_cast<const uint2*>(pb + (c + u) * ostride + d);
+#pragma unroll
+        for (int u = 0; u < MB; ++u) acc4(v[u], wts[c + u]);
+      }
+      for (; c < nch; ++c) acc4(*reinterpret_cast<const uint2*>(pb + c * ostride + d), wts[c]);
+      store4(d, o);
+    }
+  } else if ((a.dv & 3) == 0) {
+    constexpr int MB = 16;
+    for (int d = 4 * tid; d < a.dv; d += 4 * 128) {
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+      int c = 0;
+      for (; c + MB <= nch; c += MB) {
+        float4 v[MB];
+#pragma unroll
+        for (int u = 0; u < MB; ++u) v[u] = *reinterpret_cast<const float4*>(po + (c + u) * ostride + d);
+#pragma unroll
+        for (int u = 0; u < MB; ++u) {
+          const float w = wts[c + u];
+          o.x += v[u].x * w;
+          o.y += v[u].y * w;
+          o.z += v[u].z * w;
+          o.w += v[u].w * w;
+        }
+      }
+      for (; c < nch; ++c) {
+        const float4 v = *reinterpret_cast<const float4*>(po + c * ostride + d);
+        const float w = wts[c];
+        o.x += v.x * w;
+        o.y += v.y * w;
+        o.z += v.z * w;
+        o.w += v.w * w;
+      }
+      store4(d, o);
+    }
+  } else {
+    for (int d = tid; d < a.dv; d += 128) {
+      float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+      int c = 0;
+      for (; c + 4 <= nch; c += 4) {
+        o0 += po[(c + 0) * ostride + d] * wts[c + 0];
+        o1 += po[(c + 1) * ostride + d] * wts[c + 1];
+        o2 += po[(c + 2) * ostride + d] * wts[c + 2];
+        o3 += po[(c + 3) * ostride + d] * wts[c + 3];
+      }
+      for (; c < nch; ++c) o0 += po[c * ostride + d] * wts[c];
+      const float o = ((o0 + o1) + (o2 + o3)) * f;
+      if (sizeof(T) == 4) reinterpret_cast<float*>(a.out)[orow + d] = o;
+      else reinterpret_cast<uint16_t*>(a.out)[orow + d] = (uint16_t)f32_to_bf16_bits(o);
+    }
   }
   if (a.lse && tid == 0) a.lse[(int64_t)r * a.H + h] = fin[1];
 }
@@ -1539,6 +1712,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 struct AttnPlan {
   int chunk, nch, tiles, extra;
   bool mfma, whole;
+  bool row32;   // 64 heads: the streaming 32x32 kernel, rows split over nch workgroups
   bool qtile;   // dense prefill: query-row tiles
   int qt_ct;    // column tiles per wave of the query-tile kernel
   size_t off_o, off_ml, total;
@@ -1562,8 +1736,8 @@ static int qtile_ct(int H, int D) {
   return (D <= 256 && (4 * ct) % (H / 16) == 0) ? ct : 0;
 }
 
-// The 32x32 whole-row kernel: 64 heads, value dims split into two halves of
-// 32-row tiles, DMA chunks split over four waves.
+// The 32x32 streamed-row kernel: 64 heads, value dims split into two halves
+// of 32-row tiles, DMA chunks split over four waves.
 static bool row32_shape(int D, int dv) {
   return (D == 576 && dv == 512) || (D == 256 && dv == 256) || (D == 128 && dv == 128) || (D == 64 && dv == 64);
 }
@@ -1582,6 +1756,17 @@ static AttnPlan plan_attn(bool dense, int B, int T, int H, int D, int dv, int Lc
     p.nch = 1;
     return p;
   }
+  // 64 heads of a supported shape: the streaming 32x32 kernel; rows are
+  // split into runs of 64-row tiles until about one workgroup per CU
+  // (few rows with long candidate lists: decode)
+  if (p.mfma && H == 64 && row32_shape(D, dv) && (dense || Lc >= 1)) {
+    const int64_t nt = ceil_div(total, 64);
+    int64_t nch = ceil_div(256, R);
+    nch = nch < nt ? nch : nt;
+    p.row32 = true;
+    p.chunk = total;
+    p.nch = (int)(nch < 1 ? 1 : nch);
+  } else {
   const int gran = p.mfma ? 32 : 64;
   int64_t want = ceil_div(R * (int64_t)total, 256);  // aim at ~256 workgroups
   int64_t ch = ceil_div(want < 128 ? 128 : want, gran) * gran;
@@ -1616,10 +1801,11 @@ static AttnPlan plan_attn(bool dense, int B, int T, int H, int D, int dv, int Lc
   }
   p.chunk = (int)ch;
   p.nch = (int)ceil_div(total > 0 ? total : 1, ch);
+  }
   size_t o = 0;
   if (p.nch > 1) {
     p.off_o = o;
-    o += (size_t)R * p.nch * H * dv * 4;
+    o += (size_t)R * p.nch * H * dv * (p.row32 ? 2 : 4);  // the streamed-row kernel writes bf16
     o = (o + 255) & ~(size_t)255;
     p.off_ml = o;
     o += (size_t)R * p.nch * H * 2 * 4;
@@ -1670,6 +1856,7 @@ static int attn_common(const char* fn, bool dense, const void* q, const int32_t*
   char* ws = reinterpret_cast<char*>(workspace);
   a.part_o = p.nch > 1 ? reinterpret_cast<float*>(ws + p.off_o) : nullptr;
   a.part_ml = p.nch > 1 ? reinterpret_cast<float*>(ws + p.off_ml) : nullptr;
+  a.part_bf16 = p.row32;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const unsigned R = (unsigned)(B * T);
   int rc;
@@ -1687,15 +1874,16 @@ static int attn_common(const char* fn, bool dense, const void* q, const int32_t*
 #undef CSK_QT_CASE
     return rc;
   }
-  if (p.mfma && !dense && !p.whole && p.nch == 1 && H == 64 && k >= 1 && row32_shape(D, dv)) {
+  if (p.row32) {
     rc = CSK_EUNSUPPORTED;
-#define CSK_R32_CASE(d, v) \
-  if (D == d && dv == v) rc = launch("attn_bf16_sparse", attn_bf16_row32_kernel<d, v>, dim3(R), dim3(256), 0, s, a);
+    const dim3 grid(R, p.nch);
+#define CSK_R32_CASE(d, v)                                                                       \
+  if (D == d && dv == v)                                                                         \
+    rc = dense ? launch("attn_bf16_dense", attn_bf16_row32_kernel<d, v, true>, grid, dim3(256), 0, s, a) \
+               : launch("attn_bf16_sparse", attn_bf16_row32_kernel<d, v, false>, grid, dim3(256), 0, s, a);
     CSK_R32_CASE(576, 512) CSK_R32_CASE(256, 256) CSK_R32_CASE(128, 128) CSK_R32_CASE(64, 64)
 #undef CSK_R32_CASE
-    return rc;
-  }
-  if (p.mfma) {
+  } else if (p.mfma) {
     dim3 grid(R, p.nch), block(64 * (H / 16));
 const int NW = H / 16;
     const char* kname = dense ? "attn_bf16_dense" : "attn_bf16_sparse";
@@ -1724,7 +1912,7 @@ const int NW = H / 16;
                           : launch("attn_valu", attn_valu_kernel<uint16_t>, grid, block, lds, s, a);
   }
   if (rc != CSK_OK || p.nch == 1) return rc;
-  dim3 mg(R, H), mb(256);
+  dim3 mg(R, H), mb(128);
   return dtype == CSK_F32 ? launch("attn_merge", attn_merge_kernel<float>, mg, mb, 0, s, a)
                           : launch("attn_merge", attn_merge_kernel<uint16_t>, mg, mb, 0, s, a);
 }
