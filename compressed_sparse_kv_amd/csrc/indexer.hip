@@ -21,14 +21,16 @@
 // holds every head of key 64*iter + l and runs the chain in registers.
 //
 // Top-k: the k highest scores (ties to the lower index) in ascending index
-// order. Rows with at most TOPK_CAP candidates are selected in LDS by an
-// 8-bit radix select on an order-preserving 32-bit key followed by an
-// index-ordered compaction. Longer rows (decode over 32K-1M entries) are
+// order. Rows with at most TOPK_CAP candidates are selected in LDS on an
+// order-preserving 32-bit key, by histograms over the keys' own range that
+// narrow it to the k-th largest key, followed by an index-ordered
+// compaction. Longer rows (decode over 32K-1M entries) are
 // first filtered with a threshold L that provably keeps at least k keys:
 // the scoring kernel writes the maximum of every group of GS consecutive
-// keys, and L is the k-th largest of those group maxima (each is a distinct
-// element, so at least k elements are >= L). Filtering writes per-slice
-// candidate lists in index order, and the same radix select finishes.
+// keys, and L is at most the k-th largest of those group maxima (each is a
+// distinct element, so at least k elements are >= L). Filtering writes
+// per-slice candidate lists in index order, and the same range select
+// finishes.
 #include <algorithm>
 #include <mutex>
 
@@ -342,87 +344,30 @@ __device__ __forceinline__ int2 block_scan2(int a, int b, ScanShared& sh, int2* 
   return make_int2(off.x + x - a, off.y + y - b);
 }
 
-// ---------------------------------------------------- LDS histogram adds
-// hist[bin] += 1 for every active lane. Keys near a top-k threshold share
-// their leading digits, so many lanes of a wave hit the same bin; same-bin
-// lanes are combined into one atomic (up to four distinct bins per call),
-// and whatever is left goes through plain per-lane atomics.
-__device__ __forceinline__ void hist_add(int* hist, uint32_t bin, bool active) {
-  const int lane = threadIdx.x & 63;
-  unsigned long long todo = __ballot(active);
-#pragma unroll
-  for (int round = 0; round < 4; ++round) {
-    if (todo == 0ull) return;
-    const int leader = __ffsll((long long)todo) - 1;
-    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
-    const unsigned long long same = __ballot(active && bin == b) & todo;
-    if (lane == leader) atomicAdd(&hist[b], __popcll(same));
-    todo &= ~same;
-  }
-  if ((todo >> lane) & 1ull) atomicAdd(&hist[bin], 1);
-}
+// ------------------------------------------------------------ range select
+// Block-wide (NT threads) selection of the k largest of n keys get(e), as a
+// SelectState: every element whose masked key is > prefix, plus the first
+// `take` elements (in element order) whose masked key == prefix. The keys
+// in [kmin, kmax] are binned linearly over the range (bin = (key - lo) >>
+// sb, at most SEL_BINS bins); the bin that holds the k-th largest key is
+// found and becomes the next, narrower range. With 32-bit keys three levels
+// reach single key values (sb <= 20, then <= 8, then 0); a level ends early
+// when the whole bin is taken. Binning over the keys' own range keeps the
+// LDS atomics spread even when the keys share their leading bits (near a
+// top-k threshold they do).
+constexpr int SEL_BINS = 4096;
 
-// ------------------------------------------------------------ radix select
-// Block-wide (TOPK_THREADS) selection over n elements with keys get(e).
-// Finds (mask, prefix, take) such that the selected set is every element
-// whose masked key is > prefix, plus the first `take` elements (in element
-// order) whose masked key == prefix.
 struct SelectState {
   uint32_t mask, prefix;
   int take;
 };
 
 struct SelectShared {
-  int hist[256];
+  int hist[SEL_BINS];
   int digit, above, binc;
+  uint32_t kmin[16], kmax[16];
   ScanShared scan;
 };
-
-template <int NT, typename Get>
-__device__ SelectState radix_select(Get get, int n, int k, SelectShared& sh) {
-  SelectState st{0u, 0u, k};
-  const int tid = threadIdx.x;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += NT) sh.hist[i] = 0;
-    __syncthreads();
-    for (int e0 = 0; e0 < n; e0 += NT) {
-      const int e = e0 + tid;
-      const uint32_t u = e < n ? get(e) : 0u;
-      hist_add(sh.hist, (u >> shift) & 255u, e < n && (u & st.mask) == st.prefix);
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // lane L owns bins 4L..4L+3; suffix sums over lanes find the digit
-      int s4 = sh.hist[4 * tid] + sh.hist[4 * tid + 1] + sh.hist[4 * tid + 2] + sh.hist[4 * tid + 3];
-      const int incl = wave_incl_sum(s4);
-      const int suf = __builtin_amdgcn_readlane(incl, 63) - incl + s4;  // sum of lanes >= tid
-      // suf = sum of bins >= 4*tid; the digit lies in the highest lane with suf >= take
-      const bool ok = suf >= st.take;
-      const unsigned long long bal = __ballot(ok);
-      const int L = 63 - __clzll(bal);
-      if (tid == L) {
-        int above = suf - s4;  // bins above this lane's group
-        int d = 4 * L + 3;
-        for (; d > 4 * L; --d) {
-          if (above + sh.hist[d] >= st.take) break;
-          above += sh.hist[d];
-        }
-        sh.digit = d;
-        sh.above = above;
-        sh.binc = sh.hist[d];
-      }
-    }
-    __syncthreads();
-    st.take -= sh.above;
-    st.prefix |= (uint32_t)sh.digit << shift;
-    st.mask |= 0xffu << shift;
-    const bool whole_bin = sh.binc == st.take;  // no tie resolution needed
-    __syncthreads();
-    if (whole_bin) break;
-  }
-  return st;
-}
 
 // Index-ordered compaction of the selected elements. Each thread owns a
 // contiguous run of elements; counts of strictly-greater and tied elements
@@ -475,38 +420,55 @@ struct TopkShared {
   int slice_off[1024 + 1];
 };
 
-// Threshold from the group maxima, to 20 bits of the order-preserving key:
-// a 4096-bin histogram of the top 12 bits finds the bin that holds the k-th
-// largest sample, a 256-bin histogram of the next 8 bits of the samples in
-// that bin refines it; the threshold is the lower edge of the sub-bin that
-// holds the k-th largest sample, so at least k samples (hence at least k
-// elements of the row) are >= it. 0 keeps everything when the row has at
-// most k entries or too few samples. Every workgroup of the row forms it
-// (the samples are a few KB, read from L2), which saves a launch.
+// Threshold from the group maxima: the samples' order-preserving keys are
+// binned linearly over their own range [kmin, kmax] (bin = (key - kmin) >>
+// sb, at most 4096 bins), the bin d holding the k-th largest sample is
+// found, and the threshold is its lower edge kmin + (d << sb), so at least k
+// samples (hence at least k elements of the row) are >= it. (Binning by the
+// leading key bits would put nearly all maxima, which share sign and
+// exponent, into a handful of bins, and the histogram's LDS atomics would
+// then serialise.) 0 keeps everything when the row has at most k entries or
+// too few samples. Every workgroup of the row forms it (the samples are a
+// few KB, read from L2), which saves a launch.
 constexpr int THR_BINS = 4096;
-constexpr int THR_BATCH = 32;       // samples per thread per load batch
+constexpr int THR_BATCH = 16;       // samples per thread per load batch
 constexpr int FUSED_THREADS = 256;
 
 struct FusedShared {
   int hist[THR_BINS];
   ScanShared scan;
   uint32_t thr;
-  int sub_bin;
+  uint32_t kmin[FUSED_THREADS / 64], kmax[FUSED_THREADS / 64];
 };
+
+// Wave-wide minimum / maximum of an unsigned value (DPP within rows, then
+// the row swaps).
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_ext_u32(uint32_t x) {
+  auto op = [](uint32_t u, uint32_t v) { return MAX ? (u > v ? u : v) : (u < v ? u : v); };
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xf, 0xf, false));  // row_ror:4
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xf, 0xf, false));  // row_ror:8
+  const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  x = op(p[0], p[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return op(q[0], q[1]);
+}
 
 // Suffix search over PER * FUSED_THREADS bins: the bin d holding the
 // element of rank `want` (1-based, from the top) and the count of elements
 // in bins above it. Exactly one thread returns true (none when fewer than
 // `want` elements exist).
-template <int PER>
+template <int NT, int PER>
 __device__ bool find_rank_bin(const int* hist, int want, ScanShared& scan, int* out_d, int* out_above) {
   const int tid = threadIdx.x;
-  const int G = FUSED_THREADS - 1 - tid;  // thread t owns bins PER*G .. PER*G+PER-1
+  const int G = NT - 1 - tid;  // thread t owns bins PER*G .. PER*G+PER-1
   int sg = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) sg += hist[PER * G + i];
   int2 tot;
-  const int ex = block_scan2<FUSED_THREADS>(sg, 0, scan, &tot).x;  // bins above this group
+  const int ex = block_scan2<NT>(sg, 0, scan, &tot).x;  // bins above this group
   if (ex < want && ex + sg >= want) {
     int above = ex;
     int d = PER * G + PER - 1;
@@ -519,6 +481,40 @@ __device__ bool find_rank_bin(const int* hist, int want, ScanShared& scan, int* 
     return true;
   }
   return false;
+}
+
+template <int NT, typename Get>
+__device__ SelectState range_select(Get get, int n, int k, uint32_t kmin, uint32_t kmax, SelectShared& sh) {
+  const int tid = threadIdx.x;
+  uint32_t lo = kmin, span = kmax - kmin;  // the current range [lo, lo + span]
+  int want = k;                            // rank of the target inside it
+  for (int level = 0; level < 3; ++level) {
+    const int sb = span < (uint32_t)SEL_BINS ? 0 : 20 - __clz(span);  // span >> sb < SEL_BINS
+    for (int i = tid; i < SEL_BINS; i += NT) sh.hist[i] = 0;
+    __syncthreads();
+    for (int e = tid; e < n; e += NT) {
+      const uint32_t u = get(e) - lo;  // wraps for keys below the range
+      if (u <= span) atomicAdd(&sh.hist[u >> sb], 1);
+    }
+    __syncthreads();
+    int d = 0, above = 0;
+    if (find_rank_bin<NT, SEL_BINS / NT>(sh.hist, want, sh.scan, &d, &above)) {
+      sh.digit = d;
+      sh.above = above;
+      sh.binc = sh.hist[d];
+    }
+    __syncthreads();
+    d = sh.digit;
+    want -= sh.above;
+    const int binc = sh.binc;
+    const uint32_t edge = lo + ((uint32_t)d << sb);
+    __syncthreads();  // the shared results and bins are reused
+    if (sb == 0) return SelectState{0xffffffffu, edge, want};  // one key value: ties by element order
+    if (binc == want && edge > 0u) return SelectState{0xffffffffu, edge - 1u, 0};  // every key >= edge
+    lo = edge;
+    span = (1u << sb) - 1u;
+  }
+  return SelectState{0xffffffffu, lo, want};  // not reached: the third level has sb == 0
 }
 
 // Candidate filter for long rows: workgroup (r, f) forms the row's
@@ -556,43 +552,48 @@ __global__ __launch_bounds__(FUSED_THREADS) void topk_filter_kernel(TopkArgs a) 
     uint32_t thr = 0u;
     if (thresholded) {
       const float* smp = a.ia.samples + (int64_t)r * a.ia.ng;
-      // level 1: top 12 key bits (plain LDS atomics: the maxima spread over
-      // enough bins that combining same-bin lanes first costs more)
+      // the samples' key range (the keys of a single batch stay in
+      // registers for the histogram; longer rows load them again)
+      uint32_t kx[THR_BATCH];
+      uint32_t kmin = 0xffffffffu, kmax = 0u;
       for (int e0 = 0; e0 < ng; e0 += FUSED_THREADS * THR_BATCH) {
-        float x[THR_BATCH];
 #pragma unroll
-        for (int i = 0; i < THR_BATCH; ++i) x[i] = smp[min(e0 + FUSED_THREADS * i + tid, ng - 1)];
+        for (int i = 0; i < THR_BATCH; ++i) kx[i] = order_key(smp[min(e0 + FUSED_THREADS * i + tid, ng - 1)]);
+#pragma unroll
+        for (int i = 0; i < THR_BATCH; ++i) {
+          kmin = min(kmin, kx[i]);
+          kmax = max(kmax, kx[i]);
+        }
+      }
+      kmin = wave_ext_u32<false>(kmin);
+      kmax = wave_ext_u32<true>(kmax);
+      if ((tid & 63) == 0) {
+        sh.kmin[tid >> 6] = kmin;
+        sh.kmax[tid >> 6] = kmax;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < FUSED_THREADS / 64; ++w) {
+        kmin = min(kmin, sh.kmin[w]);
+        kmax = max(kmax, sh.kmax[w]);
+      }
+      const uint32_t span = kmax - kmin;
+      const int sb = span < (uint32_t)THR_BINS ? 0 : 20 - __clz(span);  // span >> sb < 4096
+      const bool one_batch = ng <= FUSED_THREADS * THR_BATCH;
+      for (int e0 = 0; e0 < ng; e0 += FUSED_THREADS * THR_BATCH) {
+        if (!one_batch) {
+#pragma unroll
+          for (int i = 0; i < THR_BATCH; ++i) kx[i] = order_key(smp[min(e0 + FUSED_THREADS * i + tid, ng - 1)]);
+        }
 #pragma unroll
         for (int i = 0; i < THR_BATCH; ++i)
-          if (e0 + FUSED_THREADS * i + tid < ng) atomicAdd(&sh.hist[order_key(x[i]) >> 20], 1);
+          if (e0 + FUSED_THREADS * i + tid < ng) atomicAdd(&sh.hist[(kx[i] - kmin) >> sb], 1);
       }
       __syncthreads();
       int d = 0, above = 0;
-      // the owner of the bin publishes it
-      if (find_rank_bin<16>(sh.hist, k, sh.scan, &d, &above)) {
-        sh.thr = (uint32_t)d;
-        sh.sub_bin = above;
-      }
-      __syncthreads();
-      const uint32_t d1 = sh.thr;
-      const int above1 = sh.sub_bin;
-      __syncthreads();
-      // level 2: bits 19..12 of the samples in bin d1
-      for (int i = tid; i < 256; i += FUSED_THREADS) sh.hist[i] = 0;
-      __syncthreads();
-      for (int e0 = 0; e0 < ng; e0 += FUSED_THREADS * THR_BATCH) {
-        float x[THR_BATCH];
-#pragma unroll
-        for (int i = 0; i < THR_BATCH; ++i) x[i] = smp[min(e0 + FUSED_THREADS * i + tid, ng - 1)];
-#pragma unroll
-        for (int i = 0; i < THR_BATCH; ++i) {
-          const uint32_t u = order_key(x[i]);
-          if (e0 + FUSED_THREADS * i + tid < ng && (u >> 20) == d1) atomicAdd(&sh.hist[(u >> 12) & 255u], 1);
-        }
-      }
-      __syncthreads();
-      int e = 0, above2 = 0;
-      if (find_rank_bin<1>(sh.hist, k - above1, sh.scan, &e, &above2)) sh.thr = (d1 << 20) | ((uint32_t)e << 12);
+      // the owner of the bin publishes its lower edge
+      if (find_rank_bin<FUSED_THREADS, THR_BINS / FUSED_THREADS>(sh.hist, k, sh.scan, &d, &above))
+        sh.thr = kmin + ((uint32_t)d << sb);
       __syncthreads();
       thr = sh.thr;
     }
@@ -651,52 +652,71 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkArgs a) {
   int* gidx = a.flat_idx + (int64_t)r * a.ia.Nmax;
   const float* srow = a.ia.scores + (int64_t)r * a.ia.Nmax;
 
-  // gather elements (in index order) into LDS, or into the spill buffer
+  // gather elements (in index order) into LDS, or into the spill buffer,
+  // with the range of their keys
+  uint32_t umin = 0xffffffffu, umax = 0u;
   if (!FILTERED) {
-    if (in_lds)
-      for (int e = tid; e < n; e += TOPK_THREADS) sh.key[e] = order_key(srow[e]);
+    // (unfiltered rows have at most TOPK_CAP entries: always in LDS)
+    for (int e = tid; e < n; e += TOPK_THREADS) {
+      const uint32_t u = order_key(srow[e]);
+      sh.key[e] = u;
+      umin = min(umin, u);
+      umax = max(umax, u);
+    }
   } else {
-    // element e lives in slice f with slice_off[f] <= e < slice_off[f+1];
-    // GATHER elements per thread are located first, then all their loads
-    // are issued together
-    constexpr int GATHER = 4;
-    for (int e0 = 0; e0 < n; e0 += GATHER * TOPK_THREADS) {
-      int64_t src[GATHER];
-#pragma unroll
-      for (int i = 0; i < GATHER; ++i) {
-        const int e = e0 + i * TOPK_THREADS + tid;
-        int lo = 0, hi = ns - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (sh.slice_off[mid] <= e) lo = mid;
-          else hi = mid - 1;
-        }
-        // past the end: a valid element is read and dropped below
-        src[i] = (int64_t)r * a.ia.Nmax + (e < n ? (int64_t)lo * SLICE + (e - sh.slice_off[lo]) : 0);
+    // each wave copies whole slices (wave w: slices w, w + NW, ...), up to
+    // 64 candidates of a slice per load round and four slices' loads in
+    // flight together; slices longer than 64 candidates finish in a loop
+    constexpr int NW = TOPK_THREADS / 64;
+    const int lane = tid & 63, wv = tid >> 6;
+    auto put = [&](int e, float sv, int iv) {
+      const uint32_t u = order_key(sv);
+      umin = min(umin, u);
+      umax = max(umax, u);
+      if (in_lds) {
+        sh.key[e] = u;
+        sh.eidx[e] = iv;
+      } else {
+        gkey[e] = u;
+        gidx[e] = iv;
       }
-      float sv[GATHER];
-      int iv[GATHER];
+    };
+    const int64_t rbase = (int64_t)r * a.ia.Nmax;
+    for (int f0 = wv; f0 < ns; f0 += 4 * NW) {
+      float sv[4];
+      int iv[4], dst[4], cnt[4];
 #pragma unroll
-      for (int i = 0; i < GATHER; ++i) {
-        sv[i] = a.cand_score[src[i]];
-        iv[i] = a.cand_idx[src[i]];
+      for (int u = 0; u < 4; ++u) {
+        const int f = f0 + u * NW;
+        dst[u] = f < ns ? sh.slice_off[f] : 0;
+        cnt[u] = f < ns ? sh.slice_off[f + 1] - dst[u] : 0;
+        if (lane < cnt[u]) {
+          sv[u] = a.cand_score[rbase + (int64_t)f * SLICE + lane];
+          iv[u] = a.cand_idx[rbase + (int64_t)f * SLICE + lane];
+        }
       }
 #pragma unroll
-      for (int i = 0; i < GATHER; ++i) {
-        const int e = e0 + i * TOPK_THREADS + tid;
-        if (e >= n) continue;
-        const uint32_t u = order_key(sv[i]);
-        if (in_lds) {
-          sh.key[e] = u;
-          sh.eidx[e] = iv[i];
-        } else {
-          gkey[e] = u;
-          gidx[e] = iv[i];
-        }
+      for (int u = 0; u < 4; ++u)
+        if (lane < cnt[u]) put(dst[u] + lane, sv[u], iv[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t src = rbase + (int64_t)(f0 + u * NW) * SLICE;
+        for (int j = 64 + lane; j < cnt[u]; j += 64) put(dst[u] + j, a.cand_score[src + j], a.cand_idx[src + j]);
       }
     }
   }
+  umin = wave_ext_u32<false>(umin);
+  umax = wave_ext_u32<true>(umax);
+  if ((tid & 63) == 0) {
+    sh.sel.kmin[tid >> 6] = umin;
+    sh.sel.kmax[tid >> 6] = umax;
+  }
   __syncthreads();
+#pragma unroll
+  for (int w = 0; w < TOPK_THREADS / 64; ++w) {
+    umin = min(umin, sh.sel.kmin[w]);
+    umax = max(umax, sh.sel.kmax[w]);
+  }
 
   auto get = [&](int e) -> uint32_t {
     if (in_lds) return sh.key[e];
@@ -717,7 +737,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkArgs a) {
     for (int e = tid; e < n; e += TOPK_THREADS) emit(e, e);
     nsel = n;
   } else {
-    SelectState st = radix_select<TOPK_THREADS>(get, n, k, sh.sel);
+    SelectState st = range_select<TOPK_THREADS>(get, n, k, umin, umax, sh.sel);
     compact_selected<TOPK_THREADS>(get, emit, n, st, sh.sel);
     nsel = k;
   }
