@@ -97,13 +97,25 @@ __device__ __forceinline__ void swap16(float& x, float& y) {
 }
 
 // Group maxima of the scores held by a wave (one per lane, key = base+lane),
-// written for groups of 2^gs_log2 keys (gs <= 64).
+// written for groups of 2^gs_log2 keys (gs <= 64): maxima within aligned
+// lane groups of 2, 4 (quad permutes), 8 (half-row mirror), 16 (row
+// mirror), then across rows (permlane swaps), all VALU steps.
 __device__ __forceinline__ void write_samples(const IdxArgs& a, int r, int base, float v) {
   const int gs = 1 << a.gs_log2;
+  const int g = a.gs_log2;
   float mx = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1)
-    if (o < gs) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (g >= 1) mx = fmaxf(mx, CSK_DPP_F(mx, 0xB1));   // quad_perm [1,0,3,2]
+  if (g >= 2) mx = fmaxf(mx, CSK_DPP_F(mx, 0x4E));   // quad_perm [2,3,0,1]
+  if (g >= 3) mx = fmaxf(mx, CSK_DPP_F(mx, 0x141));  // row_half_mirror
+  if (g >= 4) mx = fmaxf(mx, CSK_DPP_F(mx, 0x140));  // row_mirror
+  if (g >= 5) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  }
+  if (g >= 6) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  }
   const int lane = threadIdx.x & 63;
   const int key = base + lane;
   if ((lane & (gs - 1)) == 0 && key < a.Nmax)
@@ -150,7 +162,7 @@ __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
   // the row's head weights, one LDS copy per wave, read back as broadcast
   // LDS reads (a global load here would be counted with the in-flight key
   // loads, and waiting for it would drain them)
-  __shared__ float wsh[4][64];
+  __shared__ __align__(16) float wsh[4][64];
   if (lane < HI) wsh[wave][lane] = a.w[(int64_t)r * HI + lane];
   const float* wr = wsh[wave];
 
@@ -227,12 +239,15 @@ __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
     for (int g = 0; g < 4; ++g) {
       asm volatile("" ::: "memory");
 #pragma unroll
-      for (int t = 0; t < HT; ++t)
+      for (int t = 0; t < HT; ++t) {
+        const float4 w4 = *reinterpret_cast<const float4*>(wr + 4 * HT * g + 4 * t);
+        const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float v = __int_as_float(max(__float_as_int(d[g][t][j]), 0));
-          score = __builtin_fmaf(wr[4 * HT * g + 4 * t + j], v, score);
+          score = __builtin_fmaf(wv[j], v, score);
         }
+      }
     }
 
     const int key = base + lane;
