@@ -1415,7 +1415,7 @@ void attn_bf16_row32_kernel(AttnArgs a) {
   // (h%32)*DV/4 + (du ^ h%16), which keeps the scattered writes and the
   // row-wise reads on distinct bank groups.
   constexpr int DU = DV / 4;
-  static_assert(DU % 16 == 0 && 32 * DV * 4 <= TU * 16, "staging layout");
+  static_assert(DU % 16 == 0 && (64 * DU) % 512 == 0 && 32 * DV * 4 <= TU * 16, "staging layout");
   {
     float* st = reinterpret_cast<float*>(hg ? buf1 : buf0);
 #pragma unroll
@@ -1430,25 +1430,22 @@ void attn_bf16_row32_kernel(AttnArgs a) {
   }
   lds_barrier();
   {
+    // eight value dims (two staged units) per lane and store: bf16, 16 bytes
     const int ls = fresh_lane() + 64 * wave;
     const int64_t row0 = a.nch > 1 ? ((int64_t)r * a.nch + split) * a.H : (int64_t)r * a.H;
+    uint16_t* dst = reinterpret_cast<uint16_t*>(a.nch > 1 ? static_cast<void*>(a.part_o) : a.out);
 #pragma unroll 4
-    for (int k = 0; k < 64 * DU / 256; ++k) {
+    for (int k = 0; k < 64 * DU / 512; ++k) {
       const int idx = 256 * k + ls;
-      const int h = idx / DU, du = idx % DU;
+      const int h = idx / (DU / 2), du = 2 * (idx % (DU / 2));
       const float* st = reinterpret_cast<const float*>(h >= 32 ? buf1 : buf0);
-      const float4 v = *reinterpret_cast<const float4*>(st + 4 * ((h & 31) * DU + (du ^ (h & 15))));
-      if (a.nch > 1) {
-        const v2bf lo = {(__bf16)v.x, (__bf16)v.y};
-        const v2bf hh = {(__bf16)v.z, (__bf16)v.w};
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.part_o) + (row0 + h) * DV + 4 * du) =
-            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hh));
-      } else {
-        const v2bf lo = {(__bf16)v.x, (__bf16)v.y};
-        const v2bf hh = {(__bf16)v.z, (__bf16)v.w};
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + (row0 + h) * DV + 4 * du) =
-            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hh));
-      }
+      const float4 v0 = *reinterpret_cast<const float4*>(st + 4 * ((h & 31) * DU + (du ^ (h & 15))));
+      const float4 v1 = *reinterpret_cast<const float4*>(st + 4 * ((h & 31) * DU + ((du + 1) ^ (h & 15))));
+      const v2bf p0 = {(__bf16)v0.x, (__bf16)v0.y}, p1 = {(__bf16)v0.z, (__bf16)v0.w};
+      const v2bf p2 = {(__bf16)v1.x, (__bf16)v1.y}, p3 = {(__bf16)v1.z, (__bf16)v1.w};
+      *reinterpret_cast<uint4*>(dst + (row0 + h) * DV + 4 * du) =
+          make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                     __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
     }
   }
   if (ch == 0 && hio == 0) {

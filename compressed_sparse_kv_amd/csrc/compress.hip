@@ -153,7 +153,19 @@ __global__ __launch_bounds__(64) void compress_kernel(CompressArgs a) {
   const IN* ca = reinterpret_cast<const IN*>(a.ca) + src0 * a.D;
   const IN* za = reinterpret_cast<const IN*>(a.za) + src0 * a.D;
   const bool has_b = CSA && (a.entry0 + i) > 0;
-  if (CSA && a.m <= 8) {
+  if (CSA && a.m == 4) {
+    // 4x compression (the CSA ratio): both series, 8 slots, one batch
+    const IN* cb = reinterpret_cast<const IN*>(a.cb) + src0 * a.D;
+    const IN* zb = reinterpret_cast<const IN*>(a.zb) + src0 * a.D;
+    float2 l[8], v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      load_slot(ca, za, a.bias_a, 4 * (int64_t)i + j, j, a.D, ch, true, 4 * (int64_t)i, l[j], v[j]);
+      load_slot(cb, zb, a.bias_b, 4 * ((int64_t)i - 1) + j, j, a.D, ch, has_b, 4 * (int64_t)i, l[4 + j],
+                v[4 + j]);
+    }
+    fold<8>(l, v, mx, den, num);
+  } else if (CSA && a.m <= 8) {
     // both series of the entry in one batch: 2m loads in flight together
     const IN* cb = reinterpret_cast<const IN*>(a.cb) + src0 * a.D;
     const IN* zb = reinterpret_cast<const IN*>(a.zb) + src0 * a.D;
