@@ -62,7 +62,8 @@ def test_sparse_fp32_tiny_shapes():
     _sparse_case(602, B=1, T=256, H=4, D=64, dv=64, N=64, k=8, S_w=256, W=32, bf16=False, d_rope=32)
 
 
-@pytest.mark.parametrize("H,D,dv", [(64, 576, 512), (16, 128, 128), (32, 576, 576), (64, 64, 64), (8, 96, 80)])
+@pytest.mark.parametrize("H,D,dv", [(64, 576, 512), (16, 128, 128), (32, 576, 576), (64, 64, 64), (8, 96, 80),
+                                    (64, 256, 256), (64, 128, 128)])
 def test_sparse_decode_split(H, D, dv):
     # decode rows: long candidate lists split across workgroups and merged
     _sparse_case(603 + H + D, B=3, T=1, H=H, D=D, dv=dv, N=5000, k=2048, S_w=128, W=128, bf16=True,
@@ -150,11 +151,33 @@ def test_dense_decode_split():
                 decode=True)
 
 
+@pytest.mark.parametrize("D", [256, 128, 64])
+def test_dense_decode_split_shapes(D):
+    # 64 heads at the other streamed-row shapes: rows split over runs of
+    # 64-row tiles (a ragged last tile, shorter visible lists on rows 1..)
+    _dense_case(740 + D, B=3, T=1, H=64, D=D, dv=D, N=1500, m=128, S_w=128, W=128, bf16=True,
+                d_rope=min(64, D // 2), decode=True)
+
+
+def test_dense_many_rows_kept_whole():
+    # more rows than CUs: each row stays in one workgroup, which writes the
+    # normalised output itself (no partials, no merge)
+    _dense_case(750, B=260, T=1, H=64, D=128, dv=128, N=40, m=4, S_w=160, W=32, bf16=True, d_rope=64,
+                decode=True)
+
+
+def test_dense_few_query_rows():
+    # a short run of query rows per sequence (below the query-tile path):
+    # each row has its own visible count and window
+    _dense_case(751, B=2, T=9, H=64, D=576, dv=512, N=300, m=4, S_w=1300, W=64, bf16=True, d_rope=64,
+                decode=False, q_pos=np.array([[1190 + 3 * t for t in range(9)]] * 2, np.int32))
+
+
 @pytest.mark.parametrize("B,N", [(2, 16384), (4, 8192)])
 def test_dense_decode_extra_rows(B, N):
-    # rows of 16512 / 8320 candidates: 128-candidate chunks would need one
-    # workgroup more than a wave of the chip, so each chunk also takes one or
-    # two rows past its MFMA tiles (scored on the VALU)
+    # rows of 16512 / 8320 candidates (the 1M-context HCA shape): each row
+    # split over 64 or 128 workgroups of two or three 64-row tiles, bf16
+    # partials merged
     _dense_case(705 + B, B=B, T=1, H=64, D=576, dv=512, N=N, m=128, S_w=128, W=128, bf16=True, d_rope=64,
                 decode=True)
 
