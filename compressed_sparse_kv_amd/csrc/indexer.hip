@@ -377,10 +377,14 @@ struct SelectState {
   int take;
 };
 
+constexpr int SEL_SMALL = 64;  // a bin this small is finished by one wave's rank count
+
 struct SelectShared {
   int hist[SEL_BINS];
-  int digit, above, binc;
+  int digit, above, binc, nsmall, take;
+  uint32_t thr;
   uint32_t kmin[16], kmax[16];
+  uint32_t small[SEL_SMALL];
   ScanShared scan;
 };
 
@@ -526,6 +530,34 @@ __device__ SelectState range_select(Get get, int n, int k, uint32_t kmin, uint32
     __syncthreads();  // the shared results and bins are reused
     if (sb == 0) return SelectState{0xffffffffu, edge, want};  // one key value: ties by element order
     if (binc == want && edge > 0u) return SelectState{0xffffffffu, edge - 1u, 0};  // every key >= edge
+    if (binc <= SEL_SMALL) {
+      // the few keys of the bin: wave 0 ranks them (lane j counts the keys
+      // above and equal to its own) and publishes the want-th largest
+      if (tid == 0) sh.nsmall = 0;
+      __syncthreads();
+      for (int e = tid; e < n; e += NT) {
+        const uint32_t u = get(e);
+        if (u - edge < (1u << sb)) sh.small[atomicAdd(&sh.nsmall, 1)] = u;
+      }
+      __syncthreads();
+      if (tid < 64) {
+        const uint32_t kj = tid < binc ? sh.small[tid] : 0u;
+        int gt = 0, eq = 0;
+        for (int i = 0; i < binc; ++i) {
+          const uint32_t ki = (uint32_t)__builtin_amdgcn_readlane((int)kj, i);
+          gt += ki > kj;
+          eq += ki == kj;
+        }
+        if (tid < binc && gt < want && want <= gt + eq) {  // every lane holding the target agrees
+          sh.thr = kj;
+          sh.take = want - gt;
+        }
+      }
+      __syncthreads();
+      const SelectState st{0xffffffffu, sh.thr, sh.take};
+      __syncthreads();
+      return st;
+    }
     lo = edge;
     span = (1u << sb) - 1u;
   }
