@@ -95,10 +95,20 @@ struct RowInfo {
 __device__ __forceinline__ RowInfo row_info(const AttnArgs& a, int r) {
   RowInfo ri;
   ri.b = (int)((unsigned)r / (unsigned)a.T);
-  // the row's three loads first, so that they are in flight together
+  // the row's three loads first and unconditionally (an array the row does
+  // not use is replaced by q_pos, which has at least B entries), so that
+  // they are in flight together
+  const bool win = a.W > 0 && a.S_w > 0;
+  const int32_t* ne_src = a.dense ? a.n_entries : a.q_pos;
+  const int32_t* w0_src = win ? a.w_pos0 : a.q_pos;
   const int p = a.q_pos[r];
-  const int ne = a.dense ? a.n_entries[ri.b] : 0;
-  const int w0 = (a.W > 0 && a.S_w > 0) ? a.w_pos0[ri.b] : 0;
+  const int ne_raw = ne_src[ri.b];
+  const int w0_raw = w0_src[ri.b];
+  // (an empty asm that takes all three keeps the compiler from sinking each
+  // load into the branch that uses it, which would serialise them)
+  asm volatile("" ::"s"(p), "s"(ne_raw), "s"(w0_raw));
+  const int ne = a.dense ? ne_raw : 0;
+  const int w0 = win ? w0_raw : 0;
   ri.p = p;
   ri.nvis = 0;
   if (a.dense && p >= 0) {
@@ -109,7 +119,7 @@ __device__ __forceinline__ RowInfo row_info(const AttnArgs& a, int r) {
     ri.nvis = nv < 0 ? 0 : nv;
   }
   ri.wr0 = ri.wr1 = 0;
-  if (a.W > 0 && a.S_w > 0) {
+  if (win) {
     int64_t lo = (int64_t)p - a.W + 1;
     lo = lo < 0 ? 0 : lo;
     int64_t r0 = lo - w0, r1 = (int64_t)p - w0 + 1;
