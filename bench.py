@@ -15,8 +15,9 @@ the whole hot path for one new token per sequence:
   6. hca_compress  - the newest HCA entry (128 source tokens)
   7. dense_compressed_attn - HCA attention over all 8192 entries + window + sink
 The HCA branch (6, 7) runs on a side stream next to the CSA chain (2, 3, 1,
-4, 5 in that order on the main stream); --streams 1 runs every call in order
-on one stream. The timed steps are HIP graph
+4, 5 in that order on the main stream), its attention capped at 32
+workgroups (--hca-workgroups) so that the chain keeps most of the CUs;
+--streams 1 runs every call in order on one stream, uncapped. The timed steps are HIP graph
 replays, four steps per graph (--mode eager launches them directly). Four
 copies of the layer-pair state rotate between steps (as successive layers
 would), so a step never finds its 121 MB working set in the 256 MB Infinity
@@ -51,7 +52,7 @@ class DecodeWorkload:
     """Decode-step state on the GPU for 'decode_1m_pair' (CSA + HCA) or
     'csa_decode_128k' (CSA only), with host copies for the oracle."""
 
-    def __init__(self, name, copies=4, overrides=None, keep_host=True, streams=1):
+    def __init__(self, name, copies=4, overrides=None, keep_host=True, streams=1, hca_workgroups=32):
         import torch
 
         import compressed_sparse_kv_amd as csk
@@ -129,8 +130,10 @@ class DecodeWorkload:
             ws_d = csk.dense_compressed_attn_workspace_size(B, 1, H, self.D, dv, self.Nh, 128, self.W,
                                                             csk.CSK_BF16)
             self.ws_d = torch.empty(max(ws_d, 1), dtype=torch.uint8, device=dev)
-        # the side stream of the HCA branch (default priority)
+        # the side stream of the HCA branch (default priority), and the
+        # workgroup cap of its attention when it runs beside the CSA chain
         self.streams = streams
+        self.hca_workgroups = hca_workgroups
         self.side = torch.cuda.Stream()
         torch.cuda.synchronize()
         if not keep_host:
@@ -181,9 +184,17 @@ class DecodeWorkload:
         csk, Nh = self.csk, self.Nh
         csk.hca_compress(x["src_c"], x["src_z"], x["bias_h"], 128, d_rope=64, entry0=Nh - 1,
                          out=st["kvh_new"], dst_bstride=Nh)
-        csk.dense_compressed_attn(x["q_h"], x["q_pos"], st["kv_h"], x["n_entries_h"], 128, st["kv_w_h"],
-                                  x["w_pos0"], self.W, x["sink_h"], self.dv, 64, self.scale, out=self.out_h,
-                                  lse=self.lse_h, workspace=self.ws_d)
+        # beside the CSA chain the dense attention takes at most
+        # hca_workgroups workgroups (each holds a whole CU), which leaves the
+        # rest of the chip to the chain's kernels
+        cap = self.hca_workgroups if self.streams > 1 else 0
+        prev = csk.set_attn_workgroups(cap)
+        try:
+            csk.dense_compressed_attn(x["q_h"], x["q_pos"], st["kv_h"], x["n_entries_h"], 128, st["kv_w_h"],
+                                      x["w_pos0"], self.W, x["sink_h"], self.dv, 64, self.scale,
+                                      out=self.out_h, lse=self.lse_h, workspace=self.ws_d)
+        finally:
+            csk.set_attn_workgroups(prev)
 
     def kernels(self):
         names = ["csa_compress", "mxfp4_quantize", "indexer_scores_fp4", "topk_filter",
@@ -468,7 +479,8 @@ def run(args):
 
     import compressed_sparse_kv_amd as csk
 
-    wl = DecodeWorkload(args.workload, copies=args.copies, streams=args.streams)
+    wl = DecodeWorkload(args.workload, copies=args.copies, streams=args.streams,
+                        hca_workgroups=args.hca_workgroups)
     K, Wm = args.steps, args.warmup
     # eager warm-up (first calls set kernel attributes outside any capture)
     for i in range(max(Wm, 1)):
@@ -553,7 +565,8 @@ def run(args):
         "vs_baseline": None,
         "dtype": "bf16+mxfp4",
         "data": "synthetic",
-        "config": dict(wl.config(), launch=args.mode, streams=args.streams),
+        "config": dict(wl.config(), launch=args.mode, streams=args.streams,
+                       **({"hca_attn_workgroups": args.hca_workgroups} if wl.pair and args.streams > 1 else {})),
         "roofline": {
             "kernel": dom,
             "bound": "hbm",
@@ -746,6 +759,8 @@ def main():
     ap.add_argument("--graph-steps", type=int, default=4, help="steps captured per graph")
     ap.add_argument("--streams", type=int, default=2, choices=[1, 2],
                     help="1: every call on one stream; 2: the HCA branch on a side stream")
+    ap.add_argument("--hca-workgroups", type=int, default=32,
+                    help="workgroup cap of the HCA attention beside the CSA chain (0: one per CU)")
     ap.add_argument("--cpu-rows", type=int, default=4, help="decode: sequences the oracle runs")
     ap.add_argument("--cpu-rows-prefill", type=int, default=None,
                     help="prefill: query rows the oracle runs (default 384 for CSA, every row for HCA)")

@@ -52,6 +52,8 @@ def lib():
         L.sparse_attn_workspace_size.restype = _sz
         L.dense_compressed_attn_workspace_size.argtypes = [_i] * 9
         L.dense_compressed_attn_workspace_size.restype = _sz
+        L.csk_set_attn_workgroups.argtypes = [_i]
+        L.csk_set_attn_workgroups.restype = _i
         L.csk_kernel_timer_arm.argtypes = [ctypes.c_char_p, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i]
         L.csk_kernel_timer_count.restype = _i
         L.csk_kernel_timer_disarm.restype = None
@@ -222,6 +224,15 @@ def dense_compressed_attn(q, q_pos, kv_c, n_entries, m, kv_w, w_pos0, W, sink, d
                                      _dt(q), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream())
     _check(rc, "dense_compressed_attn")
     return out, lse
+
+
+def set_attn_workgroups(max_workgroups):
+    """Cap the workgroups of one split-row attention launch (0 = one per CU);
+    see csk_set_attn_workgroups in csk.h. Returns the previous cap."""
+    prev = lib().csk_set_attn_workgroups(int(max_workgroups))
+    if prev < 0:
+        raise CskError(lib().csk_last_error().decode())
+    return prev
 
 
 class KernelTimer:

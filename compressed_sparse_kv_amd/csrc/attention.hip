@@ -1749,6 +1749,9 @@ static bool row32_shape(int D, int dv) {
   return (D == 576 && dv == 512) || (D == 256 && dv == 256) || (D == 128 && dv == 128) || (D == 64 && dv == 64);
 }
 
+// Workgroup cap of split-row launches (0: one per CU), per calling thread.
+static thread_local int g_attn_workgroups = 0;
+
 static AttnPlan plan_attn(bool dense, int B, int T, int H, int D, int dv, int Lc, int W, int dtype) {
   AttnPlan p{};
   const int64_t R = (int64_t)B * T;
@@ -1768,7 +1771,7 @@ static AttnPlan plan_attn(bool dense, int B, int T, int H, int D, int dv, int Lc
   // (few rows with long candidate lists: decode)
   if (p.mfma && H == 64 && row32_shape(D, dv) && (dense || Lc >= 1)) {
     const int64_t nt = ceil_div(total, 64);
-    int64_t nch = ceil_div(256, R);
+    int64_t nch = ceil_div(g_attn_workgroups > 0 ? g_attn_workgroups : 256, R);
     nch = nch < nt ? nch : nt;
     p.row32 = true;
     p.chunk = total;
@@ -1927,6 +1930,14 @@ const int NW = H / 16;
 }  // namespace csk
 
 extern "C" {
+
+int csk_set_attn_workgroups(int max_workgroups) {
+  if (max_workgroups < 0) return csk::fail(CSK_EINVAL, "csk_set_attn_workgroups: negative cap");
+  csk::clear_error();
+  const int prev = csk::g_attn_workgroups;
+  csk::g_attn_workgroups = max_workgroups;
+  return prev;
+}
 
 size_t sparse_attn_workspace_size(int B, int T, int H, int D, int dv, int k, int W, int dtype) {
   if (B <= 0 || T <= 0 || H <= 0 || D <= 0 || dv <= 0 || k < 0 || W < 0) return 0;

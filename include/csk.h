@@ -201,6 +201,21 @@ size_t dense_compressed_attn_workspace_size(int B, int T, int H, int D, int dv, 
                                             int W, int dtype);
 
 /*
+ * csk_set_attn_workgroups - scheduling knob for split-row attention. A
+ * launch of sparse_attn or dense_compressed_attn over fewer query rows than
+ * the chip has CUs splits each row into runs of candidate tiles, by default
+ * about one workgroup per CU (256); each such workgroup holds a whole CU
+ * while it runs. max_workgroups > 0 caps that split at max_workgroups
+ * workgroups in all (rows are never split below one workgroup each), so a
+ * caller that runs other work on another stream at the same time can leave
+ * CUs to it; 0 restores the default. The setting is per calling thread and
+ * applies to the launches and *_workspace_size calls made after it (a
+ * smaller cap never needs more workspace than the default). Returns the
+ * previous value, or -1 with csk_last_error() set for a negative argument.
+ */
+int csk_set_attn_workgroups(int max_workgroups);
+
+/*
  * csk_kernel_timer_arm - measurement hook. The next n launches of the
  * library kernel named `kernel` ("indexer_scores_fp4", "attn_bf16", ...)
  * are each bracketed by hipEventRecord(ev_start[j]) / hipEventRecord(

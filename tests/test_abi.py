@@ -55,3 +55,18 @@ def test_argument_errors_without_device(lib):
     assert rc == -2
     lib.csk_abi_version.restype = ctypes.c_int
     assert lib.csk_abi_version() == 1
+
+
+def test_attn_workgroup_cap(lib):
+    # host-side plan only: the cap shrinks the split (and its workspace) and
+    # is restored; a negative cap is rejected
+    lib.csk_set_attn_workgroups.restype = ctypes.c_int
+    lib.csk_last_error.restype = ctypes.c_char_p
+    lib.dense_compressed_attn_workspace_size.restype = ctypes.c_size_t
+    full = lib.dense_compressed_attn_workspace_size(4, 1, 64, 576, 512, 8192, 128, 128, 1)
+    assert lib.csk_set_attn_workgroups(64) == 0
+    capped = lib.dense_compressed_attn_workspace_size(4, 1, 64, 576, 512, 8192, 128, 128, 1)
+    assert 0 < capped < full
+    assert lib.csk_set_attn_workgroups(-3) == -1 and b"negative" in lib.csk_last_error()
+    assert lib.csk_set_attn_workgroups(0) == 64
+    assert lib.dense_compressed_attn_workspace_size(4, 1, 64, 576, 512, 8192, 128, 128, 1) == full

@@ -173,6 +173,16 @@ def test_dense_few_query_rows():
                 decode=False, q_pos=np.array([[1190 + 3 * t for t in range(9)]] * 2, np.int32))
 
 
+def test_dense_decode_workgroup_cap():
+    # the split capped at 8 workgroups: two runs of about 25 tiles per row
+    prev = csk.set_attn_workgroups(8)
+    try:
+        _dense_case(760, B=4, T=1, H=64, D=576, dv=512, N=3000, m=128, S_w=128, W=128, bf16=True, d_rope=64,
+                    decode=True)
+    finally:
+        csk.set_attn_workgroups(prev)
+
+
 @pytest.mark.parametrize("B,N", [(2, 16384), (4, 8192)])
 def test_dense_decode_extra_rows(B, N):
     # rows of 16512 / 8320 candidates (the 1M-context HCA shape): each row
