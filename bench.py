@@ -7,15 +7,15 @@ Default workload: decode at 1M context of one interleaved CSA + HCA layer
 pair, batch 4 (262144 CSA entries, 8192 HCA entries, 64 heads, KV 512+64,
 MXFP4 indexer 64x128, top-k 2048, window 128, sink). One step is one pass of
 the whole hot path for one new token per sequence:
-  1. csa_compress  - the newest CSA entry (8 source tokens, two series)
-  2. csa_compress  - its indexer key, MXFP4 output
-  3. mxfp4_quantize - the indexer queries
-  4. indexer_topk  - scores over all 262144 entries, top-2048 per row
-  5. sparse_attn   - CSA attention over selected entries + window + sink
-  6. hca_compress  - the newest HCA entry (128 source tokens)
-  7. dense_compressed_attn - HCA attention over all 8192 entries + window + sink
-The HCA branch (6, 7) runs on a side stream next to the CSA chain (2, 3, 1,
-4, 5 in that order on the main stream), its attention capped at 32
+  1. csk_compress_batch - one launch of three small calls: csa_compress of
+     the newest CSA entry (8 source tokens, two series), csa_compress of its
+     indexer key (MXFP4 output), mxfp4_quantize of the indexer queries
+  2. indexer_topk  - scores over all 262144 entries, top-2048 per row
+  3. sparse_attn   - CSA attention over selected entries + window + sink
+  4. hca_compress  - the newest HCA entry (128 source tokens)
+  5. dense_compressed_attn - HCA attention over all 8192 entries + window + sink
+The HCA branch (4, 5) runs on a side stream next to the CSA chain (1, 2, 3
+in that order on the main stream), its attention capped at 64
 workgroups (--hca-workgroups) so that the chain keeps most of the CUs;
 --streams 1 runs every call in order on one stream, uncapped. The timed steps are HIP graph
 replays, four steps per graph (--mode eager launches them directly). Four
@@ -52,7 +52,7 @@ class DecodeWorkload:
     """Decode-step state on the GPU for 'decode_1m_pair' (CSA + HCA) or
     'csa_decode_128k' (CSA only), with host copies for the oracle."""
 
-    def __init__(self, name, copies=4, overrides=None, keep_host=True, streams=1, hca_workgroups=32):
+    def __init__(self, name, copies=4, overrides=None, keep_host=True, streams=1, hca_workgroups=64):
         import torch
 
         import compressed_sparse_kv_amd as csk
@@ -130,6 +130,20 @@ class DecodeWorkload:
             ws_d = csk.dense_compressed_attn_workspace_size(B, 1, H, self.D, dv, self.Nh, 128, self.W,
                                                             csk.CSK_BF16)
             self.ws_d = torch.empty(max(ws_d, 1), dtype=torch.uint8, device=dev)
+        # the step's three small per-token calls as one batched launch: the
+        # newest indexer key (MXFP4), the query encode, and the newest CSA
+        # entry N-1 (a-block = source rows 4..7 of the 8-token window,
+        # previous block = rows 0..3)
+        x, N = self.x, self.N
+        for st in self.copies:
+            st["jobs"] = [
+                csk.csa_job(x["src_ia4"], x["src_iza4"], x["src_ib4"], x["src_izb4"], x["ibias_a"],
+                            x["ibias_b"], 4, entry0=N - 1, src_bstride=8, out_dtype=csk.CSK_MXFP4,
+                            out=st["kc_new"], out_scale=st["ks_new"], dst_bstride=N, S=4, B=B),
+                csk.mxfp4_job(x["qI"], self.qc, self.qs),
+                csk.csa_job(x["src_ca4"], x["src_za4"], x["src_cb4"], x["src_zb4"], x["bias_a"], x["bias_b"],
+                            4, d_rope=64, entry0=N - 1, src_bstride=8, out=st["kv_new"], dst_bstride=N,
+                            S=4, B=B)]
         # the side stream of the HCA branch (default priority), and the
         # workgroup cap of its attention when it runs beside the CSA chain
         self.streams = streams
@@ -146,29 +160,21 @@ class DecodeWorkload:
         """One decode step. With one stream (default) the calls run in data
         flow order on torch's current stream. With several streams the HCA
         branch (its newest entry, then the dense attention) runs on a side
-        stream from the start of the step, and the CSA chain (newest indexer
-        key, query encoding, newest KV entry, scores and top-k, sparse
-        attention) stays on the main stream: every cross-stream wait inside
+        stream from the start of the step, and the CSA chain (the batched
+        newest indexer key, query encoding and newest KV entry; scores and
+        top-k; sparse attention) stays on the main stream: every cross-stream wait inside
         the chain costs more on this runtime than running its small kernels
         back to back."""
         torch, csk, x, st = self.torch, self.csk, self.x, self.copies[c % len(self.copies)]
-        B, N = self.B, self.N
         main = torch.cuda.current_stream()
         multi = self.streams > 1
         if self.pair and multi:
             self.side.wait_stream(main)
             with torch.cuda.stream(self.side):
                 self._hca(x, st)
-        # the newest indexer key, MXFP4
-        csk.csa_compress(x["src_ia4"], x["src_iza4"], x["src_ib4"], x["src_izb4"],
-                         x["ibias_a"], x["ibias_b"], 4, entry0=N - 1, src_bstride=8, out_dtype=csk.CSK_MXFP4,
-                         out=st["kc_new"], out_scale=st["ks_new"], dst_bstride=N, S=4, B=B)
-        csk.mxfp4_quantize(x["qI"], self.qc, self.qs)
-        # the newest CSA entry N-1 (a-block = source rows 4..7, previous
-        # block = rows 0..3 of the 8-token window)
-        csk.csa_compress(x["src_ca4"], x["src_za4"], x["src_cb4"], x["src_zb4"],
-                         x["bias_a"], x["bias_b"], 4, d_rope=64, entry0=N - 1, src_bstride=8,
-                         out=st["kv_new"], dst_bstride=N, S=4, B=B)
+        # the newest indexer key (MXFP4), the query encode and the newest
+        # CSA entry: one launch (records formed once per state copy)
+        csk.compress_batch(st["jobs"])
         csk.indexer_topk(self.qc, x["w"], st["kc"], x["q_pos"], x["n_entries"], 4, self.k, q_scale=self.qs,
                          k_scale=st["ks"], idx=self.idx, score=self.score, workspace=self.ws_i)
         csk.sparse_attn(x["q"], x["q_pos"], st["kv_c"], self.idx, st["kv_w"], x["w_pos0"], self.W, x["sink"],
@@ -197,7 +203,7 @@ class DecodeWorkload:
             csk.set_attn_workgroups(prev)
 
     def kernels(self):
-        names = ["csa_compress", "mxfp4_quantize", "indexer_scores_fp4", "topk_filter",
+        names = ["csk_compress_batch", "indexer_scores_fp4", "topk_filter",
                  "topk_select", "attn_bf16_sparse", "attn_merge"]
         if self.pair:
             names += ["hca_compress", "attn_bf16_dense"]
@@ -759,7 +765,7 @@ def main():
     ap.add_argument("--graph-steps", type=int, default=4, help="steps captured per graph")
     ap.add_argument("--streams", type=int, default=2, choices=[1, 2],
                     help="1: every call on one stream; 2: the HCA branch on a side stream")
-    ap.add_argument("--hca-workgroups", type=int, default=32,
+    ap.add_argument("--hca-workgroups", type=int, default=64,
                     help="workgroup cap of the HCA attention beside the CSA chain (0: one per CU)")
     ap.add_argument("--cpu-rows", type=int, default=4, help="decode: sequences the oracle runs")
     ap.add_argument("--cpu-rows-prefill", type=int, default=None,

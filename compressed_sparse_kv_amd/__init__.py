@@ -41,6 +41,7 @@ def lib():
         L.csa_compress.argtypes = [_vp] * 6 + [_i] * 5 + [_i64, _i, _f, _vp, _i, _i, _vp, _vp, _i64, _vp]
         L.hca_compress.argtypes = [_vp] * 3 + [_i] * 5 + [_i64, _i, _f, _vp, _i, _i, _vp, _vp, _i64, _vp]
         L.mxfp4_quantize.argtypes = [_vp, _i, _i64, _i, _vp, _vp, _vp]
+        L.csk_compress_batch.argtypes = [ctypes.POINTER(CompressJob), _i, _vp]
         L.indexer_topk.argtypes = [_vp] * 7 + [_i] * 8 + [_vp, _vp, _vp, _sz, _vp]
         L.indexer_topk_workspace_size.argtypes = [_i] * 7
         L.indexer_topk_workspace_size.restype = _sz
@@ -145,6 +146,66 @@ def mxfp4_quantize(x, codes=None, scales=None):
     rc = lib().mxfp4_quantize(_ptr(x), _dt(x), rows, cols, _ptr(codes), _ptr(scales), _stream())
     _check(rc, "mxfp4_quantize")
     return codes, scales
+
+
+CSK_JOB_CSA, CSK_JOB_MXFP4 = 1, 2
+CSK_MAX_JOBS = 4
+
+
+class CompressJob(ctypes.Structure):
+    """csk_compress_job of csk.h (same fields, same order)."""
+    _fields_ = [("kind", _i), ("ca", _vp), ("za", _vp), ("cb", _vp), ("zb", _vp), ("bias_a", _vp),
+                ("bias_b", _vp), ("B", _i), ("S", _i), ("D", _i), ("m", _i), ("entry0", _i),
+                ("src_bstride", _i64), ("d_rope", _i), ("rope_base", _f), ("entry_pos", _vp),
+                ("in_dtype", _i), ("out_dtype", _i), ("out", _vp), ("out_scale", _vp),
+                ("dst_bstride", _i64), ("x", _vp), ("rows", _i64), ("cols", _i)]
+
+
+class BatchJob:
+    """One job of compress_batch: its C record, the tensors it names (kept
+    alive until the launch) and its outputs."""
+
+    def __init__(self, rec, tensors, result):
+        self.rec, self.tensors, self.result = rec, tensors, result
+
+
+def csa_job(ca, za, cb, zb, bias_a, bias_b, m, d_rope=0, rope_base=10000.0, entry_pos=None,
+            out_dtype=None, entry0=0, src_bstride=0, out=None, out_scale=None, dst_bstride=0,
+            B=None, S=None):
+    """A csa_compress call (same arguments) for compress_batch."""
+    B = ca.shape[0] if B is None else B
+    S = ca.shape[1] if S is None else S
+    D = ca.shape[-1]
+    out_dtype = _dt(ca) if out_dtype is None else out_dtype
+    out, out_scale = _alloc_compress_out(out, out_scale, B, S // m, D, out_dtype, ca.device)
+    rec = CompressJob(kind=CSK_JOB_CSA, ca=_ptr(ca), za=_ptr(za), cb=_ptr(cb), zb=_ptr(zb),
+                      bias_a=_ptr(bias_a), bias_b=_ptr(bias_b), B=B, S=S, D=D, m=m, entry0=entry0,
+                      src_bstride=src_bstride, d_rope=d_rope, rope_base=rope_base,
+                      entry_pos=_ptr(entry_pos), in_dtype=_dt(ca), out_dtype=out_dtype, out=_ptr(out),
+                      out_scale=_ptr(out_scale), dst_bstride=dst_bstride)
+    result = (out, out_scale) if out_dtype == CSK_MXFP4 else out
+    return BatchJob(rec, (ca, za, cb, zb, bias_a, bias_b, entry_pos, out, out_scale), result)
+
+
+def mxfp4_job(x, codes=None, scales=None):
+    """An mxfp4_quantize call (same arguments) for compress_batch."""
+    cols = x.shape[-1]
+    rows = x.numel() // cols
+    if codes is None:
+        codes = torch.empty(x.shape[:-1] + (cols // 2,), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1] + (cols // 32,), dtype=torch.uint8, device=x.device)
+    rec = CompressJob(kind=CSK_JOB_MXFP4, x=_ptr(x), in_dtype=_dt(x), rows=rows, cols=cols, out=_ptr(codes),
+                      out_scale=_ptr(scales))
+    return BatchJob(rec, (x, codes, scales), (codes, scales))
+
+
+def compress_batch(jobs):
+    """Runs csa_job / mxfp4_job records in one launch (csk_compress_batch);
+    returns each job's result as its own call would."""
+    arr = (CompressJob * len(jobs))(*[j.rec for j in jobs])
+    _check(lib().csk_compress_batch(arr, len(jobs), _stream()), "csk_compress_batch")
+    return [j.result for j in jobs]
 
 
 def indexer_topk_workspace_size(B, T, HI, dI, Nmax, k, dtype):

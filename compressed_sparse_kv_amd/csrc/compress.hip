@@ -11,6 +11,8 @@
 // RoPE rotation and the output rounding or MXFP4 encoding in registers. For
 // MXFP4, 16 consecutive lanes own one 1x32 tile; the tile maximum is a
 // 16-lane shuffle reduction.
+#include <cstring>
+
 #include "common.h"
 
 namespace csk {
@@ -135,14 +137,10 @@ __device__ __forceinline__ void store_pair(const CompressArgs& a, int64_t orow, 
   }
 }
 
+// Channel pair p of entry `row` (batch-major) of a one-wave-per-row
+// compression: pool the entry's slots, rotate, round or encode, store.
 template <typename IN, int OUT, bool CSA>
-__global__ __launch_bounds__(64) void compress_kernel(CompressArgs a) {
-  const int half = a.D / 2;
-  // grid: x = channel-pair blocks of one row, y = rows (b, i) in two levels
-  const int p = blockIdx.x * blockDim.x + threadIdx.x;
-  if (p >= half) return;
-  const int64_t row = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
-  if (row >= (int64_t)a.B * a.N) return;
+__device__ __forceinline__ void compress_pair(const CompressArgs& a, int p, int64_t row) {
   const int b = (int)(row / a.N);
   const int i = (int)(row - (int64_t)b * a.N);
   const int ch = 2 * p;
@@ -199,6 +197,17 @@ __global__ __launch_bounds__(64) void compress_kernel(CompressArgs a) {
     v1 = r1;
   }
   store_pair<OUT>(a, (int64_t)b * a.dst_bstride + i, p, v0, v1);
+}
+
+template <typename IN, int OUT, bool CSA>
+__global__ __launch_bounds__(64) void compress_kernel(CompressArgs a) {
+  const int half = a.D / 2;
+  // grid: x = channel-pair blocks of one row, y = rows (b, i) in two levels
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= half) return;
+  const int64_t row = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
+  if (row >= (int64_t)a.B * a.N) return;
+  compress_pair<IN, OUT, CSA>(a, p, row);
 }
 
 // Wide blocks (HCA, m >= 32): the m slots of a channel pair are split over
@@ -260,14 +269,12 @@ __global__ __launch_bounds__(256) void compress_wide_kernel(CompressArgs a) {
   store_pair<OUT>(a, (int64_t)b * a.dst_bstride + i, p, v0, v1);
 }
 
+// MXFP4 encode of channel pair p of row r; 16 consecutive lanes hold one
+// 1x32 tile, so a tile's lanes must be converged here.
 template <typename IN>
-__global__ __launch_bounds__(256) void mxfp4_quant_kernel(const IN* x, int64_t rows, int cols,
-                                                           uint8_t* codes, uint8_t* scales) {
+__device__ __forceinline__ void quant_pair(const IN* x, int64_t r, int cols, int p, uint8_t* codes,
+                                           uint8_t* scales) {
   const int half = cols / 2;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= rows * half) return;
-  const int p = (int)(gid % half);
-  const int64_t r = gid / half;
   float2 v = io<IN>::load2(x + r * cols + 2 * p);
   float amax = fmaxf(fabsf(v.x), fabsf(v.y));
   amax = row16_max(amax);
@@ -282,6 +289,58 @@ __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const IN* x, int64_t r
   }
   codes[r * half + p] = (uint8_t)byte;
   if ((p & 15) == 0) scales[r * (cols / 32) + p / 16] = (uint8_t)sc;
+}
+
+template <typename IN>
+__global__ __launch_bounds__(256) void mxfp4_quant_kernel(const IN* x, int64_t rows, int cols,
+                                                           uint8_t* codes, uint8_t* scales) {
+  const int half = cols / 2;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= rows * half) return;
+  quant_pair<IN>(x, gid / half, cols, (int)(gid % half), codes, scales);
+}
+
+// Several independent small compressions and MXFP4 encodes in one launch
+// (a decode step issues a few, each too small to fill the chip, and each
+// launch boundary costs more than its work). The grid is one dimension:
+// job z owns blocks [first[z], first[z+1]), one block per 64 channel pairs
+// of one of its rows (entry rows of a compression, rows of an encode), so
+// no block is idle. Every job runs the same per-pair code as its own
+// kernel, so results are identical.
+struct BatchJob {
+  CompressArgs a;  // compression job; an encode job uses out, out_scale, D
+  const void* x;   // encode job input
+  int64_t rows;    // rows of the job (compression: B * N)
+  int kind, in_bf16, out_kind, xblocks;
+};
+struct BatchArgs {
+  BatchJob j[CSK_MAX_JOBS];
+  int first[CSK_MAX_JOBS + 1];
+  int n;
+};
+
+__global__ __launch_bounds__(64) void compress_batch_kernel(BatchArgs args) {
+  const int blk = blockIdx.x;
+  int z = 0;
+  while (z + 1 < args.n && blk >= args.first[z + 1]) ++z;
+  const BatchJob& j = args.j[z];
+  const int local = blk - args.first[z];
+  const int row = local / j.xblocks;
+  const int p = (local - row * j.xblocks) * 64 + threadIdx.x;
+  if (p >= j.a.D / 2) return;
+  if (j.kind == CSK_JOB_MXFP4) {
+    uint8_t* codes = reinterpret_cast<uint8_t*>(j.a.out);
+    if (j.in_bf16) quant_pair<uint16_t>(reinterpret_cast<const uint16_t*>(j.x), row, j.a.D, p, codes, j.a.out_scale);
+    else quant_pair<float>(reinterpret_cast<const float*>(j.x), row, j.a.D, p, codes, j.a.out_scale);
+  } else if (j.in_bf16) {
+    if (j.out_kind == OUT_BF16) compress_pair<uint16_t, OUT_BF16, true>(j.a, p, row);
+    else if (j.out_kind == OUT_MXFP4) compress_pair<uint16_t, OUT_MXFP4, true>(j.a, p, row);
+    else compress_pair<uint16_t, OUT_F32, true>(j.a, p, row);
+  } else {
+    if (j.out_kind == OUT_BF16) compress_pair<float, OUT_BF16, true>(j.a, p, row);
+    else if (j.out_kind == OUT_MXFP4) compress_pair<float, OUT_MXFP4, true>(j.a, p, row);
+    else compress_pair<float, OUT_F32, true>(j.a, p, row);
+  }
 }
 
 template <typename IN, bool CSA>
@@ -308,14 +367,15 @@ static int launch_compress_out(const char* name, const CompressArgs& a, int out_
   }
 }
 
-static int compress_common(const char* fn, bool csa, const void* ca, const void* za,
-                           const void* cb, const void* zb, const float* bias_a,
-                           const float* bias_b, int B, int S, int D, int m, int entry0,
-                           int64_t src_bstride, int d_rope, float rope_base,
-                           const int32_t* entry_pos, int in_dtype, int out_dtype, void* out,
-                           uint8_t* out_scale, int64_t dst_bstride, void* stream) {
-  clear_error();
-  std::string f(fn);
+// Checks the arguments of one compression call and fills its kernel
+// arguments; *empty is set when the call reads and writes nothing.
+static int prepare_compress(const std::string& f, bool csa, const void* ca, const void* za,
+                            const void* cb, const void* zb, const float* bias_a,
+                            const float* bias_b, int B, int S, int D, int m, int entry0,
+                            int64_t src_bstride, int d_rope, float rope_base,
+                            const int32_t* entry_pos, int in_dtype, int out_dtype, void* out,
+                            uint8_t* out_scale, int64_t dst_bstride, CompressArgs* ap,
+                            bool* empty_p) {
   if (B < 0 || S < 0 || D <= 0 || (D & 1) || m <= 0 || entry0 < 0)
     return fail(CSK_EINVAL, f + ": need B >= 0, S >= 0, even D > 0, m > 0, entry0 >= 0");
   const bool empty = B == 0 || S / m == 0;  // nothing is read or written
@@ -336,8 +396,9 @@ static int compress_common(const char* fn, bool csa, const void* ca, const void*
     return fail(CSK_EINVAL, f + ": src_bstride must be 0 or >= S");
   if (dst_bstride < 0 || (dst_bstride != 0 && dst_bstride < N))
     return fail(CSK_EINVAL, f + ": dst_bstride must be 0 or >= S/m");
-  if (B == 0 || N == 0) return CSK_OK;
-  CompressArgs a;
+  *empty_p = B == 0 || N == 0;
+  if (*empty_p) return CSK_OK;
+  CompressArgs& a = *ap;
   a.ca = ca; a.za = za; a.cb = cb; a.zb = zb;
   a.bias_a = bias_a; a.bias_b = bias_b;
   a.B = B; a.N = N; a.D = D; a.m = m; a.entry0 = entry0; a.d_rope = d_rope;
@@ -346,6 +407,22 @@ static int compress_common(const char* fn, bool csa, const void* ca, const void*
   fill_rope_table(&a.rope, d_rope, (double)rope_base);
   a.entry_pos = entry_pos;
   a.out = out; a.out_scale = out_scale;
+  return CSK_OK;
+}
+
+static int compress_common(const char* fn, bool csa, const void* ca, const void* za,
+                           const void* cb, const void* zb, const float* bias_a,
+                           const float* bias_b, int B, int S, int D, int m, int entry0,
+                           int64_t src_bstride, int d_rope, float rope_base,
+                           const int32_t* entry_pos, int in_dtype, int out_dtype, void* out,
+                           uint8_t* out_scale, int64_t dst_bstride, void* stream) {
+  clear_error();
+  CompressArgs a;
+  bool empty = false;
+  const int rc = prepare_compress(fn, csa, ca, za, cb, zb, bias_a, bias_b, B, S, D, m, entry0,
+                                  src_bstride, d_rope, rope_base, entry_pos, in_dtype, out_dtype,
+                                  out, out_scale, dst_bstride, &a, &empty);
+  if (rc != CSK_OK || empty) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const char* name = csa ? "csa_compress" : "hca_compress";
   if (in_dtype == CSK_F32)
@@ -353,6 +430,73 @@ static int compress_common(const char* fn, bool csa, const void* ca, const void*
                : launch_compress_out<float, false>(name, a, out_dtype, s);
   return csa ? launch_compress_out<uint16_t, true>(name, a, out_dtype, s)
              : launch_compress_out<uint16_t, false>(name, a, out_dtype, s);
+}
+
+static int check_quantize(const std::string& f, const void* x, int in_dtype, int64_t rows,
+                          int cols, const uint8_t* codes, const uint8_t* scales) {
+  if (!x || !codes || !scales) return fail(CSK_EINVAL, f + ": null pointer");
+  if (rows < 0 || cols <= 0 || cols % 32)
+    return fail(CSK_EINVAL, f + ": need rows >= 0 and cols % 32 == 0");
+  if (in_dtype != CSK_F32 && in_dtype != CSK_BF16)
+    return fail(CSK_EUNSUPPORTED, f + ": in_dtype must be CSK_F32 or CSK_BF16");
+  return CSK_OK;
+}
+
+static int compress_batch(const csk_compress_job* jobs, int n_jobs, void* stream) {
+  clear_error();
+  if (!jobs || n_jobs < 1 || n_jobs > CSK_MAX_JOBS)
+    return fail(CSK_EINVAL, "csk_compress_batch: need 1 <= n_jobs <= CSK_MAX_JOBS and a job array");
+  BatchArgs args;
+  memset(&args, 0, sizeof(args));
+  int nz = 0;
+  int64_t total = 0;
+  for (int q = 0; q < n_jobs; ++q) {
+    const csk_compress_job& j = jobs[q];
+    const std::string f = "csk_compress_batch: job " + std::to_string(q);
+    BatchJob& bj = args.j[nz];
+    int64_t rows;
+    if (j.kind == CSK_JOB_CSA) {
+      bool empty = false;
+      const int rc = prepare_compress(f + " (csa_compress)", true, j.ca, j.za, j.cb, j.zb, j.bias_a,
+                                      j.bias_b, j.B, j.S, j.D, j.m, j.entry0, j.src_bstride,
+                                      j.d_rope, j.rope_base, j.entry_pos, j.in_dtype, j.out_dtype,
+                                      j.out, j.out_scale, j.dst_bstride, &bj.a, &empty);
+      if (rc != CSK_OK) return rc;
+      if (j.m > 8) return fail(CSK_EUNSUPPORTED, f + ": batched compression needs m <= 8");
+      if (empty) continue;
+      rows = (int64_t)bj.a.B * bj.a.N;
+      bj.in_bf16 = j.in_dtype == CSK_BF16;
+      bj.out_kind = j.out_dtype == CSK_F32 ? OUT_F32 : j.out_dtype == CSK_BF16 ? OUT_BF16 : OUT_MXFP4;
+    } else if (j.kind == CSK_JOB_MXFP4) {
+      const int rc = check_quantize(f + " (mxfp4_quantize)", j.x, j.in_dtype, j.rows, j.cols,
+                                    reinterpret_cast<const uint8_t*>(j.out), j.out_scale);
+      if (rc != CSK_OK) return rc;
+      if (j.rows == 0) continue;
+      rows = j.rows;
+      bj.x = j.x;
+      bj.a.out = j.out;
+      bj.a.out_scale = j.out_scale;
+      bj.a.D = j.cols;
+      bj.in_bf16 = j.in_dtype == CSK_BF16;
+    } else {
+      return fail(CSK_EINVAL, f + ": kind must be CSK_JOB_CSA or CSK_JOB_MXFP4");
+    }
+    if (rows > 65535) return fail(CSK_EUNSUPPORTED, f + ": at most 65535 rows per batched job");
+    bj.kind = j.kind;
+    bj.rows = rows;
+    bj.xblocks = (int)ceil_div(bj.a.D / 2, 64);
+    args.first[nz] = (int)total;
+    total += rows * bj.xblocks;
+    if (total * 64 > (int64_t)UINT32_MAX)
+      return fail(CSK_EUNSUPPORTED, "csk_compress_batch: too many channel pairs in one batch");
+    ++nz;
+  }
+  if (nz == 0) return CSK_OK;
+  args.first[nz] = (int)total;
+  args.n = nz;
+  dim3 grid((unsigned)total), block(64);
+  return launch("csk_compress_batch", compress_batch_kernel, grid, block, 0,
+                reinterpret_cast<hipStream_t>(stream), args);
 }
 
 }  // namespace csk
@@ -381,11 +525,8 @@ int hca_compress(const void* c, const void* z, const float* bias, int B, int S, 
 int mxfp4_quantize(const void* x, int in_dtype, int64_t rows, int cols, uint8_t* codes,
                    uint8_t* scales, void* stream) {
   csk::clear_error();
-  if (!x || !codes || !scales) return csk::fail(CSK_EINVAL, "mxfp4_quantize: null pointer");
-  if (rows < 0 || cols <= 0 || cols % 32)
-    return csk::fail(CSK_EINVAL, "mxfp4_quantize: need rows >= 0 and cols % 32 == 0");
-  if (in_dtype != CSK_F32 && in_dtype != CSK_BF16)
-    return csk::fail(CSK_EUNSUPPORTED, "mxfp4_quantize: in_dtype must be CSK_F32 or CSK_BF16");
+  const int rc = csk::check_quantize("mxfp4_quantize", x, in_dtype, rows, cols, codes, scales);
+  if (rc != CSK_OK) return rc;
   if (rows == 0) return CSK_OK;
   const int64_t total = rows * (cols / 2);
   dim3 grid((unsigned)csk::ceil_div(total, 256)), block(256);
@@ -395,6 +536,10 @@ int mxfp4_quantize(const void* x, int in_dtype, int64_t rows, int cols, uint8_t*
                        reinterpret_cast<const float*>(x), rows, cols, codes, scales);
   return csk::launch("mxfp4_quantize", csk::mxfp4_quant_kernel<uint16_t>, grid, block, 0, s,
                      reinterpret_cast<const uint16_t*>(x), rows, cols, codes, scales);
+}
+
+int csk_compress_batch(const csk_compress_job* jobs, int n_jobs, void* stream) {
+  return csk::compress_batch(jobs, n_jobs, stream);
 }
 
 }  // extern "C"

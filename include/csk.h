@@ -124,6 +124,57 @@ int mxfp4_quantize(const void* x, int in_dtype, int64_t rows, int cols, uint8_t*
                    uint8_t* scales, void* stream);
 
 /*
+ * csk_compress_batch - several csa_compress and mxfp4_quantize calls in
+ * one launch ([P1] «CSA…», step 1, and «FP4 с…»: the per-token work that
+ * precedes the indexer and attention at decode - the newest KV entry, its
+ * indexer key and the query encode - is three launches too small to fill
+ * the chip; batched, they share one kernel boundary).
+ *
+ * Each job computes exactly what its own call computes, bit for bit. The
+ * jobs run concurrently: no job may read what another writes.
+ *   jobs[q].kind == CSK_JOB_CSA  : fields ca .. dst_bstride are the
+ *       csa_compress arguments of the same names (S is the source rows),
+ *       with m <= 8 and B*(S/m) <= 65535 entries.
+ *   jobs[q].kind == CSK_JOB_MXFP4: fields x, in_dtype, rows (<= 65535) and
+ *       cols are the mxfp4_quantize arguments; codes go to out and scales
+ *       to out_scale.
+ *   Unused fields are ignored. The job array is host memory, read during
+ *   the call; device buffers stay owned by the caller.
+ *   n_jobs : 1 .. CSK_MAX_JOBS.
+ *   stream : hipStream_t (NULL = default stream); asynchronous.
+ * Errors: CSK_EINVAL for a bad n_jobs, an unknown kind or any argument the
+ * job's own call rejects with CSK_EINVAL (the message names the job);
+ * CSK_EUNSUPPORTED for m > 8, more rows than stated or what the own call
+ * rejects with CSK_EUNSUPPORTED. Nothing is launched unless every job is
+ * valid; jobs that produce nothing are skipped.
+ */
+#define CSK_MAX_JOBS 4
+#define CSK_JOB_CSA 1
+#define CSK_JOB_MXFP4 2
+typedef struct csk_compress_job {
+  int kind;
+  const void* ca;
+  const void* za;
+  const void* cb;
+  const void* zb;
+  const float* bias_a;
+  const float* bias_b;
+  int B, S, D, m, entry0;
+  int64_t src_bstride;
+  int d_rope;
+  float rope_base;
+  const int32_t* entry_pos;
+  int in_dtype, out_dtype;
+  void* out;
+  uint8_t* out_scale;
+  int64_t dst_bstride;
+  const void* x;
+  int64_t rows;
+  int cols;
+} csk_compress_job;
+int csk_compress_batch(const csk_compress_job* jobs, int n_jobs, void* stream);
+
+/*
  * indexer_topk - lightning indexer and top-k selection ([P1] «CSA…», step
  * 2; [P3]: FP4 lightning indexer with a ReLU-scored multi-head dot product).
  *

@@ -70,3 +70,48 @@ def test_attn_workgroup_cap(lib):
     assert lib.csk_set_attn_workgroups(-3) == -1 and b"negative" in lib.csk_last_error()
     assert lib.csk_set_attn_workgroups(0) == 64
     assert lib.dense_compressed_attn_workspace_size(4, 1, 64, 576, 512, 8192, 128, 128, 1) == full
+
+
+def test_compress_job_layout(tmp_path):
+    # the binding's record must have the C struct's size and field offsets
+    import subprocess
+    from compressed_sparse_kv_amd import CompressJob
+    fields = [f for f, _ in CompressJob._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "csk.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(csk_compress_job));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(csk_compress_job, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(CompressJob)
+    assert got[1:] == [getattr(CompressJob, f).offset for f in fields]
+
+
+def test_compress_batch_errors_without_device(lib):
+    from compressed_sparse_kv_amd import CompressJob, CSK_JOB_CSA, CSK_JOB_MXFP4
+    lib.csk_last_error.restype = ctypes.c_char_p
+    lib.csk_compress_batch.argtypes = [ctypes.POINTER(CompressJob), ctypes.c_int, ctypes.c_void_p]
+    fake = 16
+
+    def run(*jobs, n=None):
+        arr = (CompressJob * max(len(jobs), 1))(*jobs)
+        return lib.csk_compress_batch(arr, len(jobs) if n is None else n, None)
+
+    quant = CompressJob(kind=CSK_JOB_MXFP4, x=fake, in_dtype=0, rows=4, cols=64, out=fake, out_scale=fake)
+    assert run(quant, n=0) == -1 and b"n_jobs" in lib.csk_last_error()
+    assert run(quant, n=5) == -1
+    assert run(CompressJob(kind=7)) == -1 and b"kind" in lib.csk_last_error()
+    # a bad second job is reported by index and nothing runs
+    bad_cols = CompressJob(kind=CSK_JOB_MXFP4, x=fake, in_dtype=0, rows=4, cols=48, out=fake, out_scale=fake)
+    assert run(quant, bad_cols) == -1 and b"job 1" in lib.csk_last_error()
+    csa = dict(kind=CSK_JOB_CSA, ca=fake, za=fake, cb=fake, zb=fake, bias_a=fake, bias_b=fake, B=1, S=64,
+               D=64, m=4, in_dtype=0, out_dtype=1, out=fake)
+    assert run(CompressJob(**dict(csa, m=16))) == -2 and b"m <= 8" in lib.csk_last_error()
+    assert run(CompressJob(**dict(csa, S=4 * 70000))) == -2 and b"65535" in lib.csk_last_error()
+    assert run(CompressJob(**dict(csa, zb=0))) == -1 and b"null" in lib.csk_last_error()
+    # jobs that produce nothing launch nothing (no device needed)
+    assert run(CompressJob(**dict(csa, S=3)), CompressJob(kind=CSK_JOB_MXFP4, x=fake, rows=0, cols=32,
+                                                          out=fake, out_scale=fake)) == 0

@@ -130,3 +130,86 @@ def test_ragged_and_empty():
     assert out.shape == (1, 0, 64)
     with pytest.raises(csk.CskError):
         csk.csa_compress(*[dev(x) for x in (ca, za, cb, zb, ba, bb)], 4, d_rope=3)
+
+
+def _batch_case(g, B, bf16_in):
+    """Decode-step jobs (the newest entry of an 8-token window written into
+    row N-1 of a cache, its MXFP4 indexer key, the MXFP4 query encode) and a
+    whole-sequence compression with a ragged tail and the generic m path."""
+    N = 10
+    cvt = (lambda a: synth.to_bf16(a)) if bf16_in else (lambda a: a)
+    kv_src = [dev(cvt(synth.normal(g, (B, 8, 576)))) for _ in range(4)]
+    ik_src = [dev(cvt(synth.normal(g, (B, 8, 128)))) for _ in range(4)]
+    seq = [dev(cvt(synth.normal(g, (B, 50, 64)))) for _ in range(4)]
+    bias = {k: dev(synth.normal(g, (m, dd), 0.1)) for k, m, dd in
+            (("kv_a", 4, 576), ("kv_b", 4, 576), ("ik_a", 4, 128), ("ik_b", 4, 128), ("s_a", 3, 64),
+             ("s_b", 3, 64))}
+    q = dev(cvt(synth.normal(g, (B, 1, 64, 128)) * np.float32(4.0)))
+    pos = dev(np.arange(B, dtype=np.int32).reshape(B, 1) * 7 + 1000)
+
+    def jobs(outs):
+        kvc, kc, ks, qc, qs, so = outs
+        return [
+            ("csa", dict(args=[x[:, 4:] for x in ik_src] + [bias["ik_a"], bias["ik_b"], 4],
+                         kw=dict(entry0=N - 1, src_bstride=8, out_dtype=csk.CSK_MXFP4, out=kc[:, N - 1:],
+                                 out_scale=ks[:, N - 1:], dst_bstride=N, S=4, B=B))),
+            ("mx", dict(args=[q], kw=dict(codes=qc, scales=qs))),
+            ("csa", dict(args=[x[:, 4:] for x in kv_src] + [bias["kv_a"], bias["kv_b"], 4],
+                         kw=dict(d_rope=64, entry0=N - 1, src_bstride=8, entry_pos=pos, out=kvc[:, N - 1:],
+                                 dst_bstride=N, S=4, B=B, out_dtype=csk.CSK_BF16))),
+            ("csa", dict(args=seq + [bias["s_a"], bias["s_b"], 3],
+                         kw=dict(d_rope=32, out_dtype=csk.CSK_F32, out=so))),
+        ]
+
+    def outs():
+        return [torch.zeros((B, N, 576), dtype=torch.bfloat16, device="cuda"),
+                torch.zeros((B, N, 64), dtype=torch.uint8, device="cuda"),
+                torch.zeros((B, N, 4), dtype=torch.uint8, device="cuda"),
+                torch.zeros((B, 1, 64, 64), dtype=torch.uint8, device="cuda"),
+                torch.zeros((B, 1, 64, 4), dtype=torch.uint8, device="cuda"),
+                torch.zeros((B, 16, 64), dtype=torch.float32, device="cuda")]
+
+    return jobs, outs, q, seq, bias
+
+
+def _same_bytes(a, b):
+    return torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+@pytest.mark.parametrize("bf16_in", [False, True])
+def test_compress_batch_matches_own_calls(bf16_in):
+    # each batched job writes exactly the bytes of its own call (whole
+    # buffers are compared, so stray writes would show), twice in a row with
+    # the second batch smaller, and in job subsets of every size
+    for B, seed in ((4, 1), (1, 2)):
+        g = synth.rng(700 + 10 * seed + bf16_in)
+        jobs, outs, q, seq, bias = _batch_case(g, B, bf16_in)
+        own, bat = outs(), outs()
+        for kind, j in jobs(own):
+            if kind == "csa":
+                csk.csa_compress(*j["args"], **j["kw"])
+            else:
+                csk.mxfp4_quantize(*j["args"], **j["kw"])
+        recs = [csk.csa_job(*j["args"], **j["kw"]) if kind == "csa" else csk.mxfp4_job(*j["args"], **j["kw"])
+                for kind, j in jobs(bat)]
+        csk.compress_batch(recs)
+        torch.cuda.synchronize()
+        for a, b in zip(own, bat):
+            assert _same_bytes(a, b)
+        # the batch against the oracle directly: the encode bit-exact, the
+        # fp32 compression within the fp32 bar
+        rc, rs = oracle.mxfp4_encode(host(q))  # bf16 inputs come back as their fp32 values
+        assert np.array_equal(host(bat[3]), rc) and np.array_equal(host(bat[4]), rs)
+        ref = oracle.csa_compress(*[host(x) for x in seq], host(bias["s_a"]), host(bias["s_b"]), 3, d_rope=32)
+        check_f32(host(bat[5]), ref, 1e-5, "batched csa fp32 out")
+    # one job alone, and a batch whose every job is empty
+    jobs, outs, *_ = _batch_case(synth.rng(799), 2, bf16_in)
+    own, bat = outs(), outs()
+    kind, j = jobs(own)[2]
+    csk.csa_compress(*j["args"], **j["kw"])
+    kind, j = jobs(bat)[2]
+    csk.compress_batch([csk.csa_job(*j["args"], **j["kw"])])
+    # fewer source rows than the ratio: no entry, nothing launched or written
+    csk.compress_batch([csk.csa_job(*j["args"], **dict(j["kw"], S=3))])
+    torch.cuda.synchronize()
+    assert _same_bytes(own[0], bat[0])
