@@ -18,7 +18,10 @@ The HCA branch (4, 5) runs on a side stream next to the CSA chain (1, 2, 3
 in that order on the main stream), its attention capped at 64
 workgroups (--hca-workgroups) so that the chain keeps most of the CUs;
 --streams 1 runs every call in order on one stream, uncapped. The timed steps are HIP graph
-replays, four steps per graph (--mode eager launches them directly). Four
+replays, up to 20 steps per graph (--graph-steps): a decode forward captures
+all its layers in one graph, and 20 layer pairs are fewer than a deep
+model's; each graph launch costs about 25 us here, paid once per graph
+(--mode eager launches every call directly). Four
 copies of the layer-pair state rotate between steps (as successive layers
 would), so a step never finds its 121 MB working set in the 256 MB Infinity
 Cache from the previous step.
@@ -52,7 +55,8 @@ class DecodeWorkload:
     """Decode-step state on the GPU for 'decode_1m_pair' (CSA + HCA) or
     'csa_decode_128k' (CSA only), with host copies for the oracle."""
 
-    def __init__(self, name, copies=4, overrides=None, keep_host=True, streams=1, hca_workgroups=64):
+    def __init__(self, name, copies=4, overrides=None, keep_host=True, streams=1, hca_workgroups=64,
+                 csa_workgroups=0):
         import torch
 
         import compressed_sparse_kv_amd as csk
@@ -148,6 +152,7 @@ class DecodeWorkload:
         # workgroup cap of its attention when it runs beside the CSA chain
         self.streams = streams
         self.hca_workgroups = hca_workgroups
+        self.csa_workgroups = csa_workgroups
         self.side = torch.cuda.Stream()
         torch.cuda.synchronize()
         if not keep_host:
@@ -177,9 +182,13 @@ class DecodeWorkload:
         csk.compress_batch(st["jobs"])
         csk.indexer_topk(self.qc, x["w"], st["kc"], x["q_pos"], x["n_entries"], 4, self.k, q_scale=self.qs,
                          k_scale=st["ks"], idx=self.idx, score=self.score, workspace=self.ws_i)
-        csk.sparse_attn(x["q"], x["q_pos"], st["kv_c"], self.idx, st["kv_w"], x["w_pos0"], self.W, x["sink"],
-                        self.dv, 64, self.scale, out=self.out, lse=self.lse,
-                        workspace=self.ws_s)
+        prev = csk.set_attn_workgroups(self.csa_workgroups)
+        try:
+            csk.sparse_attn(x["q"], x["q_pos"], st["kv_c"], self.idx, st["kv_w"], x["w_pos0"], self.W,
+                            x["sink"], self.dv, 64, self.scale, out=self.out, lse=self.lse,
+                            workspace=self.ws_s)
+        finally:
+            csk.set_attn_workgroups(prev)
         if self.pair and not multi:
             self._hca(x, st)
         if self.pair and multi:
@@ -486,7 +495,7 @@ def run(args):
     import compressed_sparse_kv_amd as csk
 
     wl = DecodeWorkload(args.workload, copies=args.copies, streams=args.streams,
-                        hca_workgroups=args.hca_workgroups)
+                        hca_workgroups=args.hca_workgroups, csa_workgroups=args.csa_workgroups)
     K, Wm = args.steps, args.warmup
     # eager warm-up (first calls set kernel attributes outside any capture)
     for i in range(max(Wm, 1)):
@@ -762,11 +771,13 @@ def main():
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--mode", default="graph", choices=["eager", "graph"],
                     help="timed steps as HIP graph replays (default) or as eager launches")
-    ap.add_argument("--graph-steps", type=int, default=4, help="steps captured per graph")
+    ap.add_argument("--graph-steps", type=int, default=20, help="steps captured per graph")
     ap.add_argument("--streams", type=int, default=2, choices=[1, 2],
                     help="1: every call on one stream; 2: the HCA branch on a side stream")
     ap.add_argument("--hca-workgroups", type=int, default=64,
                     help="workgroup cap of the HCA attention beside the CSA chain (0: one per CU)")
+    ap.add_argument("--csa-workgroups", type=int, default=0,
+                    help="workgroup cap of the CSA sparse attention (0: one per CU)")
     ap.add_argument("--cpu-rows", type=int, default=4, help="decode: sequences the oracle runs")
     ap.add_argument("--cpu-rows-prefill", type=int, default=None,
                     help="prefill: query rows the oracle runs (default 384 for CSA, every row for HCA)")

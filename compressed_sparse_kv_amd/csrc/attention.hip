@@ -1715,6 +1715,101 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
   if (a.lse && tid == 0) a.lse[(int64_t)r * a.H + h] = fin[1];
 }
 
+// Merge of bf16 partials from at most 64 chunks with dv <= 512, dv % 8 == 0
+// (split rows of the streamed-row kernel at decode): one workgroup of eight
+// waves per (row, head); wave g sums chunks g, g + 8, ... over eight value
+// dims per lane. Every partial and (m, l) load is issued before any of them
+// is needed, so the pass costs one memory round trip instead of one per
+// dependent step; each wave forms all chunk weights itself (one chunk per
+// lane, no barrier), and the eight waves' sums meet once in LDS.
+constexpr int MERGE8_WAVES = 8;
+
+template <typename T, int PER>
+__global__ __launch_bounds__(64 * MERGE8_WAVES) void attn_merge8_kernel(AttnArgs a) {
+  __shared__ float4 red[MERGE8_WAVES - 1][2][64];
+  const int r = blockIdx.x, h = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nch = a.nch;
+  const int64_t ostride = (int64_t)a.H * a.dv;
+  const uint16_t* pb = reinterpret_cast<const uint16_t*>(a.part_o) + ((int64_t)r * nch * a.H + h) * a.dv;
+  const int d = 8 * lane;
+  const bool dok = d < a.dv;
+  const int dd = dok ? d : 0;
+  uint4 v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int c = min(g + MERGE8_WAVES * u, nch - 1);  // unconditional: the loads issue together
+    v[u] = *reinterpret_cast<const uint4*>(pb + c * ostride + dd);
+  }
+  const float* ml = a.part_ml + ((int64_t)r * nch * a.H + h) * 2;
+  const float2 mlc = *reinterpret_cast<const float2*>(ml + (int64_t)min(lane, nch - 1) * a.H * 2);
+  const float mc = lane < nch ? mlc.x : -INFINITY;
+  const float m = wave_max(mc);
+  const float w = mc == -INFINITY ? 0.f : exp2f(mc - m);
+  const float l = wave_sum(lane < nch ? w * mlc.y : 0.f);
+  float M, inv_z, lse;
+  finish_row(m, l, a.sink, h, &M, &inv_z, &lse);
+  const float f = (m == -INFINITY) ? 0.f : exp2f(m - M) * inv_z;
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = 0.f;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int c = g + MERGE8_WAVES * u;  // < 64
+    const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c));
+    if (c < nch) {
+      const uint32_t q[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o[2 * i] += bf16_bits_to_f32(q[i] & 0xffffu) * wc;
+        o[2 * i + 1] += bf16_bits_to_f32(q[i] >> 16) * wc;
+      }
+    }
+  }
+  if (g > 0) {
+    red[g - 1][0][lane] = make_float4(o[0], o[1], o[2], o[3]);
+    red[g - 1][1][lane] = make_float4(o[4], o[5], o[6], o[7]);
+  }
+  __syncthreads();
+  if (g != 0) return;
+#pragma unroll
+  for (int j = 0; j < MERGE8_WAVES - 1; ++j) {
+    const float4 x = red[j][0][lane], y = red[j][1][lane];
+    o[0] += x.x; o[1] += x.y; o[2] += x.z; o[3] += x.w;
+    o[4] += y.x; o[5] += y.y; o[6] += y.z; o[7] += y.w;
+  }
+  if (dok) {
+    const int64_t orow = ((int64_t)r * a.H + h) * a.dv + d;
+    if (sizeof(T) == 4) {
+      float4* op = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + orow);
+      op[0] = make_float4(o[0] * f, o[1] * f, o[2] * f, o[3] * f);
+      op[1] = make_float4(o[4] * f, o[5] * f, o[6] * f, o[7] * f);
+    } else {
+      uint32_t q[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = f32_to_bf16_bits(o[2 * i] * f) | (f32_to_bf16_bits(o[2 * i + 1] * f) << 16);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + orow) = make_uint4(q[0], q[1], q[2], q[3]);
+    }
+  }
+  if (a.lse && lane == 0) a.lse[(int64_t)r * a.H + h] = lse;
+}
+
+template <typename T>
+static int launch_merge8(const AttnArgs& a, unsigned R, int H, hipStream_t s) {
+  dim3 grid(R, H), block(64 * MERGE8_WAVES);
+  switch ((a.nch + MERGE8_WAVES - 1) / MERGE8_WAVES) {
+    case 1: return launch("attn_merge", attn_merge8_kernel<T, 1>, grid, block, 0, s, a);
+    case 2: return launch("attn_merge", attn_merge8_kernel<T, 2>, grid, block, 0, s, a);
+    case 3: return launch("attn_merge", attn_merge8_kernel<T, 3>, grid, block, 0, s, a);
+    case 4: return launch("attn_merge", attn_merge8_kernel<T, 4>, grid, block, 0, s, a);
+    case 5: return launch("attn_merge", attn_merge8_kernel<T, 5>, grid, block, 0, s, a);
+    case 6: return launch("attn_merge", attn_merge8_kernel<T, 6>, grid, block, 0, s, a);
+    case 7: return launch("attn_merge", attn_merge8_kernel<T, 7>, grid, block, 0, s, a);
+    default: return launch("attn_merge", attn_merge8_kernel<T, 8>, grid, block, 0, s, a);
+  }
+}
+
 // ------------------------------------------------------------ host side
 struct AttnPlan {
   int chunk, nch, tiles, extra;
@@ -1922,6 +2017,8 @@ const int NW = H / 16;
                           : launch("attn_valu", attn_valu_kernel<uint16_t>, grid, block, lds, s, a);
   }
   if (rc != CSK_OK || p.nch == 1) return rc;
+  if (a.part_bf16 && p.nch <= 8 * MERGE8_WAVES && dv % 8 == 0 && dv <= 512)
+    return dtype == CSK_F32 ? launch_merge8<float>(a, R, H, s) : launch_merge8<uint16_t>(a, R, H, s);
   dim3 mg(R, H), mb(128);
   return dtype == CSK_F32 ? launch("attn_merge", attn_merge_kernel<float>, mg, mb, 0, s, a)
                           : launch("attn_merge", attn_merge_kernel<uint16_t>, mg, mb, 0, s, a);
