@@ -64,14 +64,18 @@ struct IdxArgs {
   int iters;           // 64-key groups per wave (MFMA path; also a template value)
 };
 
+// (r is the workgroup's row: uniform.) Both loads are issued before either
+// value is used (the empty asm takes them as scalar operands), so they
+// cost one memory round trip; the arithmetic is branch-free 32-bit.
 __device__ __forceinline__ int visible_count(const IdxArgs& a, int r) {
-  const int b = r / a.T;
-  const int64_t p = a.q_pos[r];
-  if (p < 0) return 0;
-  int64_t nv = (p + 1) / a.m;
-  nv = nv < a.n_entries[b] ? nv : a.n_entries[b];
-  nv = nv < a.Nmax ? nv : a.Nmax;
-  return nv < 0 ? 0 : (int)nv;
+  const unsigned b = (unsigned)r / (unsigned)a.T;
+  const int p = a.q_pos[r];
+  const int ne = a.n_entries[b];
+  asm volatile("" ::"s"(p), "s"(ne));
+  unsigned nv = p < 0 ? 0u : ((unsigned)p + 1u) / (unsigned)a.m;  // p + 1 <= 2^31 fits
+  nv = min(nv, ne < 0 ? 0u : (unsigned)ne);
+  nv = min(nv, (unsigned)a.Nmax);
+  return (int)nv;
 }
 
 // order-preserving key: larger score -> larger key; -0 is folded onto +0
@@ -676,17 +680,36 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkArgs a) {
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int k = a.k;
-  const int nv = visible_count(a.ia, r);
   int32_t* oidx = a.idx + (int64_t)r * k;
   float* osc = a.out_score ? a.out_score + (int64_t)r * k : nullptr;
 
+  // the first 64 candidates of each of a wave's first PRE slices, and the
+  // slice counts, are loaded before the visible count is known (addresses
+  // clamped to the allocated row); validity is decided once it is
+  constexpr int NW = TOPK_THREADS / 64, PRE = 8;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int64_t rbase = (int64_t)r * a.ia.Nmax;
+  float psv[PRE];
+  int piv[PRE];
+  int craw = 0;
+  if (FILTERED) {
+#pragma unroll
+    for (int u = 0; u < PRE; ++u) {
+      const int fc = min(wv + u * NW, a.n_slices - 1);
+      const int64_t off = rbase + min((int64_t)fc * SLICE + lane, (int64_t)a.ia.Nmax - 1);
+      psv[u] = a.cand_score[off];
+      piv[u] = a.cand_idx[off];
+    }
+    craw = a.cand_cnt[(int64_t)r * a.n_slices + min(tid, a.n_slices - 1)];
+  }
+  const int nv = visible_count(a.ia, r);
   int n;
   const int ns = (nv + SLICE - 1) / SLICE;
   if (!FILTERED) {
     n = nv;
   } else {
     // slice offsets: exclusive scan of the per-slice counts (ns <= 1024)
-    const int cnt = tid < ns ? a.cand_cnt[(int64_t)r * a.n_slices + tid] : 0;
+    const int cnt = tid < ns ? craw : 0;
     int2 tot;
     const int off = block_scan2<TOPK_THREADS>(cnt, 0, sh.sel.scan, &tot).x;
     if (tid < ns) sh.slice_off[tid] = off;
@@ -711,11 +734,8 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkArgs a) {
       umax = max(umax, u);
     }
   } else {
-    // each wave copies whole slices (wave w: slices w, w + NW, ...), up to
-    // 64 candidates of a slice per load round and four slices' loads in
-    // flight together; slices longer than 64 candidates finish in a loop
-    constexpr int NW = TOPK_THREADS / 64;
-    const int lane = tid & 63, wv = tid >> 6;
+    // each wave copies whole slices (wave w: slices w, w + NW, ...): the
+    // preloaded first 64 candidates of its first PRE slices, then the rest
     auto put = [&](int e, float sv, int iv) {
       const uint32_t u = order_key(sv);
       umin = min(umin, u);
@@ -728,28 +748,20 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkArgs a) {
         gidx[e] = iv;
       }
     };
-    const int64_t rbase = (int64_t)r * a.ia.Nmax;
-    for (int f0 = wv; f0 < ns; f0 += 4 * NW) {
-      float sv[4];
-      int iv[4], dst[4], cnt[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int f = f0 + u * NW;
-        dst[u] = f < ns ? sh.slice_off[f] : 0;
-        cnt[u] = f < ns ? sh.slice_off[f + 1] - dst[u] : 0;
-        if (lane < cnt[u]) {
-          sv[u] = a.cand_score[rbase + (int64_t)f * SLICE + lane];
-          iv[u] = a.cand_idx[rbase + (int64_t)f * SLICE + lane];
-        }
+    for (int u = 0; u < PRE; ++u) {
+      const int f = wv + u * NW;
+      if (f < ns) {
+        const int dst = sh.slice_off[f], cnt = sh.slice_off[f + 1] - dst;
+        if (lane < cnt) put(dst + lane, psv[u], piv[u]);
+        const int64_t src = rbase + (int64_t)f * SLICE;
+        for (int j = 64 + lane; j < cnt; j += 64) put(dst + j, a.cand_score[src + j], a.cand_idx[src + j]);
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (lane < cnt[u]) put(dst[u] + lane, sv[u], iv[u]);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t src = rbase + (int64_t)(f0 + u * NW) * SLICE;
-        for (int j = 64 + lane; j < cnt[u]; j += 64) put(dst[u] + j, a.cand_score[src + j], a.cand_idx[src + j]);
-      }
+    }
+    for (int f = wv + PRE * NW; f < ns; f += NW) {
+      const int dst = sh.slice_off[f], cnt = sh.slice_off[f + 1] - dst;
+      const int64_t src = rbase + (int64_t)f * SLICE;
+      for (int j = lane; j < cnt; j += 64) put(dst + j, a.cand_score[src + j], a.cand_idx[src + j]);
     }
   }
   umin = wave_ext_u32<false>(umin);
