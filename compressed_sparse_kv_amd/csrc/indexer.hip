@@ -577,9 +577,27 @@ __global__ __launch_bounds__(FUSED_THREADS) void topk_filter_kernel(TopkArgs a) 
   __shared__ FusedShared sh;
   const int r = blockIdx.x, f = blockIdx.y;
   const int tid = threadIdx.x;
-  const int nv = visible_count(a.ia, r);
   const int s0 = f * SLICE;
   const int k = a.k;
+
+  // The slice's scores and (when they fit one batch) the row's samples are
+  // loaded before the row's visible count is known, their addresses clamped
+  // to the allocated row, so that the count and all of them arrive in one
+  // memory round trip; the count then decides which of them are valid. (A
+  // barrier waits for every load in flight, so each barrier comes after
+  // loads that are needed anyway.)
+  const float* sc = a.ia.scores + (int64_t)r * a.ia.Nmax + s0;
+  const int slim = min(SLICE, a.ia.Nmax - s0);
+  const int j0 = tid * (SLICE / FUSED_THREADS);
+  float v[SLICE / FUSED_THREADS];
+#pragma unroll
+  for (int i = 0; i < SLICE / FUSED_THREADS; ++i) v[i] = sc[min(j0 + i, slim - 1)];  // unconditional
+  const float* smp = a.ia.samples + (int64_t)r * a.ia.ng;
+  const bool one_batch = a.ia.ng <= FUSED_THREADS * THR_BATCH;
+  float sraw[THR_BATCH];  // raw values: converted only once the count is in
+#pragma unroll
+  for (int i = 0; i < THR_BATCH; ++i) sraw[i] = smp[min(FUSED_THREADS * i + tid, a.ia.ng - 1)];
+  const int nv = visible_count(a.ia, r);
 
   // ---- filter
   if (s0 < nv) {
@@ -591,29 +609,30 @@ __global__ __launch_bounds__(FUSED_THREADS) void topk_filter_kernel(TopkArgs a) 
       if (tid == 0) sh.thr = 0u;
       __syncthreads();
     }
-    // the slice's scores are loaded first; their latency overlaps the
-    // threshold (a barrier waits for every load in flight, so each barrier
-    // comes after loads that are needed anyway)
-    const float* sc = a.ia.scores + (int64_t)r * a.ia.Nmax + s0;
     const int lim = min(SLICE, nv - s0);
-    const int j0 = tid * (SLICE / FUSED_THREADS);
-    float v[SLICE / FUSED_THREADS];
-#pragma unroll
-    for (int i = 0; i < SLICE / FUSED_THREADS; ++i) v[i] = sc[min(j0 + i, lim - 1)];  // unconditional
     uint32_t thr = 0u;
     if (thresholded) {
-      const float* smp = a.ia.samples + (int64_t)r * a.ia.ng;
-      // the samples' key range (the keys of a single batch stay in
-      // registers for the histogram; longer rows load them again)
+      // the samples' key range (a single batch stays in registers for the
+      // histogram; longer rows load theirs in batches, twice)
       uint32_t kx[THR_BATCH];
       uint32_t kmin = 0xffffffffu, kmax = 0u;
-      for (int e0 = 0; e0 < ng; e0 += FUSED_THREADS * THR_BATCH) {
-#pragma unroll
-        for (int i = 0; i < THR_BATCH; ++i) kx[i] = order_key(smp[min(e0 + FUSED_THREADS * i + tid, ng - 1)]);
+      if (one_batch) {
 #pragma unroll
         for (int i = 0; i < THR_BATCH; ++i) {
-          kmin = min(kmin, kx[i]);
-          kmax = max(kmax, kx[i]);
+          kx[i] = order_key(sraw[i]);
+          const bool ok = FUSED_THREADS * i + tid < ng;
+          kmin = min(kmin, ok ? kx[i] : 0xffffffffu);
+          kmax = max(kmax, ok ? kx[i] : 0u);
+        }
+      } else {
+        for (int e0 = 0; e0 < ng; e0 += FUSED_THREADS * THR_BATCH) {
+#pragma unroll
+          for (int i = 0; i < THR_BATCH; ++i) kx[i] = order_key(smp[min(e0 + FUSED_THREADS * i + tid, ng - 1)]);
+#pragma unroll
+          for (int i = 0; i < THR_BATCH; ++i) {
+            kmin = min(kmin, kx[i]);
+            kmax = max(kmax, kx[i]);
+          }
         }
       }
       kmin = wave_ext_u32<false>(kmin);
@@ -630,7 +649,6 @@ __global__ __launch_bounds__(FUSED_THREADS) void topk_filter_kernel(TopkArgs a) 
       }
       const uint32_t span = kmax - kmin;
       const int sb = span < (uint32_t)THR_BINS ? 0 : 20 - __clz(span);  // span >> sb < 4096
-      const bool one_batch = ng <= FUSED_THREADS * THR_BATCH;
       for (int e0 = 0; e0 < ng; e0 += FUSED_THREADS * THR_BATCH) {
         if (!one_batch) {
 #pragma unroll
