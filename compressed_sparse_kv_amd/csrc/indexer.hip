@@ -338,29 +338,26 @@ __global__ __launch_bounds__(256) void idx_samples_kernel(IdxArgs a) {
 
 // ------------------------------------------------------------ block scans
 // Exclusive prefix sums of two ints over a workgroup of NT threads (NT/64
-// waves <= 64): wave shuffles, then one wave scans the wave totals.
+// waves <= 16): wave scans, then every wave scans the wave totals itself
+// (one barrier between, one before the totals can be reused).
 struct ScanShared {
   int2 wtot[16];
-  int2 total;
 };
 
 template <int NT>
 __device__ __forceinline__ int2 block_scan2(int a, int b, ScanShared& sh, int2* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int x = wave_incl_sum(a), y = wave_incl_sum(b);
   if (lane == 63) sh.wtot[wave] = make_int2(x, y);
   __syncthreads();
-  if (wave == 0) {
-    const int2 w = lane < NT / 64 ? sh.wtot[lane] : make_int2(0, 0);
-    const int wx = wave_incl_sum(w.x), wy = wave_incl_sum(w.y);
-    if (lane < NT / 64) sh.wtot[lane] = make_int2(wx - w.x, wy - w.y);
-    if (lane == NT / 64 - 1) sh.total = make_int2(wx, wy);
-  }
-  __syncthreads();
-  const int2 off = sh.wtot[wave];
-  *total = sh.total;
-  __syncthreads();  // the shared totals may be reused by the next scan
-  return make_int2(off.x + x - a, off.y + y - b);
+  const int2 w = lane < NT / 64 ? sh.wtot[lane] : make_int2(0, 0);
+  const int wx = wave_incl_sum(w.x), wy = wave_incl_sum(w.y);
+  const int offx = __builtin_amdgcn_readlane(wx - w.x, wave);
+  const int offy = __builtin_amdgcn_readlane(wy - w.y, wave);
+  *total = make_int2(__builtin_amdgcn_readlane(wx, NT / 64 - 1), __builtin_amdgcn_readlane(wy, NT / 64 - 1));
+  __syncthreads();  // the wave totals may be reused by the next scan
+  return make_int2(offx + x - a, offy + y - b);
 }
 
 // ------------------------------------------------------------ range select
@@ -506,15 +503,21 @@ __device__ bool find_rank_bin(const int* hist, int want, ScanShared& scan, int* 
   return false;
 }
 
+// (cleared: the caller has zeroed sh.hist and sh.nsmall, and passed a
+// barrier since, so level 0 skips its own clear.)
 template <int NT, typename Get>
-__device__ SelectState range_select(Get get, int n, int k, uint32_t kmin, uint32_t kmax, SelectShared& sh) {
+__device__ SelectState range_select(Get get, int n, int k, uint32_t kmin, uint32_t kmax, SelectShared& sh,
+                                    bool cleared) {
   const int tid = threadIdx.x;
   uint32_t lo = kmin, span = kmax - kmin;  // the current range [lo, lo + span]
   int want = k;                            // rank of the target inside it
   for (int level = 0; level < 3; ++level) {
     const int sb = span < (uint32_t)SEL_BINS ? 0 : 20 - __clz(span);  // span >> sb < SEL_BINS
-    for (int i = tid; i < SEL_BINS; i += NT) sh.hist[i] = 0;
-    __syncthreads();
+    if (level > 0 || !cleared) {
+      for (int i = tid; i < SEL_BINS; i += NT) sh.hist[i] = 0;
+      if (tid == 0) sh.nsmall = 0;
+      __syncthreads();
+    }
     for (int e = tid; e < n; e += NT) {
       const uint32_t u = get(e) - lo;  // wraps for keys below the range
       if (u <= span) atomicAdd(&sh.hist[u >> sb], 1);
@@ -537,8 +540,7 @@ __device__ SelectState range_select(Get get, int n, int k, uint32_t kmin, uint32
     if (binc <= SEL_SMALL) {
       // the few keys of the bin: wave 0 ranks them (lane j counts the keys
       // above and equal to its own) and publishes the want-th largest
-      if (tid == 0) sh.nsmall = 0;
-      __syncthreads();
+      // (nsmall was zeroed with this level's histogram)
       for (int e = tid; e < n; e += NT) {
         const uint32_t u = get(e);
         if (u - edge < (1u << sb)) sh.small[atomicAdd(&sh.nsmall, 1)] = u;
@@ -558,9 +560,8 @@ __device__ SelectState range_select(Get get, int n, int k, uint32_t kmin, uint32
         }
       }
       __syncthreads();
-      const SelectState st{0xffffffffu, sh.thr, sh.take};
-      __syncthreads();
-      return st;
+      // (thr and take are not written again: no barrier after the reads)
+      return SelectState{0xffffffffu, sh.thr, sh.take};
     }
     lo = edge;
     span = (1u << sb) - 1u;
@@ -788,6 +789,10 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkArgs a) {
     sh.sel.kmin[tid >> 6] = umin;
     sh.sel.kmax[tid >> 6] = umax;
   }
+  // the first level's histogram is cleared here, before the barrier the
+  // key range needs anyway
+  for (int i = tid; i < SEL_BINS; i += TOPK_THREADS) sh.sel.hist[i] = 0;
+  if (tid == 0) sh.sel.nsmall = 0;
   __syncthreads();
 #pragma unroll
   for (int w = 0; w < TOPK_THREADS / 64; ++w) {
@@ -814,7 +819,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkArgs a) {
     for (int e = tid; e < n; e += TOPK_THREADS) emit(e, e);
     nsel = n;
   } else {
-    SelectState st = range_select<TOPK_THREADS>(get, n, k, umin, umax, sh.sel);
+    SelectState st = range_select<TOPK_THREADS>(get, n, k, umin, umax, sh.sel, true);
     compact_selected<TOPK_THREADS>(get, emit, n, st, sh.sel);
     nsel = k;
   }
