@@ -181,7 +181,10 @@ __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
   // (the lane's code and scale pointers for key 0 of the batch, formed once;
   // keys are then a 32-bit offset from them)
   const uint8_t* kc_lane = a.kc + (int64_t)b * a.Nmax * (a.dI / 2) + kb * 16;
-  const uint8_t* ks_lane = a.ks + (int64_t)b * a.Nmax * (a.dI / 32) + kb;
+  // (a key's KS*4 scales are KS whole dwords: each lane loads the dword of
+  // its K-step and takes byte kb, so a load instruction reads dwords, not
+  // single bytes)
+  const uint32_t* ks_row = reinterpret_cast<const uint32_t*>(a.ks + (int64_t)b * a.Nmax * (a.dI / 32));
   auto load_keys = [&](Group& gr, int base) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
       for (int s = 0; s < KS; ++s) {
         gr.v[kt][s] = __builtin_nontemporal_load(
             reinterpret_cast<const v4u*>(kc_lane + (uint32_t)key * (uint32_t)(a.dI / 2) + s * 64));
-        gr.sc[kt][s] = ks_lane[(uint32_t)key * (uint32_t)(a.dI / 32) + s * 4];
+        gr.sc[kt][s] = (int)((ks_row[(uint32_t)key * (uint32_t)KS + s] >> (8 * kb)) & 0xffu);
       }
     }
   };
@@ -889,6 +892,8 @@ int indexer_topk(const void* q, const uint8_t* q_scale, const float* w, const vo
     return fail(CSK_EUNSUPPORTED, "indexer_topk: dtype must be CSK_MXFP4 or CSK_F32");
   if (dtype == CSK_MXFP4 && (dI % 32 || !q_scale || !k_scale))
     return fail(CSK_EINVAL, "indexer_topk: MXFP4 needs dI % 32 == 0 and both scale arrays");
+  if (dtype == CSK_MXFP4 && (reinterpret_cast<uintptr_t>(k_scale) & 3))
+    return fail(CSK_EINVAL, "indexer_topk: k_scale must be 4-byte aligned (read as dwords)");
   if ((int64_t)B * T > (1LL << 30) || ceil_div(Nmax, 256 * IDX_MIN_ITERS) > 65535)
     return fail(CSK_EUNSUPPORTED, "indexer_topk: B*T or Nmax too large");
   IdxPlan p = plan_indexer(B, T, Nmax, k);

@@ -115,3 +115,15 @@ def test_compress_batch_errors_without_device(lib):
     # jobs that produce nothing launch nothing (no device needed)
     assert run(CompressJob(**dict(csa, S=3)), CompressJob(kind=CSK_JOB_MXFP4, x=fake, rows=0, cols=32,
                                                           out=fake, out_scale=fake)) == 0
+
+
+def test_indexer_rejects_misaligned_key_scales(lib):
+    # the MXFP4 key scales are read as whole dwords: a misaligned array is an
+    # argument error, caught before any launch
+    lib.csk_last_error.restype = ctypes.c_char_p
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.indexer_topk.argtypes = [vp] * 7 + [i] * 8 + [vp, vp, vp, ctypes.c_size_t, vp]
+    fake, odd = 4096, 4097
+    rc = lib.indexer_topk(fake, fake, fake, fake, odd, fake, fake, 1, 1, 64, 128, 4096, 4, 8, 2,
+                          fake, fake, fake, ctypes.c_size_t(1 << 30), None)
+    assert rc == -1 and b"aligned" in lib.csk_last_error()
