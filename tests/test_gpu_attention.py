@@ -70,6 +70,19 @@ def test_sparse_decode_split(H, D, dv):
                  d_rope=min(64, D // 2), decode=True)
 
 
+@pytest.mark.parametrize("cap", [4, 40])
+def test_sparse_decode_workgroup_cap(cap):
+    # the sparse split capped: 4 workgroups over 4 rows (each row whole in
+    # one workgroup, no merge) and 40 (ten runs of three or four tiles a
+    # row, merged)
+    prev = csk.set_attn_workgroups(cap)
+    try:
+        _sparse_case(770 + cap, B=4, T=1, H=64, D=576, dv=512, N=5000, k=2048, S_w=128, W=128, bf16=True,
+                     d_rope=64, decode=True)
+    finally:
+        csk.set_attn_workgroups(prev)
+
+
 @pytest.mark.parametrize("D,dv", [(576, 512), (256, 256), (128, 128), (64, 64)])
 def test_sparse_prefill_whole_rows(D, dv):
     # 320 rows of up to 150 selected entries + 40 window tokens: rows stay
