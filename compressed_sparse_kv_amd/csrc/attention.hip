@@ -1866,7 +1866,9 @@ static AttnPlan plan_attn(bool dense, int B, int T, int H, int D, int dv, int Lc
   // (few rows with long candidate lists: decode)
   if (p.mfma && H == 64 && row32_shape(D, dv) && (dense || Lc >= 1)) {
     const int64_t nt = ceil_div(total, 64);
-    int64_t nch = ceil_div(g_attn_workgroups > 0 ? g_attn_workgroups : 256, R);
+    // about one workgroup per CU, or at most the cap in all (at least one a row)
+    int64_t nch = g_attn_workgroups > 0 ? g_attn_workgroups / (int64_t)R : ceil_div(256, R);
+    nch = nch < 1 ? 1 : nch;
     nch = nch < nt ? nch : nt;
     p.row32 = true;
     p.chunk = total;
