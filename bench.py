@@ -188,13 +188,9 @@ class DecodeWorkload:
         csk.compress_batch(st["jobs"])
         csk.indexer_topk(self.qc, x["w"], st["kc"], x["q_pos"], x["n_entries"], 4, self.k, q_scale=self.qs,
                          k_scale=st["ks"], idx=self.idx, score=self.score, workspace=self.ws_i)
-        prev = csk.set_attn_workgroups(self.csa_workgroups)
-        try:
-            csk.sparse_attn(x["q"], x["q_pos"], st["kv_c"], self.idx, st["kv_w"], x["w_pos0"], self.W,
-                            x["sink"], self.dv, 64, self.scale, out=self.out, lse=self.lse,
-                            workspace=self.ws_s)
-        finally:
-            csk.set_attn_workgroups(prev)
+        csk.sparse_attn(x["q"], x["q_pos"], st["kv_c"], self.idx, st["kv_w"], x["w_pos0"], self.W,
+                        x["sink"], self.dv, 64, self.scale, out=self.out, lse=self.lse,
+                        workspace=self.ws_s, max_workgroups=self.csa_workgroups)
         if self.pair and not multi:
             self._hca(x, st)
         if self.pair and multi:
@@ -209,13 +205,9 @@ class DecodeWorkload:
         # hca_workgroups workgroups (each holds a whole CU), which leaves the
         # rest of the chip to the chain's kernels
         cap = self.hca_workgroups if self.streams > 1 else 0
-        prev = csk.set_attn_workgroups(cap)
-        try:
-            csk.dense_compressed_attn(x["q_h"], x["q_pos"], st["kv_h"], x["n_entries_h"], 128, st["kv_w_h"],
-                                      x["w_pos0"], self.W, x["sink_h"], self.dv, 64, self.scale,
-                                      out=self.out_h, lse=self.lse_h, workspace=self.ws_d)
-        finally:
-            csk.set_attn_workgroups(prev)
+        csk.dense_compressed_attn(x["q_h"], x["q_pos"], st["kv_h"], x["n_entries_h"], 128, st["kv_w_h"],
+                                  x["w_pos0"], self.W, x["sink_h"], self.dv, 64, self.scale,
+                                  out=self.out_h, lse=self.lse_h, workspace=self.ws_d, max_workgroups=cap)
 
     def kernels(self):
         names = ["csk_compress_batch", "indexer_scores_fp4", "topk_filter",
@@ -283,9 +275,11 @@ class DecodeWorkload:
         qc, qs = oracle.mxfp4_encode(d["qI"][sel])
         out["qc"], out["qs"] = qc, qs
         npos = d["q_pos"][sel]
-        idx, sc = oracle.indexer_topk(qc, d["w"][sel], kc, npos, d["n_entries"][sel], 4, self.k, q_scale=qs,
-                                      k_scale=ks)
+        scores, nvis = oracle.indexer_scores(qc, d["w"][sel], kc, npos, d["n_entries"][sel], 4, q_scale=qs,
+                                             k_scale=ks)
+        idx, sc = oracle.topk(scores, nvis, self.k)
         out["idx"], out["score"] = idx, sc
+        out["scores_full"], out["n_vis"] = scores, nvis
         o, l = oracle.sparse_attn(d["q"][sel], npos, kv_c, idx[:, None, :], d["kv_w"][sel], d["w_pos0"][sel],
                                   self.W, d["sink"], self.dv, 64, d["scale"])
         out["out"], out["lse"] = o, l
@@ -410,26 +404,37 @@ class PrefillWorkload:
 
     def kernels(self):
         if self.csa:
-            return ["csa_compress", "mxfp4_quantize", "indexer_scores_fp4", "topk_filter", "topk_select",
-                    "attn_bf16_sparse", "attn_merge"]
+            return ["csa_compress", "csa_compress_mxfp4", "mxfp4_quantize", "indexer_scores_fp4", "topk_filter",
+                    "topk_select", "attn_bf16_sparse", "attn_merge"]
         return ["hca_compress", "attn_bf16_dense", "attn_merge"]
 
     def algorithmic_work(self, kernel):
-        """(bound, work per launch, peak, unit): the roofline a launch of
-        `kernel` is held to. Attention: 2*(D+dv) flops per (query, head,
-        candidate); indexer: 2*HI*dI per (query, visible key); compression:
-        its source and output bytes."""
-        S, H, D, dv, N = self.S, self.H, self.D, self.dv, self.N
+        """(bound, work per launch, peak, unit): the binding roofline of one
+        launch of `kernel`, the one whose time at peak is the longer.
+        Attention: 2*(D+dv) flops per (query, head, candidate) against its
+        HBM bytes (q, out, window, cache once, idx); indexer: 2*HI*dI flops
+        per (query, visible key); compression and the query encode: their
+        source and output bytes (each compress launch with its own)."""
+        S, H, D, dv, N, dI, HI = self.S, self.H, self.D, self.dv, self.N, self.dI, self.HI
         if kernel in ("attn_bf16_sparse", "attn_bf16_dense"):
-            return ("mfma", 2.0 * (D + dv) * H * self.attn_pairs, self.BF16_PEAK_TFLOPS, "TFLOP/s")
+            flops = 2.0 * (D + dv) * H * self.attn_pairs
+            nbytes = self.attention_hbm_bytes()
+            if flops / (self.BF16_PEAK_TFLOPS * 1e12) >= nbytes / (HBM_PEAK_GBS * 1e9):
+                return ("mfma", flops, self.BF16_PEAK_TFLOPS, "TFLOP/s")
+            return ("hbm", nbytes, HBM_PEAK_GBS, "GB/s")
         if kernel == "indexer_scores_fp4":
-            return ("mfma", 2.0 * self.HI * self.dI * self.idx_pairs, self.FP4_PEAK_TFLOPS, "TFLOP/s")
+            return ("mfma", 2.0 * HI * dI * self.idx_pairs, self.FP4_PEAK_TFLOPS, "TFLOP/s")
         if kernel in ("csa_compress", "hca_compress"):
-            # the CSA step launches it twice (KV, then indexer keys); per
-            # launch: the KV launch's bytes (the larger)
             n_series = 4 if self.csa else 2
             return ("hbm", n_series * S * D * 2 + N * D * 2, HBM_PEAK_GBS, "GB/s")
+        if kernel == "csa_compress_mxfp4":
+            return ("hbm", 4 * S * dI * 2 + N * (dI // 2 + dI // 32), HBM_PEAK_GBS, "GB/s")
+        if kernel == "mxfp4_quantize":
+            return ("hbm", S * HI * dI * 4 + S * HI * (dI // 2 + dI // 32), HBM_PEAK_GBS, "GB/s")
         return None
+
+    def attention_mfma_work(self):
+        return 2.0 * (self.D + self.dv) * self.H * self.attn_pairs
 
     def attention_hbm_bytes(self):
         """Bytes the attention kernel must move: q, out, window KV, the
@@ -694,9 +699,12 @@ def run_prefill(args):
         kern[n] = rec
     attn = [n for n in per if n.startswith("attn_bf16")]
     if attn:
-        ab = wl.attention_hbm_bytes() / (per[attn[0]][0] * 1e-3) / 1e9
-        kern[attn[0]]["hbm_achieved_gbs"] = round(ab, 1)
-        kern[attn[0]]["hbm_frac"] = round(ab / HBM_PEAK_GBS, 4)
+        # both roofs of the attention kernel: HBM bytes and MFMA flops
+        t = per[attn[0]][0] * 1e-3
+        ab = wl.attention_hbm_bytes() / t / 1e9
+        af = wl.attention_mfma_work() / t / 1e12
+        kern[attn[0]].update(hbm_achieved_gbs=round(ab, 1), hbm_frac=round(ab / HBM_PEAK_GBS, 4),
+                             mfma_achieved_tflops=round(af, 1), mfma_frac=round(af / wl.BF16_PEAK_TFLOPS, 4))
     _log(f"{K} steps in {elapsed*1e3:.1f} ms -> {ms_per_step:.3f} ms/step; dominant {dom} {avg_ms:.3f} ms avg "
          f"-> {achieved:.1f} {unit} ({achieved / peak:.1%})")
     line = {
@@ -727,16 +735,132 @@ def run_prefill(args):
         },
         "kernels": kern,
     }
+    if dom.startswith("attn_bf16"):
+        # the attention kernel's other roof beside its binding one
+        other = "mfma" if bound == "hbm" else "hbm"
+        line["roofline"]["other_roof"] = {
+            "bound": other, "frac": kern[dom]["mfma_frac" if other == "mfma" else "hbm_frac"],
+            "achieved": kern[dom]["mfma_achieved_tflops" if other == "mfma" else "hbm_achieved_gbs"],
+            "unit": "TFLOP/s" if other == "mfma" else "GB/s"}
     if not args.no_cpu_baseline:
         n_rows = args.cpu_rows_prefill or (384 if wl.csa else wl.S)
         tc, tr, n = wl.oracle_sample(n_rows)
         import oracle
 
         per_tok = tc / wl.S + tr / n
-        line["cpu_baseline"] = {
+        line["cpu_baseline"] = dict({
             "value": round(1.0 / per_tok, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"compression of all {wl.N} entries ({tc:.1f} s) plus {n} query rows spread over the "
-                      f"sequence ({tr:.1f} s); tokens/s = 1 / (compression time per token + time per row)"}
+                      f"sequence ({tr:.1f} s); tokens/s = 1 / (compression time per token + time per row)"},
+            **host_cpu())
+    print(json.dumps(line), flush=True)
+
+
+def run_tiny(args):
+    """The tiny fp32 CSA prefill (batch 1, seq 256): one whole layer pass -
+    compression of the KV and indexer-key series, fp32 indexer scores and
+    top-8, sparse attention over the selection, window 32 and sink. Far too
+    small to fill the chip, so its figure is the latency of one pass in
+    microseconds (graph replays of K passes, and eager launches)."""
+    import torch
+
+    import compressed_sparse_kv_amd as csk
+    import synth
+
+    d = synth.make("tiny_csa_prefill")
+    dev = torch.device("cuda:0")
+    t = {n: _to_dev(torch, d[n], dev) for n in d if isinstance(d[n], np.ndarray)}
+    m, k, W, dr, sc, S, H, D = d["m"], d["k"], d["W"], d["d_rope"], d["scale"], d["S"], d["H"], d["D"]
+    N = S // m
+    kv = torch.empty((1, N, D), dtype=torch.float32, device=dev)
+    keys = torch.empty((1, N, d["dI"]), dtype=torch.float32, device=dev)
+    ne = torch.full((1,), N, dtype=torch.int32, device=dev)
+    idx = torch.empty((1, S, k), dtype=torch.int32, device=dev)
+    out = torch.empty((1, S, H, d["dv"]), dtype=torch.float32, device=dev)
+    lse = torch.empty((1, S, H), dtype=torch.float32, device=dev)
+    ws_i = torch.empty(max(csk.indexer_topk_workspace_size(1, S, d["HI"], d["dI"], N, k, csk.CSK_F32), 1),
+                       dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(max(csk.sparse_attn_workspace_size(1, S, H, D, d["dv"], k, W, csk.CSK_F32), 1),
+                       dtype=torch.uint8, device=dev)
+
+    def step():
+        csk.csa_compress(t["ca"], t["za"], t["cb"], t["zb"], t["bias_a"], t["bias_b"], m, d_rope=dr, out=kv)
+        csk.csa_compress(t["ia"], t["iza"], t["ib"], t["izb"], t["ibias_a"], t["ibias_b"], m, out=keys)
+        csk.indexer_topk(t["qI"], t["w"], keys, t["q_pos"], ne, m, k, idx=idx, workspace=ws_i, with_score=False)
+        csk.sparse_attn(t["q"], t["q_pos"], kv, idx, t["kv_w"], t["w_pos0"], W, t["sink"], d["dv"], dr, sc,
+                        out=out, lse=lse, workspace=ws_a)
+
+    K, Wm = args.steps, args.warmup
+    for _ in range(max(Wm, 1)):
+        step()
+    torch.cuda.synchronize()
+    names = ["csa_compress", "indexer_scores_valu", "topk_select", "attn_valu"]
+    per = {}
+    for name in names:
+        tm = csk.KernelTimer(name, 8)
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        ds = tm.durations_ms()
+        tm.disarm()
+        if ds:
+            per[name] = (sum(ds) / len(ds), len(ds) / 2.0)
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    eager_us = (time.perf_counter() - t0) * 1e6 / K
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap):
+        for _ in range(K):
+            step()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    us = elapsed * 1e6 / K
+    dom = max(per, key=lambda n: per[n][0] * per[n][1])
+    _log(f"tiny_csa_prefill: {us:.1f} us per pass in a graph, {eager_us:.1f} us eager; kernels " +
+         ", ".join(f"{n}={v[0]*1e3:.1f}us x{v[1]:g}" for n, v in per.items()))
+    # the attention kernel's algorithmic bytes: q, out, lse, idx and every
+    # (row, candidate) pair's KV row, all fp32
+    pairs = sum(min(k, min(N, (tt + 1) // m)) + min(W, tt + 1) for tt in range(S))
+    abytes = S * H * D * 4 + S * H * d["dv"] * 4 + S * H * 4 + S * k * 4 + pairs * D * 4
+    dms = per["attn_valu"][0]
+    line = {
+        "metric": METRIC, "value": round(S * K / elapsed, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": Wm, "ms_per_step": round(us / 1e3, 5), "latency_us": round(us, 2),
+        "eager_latency_us": round(eager_us, 2), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "tiny_csa_prefill", "batch": 1, "seq_len": S, "compressed_entries": N,
+                   "heads": H, "kv_dim": D, "rope_dims": dr, "indexer_heads": d["HI"], "indexer_dim": d["dI"],
+                   "indexer_dtype": "f32", "top_k": k, "window": W, "sink": True, "launch": "graph"},
+        "roofline": {"kernel": "attn_valu", "bound": "hbm", "achieved": round(abytes / (dms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(abytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5), "traffic": None,
+                     "algorithmic_bytes": abytes, "avg_launch_us": round(dms * 1e3, 2),
+                     "note": "latency-bound: a few microseconds of launches over 256 rows; the pass time is the figure",
+                     "dominant_by_time": dom},
+        "kernels": {n: {"avg_launch_us": round(v[0] * 1e3, 2), "launches_per_step": v[1]} for n, v in per.items()},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        t0 = time.perf_counter()
+        rkv = oracle.round_f32(oracle.csa_compress(d["ca"], d["za"], d["cb"], d["zb"], d["bias_a"], d["bias_b"], m,
+                                                   d_rope=dr))
+        rkeys = oracle.round_f32(oracle.csa_compress(d["ia"], d["iza"], d["ib"], d["izb"], d["ibias_a"],
+                                                     d["ibias_b"], m))
+        ridx, _ = oracle.indexer_topk(d["qI"], d["w"], rkeys, d["q_pos"], np.array([N], np.int32), m, k)
+        oracle.sparse_attn(d["q"], d["q_pos"], rkv, ridx[None], d["kv_w"], d["w_pos0"], W, d["sink"], d["dv"], dr,
+                           sc)
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = dict({"value": round(S / dt, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
+                                     "kind": "oracle", "sample": f"the whole pass over all {S} rows, {dt*1e3:.1f} ms"},
+                                    **host_cpu())
     print(json.dumps(line), flush=True)
 
 
@@ -786,6 +910,25 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
 
 
+def host_cpu():
+    """The host's logical CPU count (as this process may use them) and CPU
+    model, for the record beside the oracle's timing."""
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"host_nproc": nproc, "host_cpu_model": model}
+
+
 def cpu_baseline(wl, args):
     import oracle
 
@@ -794,11 +937,14 @@ def cpu_baseline(wl, args):
     t0 = time.perf_counter()
     wl.oracle_step(rows)
     dt = time.perf_counter() - t0
+    # the oracle parallelises over query rows (OpenMP): one decode step has
+    # one row per sequence, so it keeps min(threads, rows) cores busy
     threads = min(oracle.num_threads(), len(rows))
-    return {"value": round(len(rows) / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full decode step for {len(rows)} of {wl.B} sequences (compression of the newest "
-                      f"entries, MXFP4 query encoding, indexer over all {wl.N} entries, top-{wl.k}, sparse "
-                      f"attention" + (", dense HCA attention" if wl.pair else "") + f"); {dt:.1f} s wall"}
+    return dict({"value": round(len(rows) / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                 "sample": f"one full decode step for {len(rows)} of {wl.B} sequences (compression of the newest "
+                           f"entries, MXFP4 query encoding, indexer over all {wl.N} entries, top-{wl.k}, sparse "
+                           f"attention" + (", dense HCA attention" if wl.pair else "") + f"); {dt:.1f} s wall; "
+                           f"the oracle runs one OpenMP thread per query row"}, **host_cpu())
 
 
 def main():
@@ -807,7 +953,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_1m_pair",
-                    choices=["decode_1m_pair", "csa_decode_128k", "hca_prefill_16k", "csa_prefill_64k"])
+                    choices=["decode_1m_pair", "csa_decode_128k", "hca_prefill_16k", "csa_prefill_64k",
+                             "tiny_csa_prefill"])
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--mode", default="graph", choices=["eager", "graph"],
                     help="timed steps as HIP graph replays (default) or as eager launches")
@@ -832,7 +979,9 @@ def main():
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
-    if args.workload.endswith("prefill_16k") or args.workload.endswith("prefill_64k"):
+    if args.workload == "tiny_csa_prefill":
+        run_tiny(args)
+    elif args.workload.endswith("prefill_16k") or args.workload.endswith("prefill_64k"):
         run_prefill(args)
     else:
         run(args)

@@ -46,15 +46,13 @@ def lib():
         L.indexer_topk_workspace_size.argtypes = [_i] * 7
         L.indexer_topk_workspace_size.restype = _sz
         L.sparse_attn.argtypes = ([_vp, _vp, _vp, _i, _vp, _i, _vp, _vp, _i, _i, _vp] + [_i] * 6
-                                  + [_f, _f, _i, _vp, _vp, _vp, _sz, _vp])
+                                  + [_f, _f, _i, _vp, _vp, _i, _vp, _sz, _vp])
         L.dense_compressed_attn.argtypes = ([_vp, _vp, _vp, _i, _vp, _i, _vp, _vp, _i, _i, _vp] + [_i] * 6
-                                            + [_f, _f, _i, _vp, _vp, _vp, _sz, _vp])
-        L.sparse_attn_workspace_size.argtypes = [_i] * 8
+                                            + [_f, _f, _i, _vp, _vp, _i, _vp, _sz, _vp])
+        L.sparse_attn_workspace_size.argtypes = [_i] * 9
         L.sparse_attn_workspace_size.restype = _sz
-        L.dense_compressed_attn_workspace_size.argtypes = [_i] * 9
+        L.dense_compressed_attn_workspace_size.argtypes = [_i] * 10
         L.dense_compressed_attn_workspace_size.restype = _sz
-        L.csk_set_attn_workgroups.argtypes = [_i]
-        L.csk_set_attn_workgroups.restype = _i
         L.csk_kernel_timer_arm.argtypes = [ctypes.c_char_p, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i]
         L.csk_kernel_timer_count.restype = _i
         L.csk_kernel_timer_disarm.restype = None
@@ -239,12 +237,12 @@ def indexer_topk(q, w, kk, q_pos, n_entries, m, k, q_scale=None, k_scale=None, i
     return idx, score
 
 
-def sparse_attn_workspace_size(B, T, H, D, dv, k, W, dtype):
-    return lib().sparse_attn_workspace_size(B, T, H, D, dv, k, W, dtype)
+def sparse_attn_workspace_size(B, T, H, D, dv, k, W, dtype, max_workgroups=0):
+    return lib().sparse_attn_workspace_size(B, T, H, D, dv, k, W, dtype, max_workgroups)
 
 
-def dense_compressed_attn_workspace_size(B, T, H, D, dv, Nmax, m, W, dtype):
-    return lib().dense_compressed_attn_workspace_size(B, T, H, D, dv, Nmax, m, W, dtype)
+def dense_compressed_attn_workspace_size(B, T, H, D, dv, Nmax, m, W, dtype, max_workgroups=0):
+    return lib().dense_compressed_attn_workspace_size(B, T, H, D, dv, Nmax, m, W, dtype, max_workgroups)
 
 
 def _attn_io(q, kv_w, dv, out, lse, want_lse):
@@ -258,42 +256,36 @@ def _attn_io(q, kv_w, dv, out, lse, want_lse):
 
 
 def sparse_attn(q, q_pos, kv_c, idx, kv_w, w_pos0, W, sink, dv, d_rope, scale, rope_base=10000.0,
-                out=None, lse=None, workspace=None, want_lse=True):
+                out=None, lse=None, workspace=None, want_lse=True, max_workgroups=0):
     """CSA attention (see sparse_attn in csk.h). Returns (out, lse)."""
     B, T, H, D, S_w, out, lse = _attn_io(q, kv_w, dv, out, lse, want_lse)
     k = idx.shape[-1]
-    nbytes = sparse_attn_workspace_size(B, T, H, D, dv, k, W if S_w else 0, _dt(q))
+    nbytes = sparse_attn_workspace_size(B, T, H, D, dv, k, W if S_w else 0, _dt(q), max_workgroups)
     if workspace is None:
         workspace = _ws(nbytes, q.device)
     rc = lib().sparse_attn(_ptr(q), _ptr(q_pos), _ptr(kv_c), kv_c.shape[1], _ptr(idx), k, _ptr(kv_w),
                            _ptr(w_pos0), S_w, W, _ptr(sink), B, T, H, D, dv, d_rope, rope_base, scale, _dt(q),
-                           _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream())
+                           _ptr(out), _ptr(lse), max_workgroups, _ptr(workspace), workspace.numel(), _stream())
     _check(rc, "sparse_attn")
     return out, lse
 
 
 def dense_compressed_attn(q, q_pos, kv_c, n_entries, m, kv_w, w_pos0, W, sink, dv, d_rope, scale,
-                          rope_base=10000.0, out=None, lse=None, workspace=None, want_lse=True):
+                          rope_base=10000.0, out=None, lse=None, workspace=None, want_lse=True,
+                          max_workgroups=0):
     """HCA attention (see dense_compressed_attn in csk.h). Returns (out, lse)."""
     B, T, H, D, S_w, out, lse = _attn_io(q, kv_w, dv, out, lse, want_lse)
     Nmax = kv_c.shape[1]
-    nbytes = dense_compressed_attn_workspace_size(B, T, H, D, dv, Nmax, m, W if S_w else 0, _dt(q))
+    nbytes = dense_compressed_attn_workspace_size(B, T, H, D, dv, Nmax, m, W if S_w else 0, _dt(q),
+                                                  max_workgroups)
     if workspace is None:
         workspace = _ws(nbytes, q.device)
     rc = lib().dense_compressed_attn(_ptr(q), _ptr(q_pos), _ptr(kv_c), Nmax, _ptr(n_entries), m, _ptr(kv_w),
                                      _ptr(w_pos0), S_w, W, _ptr(sink), B, T, H, D, dv, d_rope, rope_base, scale,
-                                     _dt(q), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream())
+                                     _dt(q), _ptr(out), _ptr(lse), max_workgroups, _ptr(workspace),
+                                     workspace.numel(), _stream())
     _check(rc, "dense_compressed_attn")
     return out, lse
-
-
-def set_attn_workgroups(max_workgroups):
-    """Cap the workgroups of one split-row attention launch (0 = one per CU);
-    see csk_set_attn_workgroups in csk.h. Returns the previous cap."""
-    prev = lib().csk_set_attn_workgroups(int(max_workgroups))
-    if prev < 0:
-        raise CskError(lib().csk_last_error().decode())
-    return prev
 
 
 class KernelTimer:

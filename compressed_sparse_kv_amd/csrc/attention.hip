@@ -1844,10 +1844,9 @@ static bool row32_shape(int D, int dv) {
   return (D == 576 && dv == 512) || (D == 256 && dv == 256) || (D == 128 && dv == 128) || (D == 64 && dv == 64);
 }
 
-// Workgroup cap of split-row launches (0: one per CU), per calling thread.
-static thread_local int g_attn_workgroups = 0;
-
-static AttnPlan plan_attn(bool dense, int B, int T, int H, int D, int dv, int Lc, int W, int dtype) {
+// max_wg: workgroup cap of a split-row launch (0: about one per CU).
+static AttnPlan plan_attn(bool dense, int B, int T, int H, int D, int dv, int Lc, int W, int dtype,
+                          int max_wg) {
   AttnPlan p{};
   const int64_t R = (int64_t)B * T;
   const int total = Lc + W;
@@ -1867,7 +1866,7 @@ static AttnPlan plan_attn(bool dense, int B, int T, int H, int D, int dv, int Lc
   if (p.mfma && H == 64 && row32_shape(D, dv) && (dense || Lc >= 1)) {
     const int64_t nt = ceil_div(total, 64);
     // about one workgroup per CU, or at most the cap in all (at least one a row)
-    int64_t nch = g_attn_workgroups > 0 ? g_attn_workgroups / (int64_t)R : ceil_div(256, R);
+    int64_t nch = max_wg > 0 ? max_wg / (int64_t)R : ceil_div(256, R);
     nch = nch < 1 ? 1 : nch;
     nch = nch < nt ? nch : nt;
     p.row32 = true;
@@ -1927,7 +1926,8 @@ static int attn_common(const char* fn, bool dense, const void* q, const int32_t*
                        const int32_t* n_entries, int m, const void* kv_w,
                        const int32_t* w_pos0, int S_w, int W, const float* sink, int B, int T,
                        int H, int D, int dv, int d_rope, float rope_base, float scale, int dtype,
-                       void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+                       void* out, float* lse, int max_wg, void* workspace, size_t ws_bytes,
+                       void* stream) {
   clear_error();
   std::string f(fn);
   if (!q || !q_pos || !kv_c || !out) return fail(CSK_EINVAL, f + ": null pointer");
@@ -1945,13 +1945,15 @@ static int attn_common(const char* fn, bool dense, const void* q, const int32_t*
   if (dtype != CSK_BF16 && dtype != CSK_F32)
     return fail(CSK_EUNSUPPORTED, f + ": dtype must be CSK_BF16 or CSK_F32");
   if (dv > 576) return fail(CSK_EUNSUPPORTED, f + ": dv > 576 not built");
+  if (max_wg < 0) return fail(CSK_EINVAL, f + ": max_workgroups must be >= 0");
   const int Wslots = S_w > 0 ? W : 0;
   const int Lc = dense ? Nmax : k;
-  AttnPlan p = plan_attn(dense, B, T, H, D, dv, Lc, Wslots, dtype);
+  AttnPlan p = plan_attn(dense, B, T, H, D, dv, Lc, Wslots, dtype, max_wg);
   if (p.nch > MERGE_MAX_CH || (int64_t)p.nch * H > 65535 || (int64_t)B * T > (1LL << 30))
     return fail(CSK_EUNSUPPORTED, f + ": problem too large");
   if (p.total > 0 && (!workspace || ws_bytes < p.total))
     return fail(CSK_EWORKSPACE, f + ": workspace smaller than the *_workspace_size() value");
+  if (const int dc = check_device(f); dc != CSK_OK) return dc;
   AttnArgs a{};
   a.q = q; a.q_pos = q_pos; a.kv_c = kv_c; a.idx = idx; a.n_entries = n_entries;
   a.kv_w = kv_w; a.w_pos0 = w_pos0; a.sink = sink;
@@ -2005,7 +2007,7 @@ const int NW = H / 16;
         rc = dense ? launch(kname, attn_bf16_chunk_kernel<d, v, nwc, true, 4>, grid, block, 0, s, a) \
                    : launch(kname, attn_bf16_chunk_kernel<d, v, nwc, false, 4>, grid, block, 0, s, a); \
     } else                                                                             \
-      rc = launch(kname, attn_bf16_kernel<d, v, nw>, grid, block, 0, s, a);            \
+      rc = launch("attn_bf16_stream", attn_bf16_kernel<d, v, nw>, grid, block, 0, s, a); \
   }
 #define CSK_ATT_NW(d, v) CSK_ATT_CASE(d, v, 1) CSK_ATT_CASE(d, v, 2) CSK_ATT_CASE(d, v, 3) CSK_ATT_CASE(d, v, 4)
     rc = CSK_EUNSUPPORTED;
@@ -2030,45 +2032,39 @@ const int NW = H / 16;
 
 extern "C" {
 
-int csk_set_attn_workgroups(int max_workgroups) {
-  if (max_workgroups < 0) return csk::fail(CSK_EINVAL, "csk_set_attn_workgroups: negative cap");
-  csk::clear_error();
-  const int prev = csk::g_attn_workgroups;
-  csk::g_attn_workgroups = max_workgroups;
-  return prev;
-}
-
-size_t sparse_attn_workspace_size(int B, int T, int H, int D, int dv, int k, int W, int dtype) {
-  if (B <= 0 || T <= 0 || H <= 0 || D <= 0 || dv <= 0 || k < 0 || W < 0) return 0;
-  return csk::plan_attn(false, B, T, H, D, dv, k, W, dtype).total;
+size_t sparse_attn_workspace_size(int B, int T, int H, int D, int dv, int k, int W, int dtype,
+                                  int max_workgroups) {
+  if (B <= 0 || T <= 0 || H <= 0 || D <= 0 || dv <= 0 || k < 0 || W < 0 || max_workgroups < 0) return 0;
+  return csk::plan_attn(false, B, T, H, D, dv, k, W, dtype, max_workgroups).total;
 }
 
 size_t dense_compressed_attn_workspace_size(int B, int T, int H, int D, int dv, int Nmax, int m,
-                                            int W, int dtype) {
+                                            int W, int dtype, int max_workgroups) {
   (void)m;
-  if (B <= 0 || T <= 0 || H <= 0 || D <= 0 || dv <= 0 || Nmax <= 0 || W < 0) return 0;
-  return csk::plan_attn(true, B, T, H, D, dv, Nmax, W, dtype).total;
+  if (B <= 0 || T <= 0 || H <= 0 || D <= 0 || dv <= 0 || Nmax <= 0 || W < 0 || max_workgroups < 0) return 0;
+  return csk::plan_attn(true, B, T, H, D, dv, Nmax, W, dtype, max_workgroups).total;
 }
 
 int sparse_attn(const void* q, const int32_t* q_pos, const void* kv_c, int Nmax,
                 const int32_t* idx, int k, const void* kv_w, const int32_t* w_pos0, int S_w,
                 int W, const float* sink, int B, int T, int H, int D, int dv, int d_rope,
-                float rope_base, float scale, int dtype, void* out, float* lse, void* workspace,
-                size_t ws_bytes, void* stream) {
+                float rope_base, float scale, int dtype, void* out, float* lse, int max_workgroups,
+                void* workspace, size_t ws_bytes, void* stream) {
   return csk::attn_common("sparse_attn", false, q, q_pos, kv_c, Nmax, idx, k, nullptr, 1, kv_w,
                           w_pos0, S_w, W, sink, B, T, H, D, dv, d_rope, rope_base, scale, dtype,
-                          out, lse, workspace, ws_bytes, stream);
+                          out, lse, max_workgroups, workspace, ws_bytes, stream);
 }
 
 int dense_compressed_attn(const void* q, const int32_t* q_pos, const void* kv_c, int Nmax,
                           const int32_t* n_entries, int m, const void* kv_w,
                           const int32_t* w_pos0, int S_w, int W, const float* sink, int B, int T,
                           int H, int D, int dv, int d_rope, float rope_base, float scale,
-                          int dtype, void* out, float* lse, void* workspace, size_t ws_bytes,
-                          void* stream) {
+                          int dtype, void* out, float* lse, int max_workgroups, void* workspace,
+                          size_t ws_bytes, void* stream) {
   return csk::attn_common("dense_compressed_attn", true, q, q_pos, kv_c, Nmax, nullptr, 0,
                           n_entries, m, kv_w, w_pos0, S_w, W, sink, B, T, H, D, dv, d_rope,
-                          rope_base, scale, dtype, out, lse, workspace, ws_bytes, stream);
+                          rope_base, scale, dtype, out, lse, max_workgroups, workspace, ws_bytes,
+                          stream);
 }
 
 }  // extern "C"

@@ -17,6 +17,11 @@ void set_error(const std::string& msg);
 int fail(int code, const std::string& msg);
 void clear_error();
 
+// CSK_OK when the calling thread's current HIP device is a gfx950 (the
+// answer is kept per device after the first query); CSK_EUNSUPPORTED with a
+// message naming fn otherwise, or when no device is visible.
+int check_device(const std::string& fn);
+
 // Measurement hook: brackets the armed kernel's launches with events.
 void timer_before(const char* kernel, hipStream_t s);
 void timer_after(const char* kernel, hipStream_t s);

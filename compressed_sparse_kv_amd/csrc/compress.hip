@@ -423,8 +423,12 @@ static int compress_common(const char* fn, bool csa, const void* ca, const void*
                                   src_bstride, d_rope, rope_base, entry_pos, in_dtype, out_dtype,
                                   out, out_scale, dst_bstride, &a, &empty);
   if (rc != CSK_OK || empty) return rc;
+  if (const int dc = check_device(fn); dc != CSK_OK) return dc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const char* name = csa ? "csa_compress" : "hca_compress";
+  // (a launch with MXFP4 output - an indexer-key series - is timed apart
+  // from the KV series' launch)
+  const char* name = csa ? (out_dtype == CSK_MXFP4 ? "csa_compress_mxfp4" : "csa_compress")
+                         : (out_dtype == CSK_MXFP4 ? "hca_compress_mxfp4" : "hca_compress");
   if (in_dtype == CSK_F32)
     return csa ? launch_compress_out<float, true>(name, a, out_dtype, s)
                : launch_compress_out<float, false>(name, a, out_dtype, s);
@@ -492,6 +496,7 @@ static int compress_batch(const csk_compress_job* jobs, int n_jobs, void* stream
     ++nz;
   }
   if (nz == 0) return CSK_OK;
+  if (const int dc = check_device("csk_compress_batch"); dc != CSK_OK) return dc;
   args.first[nz] = (int)total;
   args.n = nz;
   dim3 grid((unsigned)total), block(64);
@@ -528,6 +533,7 @@ int mxfp4_quantize(const void* x, int in_dtype, int64_t rows, int cols, uint8_t*
   const int rc = csk::check_quantize("mxfp4_quantize", x, in_dtype, rows, cols, codes, scales);
   if (rc != CSK_OK) return rc;
   if (rows == 0) return CSK_OK;
+  if (const int dc = csk::check_device("mxfp4_quantize"); dc != CSK_OK) return dc;
   const int64_t total = rows * (cols / 2);
   dim3 grid((unsigned)csk::ceil_div(total, 256)), block(256);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -900,6 +900,7 @@ int indexer_topk(const void* q, const uint8_t* q_scale, const float* w, const vo
   if (p.n_slices > 1024) return fail(CSK_EUNSUPPORTED, "indexer_topk: Nmax too large");
   if (!workspace || ws_bytes < p.total)
     return fail(CSK_EWORKSPACE, "indexer_topk: workspace smaller than indexer_topk_workspace_size()");
+  if (const int dc = check_device("indexer_topk"); dc != CSK_OK) return dc;
   char* ws = reinterpret_cast<char*>(workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int R = B * T;

@@ -14,8 +14,14 @@
  * --------------------------------
  * - Pointers: every tensor pointer is a DEVICE pointer (hipMalloc'd or a
  *   torch CUDA tensor's data_ptr) to a dense row-major array, 4-byte aligned
- *   (16-byte alignment is faster). The caller owns every buffer; the library
- *   never allocates, frees or keeps pointers after the call returns.
+ *   (16-byte alignment is faster). The caller owns every buffer; the compute
+ *   calls never allocate or free device memory and keep no pointer or other
+ *   state between calls (the one exception is the opt-in measurement hook
+ *   csk_kernel_timer_arm, which keeps the caller's event arrays until
+ *   csk_kernel_timer_disarm).
+ * - Device: the calling thread's current HIP device must be a gfx950
+ *   (MI355X); any other device, or none, makes a call that would launch
+ *   return CSK_EUNSUPPORTED (argument errors are reported first).
  * - Streams: `stream` is a hipStream_t (NULL = the default stream). Every
  *   call only enqueues kernels on it and returns without synchronising, so
  *   a non-zero return code reports argument errors and launch failures, not
@@ -29,10 +35,17 @@
  *   plus one E8M0 scale byte (2^(byte-127)) per 32 consecutive elements.
  * - Errors: every call returns CSK_OK (0) or a negative code and leaves a
  *   message for csk_last_error() (thread-local). Nothing aborts or prints.
- * - Determinism: results are bitwise reproducible run to run (no floating-
- *   point atomics on any result path).
- * - Rounding: floating-point results are computed in fp32 and rounded once
- *   to the output dtype (round to nearest even).
+ * - Determinism: results are bitwise reproducible run to run for the same
+ *   arguments (no floating-point atomics on any result path). The attention
+ *   calls' max_workgroups argument decides how a row is split, so results
+ *   are reproducible for a fixed value of it.
+ * - Rounding: compression and MXFP4 encoding compute in fp32 and round once
+ *   to the output dtype (round to nearest even). Attention computes logits,
+ *   softmax sums and outputs in fp32; with bf16 data its intermediates are
+ *   bf16 where the matrix cores take them: the rotated query, the
+ *   probabilities entering the P.V product, and (rows split over several
+ *   workgroups) the partial outputs, which the merge combines in fp32 before
+ *   the final rounding.
  */
 #ifndef CSK_H
 #define CSK_H
@@ -59,7 +72,7 @@ const char* csk_last_error(void);
 
 /* ABI revision of this header (incremented on incompatible change). */
 int csk_abi_version(void);
-#define CSK_ABI_VERSION 1
+#define CSK_ABI_VERSION 2
 
 /*
  * csa_compress - CSA compression ([P1] «CSA: сжать в 4 раза и выбрать
@@ -226,14 +239,24 @@ size_t indexer_topk_workspace_size(int B, int T, int HI, int dI, int Nmax, int k
  *   sink    : [H] fp32 or NULL (no sink).
  *   dtype   : CSK_BF16 (fp32 accumulation) or CSK_F32.
  *   out     : [B,T,H,dv] dtype;  lse: [B,T,H] fp32 or NULL.
- *   workspace: >= sparse_attn_workspace_size(...).
+ *   max_workgroups: scheduling cap (>= 0). A launch over fewer query rows
+ *             than the chip has CUs splits each row's candidates over
+ *             several workgroups, about one per CU by default (0); a value
+ *             > 0 caps that split at max_workgroups workgroups in all (a row
+ *             never gets fewer than one), so that a caller running other
+ *             work beside the call on another stream can leave CUs to it.
+ *             The split decides the order in which partial results are
+ *             combined, so it is part of what the result bits depend on; a
+ *             smaller cap never needs a larger workspace.
+ *   workspace: >= sparse_attn_workspace_size(..., max_workgroups).
  */
 int sparse_attn(const void* q, const int32_t* q_pos, const void* kv_c, int Nmax,
                 const int32_t* idx, int k, const void* kv_w, const int32_t* w_pos0, int S_w,
                 int W, const float* sink, int B, int T, int H, int D, int dv, int d_rope,
-                float rope_base, float scale, int dtype, void* out, float* lse, void* workspace,
-                size_t ws_bytes, void* stream);
-size_t sparse_attn_workspace_size(int B, int T, int H, int D, int dv, int k, int W, int dtype);
+                float rope_base, float scale, int dtype, void* out, float* lse,
+                int max_workgroups, void* workspace, size_t ws_bytes, void* stream);
+size_t sparse_attn_workspace_size(int B, int T, int H, int D, int dv, int k, int W, int dtype,
+                                  int max_workgroups);
 
 /*
  * dense_compressed_attn - HCA attention ([P1] «HCA…»: attention over the
@@ -246,33 +269,21 @@ int dense_compressed_attn(const void* q, const int32_t* q_pos, const void* kv_c,
                           const int32_t* n_entries, int m, const void* kv_w,
                           const int32_t* w_pos0, int S_w, int W, const float* sink, int B, int T,
                           int H, int D, int dv, int d_rope, float rope_base, float scale,
-                          int dtype, void* out, float* lse, void* workspace, size_t ws_bytes,
-                          void* stream);
+                          int dtype, void* out, float* lse, int max_workgroups, void* workspace,
+                          size_t ws_bytes, void* stream);
 size_t dense_compressed_attn_workspace_size(int B, int T, int H, int D, int dv, int Nmax, int m,
-                                            int W, int dtype);
+                                            int W, int dtype, int max_workgroups);
 
 /*
- * csk_set_attn_workgroups - scheduling knob for split-row attention. A
- * launch of sparse_attn or dense_compressed_attn over fewer query rows than
- * the chip has CUs splits each row into runs of candidate tiles, by default
- * about one workgroup per CU (256); each such workgroup holds a whole CU
- * while it runs. max_workgroups > 0 caps that split at max_workgroups
- * workgroups in all (rows are never split below one workgroup each), so a
- * caller that runs other work on another stream at the same time can leave
- * CUs to it; 0 restores the default. The setting is per calling thread and
- * applies to the launches and *_workspace_size calls made after it (a
- * smaller cap never needs more workspace than the default). Returns the
- * previous value, or -1 with csk_last_error() set for a negative argument.
- */
-int csk_set_attn_workgroups(int max_workgroups);
-
-/*
- * csk_kernel_timer_arm - measurement hook. The next n launches of the
- * library kernel named `kernel` ("indexer_scores_fp4", "attn_bf16", ...)
- * are each bracketed by hipEventRecord(ev_start[j]) / hipEventRecord(
- * ev_stop[j]) on the launch stream. The events are caller-created
- * hipEvent_t handles. csk_kernel_timer_count() returns how many launches
- * were recorded; csk_kernel_timer_disarm() stops recording.
+ * csk_kernel_timer_arm - opt-in measurement hook (process-wide, one armed
+ * timer at a time). The next n launches of the library kernel named
+ * `kernel` ("indexer_scores_fp4", "attn_bf16_sparse", ...) are each
+ * bracketed by hipEventRecord(ev_start[j]) / hipEventRecord(ev_stop[j]) on
+ * the launch stream. The events are caller-created hipEvent_t handles; the
+ * library keeps the two arrays (not copies) until csk_kernel_timer_disarm(),
+ * so they must stay valid until then. csk_kernel_timer_count() returns how
+ * many launches were recorded. While no timer is armed a launch reads one
+ * atomic flag and nothing else.
  */
 int csk_kernel_timer_arm(const char* kernel, void** ev_start, void** ev_stop, int n);
 int csk_kernel_timer_count(void);

@@ -38,9 +38,9 @@ def test_workspace_sizes(lib):
     assert lib.indexer_topk_workspace_size(1, 256, 2, 32, 64, 8, 0) >= 256 * 64 * 4
     assert lib.indexer_topk_workspace_size(0, 1, 1, 32, 1, 1, 0) == 0
     # prefill rows fit one chunk: no split-K partials
-    assert lib.sparse_attn_workspace_size(1, 65536, 64, 576, 512, 2048, 128, 1) == 0
+    assert lib.sparse_attn_workspace_size(1, 65536, 64, 576, 512, 2048, 128, 1, 0) == 0
     # decode splits the candidates: partial (m, l, o) per chunk
-    assert lib.dense_compressed_attn_workspace_size(4, 1, 64, 576, 512, 8192, 128, 128, 1) > 0
+    assert lib.dense_compressed_attn_workspace_size(4, 1, 64, 576, 512, 8192, 128, 128, 1, 0) > 0
 
 
 def test_argument_errors_without_device(lib):
@@ -54,22 +54,45 @@ def test_argument_errors_without_device(lib):
     rc = lib.mxfp4_quantize(fake, 7, ctypes.c_int64(4), 32, fake, fake, nul)
     assert rc == -2
     lib.csk_abi_version.restype = ctypes.c_int
-    assert lib.csk_abi_version() == 1
+    assert lib.csk_abi_version() == 2
 
 
 def test_attn_workgroup_cap(lib):
-    # host-side plan only: the cap shrinks the split (and its workspace) and
-    # is restored; a negative cap is rejected
-    lib.csk_set_attn_workgroups.restype = ctypes.c_int
+    # host-side plan only: the per-call cap shrinks the split (and its
+    # workspace); a negative cap is rejected by the workspace query (0) and
+    # by the call itself before anything else is checked against a device
     lib.csk_last_error.restype = ctypes.c_char_p
     lib.dense_compressed_attn_workspace_size.restype = ctypes.c_size_t
-    full = lib.dense_compressed_attn_workspace_size(4, 1, 64, 576, 512, 8192, 128, 128, 1)
-    assert lib.csk_set_attn_workgroups(64) == 0
-    capped = lib.dense_compressed_attn_workspace_size(4, 1, 64, 576, 512, 8192, 128, 128, 1)
+    lib.sparse_attn_workspace_size.restype = ctypes.c_size_t
+    full = lib.dense_compressed_attn_workspace_size(4, 1, 64, 576, 512, 8192, 128, 128, 1, 0)
+    capped = lib.dense_compressed_attn_workspace_size(4, 1, 64, 576, 512, 8192, 128, 128, 1, 64)
     assert 0 < capped < full
-    assert lib.csk_set_attn_workgroups(-3) == -1 and b"negative" in lib.csk_last_error()
-    assert lib.csk_set_attn_workgroups(0) == 64
-    assert lib.dense_compressed_attn_workspace_size(4, 1, 64, 576, 512, 8192, 128, 128, 1) == full
+    # the same query twice gives the same answer: no state carried between calls
+    assert lib.dense_compressed_attn_workspace_size(4, 1, 64, 576, 512, 8192, 128, 128, 1, 0) == full
+    assert lib.dense_compressed_attn_workspace_size(4, 1, 64, 576, 512, 8192, 128, 128, 1, -1) == 0
+    # four workgroups over four rows: every row whole, no partials
+    assert lib.sparse_attn_workspace_size(4, 1, 64, 576, 512, 2048, 128, 1, 4) == 0
+    assert lib.sparse_attn_workspace_size(4, 1, 64, 576, 512, 2048, 128, 1, 0) > 0
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.sparse_attn.argtypes = ([vp, vp, vp, i, vp, i, vp, vp, i, i, vp] + [i] * 6
+                                + [f, f, i, vp, vp, i, vp, ctypes.c_size_t, vp])
+    fake = 4096
+    rc = lib.sparse_attn(fake, fake, fake, 100, fake, 8, None, None, 0, 0, None, 1, 1, 64, 576, 512, 64,
+                         10000.0, 0.05, 1, fake, None, -5, None, 0, None)
+    assert rc == -1 and b"max_workgroups" in lib.csk_last_error()
+
+
+def test_no_device_is_unsupported(lib):
+    # valid arguments on a host without a HIP device: the call stops at the
+    # device check with CSK_EUNSUPPORTED (never launches). Skipped where a
+    # GPU is visible: there the call would run on the fake pointers.
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    lib.csk_last_error.restype = ctypes.c_char_p
+    fake = ctypes.c_void_p(4096)
+    rc = lib.mxfp4_quantize(fake, 0, ctypes.c_int64(4), 32, fake, fake, None)
+    assert rc == -2 and b"gfx950" in lib.csk_last_error()
 
 
 def test_compress_job_layout(tmp_path):

@@ -29,7 +29,7 @@ def _check(got, ref, bf16, what):
         check_f32(got, ref, 1e-5, what)
 
 
-def _sparse_case(seed, B, T, H, D, dv, N, k, S_w, W, bf16, d_rope, sink=True, decode=False):
+def _sparse_case(seed, B, T, H, D, dv, N, k, S_w, W, bf16, d_rope, sink=True, decode=False, max_workgroups=0):
     g = synth.rng(seed)
     q, kv_c, kv_w = _inputs(g, B, T, H, D, N, S_w, bf16)
     if decode:
@@ -47,7 +47,7 @@ def _sparse_case(seed, B, T, H, D, dv, N, k, S_w, W, bf16, d_rope, sink=True, de
     sk = synth.normal(g, (H,)) if sink else None
     scale = float(np.float32(1.0 / np.sqrt(D)))
     out, lse = csk.sparse_attn(dev(q), dev(q_pos), dev(kv_c), dev(idx), dev(kv_w), dev(w_pos0), W,
-                               None if sk is None else dev(sk), dv, d_rope, scale)
+                               None if sk is None else dev(sk), dv, d_rope, scale, max_workgroups=max_workgroups)
     rout, rlse = oracle.sparse_attn(q, q_pos, kv_c, idx, kv_w, w_pos0, W, sk, dv, d_rope, scale)
     _check(host(out).reshape(-1, H, dv), rout, bf16, "out")
     check_f32(host(lse).reshape(-1, H), rlse, 2e-2 if bf16 else 1e-5, "lse")
@@ -75,12 +75,8 @@ def test_sparse_decode_workgroup_cap(cap):
     # the sparse split capped: 4 workgroups over 4 rows (each row whole in
     # one workgroup, no merge) and 40 (ten runs of three or four tiles a
     # row, merged)
-    prev = csk.set_attn_workgroups(cap)
-    try:
-        _sparse_case(770 + cap, B=4, T=1, H=64, D=576, dv=512, N=5000, k=2048, S_w=128, W=128, bf16=True,
-                     d_rope=64, decode=True)
-    finally:
-        csk.set_attn_workgroups(prev)
+    _sparse_case(770 + cap, B=4, T=1, H=64, D=576, dv=512, N=5000, k=2048, S_w=128, W=128, bf16=True,
+                 d_rope=64, decode=True, max_workgroups=cap)
 
 
 @pytest.mark.parametrize("D,dv", [(576, 512), (256, 256), (128, 128), (64, 64)])
@@ -105,7 +101,7 @@ def test_sparse_no_sink_no_window_and_empty():
     assert np.all(o[0, 0] == 0) and np.all(np.isneginf(host(lse)[0, 0]))   # no candidate, no sink
 
 
-def _dense_case(seed, B, T, H, D, dv, N, m, S_w, W, bf16, d_rope, decode, q_pos=None):
+def _dense_case(seed, B, T, H, D, dv, N, m, S_w, W, bf16, d_rope, decode, q_pos=None, max_workgroups=0):
     g = synth.rng(seed)
     q, kv_c, kv_w = _inputs(g, B, T, H, D, N, S_w, bf16)
     if q_pos is not None:
@@ -120,7 +116,7 @@ def _dense_case(seed, B, T, H, D, dv, N, m, S_w, W, bf16, d_rope, decode, q_pos=
     sk = synth.normal(g, (H,))
     scale = float(np.float32(1.0 / np.sqrt(D)))
     out, lse = csk.dense_compressed_attn(dev(q), dev(q_pos), dev(kv_c), dev(ne), m, dev(kv_w), dev(w_pos0), W,
-                                         dev(sk), dv, d_rope, scale)
+                                         dev(sk), dv, d_rope, scale, max_workgroups=max_workgroups)
     rows = None
     if B * T > 600:
         rows = [(b, t) for b in range(B) for t in list(range(0, T, 37)) + [T - 1]]
@@ -188,12 +184,8 @@ def test_dense_few_query_rows():
 
 def test_dense_decode_workgroup_cap():
     # the split capped at 8 workgroups: two runs of about 25 tiles per row
-    prev = csk.set_attn_workgroups(8)
-    try:
-        _dense_case(760, B=4, T=1, H=64, D=576, dv=512, N=3000, m=128, S_w=128, W=128, bf16=True, d_rope=64,
-                    decode=True)
-    finally:
-        csk.set_attn_workgroups(prev)
+    _dense_case(760, B=4, T=1, H=64, D=576, dv=512, N=3000, m=128, S_w=128, W=128, bf16=True, d_rope=64,
+                decode=True, max_workgroups=8)
 
 
 @pytest.mark.parametrize("B,N", [(2, 16384), (4, 8192)])
@@ -223,3 +215,36 @@ def test_sparse_all_visible_equals_dense():
     d, dl = csk.dense_compressed_attn(dev(q), dev(q_pos), dev(kv_c), dev(np.array([N], np.int32)), m, dev(kv_w),
                                       dev(w_pos0), 128, dev(sk), 512, 64, 1 / 24)
     check_bf16_attention(host(a), host(d), "sparse vs dense")
+
+
+def _launches(kernel, fn):
+    """Runs fn() with the library's launch timer armed for `kernel` and
+    returns how many launches of that kernel it made."""
+    tm = csk.KernelTimer(kernel, 16)
+    try:
+        fn()
+        torch.cuda.synchronize()
+        return tm.count()
+    finally:
+        tm.disarm()
+
+
+@pytest.mark.parametrize("H,D,dv", [(16, 128, 128), (32, 576, 512), (48, 576, 576)])
+def test_sparse_whole_rows_stream_kernel(H, D, dv):
+    # fewer than 64 heads with short candidate lists over 300 rows: rows stay
+    # whole in one workgroup of the streamed-tile kernel (attn_bf16_stream);
+    # the launch timer confirms which kernel ran
+    n = _launches("attn_bf16_stream", lambda: _sparse_case(
+        780 + H, B=2, T=150, H=H, D=D, dv=dv, N=400, k=96, S_w=200, W=24, bf16=True, d_rope=64))
+    assert n == 1
+
+
+@pytest.mark.parametrize("H,D,T", [(16, 128, 8), (32, 576, 20)])
+def test_dense_few_rows_stream_kernel(H, D, T):
+    # dense rows the query-tile kernel does not take (fewer than 16 rows, or
+    # D = 576 with fewer than 64 heads) over many sequences: whole rows in the
+    # streamed-tile kernel
+    dv = 128 if D == 128 else 512
+    n = _launches("attn_bf16_stream", lambda: _dense_case(
+        790 + H, B=40, T=T, H=H, D=D, dv=dv, N=60, m=4, S_w=240, W=32, bf16=True, d_rope=64, decode=False))
+    assert n == 1

@@ -7,6 +7,7 @@ import pytest
 
 import oracle
 import synth
+from mx_regime import assert_in_regime, pair_spread_exact
 from util import dev, host
 
 pytestmark = pytest.mark.gpu
@@ -26,6 +27,7 @@ def _mx_both(x):
 def _run_mx(qI, kI, w, q_pos, n_entries, m, k):
     (gqc, gqs), (rqc, rqs) = _mx_both(qI)
     (gkc, gks), (rkc, rks) = _mx_both(kI)
+    assert_in_regime(rqc, rqs, rkc, rks)
     idx, sc = csk.indexer_topk(gqc, dev(w), gkc, dev(q_pos), dev(n_entries), m, k, q_scale=gqs, k_scale=gks)
     ridx, rsc = oracle.indexer_topk(rqc, w, rkc, q_pos, n_entries, m, k, q_scale=rqs, k_scale=rks)
     B, T = q_pos.shape
@@ -103,3 +105,42 @@ def test_invalid_arguments_raise():
     with pytest.raises(csk.CskError):
         csk.indexer_topk(q, dev(np.ones((1, 1, 2), np.float32)), dev(synth.normal(g, (1, 4, 32))),
                          dev(np.zeros((1, 1), np.int32)), dev(np.ones(1, np.int32)), 0, 4)
+
+
+@pytest.mark.parametrize("spread", [6, 8, 9])
+def test_mxfp4_bit_exact_at_exponent_spread(spread):
+    # Operands built byte by byte so that the four tile exponents of a
+    # (query head, key) pair span up to `spread` binades, the edge of the
+    # exactness regime at 9, with the largest tile products where the
+    # exponent is highest (tile 1 of both operands all +-6). Every score of
+    # every row is returned (k = N) and must equal the oracle's bit for bit.
+    g = synth.rng(530 + spread)
+    B, T, HI, dI, N, m = 1, 3, 64, 128, 512, 4
+    G = dI // 32
+    qc = g.integers(0, 256, (B, T, HI, dI // 2), dtype=np.uint8)
+    kc = g.integers(0, 256, (B, N, dI // 2), dtype=np.uint8)
+    qc[..., 16:32] = 0x77                                        # +6, +6
+    kc[..., 16:32] = np.where(g.random((B, N, 1)) < 0.5, 0x77, 0xFF).astype(np.uint8)  # +-6
+    aq_max = spread // 2
+    aq = g.integers(0, aq_max + 1, (B, T, HI))
+    aq[..., 0] = aq_max
+    ak = g.integers(0, spread - aq_max + 1, (B, N))
+    ak[..., 0] = spread - aq_max
+    qs = np.empty((B, T, HI, G), np.int64)
+    ks = np.empty((B, N, G), np.int64)
+    qs[..., 0], qs[..., 1] = 124, 124 + aq
+    ks[..., 0], ks[..., 1] = 125, 125 + ak
+    for t in (2, 3):
+        qs[..., t] = 124 + (g.random((B, T, HI)) * (aq + 1)).astype(np.int64)
+        ks[..., t] = 125 + (g.random((B, N)) * (ak + 1)).astype(np.int64)
+    qs, ks = qs.astype(np.uint8), ks.astype(np.uint8)
+    assert pair_spread_exact(qc, qs, kc, ks) == spread
+    assert_in_regime(qc, qs, kc, ks)
+    w = synth.normal(g, (B, T, HI), 1.0 / HI)
+    q_pos = np.full((B, T), 4 * N - 1, np.int32)
+    ne = np.array([N], np.int32)
+    idx, sc = csk.indexer_topk(dev(qc), dev(w), dev(kc), dev(q_pos), dev(ne), m, N, q_scale=dev(qs),
+                               k_scale=dev(ks))
+    ridx, rsc = oracle.indexer_topk(qc, w, kc, q_pos, ne, m, N, q_scale=qs, k_scale=ks)
+    _assert_same(host(idx).reshape(B * T, N), host(sc).reshape(B * T, N), ridx, rsc)
+    assert np.all(ridx == np.arange(N)[None])

@@ -140,3 +140,35 @@ def test_lse_matches_logsumexp():
         Q = _rope_complex(q[0, 0, h], 500, 8)
         l = 0.17 * (kv_c[0, [0, 3, 9, 11, 29]].astype(np.float64) @ Q)
         assert abs(lse[0, h] - scipy_special.logsumexp(np.append(l, np.float64(sink[h])))) < 1e-12
+
+
+def test_value_slice_is_the_leading_dv_dims():
+    # With dv < D (the 512 + 64 latent layout: keys span all D dims, values
+    # are the first dv of them) the closed forms pin which dims are values:
+    # a single candidate gives p * K[:dv] and q = 0 gives sum K[:dv] / (n +
+    # e^sink). The trailing dims differ from the leading ones here, so taking
+    # the last dv dims, or all D, fails both.
+    g, q, kv_c, kv_w, q_pos, w_pos0, sink = _problem(47, B=1, T=1, D=32)
+    D, dv, dr = q.shape[-1], 20, 8
+    q_pos = np.array([[900]], np.int32)
+    idx1 = np.array([[[6]]], np.int32)
+    out, lse = oracle.sparse_attn(q, q_pos, kv_c, idx1, None, None, 0, sink, dv, dr, 0.3)
+    assert out.shape[-1] == dv
+    K = kv_c[0, 6].astype(np.float64)
+    assert np.abs(K[:dv] - K[D - dv:]).max() > 0.1
+    for h in range(q.shape[2]):
+        l = 0.3 * (_rope_complex(q[0, 0, h], 900, dr) @ K)
+        p = np.exp(l) / (np.exp(l) + np.exp(np.float64(sink[h])))
+        np.testing.assert_allclose(out[0, h], p * K[:dv], atol=1e-13)
+        assert abs(lse[0, h] - np.logaddexp(l, np.float64(sink[h]))) < 1e-12
+    idx = np.array([[[1, 4, 11, 17]]], np.int32)
+    out, lse = oracle.sparse_attn(np.zeros_like(q), q_pos, kv_c, idx, None, None, 0, sink, dv, dr, 0.3)
+    V = kv_c[0, [1, 4, 11, 17]].astype(np.float64)
+    for h in range(q.shape[2]):
+        ref = V[:, :dv].sum(axis=0) / (4 + np.exp(np.float64(sink[h])))
+        np.testing.assert_allclose(out[0, h], ref, atol=1e-13)
+    # dense attention slices the same way: one visible entry, no window
+    dout, _ = oracle.dense_attn(np.zeros_like(q), np.array([[3]], np.int32), kv_c, np.array([30], np.int32), 4,
+                                None, None, 0, None, dv, dr, 0.3)
+    np.testing.assert_allclose(dout[0], np.broadcast_to(kv_c[0, 0, :dv].astype(np.float64), dout[0].shape),
+                               atol=1e-13)

@@ -57,3 +57,11 @@ def check_f32(got, ref, tol=1e-5, what=""):
     err = np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))
     assert err.max() <= tol, f"{what}: max-abs {err.max():.3e}"
     return err.max()
+
+
+def report_margin(what, max_abs, rel_l2):
+    """Prints the measured error of a parity comparison beside its bar."""
+    line = f"[margin] {what}: max-abs {max_abs:.3e}"
+    if rel_l2 is not None:
+        line += f" (bar 2e-2), rel-L2 {rel_l2:.3e} (bar 1e-2)"
+    print(line, flush=True)
