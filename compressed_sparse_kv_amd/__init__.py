@@ -45,6 +45,7 @@ def lib():
         L.indexer_topk.argtypes = [_vp] * 7 + [_i] * 8 + [_vp, _vp, _vp, _sz, _vp]
         L.indexer_topk_workspace_size.argtypes = [_i] * 7
         L.indexer_topk_workspace_size.restype = _sz
+        L.indexer_topk_noalloc.argtypes = [_vp] * 7 + [_i] * 8 + [_vp, _vp, _vp]
         L.sparse_attn.argtypes = ([_vp, _vp, _vp, _i, _vp, _i, _vp, _vp, _i, _i, _vp] + [_i] * 6
                                   + [_f, _f, _i, _vp, _vp, _i, _vp, _sz, _vp])
         L.dense_compressed_attn.argtypes = ([_vp, _vp, _vp, _i, _vp, _i, _vp, _vp, _i, _i, _vp] + [_i] * 6
@@ -234,6 +235,25 @@ def indexer_topk(q, w, kk, q_pos, n_entries, m, k, q_scale=None, k_scale=None, i
                             _ptr(n_entries), B, T, HI, dI, Nmax, m, k, dtype, _ptr(idx), _ptr(score),
                             _ptr(workspace), workspace.numel(), _stream())
     _check(rc, "indexer_topk")
+    return idx, score
+
+
+def indexer_topk_noalloc(q, w, kk, q_pos, n_entries, m, k, q_scale=None, k_scale=None, idx=None, score=None,
+                         with_score=True):
+    """indexer_topk without a workspace: the library's static device
+    scratch serves instead (see indexer_topk_noalloc in csk.h; calls that
+    overlap on one device race). Returns (idx, score or None)."""
+    B, T, HI = w.shape
+    mx = q_scale is not None
+    dI = q.shape[-1] * 2 if mx else q.shape[-1]
+    if idx is None:
+        idx = torch.empty((B, T, k), dtype=torch.int32, device=w.device)
+    if score is None and with_score:
+        score = torch.empty((B, T, k), dtype=torch.float32, device=w.device)
+    rc = lib().indexer_topk_noalloc(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(kk), _ptr(k_scale), _ptr(q_pos),
+                                    _ptr(n_entries), B, T, HI, dI, kk.shape[1], m, k,
+                                    CSK_MXFP4 if mx else CSK_F32, _ptr(idx), _ptr(score), _stream())
+    _check(rc, "indexer_topk_noalloc")
     return idx, score
 
 

@@ -32,6 +32,7 @@
 // per-slice candidate lists in index order, and the same range select
 // finishes.
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "common.h"
@@ -868,39 +869,77 @@ static IdxPlan plan_indexer(int B, int T, int Nmax, int k) {
   return p;
 }
 
-}  // namespace csk
+// Scratch of indexer_topk_noalloc: one copy per device, in the code object's
+// zero-initialised data (no allocation at call time). Host code never passes
+// this name to a kernel: it stands for a host-side shadow, not the device
+// address. The device address comes from hipGetSymbolAddress, once per
+// device, and is kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[CSK_NOALLOC_SCRATCH_BYTES];
 
-extern "C" {
+constexpr int SCRATCH_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static std::atomic<void*> g_scratch_ptr[SCRATCH_DEVICES];
 
-size_t indexer_topk_workspace_size(int B, int T, int HI, int dI, int Nmax, int k, int dtype) {
-  (void)HI; (void)dI; (void)dtype;
-  if (B <= 0 || T <= 0 || Nmax <= 0 || k <= 0) return 0;
-  return csk::plan_indexer(B, T, Nmax, k).total;
+// The calling thread's current device's scratch address (looked up on the
+// first call on that device).
+static int scratch_on_device(const char* fn, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(CSK_EUNSUPPORTED, std::string(fn) + ": no HIP device is visible");
+  }
+  if (dev >= SCRATCH_DEVICES)
+    return fail(CSK_EUNSUPPORTED, std::string(fn) + ": device index " + std::to_string(dev) + " past 63");
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return fail(CSK_EHIP, std::string(fn) + ": hipGetSymbolAddress(scratch) failed: " + hipGetErrorString(e));
+      }
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return CSK_OK;
 }
 
-int indexer_topk(const void* q, const uint8_t* q_scale, const float* w, const void* kk,
-                 const uint8_t* k_scale, const int32_t* q_pos, const int32_t* n_entries, int B,
-                 int T, int HI, int dI, int Nmax, int m, int k, int dtype, int32_t* idx,
-                 float* score, void* workspace, size_t ws_bytes, void* stream) {
-  using namespace csk;
+static int indexer_topk_impl(const char* fn, bool noalloc, const void* q, const uint8_t* q_scale,
+                             const float* w, const void* kk, const uint8_t* k_scale,
+                             const int32_t* q_pos, const int32_t* n_entries, int B, int T, int HI,
+                             int dI, int Nmax, int m, int k, int dtype, int32_t* idx, float* score,
+                             void* workspace, size_t ws_bytes, void* stream) {
   clear_error();
+  const std::string f(fn);
   if (!q || !w || !kk || !q_pos || !n_entries || !idx)
-    return fail(CSK_EINVAL, "indexer_topk: null pointer");
+    return fail(CSK_EINVAL, f + ": null pointer");
   if (B <= 0 || T <= 0 || HI <= 0 || dI <= 0 || Nmax <= 0 || m <= 0 || k <= 0)
-    return fail(CSK_EINVAL, "indexer_topk: sizes must be positive");
+    return fail(CSK_EINVAL, f + ": sizes must be positive");
   if (dtype != CSK_MXFP4 && dtype != CSK_F32)
-    return fail(CSK_EUNSUPPORTED, "indexer_topk: dtype must be CSK_MXFP4 or CSK_F32");
+    return fail(CSK_EUNSUPPORTED, f + ": dtype must be CSK_MXFP4 or CSK_F32");
   if (dtype == CSK_MXFP4 && (dI % 32 || !q_scale || !k_scale))
-    return fail(CSK_EINVAL, "indexer_topk: MXFP4 needs dI % 32 == 0 and both scale arrays");
+    return fail(CSK_EINVAL, f + ": MXFP4 needs dI % 32 == 0 and both scale arrays");
   if (dtype == CSK_MXFP4 && (reinterpret_cast<uintptr_t>(k_scale) & 3))
-    return fail(CSK_EINVAL, "indexer_topk: k_scale must be 4-byte aligned (read as dwords)");
+    return fail(CSK_EINVAL, f + ": k_scale must be 4-byte aligned (read as dwords)");
   if ((int64_t)B * T > (1LL << 30) || ceil_div(Nmax, 256 * IDX_MIN_ITERS) > 65535)
-    return fail(CSK_EUNSUPPORTED, "indexer_topk: B*T or Nmax too large");
+    return fail(CSK_EUNSUPPORTED, f + ": B*T or Nmax too large");
   IdxPlan p = plan_indexer(B, T, Nmax, k);
-  if (p.n_slices > 1024) return fail(CSK_EUNSUPPORTED, "indexer_topk: Nmax too large");
-  if (!workspace || ws_bytes < p.total)
-    return fail(CSK_EWORKSPACE, "indexer_topk: workspace smaller than indexer_topk_workspace_size()");
-  if (const int dc = check_device("indexer_topk"); dc != CSK_OK) return dc;
+  if (p.n_slices > 1024) return fail(CSK_EUNSUPPORTED, f + ": Nmax too large");
+  if (noalloc) {
+    if (p.total > (size_t)CSK_NOALLOC_SCRATCH_BYTES)
+      return fail(CSK_EWORKSPACE, f + ": needs " + std::to_string(p.total) +
+                                      " bytes of scratch; the static scratch holds " +
+                                      std::to_string((size_t)CSK_NOALLOC_SCRATCH_BYTES));
+  } else if (!workspace || ws_bytes < p.total) {
+    return fail(CSK_EWORKSPACE, f + ": workspace smaller than indexer_topk_workspace_size()");
+  }
+  if (const int dc = check_device(f); dc != CSK_OK) return dc;
+  if (noalloc) {
+    if (const int sc = scratch_on_device(fn, &workspace); sc != CSK_OK) return sc;
+  }
   char* ws = reinterpret_cast<char*>(workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int R = B * T;
@@ -976,6 +1015,32 @@ int indexer_topk(const void* q, const uint8_t* q_scale, const float* w, const vo
     rc = launch("topk_select", topk_select_kernel<false>, dim3(R), dim3(TOPK_THREADS), lds, s, ta);
   }
   return rc;
+}
+
+}  // namespace csk
+
+extern "C" {
+
+size_t indexer_topk_workspace_size(int B, int T, int HI, int dI, int Nmax, int k, int dtype) {
+  (void)HI; (void)dI; (void)dtype;
+  if (B <= 0 || T <= 0 || Nmax <= 0 || k <= 0) return 0;
+  return csk::plan_indexer(B, T, Nmax, k).total;
+}
+
+int indexer_topk(const void* q, const uint8_t* q_scale, const float* w, const void* kk,
+                 const uint8_t* k_scale, const int32_t* q_pos, const int32_t* n_entries, int B,
+                 int T, int HI, int dI, int Nmax, int m, int k, int dtype, int32_t* idx,
+                 float* score, void* workspace, size_t ws_bytes, void* stream) {
+  return csk::indexer_topk_impl("indexer_topk", false, q, q_scale, w, kk, k_scale, q_pos, n_entries, B, T, HI,
+                                dI, Nmax, m, k, dtype, idx, score, workspace, ws_bytes, stream);
+}
+
+int indexer_topk_noalloc(const void* q, const uint8_t* q_scale, const float* w, const void* kk,
+                         const uint8_t* k_scale, const int32_t* q_pos, const int32_t* n_entries, int B,
+                         int T, int HI, int dI, int Nmax, int m, int k, int dtype, int32_t* idx,
+                         float* score, void* stream) {
+  return csk::indexer_topk_impl("indexer_topk_noalloc", true, q, q_scale, w, kk, k_scale, q_pos, n_entries, B,
+                                T, HI, dI, Nmax, m, k, dtype, idx, score, nullptr, 0, stream);
 }
 
 }  // extern "C"

@@ -217,6 +217,31 @@ int indexer_topk(const void* q, const uint8_t* q_scale, const float* w, const vo
 size_t indexer_topk_workspace_size(int B, int T, int HI, int dI, int Nmax, int k, int dtype);
 
 /*
+ * indexer_topk_noalloc - indexer_topk for callers that cannot allocate:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments and results as indexer_topk (the same kernels,
+ * bit for bit), without the workspace: the scratch lives in a static
+ * device array of CSK_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * device it has run on until the process ends. The call allocates and
+ * frees nothing and needs no zeroed memory.
+ *   Limit: indexer_topk_workspace_size(B,T,HI,dI,Nmax,k,dtype) must not
+ *   exceed CSK_NOALLOC_SCRATCH_BYTES (32 MiB: 1M-context decode at batch 4,
+ *   128K-context decode at batch 32); larger problems return
+ *   CSK_EWORKSPACE before anything is launched.
+ *   Concurrency: every call on one device shares that device's scratch, so
+ *   calls that overlap in time on one device (other streams, other threads)
+ *   race and must be serialised by the caller; calls on one stream are
+ *   ordered and safe.
+ *   Set-up: the first call on a device looks up the scratch address
+ *   (hipGetSymbolAddress) with that device current.
+ */
+#define CSK_NOALLOC_SCRATCH_BYTES (32u << 20)
+int indexer_topk_noalloc(const void* q, const uint8_t* q_scale, const float* w, const void* kk,
+                         const uint8_t* k_scale, const int32_t* q_pos, const int32_t* n_entries, int B,
+                         int T, int HI, int dI, int Nmax, int m, int k, int dtype, int32_t* idx,
+                         float* score, void* stream);
+
+/*
  * sparse_attn - CSA attention: MQA over the selected compressed entries, a
  * sliding window of uncompressed tokens and an attention sink ([P1] «CSA…»,
  * step 3: every compressed entry is both key and value for all query heads;
