@@ -164,12 +164,22 @@ __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
       qsc[t][s] = a.qs[qrow * (a.dI / 32) + s * 4 + kb];
     }
   }
-  // the row's head weights, one LDS copy per wave, read back as broadcast
-  // LDS reads (a global load here would be counted with the in-flight key
-  // loads, and waiting for it would drain them)
+  // the row's head weights: one LDS copy per wave, then made wave-uniform
+  // (readfirstlane) so that they sit in scalar registers for the whole
+  // kernel and the head chain's fma reads them directly (a global load in
+  // the loop would be counted with the in-flight key loads, and an LDS read
+  // per four heads would stall the chain on its latency)
   __shared__ __align__(16) float wsh[4][64];
   if (lane < HI) wsh[wave][lane] = a.w[(int64_t)r * HI + lane];
-  const float* wr = wsh[wave];
+  float wsc[4 * HT * 4];
+#pragma unroll
+  for (int i = 0; i < HT * 4; ++i) {
+    const float4 w4 = *reinterpret_cast<const float4*>(&wsh[wave][4 * i]);
+    wsc[4 * i] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(w4.x)));
+    wsc[4 * i + 1] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(w4.y)));
+    wsc[4 * i + 2] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(w4.z)));
+    wsc[4 * i + 3] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(w4.w)));
+  }
 
   // key fragments of one 64-key group: lane (rho, kb) holds bytes 16*kb..
   // of key 16*kt + rho in each of the four key tiles kt. The loads are
@@ -237,23 +247,19 @@ __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
       }
     }
 
-    // ascending head chain; the fences keep the weight reads next to their
-    // use (hoisted together they would hold 4*HI registers). ReLU as an
+    // ascending head chain, weights from scalar registers. ReLU as an
     // integer max on the bits: +0 for every negative value and for -0, the
     // value itself otherwise (a float max would also canonicalise each
     // value coming out of the lane swaps)
     float score = 0.0f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      asm volatile("" ::: "memory");
 #pragma unroll
       for (int t = 0; t < HT; ++t) {
-        const float4 w4 = *reinterpret_cast<const float4*>(wr + 4 * HT * g + 4 * t);
-        const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float v = __int_as_float(max(__float_as_int(d[g][t][j]), 0));
-          score = __builtin_fmaf(wv[j], v, score);
+          score = __builtin_fmaf(wsc[4 * HT * g + 4 * t + j], v, score);
         }
       }
     }
