@@ -50,6 +50,8 @@ def lib():
         L.csk_ref_indexer_scores.argtypes = ([_f32p, _u8p, _u8p, _f32p, _f32p, _u8p, _u8p, _i32p, _i32p]
                                              + [ctypes.c_int] * 7 + [_i32p, ctypes.c_int, _f32p, _i32p])
         L.csk_ref_topk.argtypes = [_f32p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _f32p]
+        L.csk_ref_scores_bf16.argtypes = [_f32p, ctypes.c_int64]
+        L.csk_ref_scores_bf16.restype = None
         attn_tail = ([_f32p, _i32p, ctypes.c_int, ctypes.c_int, _f32p] + [ctypes.c_int] * 6
                      + [ctypes.c_double, ctypes.c_double, _i32p, ctypes.c_int, _f64p, _f64p])
         L.csk_ref_sparse_attn.argtypes = [_f32p, _i32p, _f32p, ctypes.c_int, _i32p, ctypes.c_int] + attn_tail
@@ -218,8 +220,19 @@ def topk(scores, n_vis, k):
     return idx, out
 
 
-def indexer_topk(q, w, k_cache, q_pos, n_entries, m, topk_k, q_scale=None, k_scale=None, rows=None):
+def scores_bf16(scores):
+    """Indexer scores rounded once to bf16 (RNE), as float32 (a new array)."""
+    y = np.array(scores, dtype=np.float32, copy=True, order="C")
+    lib().csk_ref_scores_bf16(_p(y, ctypes.c_float), y.size)
+    return y
+
+
+def indexer_topk(q, w, k_cache, q_pos, n_entries, m, topk_k, q_scale=None, k_scale=None, rows=None,
+                 score_dtype=F32):
+    """Scores, then (score_dtype BF16) their bf16 rounding, then top-k."""
     s, nv = indexer_scores(q, w, k_cache, q_pos, n_entries, m, q_scale, k_scale, rows)
+    if score_dtype == BF16:
+        s = scores_bf16(s)
     return topk(s, nv, topk_k)
 
 

@@ -73,6 +73,11 @@ int csk_ref_indexer_scores(const float* qf, const uint8_t* qc, const uint8_t* qs
                            int dI, int Nmax, int m, int dtype, const int32_t* rows, int n_rows,
                            float* scores, int32_t* n_vis);
 
+/* BF16 indexer scores: each fp32 score rounded once to the nearest bf16
+ * (ties to even), in place. [P1] «FP4 с учётом квантования» (BF16 scores
+ * for the top-k). */
+void csk_ref_scores_bf16(float* scores, int64_t n);
+
 /* Top-k per row: the min(k, n_vis) highest scores, ties to the lower index,
  * returned in ascending index order and padded with -1 (score -inf).
  * scores: [n_rows, Nmax]; idx, out_scores: [n_rows, k]. */

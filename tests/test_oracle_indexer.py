@@ -2,6 +2,7 @@
 from fractions import Fraction
 
 import numpy as np
+import pytest
 
 import oracle
 import synth
@@ -122,3 +123,53 @@ def test_topk_degenerate_cases():
     assert idx.tolist() == [[0, 1, 3]]                      # -0 ties +0: lower index wins
     idx, _ = oracle.topk(np.ones((1, 4), np.float32), np.array([0], np.int32), 2)
     assert idx.tolist() == [[-1, -1]]
+
+
+def test_bf16_scores_round_like_a_library_cast():
+    # The BF16-score step rounds each fp32 score once to the nearest bf16,
+    # ties to even: the same bits as torch's float32 -> bfloat16 cast, on
+    # random magnitudes over 80 binades, exact halfway cases, zeros, -inf
+    # and subnormals.
+    torch = pytest.importorskip("torch")
+    g = synth.rng(36)
+    x = (g.standard_normal(20000) * np.exp(g.uniform(-28, 28, 20000))).astype(np.float32)
+    j = np.arange(-300, 300, dtype=np.int64)
+    mant = 128 + np.abs(j) % 127                    # a bf16 significand (8 bits)
+    halfway = ((mant + 0.5) * 2.0 ** (j % 40 - 27) * np.sign(j + 0.5)).astype(np.float32)
+    special = np.array([0.0, -0.0, -np.inf, 1e-40, -3e-39, 2.0 ** -126, 3.3895314e38], np.float32)
+    allx = np.concatenate([x, halfway, special])
+    got = oracle.scores_bf16(allx)
+    want = torch.from_numpy(allx.copy()).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # halfway cases go to the even neighbour: the low mantissa bit is 0
+    hb = got[len(x):len(x) + len(halfway)].view(np.uint32) >> 16
+    assert np.all((hb & 1) == 0)
+
+
+def test_bf16_scores_topk_ties_and_validity():
+    # Scores that differ only below bf16 precision become ties: the lower
+    # index wins. The bf16 selection is a valid top-k of the fp32 scores
+    # within twice the rounding error (|s - bf16(s)| <= 2^-9 |s|).
+    s = np.array([[1.0, 1.0 + 2 ** -12, 1.0 + 2 ** -11, 0.5, 1.0 + 2 ** -6, 2.0]], np.float32)
+    nv = np.array([6], np.int32)
+    idx32, _ = oracle.topk(s, nv, 3)
+    idxbf, scbf = oracle.topk(oracle.scores_bf16(s), nv, 3)
+    assert idx32.tolist() == [[2, 4, 5]]
+    assert idxbf.tolist() == [[0, 4, 5]]          # 1, 1+2^-12, 1+2^-11 all round to 1.0: 0 wins
+    assert scbf.tolist() == [[1.0, 1.015625, 2.0]]
+    g = synth.rng(37)
+    B, T, N, HI, dI, k = 1, 4, 3000, 8, 128, 200
+    qc, qs = _mx(synth.normal(g, (B, T, HI, dI)))
+    kc, ks = _mx(synth.normal(g, (B, N, dI)))
+    w = synth.normal(g, (B, T, HI), 1.0 / HI)
+    q_pos = np.full((B, T), 4 * N - 1, np.int32)
+    sc, nv = oracle.indexer_scores(qc, w, kc, q_pos, np.array([N], np.int32), 4, q_scale=qs, k_scale=ks)
+    ib, _ = oracle.indexer_topk(qc, w, kc, q_pos, np.array([N], np.int32), 4, k, q_scale=qs, k_scale=ks,
+                                score_dtype=oracle.BF16)
+    for r in range(T):
+        s64 = sc[r].astype(np.float64)
+        kth = np.sort(s64)[::-1][k - 1]
+        eps = 2.0 ** -8 * np.abs(s64).max()
+        sel = np.zeros(N, bool)
+        sel[ib[r]] = True
+        assert s64[sel].min() >= kth - eps and s64[~sel].max() <= kth + eps
