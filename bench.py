@@ -60,7 +60,7 @@ class DecodeWorkload:
     'csa_decode_128k' (CSA only), with host copies for the oracle."""
 
     def __init__(self, name, copies=4, overrides=None, keep_host=True, streams=1, hca_workgroups=64,
-                 csa_workgroups=0):
+                 csa_workgroups=0, score_dtype=0):
         import torch
 
         import compressed_sparse_kv_amd as csk
@@ -157,6 +157,7 @@ class DecodeWorkload:
         self.streams = streams
         self.hca_workgroups = hca_workgroups
         self.csa_workgroups = csa_workgroups
+        self.score_dtype = score_dtype
         self.side = torch.cuda.Stream()
         torch.cuda.synchronize()
         if not keep_host:
@@ -187,7 +188,8 @@ class DecodeWorkload:
         # CSA entry: one launch (records formed once per state copy)
         csk.compress_batch(st["jobs"])
         csk.indexer_topk(self.qc, x["w"], st["kc"], x["q_pos"], x["n_entries"], 4, self.k, q_scale=self.qs,
-                         k_scale=st["ks"], idx=self.idx, score=self.score, workspace=self.ws_i)
+                         k_scale=st["ks"], idx=self.idx, score=self.score, workspace=self.ws_i,
+                         score_dtype=self.score_dtype)
         csk.sparse_attn(x["q"], x["q_pos"], st["kv_c"], self.idx, st["kv_w"], x["w_pos0"], self.W,
                         x["sink"], self.dv, 64, self.scale, out=self.out, lse=self.lse,
                         workspace=self.ws_s, max_workgroups=self.csa_workgroups)
@@ -243,7 +245,7 @@ class DecodeWorkload:
         c = {"workload": self.name, "batch": self.B, "context": int(self.N * 4), "csa_entries": self.N,
              "heads": self.H, "kv_dim": self.D, "value_dim": self.dv, "rope_dims": 64, "indexer_heads": self.HI,
              "indexer_dim": self.dI, "indexer_dtype": "mxfp4", "top_k": self.k, "window": self.W, "sink": True,
-             "state_copies": len(self.copies)}
+             "state_copies": len(self.copies), "topk_scores": "bf16" if self.score_dtype else "f32"}
         if self.pair:
             c["hca_entries"] = self.Nh
         return c
@@ -277,6 +279,8 @@ class DecodeWorkload:
         npos = d["q_pos"][sel]
         scores, nvis = oracle.indexer_scores(qc, d["w"][sel], kc, npos, d["n_entries"][sel], 4, q_scale=qs,
                                              k_scale=ks)
+        if self.score_dtype:
+            scores = oracle.scores_bf16(scores)
         idx, sc = oracle.topk(scores, nvis, self.k)
         out["idx"], out["score"] = idx, sc
         out["scores_full"], out["n_vis"] = scores, nvis
@@ -511,12 +515,23 @@ def run(args):
     import compressed_sparse_kv_amd as csk
 
     wl = DecodeWorkload(args.workload, copies=args.copies, streams=args.streams,
-                        hca_workgroups=args.hca_workgroups, csa_workgroups=args.csa_workgroups)
+                        hca_workgroups=args.hca_workgroups, csa_workgroups=args.csa_workgroups,
+                        score_dtype=csk.CSK_BF16 if args.score_dtype == "bf16" else csk.CSK_F32)
     K, Wm = args.steps, args.warmup
     # eager warm-up (first calls set kernel attributes outside any capture)
     for i in range(max(Wm, 1)):
         wl.step(i)
     torch.cuda.synchronize()
+    recall = None
+    if wl.score_dtype:
+        # untimed: the share of the fp32 selection the bf16 one keeps
+        sel16 = wl.idx.clone()
+        st, x = wl.copies[(max(Wm, 1) - 1) % len(wl.copies)], wl.x
+        sel32, _ = csk.indexer_topk(wl.qc, x["w"], st["kc"], x["q_pos"], x["n_entries"], 4, wl.k, q_scale=wl.qs,
+                                    k_scale=st["ks"])
+        a, b = sel32.cpu().numpy().reshape(wl.B, -1), sel16.cpu().numpy().reshape(wl.B, -1)
+        recall = float(np.mean([len(set(a[r][a[r] >= 0]) & set(b[r][b[r] >= 0])) / max(1, (a[r] >= 0).sum())
+                                for r in range(wl.B)]))
 
     # which kernel dominates: average event-timed duration per kernel
     per = {}
@@ -641,6 +656,8 @@ def run(args):
     }
     if side_rec:
         line["roofline"]["side_branch"] = side_rec
+    if recall is not None:
+        line["bf16_topk_recall"] = round(recall, 5)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args)
     print(json.dumps(line), flush=True)
@@ -965,6 +982,8 @@ def main():
                     help="workgroup cap of the HCA attention beside the CSA chain (0: one per CU)")
     ap.add_argument("--csa-workgroups", type=int, default=0,
                     help="workgroup cap of the CSA sparse attention (0: one per CU)")
+    ap.add_argument("--score-dtype", default="f32", choices=["f32", "bf16"],
+                    help="decode: indexer scores the top-k compares (bf16: rounded once to bf16)")
     ap.add_argument("--cpu-rows", type=int, default=4, help="decode: sequences the oracle runs")
     ap.add_argument("--cpu-rows-prefill", type=int, default=None,
                     help="prefill: query rows the oracle runs (default 384 for CSA, every row for HCA)")

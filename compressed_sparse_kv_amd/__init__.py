@@ -42,10 +42,10 @@ def lib():
         L.hca_compress.argtypes = [_vp] * 3 + [_i] * 5 + [_i64, _i, _f, _vp, _i, _i, _vp, _vp, _i64, _vp]
         L.mxfp4_quantize.argtypes = [_vp, _i, _i64, _i, _vp, _vp, _vp]
         L.csk_compress_batch.argtypes = [ctypes.POINTER(CompressJob), _i, _vp]
-        L.indexer_topk.argtypes = [_vp] * 7 + [_i] * 8 + [_vp, _vp, _vp, _sz, _vp]
+        L.indexer_topk.argtypes = [_vp] * 7 + [_i] * 9 + [_vp, _vp, _vp, _sz, _vp]
         L.indexer_topk_workspace_size.argtypes = [_i] * 7
         L.indexer_topk_workspace_size.restype = _sz
-        L.indexer_topk_noalloc.argtypes = [_vp] * 7 + [_i] * 8 + [_vp, _vp, _vp]
+        L.indexer_topk_noalloc.argtypes = [_vp] * 7 + [_i] * 9 + [_vp, _vp, _vp]
         L.sparse_attn.argtypes = ([_vp, _vp, _vp, _i, _vp, _i, _vp, _vp, _i, _i, _vp] + [_i] * 6
                                   + [_f, _f, _i, _vp, _vp, _i, _vp, _sz, _vp])
         L.dense_compressed_attn.argtypes = ([_vp, _vp, _vp, _i, _vp, _i, _vp, _vp, _i, _i, _vp] + [_i] * 6
@@ -212,11 +212,12 @@ def indexer_topk_workspace_size(B, T, HI, dI, Nmax, k, dtype):
 
 
 def indexer_topk(q, w, kk, q_pos, n_entries, m, k, q_scale=None, k_scale=None, idx=None, score=None,
-                 workspace=None, with_score=True):
+                 workspace=None, with_score=True, score_dtype=CSK_F32):
     """Top-k compressed entries per query row (see indexer_topk in csk.h).
 
     MXFP4: q [B,T,HI,dI/2] uint8 + q_scale, kk [B,Nmax,dI/2] uint8 + k_scale.
     fp32:  q [B,T,HI,dI] float32, kk [B,Nmax,dI] float32.
+    score_dtype: CSK_F32, or CSK_BF16 (scores rounded to bf16 before the top-k).
     Returns (idx [B,T,k] int32, score [B,T,k] float32 or None).
     """
     B, T, HI = w.shape
@@ -232,14 +233,14 @@ def indexer_topk(q, w, kk, q_pos, n_entries, m, k, q_scale=None, k_scale=None, i
     if workspace is None:
         workspace = _ws(nbytes, w.device)
     rc = lib().indexer_topk(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(kk), _ptr(k_scale), _ptr(q_pos),
-                            _ptr(n_entries), B, T, HI, dI, Nmax, m, k, dtype, _ptr(idx), _ptr(score),
-                            _ptr(workspace), workspace.numel(), _stream())
+                            _ptr(n_entries), B, T, HI, dI, Nmax, m, k, dtype, score_dtype, _ptr(idx),
+                            _ptr(score), _ptr(workspace), workspace.numel(), _stream())
     _check(rc, "indexer_topk")
     return idx, score
 
 
 def indexer_topk_noalloc(q, w, kk, q_pos, n_entries, m, k, q_scale=None, k_scale=None, idx=None, score=None,
-                         with_score=True):
+                         with_score=True, score_dtype=CSK_F32):
     """indexer_topk without a workspace: the library's static device
     scratch serves instead (see indexer_topk_noalloc in csk.h; calls that
     overlap on one device race). Returns (idx, score or None)."""
@@ -252,7 +253,7 @@ def indexer_topk_noalloc(q, w, kk, q_pos, n_entries, m, k, q_scale=None, k_scale
         score = torch.empty((B, T, k), dtype=torch.float32, device=w.device)
     rc = lib().indexer_topk_noalloc(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(kk), _ptr(k_scale), _ptr(q_pos),
                                     _ptr(n_entries), B, T, HI, dI, kk.shape[1], m, k,
-                                    CSK_MXFP4 if mx else CSK_F32, _ptr(idx), _ptr(score), _stream())
+                                    CSK_MXFP4 if mx else CSK_F32, score_dtype, _ptr(idx), _ptr(score), _stream())
     _check(rc, "indexer_topk_noalloc")
     return idx, score
 

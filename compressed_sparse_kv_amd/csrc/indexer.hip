@@ -63,7 +63,14 @@ struct IdxArgs {
   float* samples;      // [R, NG] or null
   int gs_log2, ng;
   int iters;           // 64-key groups per wave (MFMA path; also a template value)
+  bool bf16_scores;    // scores rounded once to bf16 before they are stored
 };
+
+// A score as the top-k sees it: the fp32 value, or its nearest bf16 (ties
+// to even) when the call asks for BF16 scores.
+__device__ __forceinline__ float topk_score(const IdxArgs& a, float x) {
+  return a.bf16_scores ? __uint_as_float(f32_to_bf16_bits(x) << 16) : x;
+}
 
 // (r is the workgroup's row: uniform.) Both loads are issued before either
 // value is used (the empty asm takes them as scalar operands), so they
@@ -264,6 +271,7 @@ __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
       }
     }
 
+    score = topk_score(a, score);
     const int key = base + lane;
     if (key < nv) a.scores[(int64_t)r * a.Nmax + key] = score;
     if (a.samples) write_samples(a, r, base, key < nv ? score : -INFINITY);
@@ -328,7 +336,7 @@ __global__ __launch_bounds__(256) void idx_valu_kernel(IdxArgs a) {
     }
     score = __builtin_fmaf(a.w[qrow], d > 0.0f ? d : 0.0f, score);
   }
-  a.scores[(int64_t)r * a.Nmax + s] = score;
+  a.scores[(int64_t)r * a.Nmax + s] = topk_score(a, score);
 }
 
 // Group maxima for the VALU path (the MFMA path writes them itself).
@@ -916,8 +924,9 @@ static int scratch_on_device(const char* fn, void** out) {
 static int indexer_topk_impl(const char* fn, bool noalloc, const void* q, const uint8_t* q_scale,
                              const float* w, const void* kk, const uint8_t* k_scale,
                              const int32_t* q_pos, const int32_t* n_entries, int B, int T, int HI,
-                             int dI, int Nmax, int m, int k, int dtype, int32_t* idx, float* score,
-                             void* workspace, size_t ws_bytes, void* stream) {
+                             int dI, int Nmax, int m, int k, int dtype, int score_dtype,
+                             int32_t* idx, float* score, void* workspace, size_t ws_bytes,
+                             void* stream) {
   clear_error();
   const std::string f(fn);
   if (!q || !w || !kk || !q_pos || !n_entries || !idx)
@@ -928,6 +937,8 @@ static int indexer_topk_impl(const char* fn, bool noalloc, const void* q, const 
     return fail(CSK_EUNSUPPORTED, f + ": dtype must be CSK_MXFP4 or CSK_F32");
   if (dtype == CSK_MXFP4 && (dI % 32 || !q_scale || !k_scale))
     return fail(CSK_EINVAL, f + ": MXFP4 needs dI % 32 == 0 and both scale arrays");
+  if (score_dtype != CSK_F32 && score_dtype != CSK_BF16)
+    return fail(CSK_EUNSUPPORTED, f + ": score_dtype must be CSK_F32 or CSK_BF16");
   if (dtype == CSK_MXFP4 && (reinterpret_cast<uintptr_t>(k_scale) & 3))
     return fail(CSK_EINVAL, f + ": k_scale must be 4-byte aligned (read as dwords)");
   if ((int64_t)B * T > (1LL << 30) || ceil_div(Nmax, 256 * IDX_MIN_ITERS) > 65535)
@@ -965,6 +976,7 @@ static int indexer_topk_impl(const char* fn, bool noalloc, const void* q, const 
   ia.samples = p.filtered ? reinterpret_cast<float*>(ws + p.off_samples) : nullptr;
   ia.gs_log2 = p.gs_log2;
   ia.ng = p.ng;
+  ia.bf16_scores = score_dtype == CSK_BF16;
 
   int rc = CSK_OK;
   const bool mfma = dtype == CSK_MXFP4 && HI % 16 == 0 && HI <= 64 && dI % 128 == 0 && dI <= 256;
@@ -1035,18 +1047,18 @@ size_t indexer_topk_workspace_size(int B, int T, int HI, int dI, int Nmax, int k
 
 int indexer_topk(const void* q, const uint8_t* q_scale, const float* w, const void* kk,
                  const uint8_t* k_scale, const int32_t* q_pos, const int32_t* n_entries, int B,
-                 int T, int HI, int dI, int Nmax, int m, int k, int dtype, int32_t* idx,
-                 float* score, void* workspace, size_t ws_bytes, void* stream) {
+                 int T, int HI, int dI, int Nmax, int m, int k, int dtype, int score_dtype,
+                 int32_t* idx, float* score, void* workspace, size_t ws_bytes, void* stream) {
   return csk::indexer_topk_impl("indexer_topk", false, q, q_scale, w, kk, k_scale, q_pos, n_entries, B, T, HI,
-                                dI, Nmax, m, k, dtype, idx, score, workspace, ws_bytes, stream);
+                                dI, Nmax, m, k, dtype, score_dtype, idx, score, workspace, ws_bytes, stream);
 }
 
 int indexer_topk_noalloc(const void* q, const uint8_t* q_scale, const float* w, const void* kk,
                          const uint8_t* k_scale, const int32_t* q_pos, const int32_t* n_entries, int B,
-                         int T, int HI, int dI, int Nmax, int m, int k, int dtype, int32_t* idx,
-                         float* score, void* stream) {
+                         int T, int HI, int dI, int Nmax, int m, int k, int dtype, int score_dtype,
+                         int32_t* idx, float* score, void* stream) {
   return csk::indexer_topk_impl("indexer_topk_noalloc", true, q, q_scale, w, kk, k_scale, q_pos, n_entries, B,
-                                T, HI, dI, Nmax, m, k, dtype, idx, score, nullptr, 0, stream);
+                                T, HI, dI, Nmax, m, k, dtype, score_dtype, idx, score, nullptr, 0, stream);
 }
 
 }  // extern "C"

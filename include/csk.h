@@ -197,6 +197,9 @@ int csk_compress_batch(const csk_compress_job* jobs, int n_jobs, void* stream);
  * is the exact dot product rounded once to fp32 (MXFP4) or an fp32 fused
  * multiply-add chain over channels in ascending order (CSK_F32), and the
  * head sum is an fp32 fused multiply-add chain over h = 0..HI-1 from +0.
+ * With score_dtype CSK_BF16 each score is then rounded once to the nearest
+ * bf16 (ties to even) before the selection ([P1] «FP4 с учётом
+ * квантования»: BF16 scores for the top-k); CSK_F32 keeps the fp32 score.
  * The min(k, #candidates) highest scores are selected, ties to the lower
  * index, and returned in ascending index order, padded with -1.
  *
@@ -206,14 +209,16 @@ int csk_compress_batch(const csk_compress_job* jobs, int n_jobs, void* stream);
  *   kk, k_scale: MXFP4 [B,Nmax,dI/2] + [B,Nmax,dI/32], or CSK_F32 [B,Nmax,dI].
  *   q_pos      : [B,T] int32 absolute positions;  n_entries: [B] int32.
  *   dtype      : CSK_MXFP4 (dI % 32 == 0) or CSK_F32.
+ *   score_dtype: CSK_F32 or CSK_BF16 (the scores the selection compares).
  *   idx        : [B,T,k] int32 output;  score: [B,T,k] fp32 or NULL
- *                (scores of the returned entries, -inf for padding).
+ *                (scores of the returned entries as selected - the bf16
+ *                values with CSK_BF16 - and -inf for padding).
  *   workspace  : >= indexer_topk_workspace_size(B,T,HI,dI,Nmax,k,dtype).
  */
 int indexer_topk(const void* q, const uint8_t* q_scale, const float* w, const void* kk,
                  const uint8_t* k_scale, const int32_t* q_pos, const int32_t* n_entries, int B,
-                 int T, int HI, int dI, int Nmax, int m, int k, int dtype, int32_t* idx,
-                 float* score, void* workspace, size_t ws_bytes, void* stream);
+                 int T, int HI, int dI, int Nmax, int m, int k, int dtype, int score_dtype,
+                 int32_t* idx, float* score, void* workspace, size_t ws_bytes, void* stream);
 size_t indexer_topk_workspace_size(int B, int T, int HI, int dI, int Nmax, int k, int dtype);
 
 /*
@@ -238,8 +243,8 @@ size_t indexer_topk_workspace_size(int B, int T, int HI, int dI, int Nmax, int k
 #define CSK_NOALLOC_SCRATCH_BYTES (32u << 20)
 int indexer_topk_noalloc(const void* q, const uint8_t* q_scale, const float* w, const void* kk,
                          const uint8_t* k_scale, const int32_t* q_pos, const int32_t* n_entries, int B,
-                         int T, int HI, int dI, int Nmax, int m, int k, int dtype, int32_t* idx,
-                         float* score, void* stream);
+                         int T, int HI, int dI, int Nmax, int m, int k, int dtype, int score_dtype,
+                         int32_t* idx, float* score, void* stream);
 
 /*
  * sparse_attn - CSA attention: MQA over the selected compressed entries, a

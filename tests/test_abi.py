@@ -145,8 +145,18 @@ def test_indexer_rejects_misaligned_key_scales(lib):
     # argument error, caught before any launch
     lib.csk_last_error.restype = ctypes.c_char_p
     vp, i = ctypes.c_void_p, ctypes.c_int
-    lib.indexer_topk.argtypes = [vp] * 7 + [i] * 8 + [vp, vp, vp, ctypes.c_size_t, vp]
+    lib.indexer_topk.argtypes = [vp] * 7 + [i] * 9 + [vp, vp, vp, ctypes.c_size_t, vp]
     fake, odd = 4096, 4097
-    rc = lib.indexer_topk(fake, fake, fake, fake, odd, fake, fake, 1, 1, 64, 128, 4096, 4, 8, 2,
+    rc = lib.indexer_topk(fake, fake, fake, fake, odd, fake, fake, 1, 1, 64, 128, 4096, 4, 8, 2, 0,
                           fake, fake, fake, ctypes.c_size_t(1 << 30), None)
     assert rc == -1 and b"aligned" in lib.csk_last_error()
+
+
+def test_indexer_rejects_unknown_score_dtype(lib):
+    lib.csk_last_error.restype = ctypes.c_char_p
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.indexer_topk.argtypes = [vp] * 7 + [i] * 9 + [vp, vp, vp, ctypes.c_size_t, vp]
+    fake = 4096
+    rc = lib.indexer_topk(fake, fake, fake, fake, fake, fake, fake, 1, 1, 64, 128, 4096, 4, 8, 2, 7,
+                          fake, fake, fake, ctypes.c_size_t(1 << 30), None)
+    assert rc == -2 and b"score_dtype" in lib.csk_last_error()

@@ -144,3 +144,32 @@ def test_mxfp4_bit_exact_at_exponent_spread(spread):
     ridx, rsc = oracle.indexer_topk(qc, w, kc, q_pos, ne, m, N, q_scale=qs, k_scale=ks)
     _assert_same(host(idx).reshape(B * T, N), host(sc).reshape(B * T, N), ridx, rsc)
     assert np.all(ridx == np.arange(N)[None])
+
+
+@pytest.mark.parametrize("B,T,N,k", [(2, 37, 1000, 64), (2, 1, 40000, 2048), (4, 1, 262144, 2048)])
+def test_bf16_scores_bit_exact(B, T, N, k):
+    # BF16 scores for the top-k: every score rounded once to bf16 before the
+    # selection, on both sides; the selection (many more ties) and the
+    # returned bf16 scores must be bit-exact. The recall of the fp32
+    # selection is reported.
+    g = synth.rng(540 + N)
+    HI, dI, m = 64, 128, 4
+    qI = synth.normal(g, (B, T, HI, dI))
+    kI = synth.normal(g, (B, N, dI))
+    w = synth.normal(g, (B, T, HI), 1.0 / HI)
+    q_pos = np.full((B, T), 4 * N - 1, np.int32) - g.integers(0, 3, (B, T)).astype(np.int32)
+    ne = np.array([N] * B, np.int32)
+    (gqc, gqs), (rqc, rqs) = _mx_both(qI)
+    (gkc, gks), (rkc, rks) = _mx_both(kI)
+    assert_in_regime(rqc, rqs, rkc, rks)
+    idx, sc = csk.indexer_topk(gqc, dev(w), gkc, dev(q_pos), dev(ne), m, k, q_scale=gqs, k_scale=gks,
+                               score_dtype=csk.CSK_BF16)
+    ridx, rsc = oracle.indexer_topk(rqc, w, rkc, q_pos, ne, m, k, q_scale=rqs, k_scale=rks,
+                                    score_dtype=oracle.BF16)
+    _assert_same(host(idx).reshape(B * T, k), host(sc).reshape(B * T, k), ridx, rsc)
+    assert np.all(host(sc).view(np.uint32)[host(idx) >= 0] & 0xffff == 0)   # bf16 values
+    i32, _ = csk.indexer_topk(gqc, dev(w), gkc, dev(q_pos), dev(ne), m, k, q_scale=gqs, k_scale=gks)
+    a, b = host(i32).reshape(B * T, k), host(idx).reshape(B * T, k)
+    rec = np.mean([len(set(a[r][a[r] >= 0]) & set(b[r][b[r] >= 0])) / max(1, (a[r] >= 0).sum())
+                   for r in range(B * T)])
+    print(f"[recall] bf16 scores, N={N}, k={k}: {rec:.4f} of the fp32 selection")

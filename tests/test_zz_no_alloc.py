@@ -38,7 +38,8 @@ def _noalloc_c(c):
     p = lambda t: ctypes.c_void_p(t.data_ptr())
     rc = L.indexer_topk_noalloc(p(c["q"]), p(c["q_scale"]), p(c["w"]), p(c["kk"]), p(c["k_scale"]), p(c["q_pos"]),
                                 p(c["n_entries"]), B, T, HI, c["q"].shape[-1] * 2, c["kk"].shape[1], c["m"], k,
-                                csk.CSK_MXFP4, p(idx), p(sc), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                                csk.CSK_MXFP4, csk.CSK_F32, p(idx), p(sc),
+                                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     assert rc == 0, L.csk_last_error().decode()
     return idx, sc
 
@@ -63,5 +64,5 @@ def test_noalloc_refuses_a_problem_past_its_scratch():
     assert need > (32 << 20)
     fake = ctypes.c_void_p(4096)
     rc = L.indexer_topk_noalloc(fake, fake, fake, fake, fake, fake, fake, B, T, HI, dI, N, 4, k, csk.CSK_MXFP4,
-                                fake, fake, None)
+                                csk.CSK_F32, fake, fake, None)
     assert rc == -3 and b"scratch" in L.csk_last_error()
