@@ -52,6 +52,9 @@ def lib():
         L.csk_ref_topk.argtypes = [_f32p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _f32p]
         L.csk_ref_scores_bf16.argtypes = [_f32p, ctypes.c_int64]
         L.csk_ref_scores_bf16.restype = None
+        L.csk_ref_fp8kv_entry_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+        L.csk_ref_fp8kv_encode.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _u8p]
+        L.csk_ref_fp8kv_decode.argtypes = [_u8p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _f32p]
         attn_tail = ([_f32p, _i32p, ctypes.c_int, ctypes.c_int, _f32p] + [ctypes.c_int] * 6
                      + [ctypes.c_double, ctypes.c_double, _i32p, ctypes.c_int, _f64p, _f64p])
         L.csk_ref_sparse_attn.argtypes = [_f32p, _i32p, _f32p, ctypes.c_int, _i32p, ctypes.c_int] + attn_tail
@@ -218,6 +221,32 @@ def topk(scores, n_vis, k):
                             _p(idx, ctypes.c_int32), _p(out, ctypes.c_float))
     _check(rc, "topk")
     return idx, out
+
+
+def fp8kv_entry_bytes(D, d_rope):
+    return lib().csk_ref_fp8kv_entry_bytes(D, d_rope)
+
+
+def fp8kv_encode(x, d_rope):
+    """x [..., D] (fp32 values; bf16 bit patterns accepted) -> FP8 KV entries
+    [..., entry_bytes] uint8."""
+    x = _f32(x)
+    D = x.shape[-1]
+    rows = x.size // D
+    out = np.empty(x.shape[:-1] + (fp8kv_entry_bytes(D, d_rope),), np.uint8)
+    _check(lib().csk_ref_fp8kv_encode(_p(x, ctypes.c_float), rows, D, d_rope, _p(out, ctypes.c_uint8)),
+           "fp8kv_encode")
+    return out
+
+
+def fp8kv_decode(entries, D, d_rope):
+    """FP8 KV entries [..., entry_bytes] -> exact fp32 values [..., D]."""
+    e = np.ascontiguousarray(entries, dtype=np.uint8)
+    rows = e.size // e.shape[-1]
+    x = np.empty(e.shape[:-1] + (D,), np.float32)
+    _check(lib().csk_ref_fp8kv_decode(_p(e, ctypes.c_uint8), rows, D, d_rope, _p(x, ctypes.c_float)),
+           "fp8kv_decode")
+    return x
 
 
 def scores_bf16(scores):

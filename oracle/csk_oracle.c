@@ -369,6 +369,101 @@ int csk_ref_indexer_scores(const float* qf, const uint8_t* qc, const uint8_t* qs
   return err;
 }
 
+/* ---------------------------------------------------------- FP8 KV entries */
+
+/* [P2] (FP8 storage finding) and [P1] «Почему это так сильно экономит»,
+ * item 1: KV entries are stored in FP8 except the RoPE dims, which stay in
+ * BF16. The pages fix no scale granularity; the reading here: the D_nope =
+ * D - d_rope non-RoPE dims are OCP E4M3 values (sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits; exponent 0 is subnormal, m * 2^-9; the all-ones
+ * code is NaN and never produced) with one power-of-two scale byte (2^(byte
+ * - 127)) per 32 consecutive dims, chosen so that the block's largest
+ * magnitude lands in [128, 256): s = floor(log2 amax) - 7, clamped to
+ * [-126, 127]; an all-zero block gets byte 127. Codes are the nearest E4M3
+ * value of x / 2^s, ties to the even mantissa; zero (and anything that
+ * rounds to it) is the +0 code. Entry bytes: [D_nope codes][d_rope bf16
+ * values][D_nope/32 scale bytes], padded with zeros to a multiple of 16. */
+static double e4m3_value(int code) {
+  const int e = (code >> 3) & 15, mnt = code & 7;
+  const double mag = e == 0 ? ldexp((double)mnt, -9) : ldexp(1.0 + mnt / 8.0, e - 7);
+  return (code & 0x80) ? -mag : mag;
+}
+
+/* Nearest non-negative E4M3 code of y in [0, 448]: the plain definition,
+ * a search over the 127 finite codes; ties go to the code whose mantissa
+ * (its low bit) is even. */
+static int e4m3_code_abs(double y) {
+  int best = 0;
+  double bd = INFINITY;
+  for (int c = 0; c < 127; ++c) {
+    const double d = fabs(e4m3_value(c) - y);
+    if (d < bd || (d == bd && (c & 1) == 0)) {
+      best = c;
+      bd = d;
+    }
+  }
+  return best;
+}
+
+int csk_ref_fp8kv_entry_bytes(int D, int d_rope) {
+  const int dn = D - d_rope;
+  const int raw = dn + 2 * d_rope + dn / 32;
+  return (raw + 15) / 16 * 16;
+}
+
+int csk_ref_fp8kv_encode(const float* x, int64_t rows, int D, int d_rope, uint8_t* out) {
+  const int dn = D - d_rope;
+  if (D <= 0 || d_rope < 0 || d_rope > D || (d_rope & 1) || dn % 32 || rows < 0) return -1;
+  const int ES = csk_ref_fp8kv_entry_bytes(D, d_rope);
+  for (int64_t r = 0; r < rows; ++r) {
+    const float* xr = x + r * D;
+    uint8_t* o = out + r * ES;
+    memset(o, 0, (size_t)ES);
+    for (int g = 0; g < dn / 32; ++g) {
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs((double)xr[32 * g + i]));
+      int s = 0, byte = 127;
+      if (amax > 0.0) {
+        int e;
+        frexp(amax, &e);  /* amax = f * 2^e, f in [0.5, 1): floor(log2 amax) = e - 1 */
+        s = e - 1 - 7;
+        if (s < -126) s = -126;
+        if (s > 127) s = 127;
+        byte = s + 127;
+      }
+      o[dn + 2 * d_rope + g] = (uint8_t)byte;
+      for (int i = 0; i < 32; ++i) {
+        const double v = (double)xr[32 * g + i];
+        const int c = amax > 0.0 ? e4m3_code_abs(ldexp(fabs(v), -s)) : 0;
+        o[32 * g + i] = (uint8_t)((v < 0.0 && c != 0) ? (c | 0x80) : c);
+      }
+    }
+    for (int j = 0; j < d_rope; ++j) {
+      const uint16_t h = round_one_bf16((double)xr[dn + j]);
+      o[dn + 2 * j] = (uint8_t)(h & 0xff);
+      o[dn + 2 * j + 1] = (uint8_t)(h >> 8);
+    }
+  }
+  return 0;
+}
+
+int csk_ref_fp8kv_decode(const uint8_t* in, int64_t rows, int D, int d_rope, float* x) {
+  const int dn = D - d_rope;
+  if (D <= 0 || d_rope < 0 || d_rope > D || (d_rope & 1) || dn % 32 || rows < 0) return -1;
+  const int ES = csk_ref_fp8kv_entry_bytes(D, d_rope);
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint8_t* e = in + r * ES;
+    float* xr = x + r * D;
+    for (int i = 0; i < dn; ++i)
+      xr[i] = (float)ldexp(e4m3_value(e[i]), (int)e[dn + 2 * d_rope + i / 32] - 127);
+    for (int j = 0; j < d_rope; ++j) {
+      const uint32_t u = ((uint32_t)e[dn + 2 * j] | ((uint32_t)e[dn + 2 * j + 1] << 8)) << 16;
+      memcpy(&xr[dn + j], &u, 4);
+    }
+  }
+  return 0;
+}
+
 /* BF16 indexer scores ([P1] «FP4 с учётом квантования»: the scores that the
  * top-k selects from are kept in BF16, which the page credits with a faster
  * top-k at a small loss of recall): every fp32 score is rounded once to the

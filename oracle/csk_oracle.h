@@ -73,6 +73,16 @@ int csk_ref_indexer_scores(const float* qf, const uint8_t* qc, const uint8_t* qs
                            int dI, int Nmax, int m, int dtype, const int32_t* rows, int n_rows,
                            float* scores, int32_t* n_vis);
 
+/* FP8 KV entries ([P2] FP8 storage; [P1] «Почему это так сильно экономит»,
+ * item 1): the D - d_rope non-RoPE dims as OCP E4M3 codes with one
+ * power-of-two scale byte per 32 dims (the block maximum scaled into
+ * [128, 256)), the d_rope RoPE dims as bf16. Entry layout: [codes][rope
+ * bf16][scales], zero-padded to a multiple of 16 bytes. x: [rows, D] fp32;
+ * out: [rows, entry_bytes]. Decode is exact (to fp32). */
+int csk_ref_fp8kv_entry_bytes(int D, int d_rope);
+int csk_ref_fp8kv_encode(const float* x, int64_t rows, int D, int d_rope, uint8_t* out);
+int csk_ref_fp8kv_decode(const uint8_t* in, int64_t rows, int D, int d_rope, float* x);
+
 /* BF16 indexer scores: each fp32 score rounded once to the nearest bf16
  * (ties to even), in place. [P1] «FP4 с учётом квантования» (BF16 scores
  * for the top-k). */
