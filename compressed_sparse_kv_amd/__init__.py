@@ -15,7 +15,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsk.so")
 
-CSK_F32, CSK_BF16, CSK_MXFP4 = 0, 1, 2
+CSK_F32, CSK_BF16, CSK_MXFP4, CSK_FP8KV = 0, 1, 2, 3
 _lib = None
 
 _vp = ctypes.c_void_p
@@ -38,6 +38,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         L.csk_last_error.restype = ctypes.c_char_p
         L.csk_abi_version.restype = _i
+        L.csk_fp8kv_entry_bytes.argtypes = [_i, _i]
+        L.csk_fp8kv_entry_bytes.restype = _i
         L.csa_compress.argtypes = [_vp] * 6 + [_i] * 5 + [_i64, _i, _f, _vp, _i, _i, _vp, _vp, _i64, _vp]
         L.hca_compress.argtypes = [_vp] * 3 + [_i] * 5 + [_i64, _i, _f, _vp, _i, _i, _vp, _vp, _i64, _vp]
         L.mxfp4_quantize.argtypes = [_vp, _i, _i64, _i, _vp, _vp, _vp]
@@ -47,9 +49,9 @@ def lib():
         L.indexer_topk_workspace_size.restype = _sz
         L.indexer_topk_noalloc.argtypes = [_vp] * 7 + [_i] * 9 + [_vp, _vp, _vp]
         L.sparse_attn.argtypes = ([_vp, _vp, _vp, _i, _vp, _i, _vp, _vp, _i, _i, _vp] + [_i] * 6
-                                  + [_f, _f, _i, _vp, _vp, _i, _vp, _sz, _vp])
+                                  + [_f, _f, _i, _i, _vp, _vp, _i, _vp, _sz, _vp])
         L.dense_compressed_attn.argtypes = ([_vp, _vp, _vp, _i, _vp, _i, _vp, _vp, _i, _i, _vp] + [_i] * 6
-                                            + [_f, _f, _i, _vp, _vp, _i, _vp, _sz, _vp])
+                                            + [_f, _f, _i, _i, _vp, _vp, _i, _vp, _sz, _vp])
         L.sparse_attn_workspace_size.argtypes = [_i] * 9
         L.sparse_attn_workspace_size.restype = _sz
         L.dense_compressed_attn_workspace_size.argtypes = [_i] * 10
@@ -90,6 +92,11 @@ def _ws(nbytes, device):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+def fp8kv_entry_bytes(D, d_rope):
+    """Bytes of one CSK_FP8KV entry (see csk.h)."""
+    return lib().csk_fp8kv_entry_bytes(D, d_rope)
+
+
 def csa_compress(ca, za, cb, zb, bias_a, bias_b, m, d_rope=0, rope_base=10000.0, entry_pos=None,
                  out_dtype=None, entry0=0, src_bstride=0, out=None, out_scale=None, dst_bstride=0,
                  B=None, S=None):
@@ -101,7 +108,7 @@ def csa_compress(ca, za, cb, zb, bias_a, bias_b, m, d_rope=0, rope_base=10000.0,
     S = ca.shape[1] if S is None else S
     D = ca.shape[-1]
     out_dtype = _dt(ca) if out_dtype is None else out_dtype
-    out, out_scale = _alloc_compress_out(out, out_scale, B, S // m, D, out_dtype, ca.device)
+    out, out_scale = _alloc_compress_out(out, out_scale, B, S // m, D, out_dtype, ca.device, d_rope)
     rc = lib().csa_compress(_ptr(ca), _ptr(za), _ptr(cb), _ptr(zb), _ptr(bias_a), _ptr(bias_b), B, S, D, m,
                             entry0, src_bstride, d_rope, rope_base, _ptr(entry_pos), _dt(ca), out_dtype,
                             _ptr(out), _ptr(out_scale), dst_bstride, _stream())
@@ -115,7 +122,7 @@ def hca_compress(c, z, bias, m, d_rope=0, rope_base=10000.0, entry_pos=None, out
     S = c.shape[1] if S is None else S
     D = c.shape[-1]
     out_dtype = _dt(c) if out_dtype is None else out_dtype
-    out, out_scale = _alloc_compress_out(out, out_scale, B, S // m, D, out_dtype, c.device)
+    out, out_scale = _alloc_compress_out(out, out_scale, B, S // m, D, out_dtype, c.device, d_rope)
     rc = lib().hca_compress(_ptr(c), _ptr(z), _ptr(bias), B, S, D, m, entry0, src_bstride, d_rope, rope_base,
                             _ptr(entry_pos), _dt(c), out_dtype, _ptr(out), _ptr(out_scale), dst_bstride,
                             _stream())
@@ -123,10 +130,12 @@ def hca_compress(c, z, bias, m, d_rope=0, rope_base=10000.0, entry_pos=None, out
     return (out, out_scale) if out_dtype == CSK_MXFP4 else out
 
 
-def _alloc_compress_out(out, out_scale, B, N, D, out_dtype, device):
+def _alloc_compress_out(out, out_scale, B, N, D, out_dtype, device, d_rope=0):
     if out is None:
         if out_dtype == CSK_MXFP4:
             out = torch.empty((B, N, D // 2), dtype=torch.uint8, device=device)
+        elif out_dtype == CSK_FP8KV:
+            out = torch.empty((B, N, fp8kv_entry_bytes(D, d_rope)), dtype=torch.uint8, device=device)
         else:
             out = torch.empty((B, N, D), dtype=_torch_dt(out_dtype), device=device)
     if out_dtype == CSK_MXFP4 and out_scale is None:
@@ -176,7 +185,7 @@ def csa_job(ca, za, cb, zb, bias_a, bias_b, m, d_rope=0, rope_base=10000.0, entr
     S = ca.shape[1] if S is None else S
     D = ca.shape[-1]
     out_dtype = _dt(ca) if out_dtype is None else out_dtype
-    out, out_scale = _alloc_compress_out(out, out_scale, B, S // m, D, out_dtype, ca.device)
+    out, out_scale = _alloc_compress_out(out, out_scale, B, S // m, D, out_dtype, ca.device, d_rope)
     rec = CompressJob(kind=CSK_JOB_CSA, ca=_ptr(ca), za=_ptr(za), cb=_ptr(cb), zb=_ptr(zb),
                       bias_a=_ptr(bias_a), bias_b=_ptr(bias_b), B=B, S=S, D=D, m=m, entry0=entry0,
                       src_bstride=src_bstride, d_rope=d_rope, rope_base=rope_base,
@@ -266,6 +275,11 @@ def dense_compressed_attn_workspace_size(B, T, H, D, dv, Nmax, m, W, dtype, max_
     return lib().dense_compressed_attn_workspace_size(B, T, H, D, dv, Nmax, m, W, dtype, max_workgroups)
 
 
+def _kv_dt(q, kv_c):
+    """The KV dtype code: uint8 entries are CSK_FP8KV, else the query's."""
+    return CSK_FP8KV if kv_c.dtype == torch.uint8 else _dt(q)
+
+
 def _attn_io(q, kv_w, dv, out, lse, want_lse):
     B, T, H, D = q.shape
     if out is None:
@@ -286,7 +300,8 @@ def sparse_attn(q, q_pos, kv_c, idx, kv_w, w_pos0, W, sink, dv, d_rope, scale, r
         workspace = _ws(nbytes, q.device)
     rc = lib().sparse_attn(_ptr(q), _ptr(q_pos), _ptr(kv_c), kv_c.shape[1], _ptr(idx), k, _ptr(kv_w),
                            _ptr(w_pos0), S_w, W, _ptr(sink), B, T, H, D, dv, d_rope, rope_base, scale, _dt(q),
-                           _ptr(out), _ptr(lse), max_workgroups, _ptr(workspace), workspace.numel(), _stream())
+                           _kv_dt(q, kv_c), _ptr(out), _ptr(lse), max_workgroups, _ptr(workspace),
+                           workspace.numel(), _stream())
     _check(rc, "sparse_attn")
     return out, lse
 
@@ -303,8 +318,8 @@ def dense_compressed_attn(q, q_pos, kv_c, n_entries, m, kv_w, w_pos0, W, sink, d
         workspace = _ws(nbytes, q.device)
     rc = lib().dense_compressed_attn(_ptr(q), _ptr(q_pos), _ptr(kv_c), Nmax, _ptr(n_entries), m, _ptr(kv_w),
                                      _ptr(w_pos0), S_w, W, _ptr(sink), B, T, H, D, dv, d_rope, rope_base, scale,
-                                     _dt(q), _ptr(out), _ptr(lse), max_workgroups, _ptr(workspace),
-                                     workspace.numel(), _stream())
+                                     _dt(q), _kv_dt(q, kv_c), _ptr(out), _ptr(lse), max_workgroups,
+                                     _ptr(workspace), workspace.numel(), _stream())
     _check(rc, "dense_compressed_attn")
     return out, lse
 

@@ -92,6 +92,11 @@ const char* csk_last_error(void) { return csk::g_err.c_str(); }
 
 int csk_abi_version(void) { return CSK_ABI_VERSION; }
 
+int csk_fp8kv_entry_bytes(int D, int d_rope) {
+  if (D <= 0 || d_rope < 0 || d_rope > D || (d_rope & 1) || (D - d_rope) % 32) return 0;
+  return csk::fp8kv_entry_bytes(D, d_rope);
+}
+
 int csk_kernel_timer_arm(const char* kernel, void** ev_start, void** ev_stop, int n) {
   if (!kernel || !ev_start || !ev_stop || n <= 0 || strlen(kernel) >= sizeof(csk::g_timer_name))
     return csk::fail(CSK_EINVAL, "csk_kernel_timer_arm: bad arguments");

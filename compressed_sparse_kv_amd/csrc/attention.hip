@@ -1084,7 +1084,7 @@ __device__ __forceinline__ int fresh_lane() {
 constexpr int R32_QB = 2;  // K fragments per pipelined block (two blocks in flight)
 constexpr int R32_VB = 2;  // V^T fragments per pipelined block
 
-template <int D, int DV, bool DENSE>
+template <int D, int DV, bool DENSE, bool KV8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bf16_row32_kernel(AttnArgs a) {
   constexpr int NCH = D / 8;             // 16-byte chunks per KV row
@@ -1098,12 +1098,30 @@ void attn_bf16_row32_kernel(AttnArgs a) {
   static_assert(NCH % 8 == 0 && DV % 64 == 0 && DV <= D && KS % QB == 0 && NQB == CPW &&
                     CPW - (CPW + 1) / 2 <= 4 * HDT / R32_VB,
                 "unsupported shape");
-  __shared__ __align__(16) uint4 buf0[TU];
-  __shared__ __align__(16) uint4 buf1[TU];
-  __shared__ __align__(16) uint4 pex[4][2][64];  // probabilities, B-operand fragments
+  // FP8 KV entries (KV8; built for 512 + 64): entry = [512 E4M3 codes][64
+  // bf16 RoPE dims][16 scale bytes] = 41 units. A tile of 64 entries is
+  // staged by DMA as-is (code units, then the rows' 9-unit tails) and
+  // converted in LDS into the bf16 tile layout below, on which the rest of
+  // the kernel runs unchanged.
+  constexpr int DN8 = D - 64;                       // code bytes per entry
+  constexpr int ESU = (DN8 + 128 + DN8 / 32 + 15) / 16;  // 16-byte units per entry
+  constexpr int ES8 = 16 * ESU;                     // entry bytes
+  constexpr int CU8 = DN8 / 16;                     // code units per entry (32)
+  constexpr int STU = 64 * ESU;                     // staged tile units
+  constexpr int TAIL0 = 64 * CU8;                   // first tail unit of a staged tile
+  static_assert(!KV8 || (D == 576 && DV == 512 && CU8 == 32 && ESU == 41), "FP8 KV tiles are built for 512 + 64");
+  // bf16: two tile buffers; KV8: the converted tile (buf0), then two staged
+  // tiles from buf1 on
+  __shared__ __align__(16) uint4 lds_kv[KV8 ? TU + 2 * STU : 2 * TU];
+  __shared__ __align__(16) uint4 pex_b[KV8 ? 1 : 4 * 2 * 64];  // probabilities, B-operand fragments
+  __shared__ int rowtab[KV8 ? 2 * 64 : 1];                     // KV8: the row codes of tiles t, t+1
   __shared__ float mx[4][32];                      // tile maxima per head
   __shared__ float xl[4][32];                      // end-of-row sums per head
   __shared__ float2 rtab[MAX_ROPE_PAIRS];
+  uint4* const buf0 = lds_kv;
+  uint4* const buf1 = lds_kv + TU;
+  // staged tile T (KV8)
+  auto stg = [&](int T) { return buf1 + STU * (T & 1); };
 
   const int r = blockIdx.x;
   const int split = blockIdx.y;
@@ -1117,6 +1135,8 @@ void attn_bf16_row32_kernel(AttnArgs a) {
   const RowInfo ri = row_info(a, r);
   const uint16_t* kvc = reinterpret_cast<const uint16_t*>(a.kv_c) + (int64_t)ri.b * a.Nmax * D;
   const uint16_t* kvw = reinterpret_cast<const uint16_t*>(a.kv_w) + (int64_t)ri.b * a.S_w * D;
+  const char* kvc8 = reinterpret_cast<const char*>(a.kv_c) + (int64_t)ri.b * a.Nmax * ES8;
+  const char* kvw8 = reinterpret_cast<const char*>(a.kv_w) + (int64_t)ri.b * a.S_w * ES8;
   const int total = a.Lc + a.W;
   // this workgroup's 64-row tiles [t0, t1) of the row's candidate slots
   // (a.nch workgroups share a row; the merge kernel combines them)
@@ -1157,11 +1177,79 @@ void attn_bf16_row32_kernel(AttnArgs a) {
     lds_dma16(src, dst + 64 * (CPW * wave + q));
   };
   // tile T's index reads of this lane: row = lane (its mask bit) and the two
-  // rows its DMAs load
+  // rows its DMAs load (KV8: the row = lane only; its code goes to the row
+  // table from which every lane takes the rows it stages)
   struct TileIdx { int em, e0, e1; };
   auto tile_idx = [&](int T, int ln) -> TileIdx {
+    if (KV8) return TileIdx{idx_load(64 * T + ln), 0, 0};
     const int dr = dma_row_of(ln);
     return TileIdx{idx_load(64 * T + ln), idx_load(64 * T + dr), idx_load(64 * T + dr + 8)};
+  };
+  // KV8 staging: this wave's DMA instruction q of tile T. q < 8: code units
+  // of instruction i = 8*wave + q, rows 8(i%8) + lane%8, code units
+  // 8(i/8) + lane/8 (eight 128-byte runs of eight rows), into staged units
+  // 64i + lane; q >= 8: tail instruction i = wave + 4(q - 8) (< 9), unit
+  // 64i + lane of the rows' tails (row t/9, unit t%9 for t = 64i + lane).
+  // Wave 0 issues 11 instructions, the others 10.
+  auto entry8 = [&](int code) -> const char* {
+    const bool win = code <= -2;
+    const int rowi = code >= 0 ? code : (win ? -2 - code : 0);
+    return (win ? kvw8 : kvc8) + (int64_t)rowi * ES8;
+  };
+  const int nq8 = wave == 0 ? 11 : 10;
+  auto dma8 = [&](int T, int q, int ln) {
+    uint4* st = stg(T);
+    const int* rt = rowtab + 64 * (T & 1);
+    if (q < 8) {
+      const int i = 8 * wave + q;
+      const int j = 8 * (i & 7) + (ln & 7), cu = 8 * (i >> 3) + (ln >> 3);
+      lds_dma16(entry8(rt[j]) + 16 * cu, st + 64 * i);
+    } else {
+      const int i = wave + 4 * (q - 8);
+      const int t = 64 * i + ln, j = t / 9;
+      lds_dma16(entry8(rt[j]) + DN8 + 16 * (t - 9 * j), st + TAIL0 + 64 * i);
+    }
+  };
+  // KV8: staged tile T -> bf16 tile buf0. Staged code unit u = 64i + l holds
+  // codes 16cu .. 16cu+15 of row j (as the DMA placed them); its two bf16
+  // chunks go to units (j/8)*GU + 8*(c ^ (j/8 & 1)) + j%8 for c = 2cu, 2cu+1
+  // (scaled by the row's scale byte of block cu/2, exact in bf16); the
+  // RoPE units are copied. Eight consecutive lanes write eight consecutive
+  // units.
+  auto convert8 = [&](int T) {
+    const uint4* st = stg(T);
+    const uint8_t* st8 = reinterpret_cast<const uint8_t*>(st);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int u = tid + 256 * k;
+      const int i = u >> 6, l = u & 63;
+      const int j = 8 * (i & 7) + (l & 7), cu = 8 * (i >> 3) + (l >> 3);
+      const uint4 c16 = st[u];
+      const uint32_t sb = st8[16 * (TAIL0 + 9 * j + 8) + (cu >> 1)];
+      const float scl = __uint_as_float(sb << 23);
+      const v2bf b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c16.x, scl, false);
+      const v2bf b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c16.x, scl, true);
+      const v2bf b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c16.y, scl, false);
+      const v2bf b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c16.y, scl, true);
+      const v2bf b4 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c16.z, scl, false);
+      const v2bf b5 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c16.z, scl, true);
+      const v2bf b6 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c16.w, scl, false);
+      const v2bf b7 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c16.w, scl, true);
+      const int G = j >> 3, g1 = G & 1;
+      buf0[G * GU + 8 * ((2 * cu) ^ g1) + (j & 7)] =
+          make_uint4(__builtin_bit_cast(uint32_t, b0), __builtin_bit_cast(uint32_t, b1),
+                     __builtin_bit_cast(uint32_t, b2), __builtin_bit_cast(uint32_t, b3));
+      buf0[G * GU + 8 * ((2 * cu + 1) ^ g1) + (j & 7)] =
+          make_uint4(__builtin_bit_cast(uint32_t, b4), __builtin_bit_cast(uint32_t, b5),
+                     __builtin_bit_cast(uint32_t, b6), __builtin_bit_cast(uint32_t, b7));
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int v = tid + 256 * k;
+      const int j = v & 63, ru = v >> 6;  // row, RoPE unit (bf16 chunk 64 + ru)
+      const int G = j >> 3;
+      buf0[G * GU + 8 * ((2 * CU8 + ru) ^ (G & 1)) + (j & 7)] = st[TAIL0 + 9 * j + ru];
+    }
   };
 
   // 1. the lane's RoPE frequency and the index reads of tiles 0..2;
@@ -1173,6 +1261,14 @@ void attn_bf16_row32_kernel(AttnArgs a) {
   TileIdx ixp = tile_idx(2, lane);  // index reads of tile t+2 during tile t
   buf0[tid] = make_uint4(0u, 0u, 0u, 0u);
   buf1[tid] = make_uint4(0u, 0u, 0u, 0u);
+  if (KV8) {
+    stg(1)[tid] = make_uint4(0u, 0u, 0u, 0u);
+    // the row codes of tiles 0 and 1 (wave w writes rows 16w .. 16w+15)
+    if ((lane >> 4) == wave) {
+      rowtab[lane] = code_of(lane, ix0.em);
+      rowtab[64 + lane] = code_of(64 + lane, ix1.em);
+    }
+  }
   lds_barrier();
 
   // 2. tile 0 requested (tile t+1 goes out during tile t's QK); bit j of
@@ -1182,8 +1278,12 @@ void attn_bf16_row32_kernel(AttnArgs a) {
   const int dma_row = dma_row_of(lane);
   const uint16_t* rp0[2] = {row_addr(code_of(dma_row, ix0.e0)), row_addr(code_of(dma_row + 8, ix0.e1))};
   const uint16_t* rp1[2] = {row_addr(code_of(64 + dma_row, ix1.e0)), row_addr(code_of(64 + dma_row + 8, ix1.e1))};
+  if (KV8) {
+    for (int q = 0; q < nq8; ++q) dma8(0, q, lane);
+  } else {
 #pragma unroll
-  for (int q = 0; q < CPW; ++q) dma_one(buf0, rp0, q, lane);
+    for (int q = 0; q < CPW; ++q) dma_one(buf0, rp0, q, lane);
+  }
 
   // 3. the row's q (64 heads, contiguous) into buf1 by DMA while tile 0
   // loads, 1 KB per instruction: 16-byte piece p = NCH*h + c (head h, chunk
@@ -1192,10 +1292,12 @@ void attn_bf16_row32_kernel(AttnArgs a) {
   // (16 heads of one chunk per 16 lanes) spread over the bank groups
   {
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)r * a.H * D;
+    // (KV8: into the bf16 tile buffer, free until tile 0 is converted)
+    uint4* qdst = KV8 ? buf0 : buf1;
 #pragma unroll
     for (int q = 0; q < CPW; ++q) {
       const int i = CPW * wave + q;
-      lds_dma16(qrow + 8 * (64 * i + (lane ^ (i & 15))), buf1 + 64 * i);
+      lds_dma16(qrow + 8 * (64 * i + (lane ^ (i & 15))), qdst + 64 * i);
     }
   }
   if (tid < a.d_rope / 2) {
@@ -1217,7 +1319,7 @@ void attn_bf16_row32_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int pc = pb + 2 * ks, ic = pc >> 6;
-      qf[ks] = *reinterpret_cast<const v8bf*>(buf1 + ((pc & ~63) | ((pc & 63) ^ (ic & 15))));
+      qf[ks] = *reinterpret_cast<const v8bf*>((KV8 ? buf0 : buf1) + ((pc & ~63) | ((pc & 63) ^ (ic & 15))));
       if (ks >= KR) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -1267,6 +1369,14 @@ void attn_bf16_row32_kernel(AttnArgs a) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const bool issue = t + 1 < ntiles;  // tile t+1
+    // KV8: the staged tile t becomes the bf16 tile (every wave is past tile
+    // t-1 and the query reads); its staging area then holds the probability
+    // exchange of this tile
+    if (KV8) {
+      convert8(t);
+      lds_barrier();
+    }
+    uint4* const pex = KV8 ? stg(t) : pex_b;
 
     // S^T[row 32ch + (8(i/4) + 4hi + i%4), head c32]; one DMA instruction
     // of tile t+1 per K-step block
@@ -1288,7 +1398,11 @@ void attn_bf16_row32_kernel(AttnArgs a) {
 #pragma unroll
       for (int blk = 0; blk < NQB; ++blk) {
         if (blk + 1 < NQB) load_k(blk + 1, kf[(blk + 1) & 1]);
-        if (issue && (blk & 1) == 0) dma_one(other, rp_nxt, blk >> 1, lq);
+        if (KV8) {
+          if (issue && (blk & 1) == 0) dma8(t + 1, blk >> 1, lq);
+        } else {
+          if (issue && (blk & 1) == 0) dma_one(other, rp_nxt, blk >> 1, lq);
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < QB; ++u) {
@@ -1332,8 +1446,8 @@ void attn_bf16_row32_kernel(AttnArgs a) {
       pf[i >> 3][i & 7] = (__bf16)pv;
     }
     l_part = l_part * alpha + ps;
-    pex[wave][0][lm] = __builtin_bit_cast(uint4, pf[0]);
-    pex[wave][1][lm] = __builtin_bit_cast(uint4, pf[1]);
+    pex[(2 * wave) * 64 + lm] = __builtin_bit_cast(uint4, pf[0]);
+    pex[(2 * wave + 1) * 64 + lm] = __builtin_bit_cast(uint4, pf[1]);
     if (__ballot(moved) != 0ull) {
 #pragma unroll
       for (int u = 0; u < HDT; ++u) acc[u] *= alpha;
@@ -1341,8 +1455,8 @@ void attn_bf16_row32_kernel(AttnArgs a) {
     lds_barrier();
     v8bf pp[2];
     const int lp = fresh_lane();
-    pp[0] = __builtin_bit_cast(v8bf, pex[pw][0][lp]);
-    pp[1] = __builtin_bit_cast(v8bf, pex[pw][1][lp]);
+    pp[0] = __builtin_bit_cast(v8bf, pex[(2 * pw) * 64 + lp]);
+    pp[1] = __builtin_bit_cast(v8bf, pex[(2 * pw + 1) * 64 + lp]);
     // O^T[dv, head] += V^T P^T over the 64 rows: K-chunk kc holds rows
     // 32(kc/2) + 16(kc%2) + {4hi+k, 8+4hi+k}, k < 4, whose probabilities are
     // elements 8(kc%2) .. +7 of half kc/2's lanes
@@ -1368,7 +1482,11 @@ void attn_bf16_row32_kernel(AttnArgs a) {
         if (blk + 1 < NVB) load_v(blk + 1, vf[(blk + 1) & 1]);
         // the second half of tile t+1's DMA, spread over the PV blocks
         constexpr int QD = (CPW + 1) / 2;  // issued during QK
-        if (issue && blk < CPW - QD) dma_one(other, rp_nxt, QD + blk, lp);
+        if (KV8) {
+          if (issue && 9 + blk < nq8) dma8(t + 1, 9 + blk, lp);  // (KV8: nine go out during QK)
+        } else {
+          if (issue && blk < CPW - QD) dma_one(other, rp_nxt, QD + blk, lp);
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < VB; ++u) {
@@ -1384,16 +1502,23 @@ void attn_bf16_row32_kernel(AttnArgs a) {
     // QK requests and its mask; then tile t+3's index reads
     const int le = fresh_lane();
     const int dre = dma_row_of(le);
-    rp_nxt[0] = row_addr(code_of(64 * (t + 2) + dre, ixp.e0));
-    rp_nxt[1] = row_addr(code_of(64 * (t + 2) + dre + 8, ixp.e1));
+    if (KV8) {
+      // tile t+2's row codes (its DMA goes out during tile t+1; tile t's
+      // table, the one overwritten, was read during tile t-1)
+      if ((le >> 4) == wave) rowtab[64 * (t & 1) + le] = code_of(64 * (t + 2) + le, ixp.em);
+    } else {
+      rp_nxt[0] = row_addr(code_of(64 * (t + 2) + dre, ixp.e0));
+      rp_nxt[1] = row_addr(code_of(64 * (t + 2) + dre + 8, ixp.e1));
+    }
     vm_cur = vm_n1;
     vm_n1 = __ballot(code_of(64 * (t + 2) + le, ixp.em) != -1);
     ixp = tile_idx(t + 3, le);
   };
 
+  // (KV8: every tile is converted into buf0; the staging areas alternate)
   for (int t = 0; t < ntiles; t += 2) {
     tile_step(buf0, buf1, t);
-    if (t + 1 < ntiles) tile_step(buf1, buf0, t + 1);
+    if (t + 1 < ntiles) tile_step(KV8 ? buf0 : buf1, buf0, t + 1);
   }
 
   // 4. the head group's sum over both halves, the sink, the output
@@ -1926,8 +2051,8 @@ static int attn_common(const char* fn, bool dense, const void* q, const int32_t*
                        const int32_t* n_entries, int m, const void* kv_w,
                        const int32_t* w_pos0, int S_w, int W, const float* sink, int B, int T,
                        int H, int D, int dv, int d_rope, float rope_base, float scale, int dtype,
-                       void* out, float* lse, int max_wg, void* workspace, size_t ws_bytes,
-                       void* stream) {
+                       int kv_dtype, void* out, float* lse, int max_wg, void* workspace,
+                       size_t ws_bytes, void* stream) {
   clear_error();
   std::string f(fn);
   if (!q || !q_pos || !kv_c || !out) return fail(CSK_EINVAL, f + ": null pointer");
@@ -1946,6 +2071,12 @@ static int attn_common(const char* fn, bool dense, const void* q, const int32_t*
     return fail(CSK_EUNSUPPORTED, f + ": dtype must be CSK_BF16 or CSK_F32");
   if (dv > 576) return fail(CSK_EUNSUPPORTED, f + ": dv > 576 not built");
   if (max_wg < 0) return fail(CSK_EINVAL, f + ": max_workgroups must be >= 0");
+  const bool kv8 = kv_dtype == CSK_FP8KV;
+  if (kv_dtype != dtype && !kv8)
+    return fail(CSK_EUNSUPPORTED, f + ": kv_dtype must equal dtype or be CSK_FP8KV");
+  if (kv8 && (dtype != CSK_BF16 || H != 64 || D != 576 || dv != 512 || d_rope != 64))
+    return fail(CSK_EUNSUPPORTED,
+                f + ": FP8 KV entries are built for bf16 queries, 64 heads, D = 576 (512 + 64 RoPE), dv = 512");
   const int Wslots = S_w > 0 ? W : 0;
   const int Lc = dense ? Nmax : k;
   AttnPlan p = plan_attn(dense, B, T, H, D, dv, Lc, Wslots, dtype, max_wg);
@@ -1983,15 +2114,20 @@ static int attn_common(const char* fn, bool dense, const void* q, const int32_t*
 #undef CSK_QT_CASE
     return rc;
   }
+  if (kv8 && !p.row32) return fail(CSK_EUNSUPPORTED, f + ": FP8 KV entries need the 64-head streamed-row kernel");
   if (p.row32) {
     rc = CSK_EUNSUPPORTED;
     const dim3 grid(R, p.nch);
 #define CSK_R32_CASE(d, v)                                                                       \
-  if (D == d && dv == v)                                                                         \
-    rc = dense ? launch("attn_bf16_dense", attn_bf16_row32_kernel<d, v, true>, grid, dim3(256), 0, s, a) \
-               : launch("attn_bf16_sparse", attn_bf16_row32_kernel<d, v, false>, grid, dim3(256), 0, s, a);
+  if (D == d && dv == v && !kv8)                                                                 \
+    rc = dense ? launch("attn_bf16_dense", attn_bf16_row32_kernel<d, v, true, false>, grid, dim3(256), 0, s, a) \
+               : launch("attn_bf16_sparse", attn_bf16_row32_kernel<d, v, false, false>, grid, dim3(256), 0, s, a);
     CSK_R32_CASE(576, 512) CSK_R32_CASE(256, 256) CSK_R32_CASE(128, 128) CSK_R32_CASE(64, 64)
 #undef CSK_R32_CASE
+    if (kv8)
+      rc = dense ? launch("attn_bf16_dense", attn_bf16_row32_kernel<576, 512, true, true>, grid, dim3(256), 0, s, a)
+                 : launch("attn_bf16_sparse", attn_bf16_row32_kernel<576, 512, false, true>, grid, dim3(256), 0,
+                          s, a);
   } else if (p.mfma) {
     dim3 grid(R, p.nch), block(64 * (H / 16));
 const int NW = H / 16;
@@ -2048,23 +2184,23 @@ size_t dense_compressed_attn_workspace_size(int B, int T, int H, int D, int dv, 
 int sparse_attn(const void* q, const int32_t* q_pos, const void* kv_c, int Nmax,
                 const int32_t* idx, int k, const void* kv_w, const int32_t* w_pos0, int S_w,
                 int W, const float* sink, int B, int T, int H, int D, int dv, int d_rope,
-                float rope_base, float scale, int dtype, void* out, float* lse, int max_workgroups,
-                void* workspace, size_t ws_bytes, void* stream) {
+                float rope_base, float scale, int dtype, int kv_dtype, void* out, float* lse,
+                int max_workgroups, void* workspace, size_t ws_bytes, void* stream) {
   return csk::attn_common("sparse_attn", false, q, q_pos, kv_c, Nmax, idx, k, nullptr, 1, kv_w,
                           w_pos0, S_w, W, sink, B, T, H, D, dv, d_rope, rope_base, scale, dtype,
-                          out, lse, max_workgroups, workspace, ws_bytes, stream);
+                          kv_dtype, out, lse, max_workgroups, workspace, ws_bytes, stream);
 }
 
 int dense_compressed_attn(const void* q, const int32_t* q_pos, const void* kv_c, int Nmax,
                           const int32_t* n_entries, int m, const void* kv_w,
                           const int32_t* w_pos0, int S_w, int W, const float* sink, int B, int T,
                           int H, int D, int dv, int d_rope, float rope_base, float scale,
-                          int dtype, void* out, float* lse, int max_workgroups, void* workspace,
-                          size_t ws_bytes, void* stream) {
+                          int dtype, int kv_dtype, void* out, float* lse, int max_workgroups,
+                          void* workspace, size_t ws_bytes, void* stream) {
   return csk::attn_common("dense_compressed_attn", true, q, q_pos, kv_c, Nmax, nullptr, 0,
                           n_entries, m, kv_w, w_pos0, S_w, W, sink, B, T, H, D, dv, d_rope,
-                          rope_base, scale, dtype, out, lse, max_workgroups, workspace, ws_bytes,
-                          stream);
+                          rope_base, scale, dtype, kv_dtype, out, lse, max_workgroups, workspace,
+                          ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -81,6 +81,38 @@ __device__ __forceinline__ int mx_scale_exp(float amax) {
   return s;
 }
 
+// OCP E4M3 code (sign bit 7, exponent bits 6..3 with bias 7, mantissa bits
+// 2..0; exponent 0 is subnormal, m * 2^-9) of x under the block exponent s,
+// for |x| / 2^s < 256 (the caller's scale choice): the nearest value, ties
+// to the even mantissa (rintf), zero as +0. Scaling by a power of two is
+// exact, so the code is decided on the exact quotient.
+__device__ __forceinline__ uint32_t e4m3_encode(float x, int s) {
+  const float y = ldexpf(fabsf(x), -s);
+  const int e = ilogbf(y);
+  uint32_t c;
+  if (y == 0.0f) c = 0u;
+  else if (e < -6) c = (uint32_t)rintf(ldexpf(y, 9));                          // 0..8 (8: 2^-6)
+  else c = ((uint32_t)(e + 7) << 3) + (uint32_t)rintf(ldexpf(y, 3 - e)) - 8u;  // carries into e+1
+  return (c != 0u && x < 0.0f) ? (c | 0x80u) : c;
+}
+
+// Block exponent of an FP8 KV block with absolute maximum amax > 0: the
+// maximum lands in [128, 256); clamped to [-126, 127] so that 2^s is a
+// normal fp32.
+__device__ __forceinline__ int fp8kv_scale_exp(float amax) {
+  int s = ilogbf(amax) - 7;
+  s = s < -126 ? -126 : s;
+  s = s > 127 ? 127 : s;
+  return s;
+}
+
+// Bytes of one FP8 KV entry: [D - d_rope codes][d_rope bf16][scales],
+// padded to a multiple of 16.
+__host__ __device__ __forceinline__ int fp8kv_entry_bytes(int D, int d_rope) {
+  const int dn = D - d_rope;
+  return (dn + 2 * d_rope + dn / 32 + 15) / 16 * 16;
+}
+
 // Signed 4-bit code of x under the tile exponent s.
 __device__ __forceinline__ uint32_t e2m1_encode(float x, int s) {
   float y = ldexpf(fabsf(x), -s);

@@ -17,7 +17,7 @@
 
 namespace csk {
 
-enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_MXFP4 = 2 };
+enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_MXFP4 = 2, OUT_FP8KV = 3 };
 
 struct CompressArgs {
   const void* ca;
@@ -119,6 +119,31 @@ __device__ __forceinline__ void store_pair(const CompressArgs& a, int64_t orow, 
   } else if (OUT == OUT_BF16) {
     uint32_t* o = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.out) + orow * a.D + 2 * p);
     *o = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+  } else if (OUT == OUT_FP8KV) {
+    // FP8 KV entry: 16 consecutive lanes hold one block of 32 non-RoPE
+    // channels (E4M3 codes under the block's scale); RoPE channels stay bf16.
+    // Every lane forms the block maximum (the DPP steps need the whole row
+    // of 16 lanes; RoPE lanes ignore it). D - d_rope is a multiple of 32, so
+    // a row of 16 lanes is all codes or all RoPE.
+    const int dn = a.D - a.d_rope;
+    const int es = fp8kv_entry_bytes(a.D, a.d_rope);
+    uint8_t* e = reinterpret_cast<uint8_t*>(a.out) + orow * es;
+    const float amax = row16_max(fmaxf(fabsf(v0), fabsf(v1)));
+    const int ch = 2 * p;
+    if (ch < dn) {
+      uint32_t codes = 0u, sc = 127u;
+      if (amax != 0.0f) {
+        const int s = fp8kv_scale_exp(amax);
+        codes = e4m3_encode(v0, s) | (e4m3_encode(v1, s) << 8);
+        sc = (uint32_t)(s + 127);
+      }
+      *reinterpret_cast<uint16_t*>(e + ch) = (uint16_t)codes;
+      if ((p & 15) == 0) e[dn + 2 * a.d_rope + ch / 32] = (uint8_t)sc;
+    } else {
+      *reinterpret_cast<uint32_t*>(e + dn + 2 * (ch - dn)) = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+    }
+    if (p == 0)  // the padding past the scales
+      for (int z = dn + 2 * a.d_rope + dn / 32; z < es; ++z) e[z] = 0;
   } else {
     // 16 consecutive lanes hold one tile of 32 channels
     float amax = fmaxf(fabsf(v0), fabsf(v1));
@@ -335,10 +360,12 @@ __global__ __launch_bounds__(64) void compress_batch_kernel(BatchArgs args) {
   } else if (j.in_bf16) {
     if (j.out_kind == OUT_BF16) compress_pair<uint16_t, OUT_BF16, true>(j.a, p, row);
     else if (j.out_kind == OUT_MXFP4) compress_pair<uint16_t, OUT_MXFP4, true>(j.a, p, row);
+    else if (j.out_kind == OUT_FP8KV) compress_pair<uint16_t, OUT_FP8KV, true>(j.a, p, row);
     else compress_pair<uint16_t, OUT_F32, true>(j.a, p, row);
   } else {
     if (j.out_kind == OUT_BF16) compress_pair<float, OUT_BF16, true>(j.a, p, row);
     else if (j.out_kind == OUT_MXFP4) compress_pair<float, OUT_MXFP4, true>(j.a, p, row);
+    else if (j.out_kind == OUT_FP8KV) compress_pair<float, OUT_FP8KV, true>(j.a, p, row);
     else compress_pair<float, OUT_F32, true>(j.a, p, row);
   }
 }
@@ -351,6 +378,7 @@ static int launch_compress_out(const char* name, const CompressArgs& a, int out_
     switch (out_dtype) {
       case CSK_F32: return launch(name, compress_wide_kernel<IN, OUT_F32, CSA>, grid, block, 0, s, a);
       case CSK_BF16: return launch(name, compress_wide_kernel<IN, OUT_BF16, CSA>, grid, block, 0, s, a);
+      case CSK_FP8KV: return launch(name, compress_wide_kernel<IN, OUT_FP8KV, CSA>, grid, block, 0, s, a);
       default: return launch(name, compress_wide_kernel<IN, OUT_MXFP4, CSA>, grid, block, 0, s, a);
     }
   }
@@ -363,6 +391,7 @@ static int launch_compress_out(const char* name, const CompressArgs& a, int out_
   switch (out_dtype) {
     case CSK_F32: return launch(name, compress_kernel<IN, OUT_F32, CSA>, grid, block, 0, s, a);
     case CSK_BF16: return launch(name, compress_kernel<IN, OUT_BF16, CSA>, grid, block, 0, s, a);
+    case CSK_FP8KV: return launch(name, compress_kernel<IN, OUT_FP8KV, CSA>, grid, block, 0, s, a);
     default: return launch(name, compress_kernel<IN, OUT_MXFP4, CSA>, grid, block, 0, s, a);
   }
 }
@@ -387,10 +416,12 @@ static int prepare_compress(const std::string& f, bool csa, const void* ca, cons
     return fail(CSK_EUNSUPPORTED, f + ": at most 128 rotated channels are built");
   if (in_dtype != CSK_F32 && in_dtype != CSK_BF16)
     return fail(CSK_EUNSUPPORTED, f + ": in_dtype must be CSK_F32 or CSK_BF16");
-  if (out_dtype != CSK_F32 && out_dtype != CSK_BF16 && out_dtype != CSK_MXFP4)
-    return fail(CSK_EUNSUPPORTED, f + ": out_dtype must be CSK_F32, CSK_BF16 or CSK_MXFP4");
+  if (out_dtype != CSK_F32 && out_dtype != CSK_BF16 && out_dtype != CSK_MXFP4 && out_dtype != CSK_FP8KV)
+    return fail(CSK_EUNSUPPORTED, f + ": out_dtype must be CSK_F32, CSK_BF16, CSK_MXFP4 or CSK_FP8KV");
   if (out_dtype == CSK_MXFP4 && (D % 32 || (!out_scale && !empty)))
     return fail(CSK_EINVAL, f + ": MXFP4 output needs D % 32 == 0 and out_scale");
+  if (out_dtype == CSK_FP8KV && (D - d_rope) % 32)
+    return fail(CSK_EINVAL, f + ": FP8KV output needs (D - d_rope) % 32 == 0");
   const int N = S / m;
   if (src_bstride < 0 || (src_bstride != 0 && src_bstride < S))
     return fail(CSK_EINVAL, f + ": src_bstride must be 0 or >= S");
@@ -470,7 +501,8 @@ static int compress_batch(const csk_compress_job* jobs, int n_jobs, void* stream
       if (empty) continue;
       rows = (int64_t)bj.a.B * bj.a.N;
       bj.in_bf16 = j.in_dtype == CSK_BF16;
-      bj.out_kind = j.out_dtype == CSK_F32 ? OUT_F32 : j.out_dtype == CSK_BF16 ? OUT_BF16 : OUT_MXFP4;
+      bj.out_kind = j.out_dtype == CSK_F32 ? OUT_F32 : j.out_dtype == CSK_BF16 ? OUT_BF16
+                    : j.out_dtype == CSK_FP8KV ? OUT_FP8KV : OUT_MXFP4;
     } else if (j.kind == CSK_JOB_MXFP4) {
       const int rc = check_quantize(f + " (mxfp4_quantize)", j.x, j.in_dtype, j.rows, j.cols,
                                     reinterpret_cast<const uint8_t*>(j.out), j.out_scale);

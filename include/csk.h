@@ -33,6 +33,17 @@
  * - Dtypes: CSK_F32 = float32, CSK_BF16 = bfloat16 (uint16 bit patterns),
  *   CSK_MXFP4 = packed E2M1 codes (element 2j in the low nibble of byte j)
  *   plus one E8M0 scale byte (2^(byte-127)) per 32 consecutive elements.
+ *   CSK_FP8KV = a KV entry of D values whose last d_rope (RoPE) dims stay
+ *   bf16 and whose first D_nope = D - d_rope dims are OCP E4M3 codes with
+ *   one power-of-two scale byte (2^(byte-127)) per 32 dims ([P2]: FP8 KV
+ *   storage; [P1] «Почему это так сильно экономит», item 1: FP8 KV with
+ *   BF16 RoPE dims). Entry bytes: [D_nope codes][d_rope bf16][D_nope/32
+ *   scales], padded with zeros to csk_fp8kv_entry_bytes(D, d_rope), a
+ *   multiple of 16 (656 for 512 + 64, against 1152 in bf16). The scale of a
+ *   block puts its largest magnitude in [128, 256) (s = floor(log2 amax) -
+ *   7, clamped to [-126, 127]; an all-zero block has byte 127); codes are
+ *   the nearest E4M3 value of x / 2^s, ties to the even mantissa, zero as
+ *   the +0 code.
  * - Errors: every call returns CSK_OK (0) or a negative code and leaves a
  *   message for csk_last_error() (thread-local). Nothing aborts or prints.
  * - Determinism: results are bitwise reproducible run to run for the same
@@ -66,6 +77,11 @@ extern "C" {
 #define CSK_F32 0
 #define CSK_BF16 1
 #define CSK_MXFP4 2
+#define CSK_FP8KV 3
+
+/* Bytes of one CSK_FP8KV entry of D values with d_rope RoPE dims (0 for a
+ * shape that has none: D - d_rope not a multiple of 32, or d_rope odd). */
+int csk_fp8kv_entry_bytes(int D, int d_rope);
 
 /* Message for the last failing call on this thread ("" if none). */
 const char* csk_last_error(void);
@@ -100,9 +116,12 @@ int csk_abi_version(void);
  *   src_bstride    : rows between batches in the sources (0 means S).
  *   d_rope         : rotated channels (even, <= D; 0 = none).
  *   entry_pos      : [B, N] int32 entry positions, or NULL for m*(entry0+i).
- *   out_dtype      : CSK_F32 | CSK_BF16 | CSK_MXFP4 (MXFP4 needs D % 32 == 0).
+ *   out_dtype      : CSK_F32 | CSK_BF16 | CSK_MXFP4 (MXFP4 needs D % 32 ==
+ *                    0) | CSK_FP8KV (needs (D - d_rope) % 32 == 0).
  *   out            : entry i of batch b at (b*dst_bstride + i)*D elements
- *                    (MXFP4: codes at byte offset (b*dst_bstride + i)*D/2).
+ *                    (MXFP4: codes at byte offset (b*dst_bstride + i)*D/2;
+ *                    FP8KV: the entry at byte (b*dst_bstride + i)*ES, ES =
+ *                    csk_fp8kv_entry_bytes(D, d_rope)).
  *   out_scale      : MXFP4 only: scales at byte (b*dst_bstride + i)*D/32.
  *   dst_bstride    : entries between batches in the output (0 means N).
  */
@@ -263,8 +282,14 @@ int indexer_topk_noalloc(const void* q, const uint8_t* q_scale, const float* w, 
  * With no candidate and no sink, out = 0 and lse = -inf.
  *
  *   q       : [B,T,H,D] dtype, unrotated;  q_pos: [B,T] int32.
- *   kv_c    : [B,Nmax,D] dtype (entries already rotated);  idx: [B,T,k].
- *   kv_w    : [B,S_w,D] dtype (already rotated) or NULL with S_w = 0.
+ *   kv_c    : [B,Nmax,D] kv_dtype (entries already rotated);  idx: [B,T,k].
+ *   kv_w    : [B,S_w,D] kv_dtype (already rotated) or NULL with S_w = 0.
+ *   kv_dtype: the dtype of kv_c and kv_w: dtype, or CSK_FP8KV entries
+ *             ([B,Nmax,ES] bytes, ES = csk_fp8kv_entry_bytes(D, d_rope); built
+ *             for dtype CSK_BF16, H = 64, D = 576, d_rope = 64, dv = 512). An
+ *             FP8 entry is used as its exact value (E4M3 code times its
+ *             block's scale, or the bf16 RoPE dim), so the result is that of
+ *             bf16 attention over the decoded entries.
  *   w_pos0  : [B] int32 position of window row 0 (may be NULL if S_w = 0).
  *   sink    : [H] fp32 or NULL (no sink).
  *   dtype   : CSK_BF16 (fp32 accumulation) or CSK_F32.
@@ -283,7 +308,7 @@ int indexer_topk_noalloc(const void* q, const uint8_t* q_scale, const float* w, 
 int sparse_attn(const void* q, const int32_t* q_pos, const void* kv_c, int Nmax,
                 const int32_t* idx, int k, const void* kv_w, const int32_t* w_pos0, int S_w,
                 int W, const float* sink, int B, int T, int H, int D, int dv, int d_rope,
-                float rope_base, float scale, int dtype, void* out, float* lse,
+                float rope_base, float scale, int dtype, int kv_dtype, void* out, float* lse,
                 int max_workgroups, void* workspace, size_t ws_bytes, void* stream);
 size_t sparse_attn_workspace_size(int B, int T, int H, int D, int dv, int k, int W, int dtype,
                                   int max_workgroups);
@@ -299,8 +324,8 @@ int dense_compressed_attn(const void* q, const int32_t* q_pos, const void* kv_c,
                           const int32_t* n_entries, int m, const void* kv_w,
                           const int32_t* w_pos0, int S_w, int W, const float* sink, int B, int T,
                           int H, int D, int dv, int d_rope, float rope_base, float scale,
-                          int dtype, void* out, float* lse, int max_workgroups, void* workspace,
-                          size_t ws_bytes, void* stream);
+                          int dtype, int kv_dtype, void* out, float* lse, int max_workgroups,
+                          void* workspace, size_t ws_bytes, void* stream);
 size_t dense_compressed_attn_workspace_size(int B, int T, int H, int D, int dv, int Nmax, int m,
                                             int W, int dtype, int max_workgroups);
 

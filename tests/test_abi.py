@@ -75,11 +75,24 @@ def test_attn_workgroup_cap(lib):
     assert lib.sparse_attn_workspace_size(4, 1, 64, 576, 512, 2048, 128, 1, 0) > 0
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.sparse_attn.argtypes = ([vp, vp, vp, i, vp, i, vp, vp, i, i, vp] + [i] * 6
-                                + [f, f, i, vp, vp, i, vp, ctypes.c_size_t, vp])
+                                + [f, f, i, i, vp, vp, i, vp, ctypes.c_size_t, vp])
     fake = 4096
     rc = lib.sparse_attn(fake, fake, fake, 100, fake, 8, None, None, 0, 0, None, 1, 1, 64, 576, 512, 64,
-                         10000.0, 0.05, 1, fake, None, -5, None, 0, None)
+                         10000.0, 0.05, 1, 1, fake, None, -5, None, 0, None)
     assert rc == -1 and b"max_workgroups" in lib.csk_last_error()
+    # FP8 KV entries are built for the 64-head 512 + 64 shape only
+    rc = lib.sparse_attn(fake, fake, fake, 100, fake, 8, None, None, 0, 0, None, 1, 1, 16, 576, 512, 64,
+                         10000.0, 0.05, 1, 3, fake, None, 0, None, 0, None)
+    assert rc == -2 and b"FP8" in lib.csk_last_error()
+    rc = lib.sparse_attn(fake, fake, fake, 100, fake, 8, None, None, 0, 0, None, 1, 1, 64, 576, 512, 64,
+                         10000.0, 0.05, 0, 3, fake, None, 0, None, 0, None)
+    assert rc == -2
+
+
+def test_fp8kv_entry_bytes(lib):
+    assert lib.csk_fp8kv_entry_bytes(576, 64) == 656
+    assert lib.csk_fp8kv_entry_bytes(64, 32) == 112
+    assert lib.csk_fp8kv_entry_bytes(576, 63) == 0 and lib.csk_fp8kv_entry_bytes(100, 20) == 0
 
 
 def test_no_device_is_unsupported(lib):
