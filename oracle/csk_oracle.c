@@ -390,13 +390,13 @@ static double e4m3_value(int code) {
 }
 
 /* Nearest non-negative E4M3 code of y in [0, 448]: the plain definition,
- * a search over the 127 finite codes; ties go to the code whose mantissa
- * (its low bit) is even. */
-static int e4m3_code_abs(double y) {
+ * a search over the 127 finite codes (their values in `val`); ties go to the
+ * code whose mantissa (its low bit) is even. */
+static int e4m3_code_abs(double y, const double* val) {
   int best = 0;
   double bd = INFINITY;
   for (int c = 0; c < 127; ++c) {
-    const double d = fabs(e4m3_value(c) - y);
+    const double d = fabs(val[c] - y);
     if (d < bd || (d == bd && (c & 1) == 0)) {
       best = c;
       bd = d;
@@ -415,6 +415,10 @@ int csk_ref_fp8kv_encode(const float* x, int64_t rows, int D, int d_rope, uint8_
   const int dn = D - d_rope;
   if (D <= 0 || d_rope < 0 || d_rope > D || (d_rope & 1) || dn % 32 || rows < 0) return -1;
   const int ES = csk_ref_fp8kv_entry_bytes(D, d_rope);
+  double val[127];
+  for (int c = 0; c < 127; ++c) val[c] = e4m3_value(c);
+  /* entries are independent: one per iteration, any thread */
+#pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; ++r) {
     const float* xr = x + r * D;
     uint8_t* o = out + r * ES;
@@ -434,7 +438,7 @@ int csk_ref_fp8kv_encode(const float* x, int64_t rows, int D, int d_rope, uint8_
       o[dn + 2 * d_rope + g] = (uint8_t)byte;
       for (int i = 0; i < 32; ++i) {
         const double v = (double)xr[32 * g + i];
-        const int c = amax > 0.0 ? e4m3_code_abs(ldexp(fabs(v), -s)) : 0;
+        const int c = amax > 0.0 ? e4m3_code_abs(ldexp(fabs(v), -s), val) : 0;
         o[32 * g + i] = (uint8_t)((v < 0.0 && c != 0) ? (c | 0x80) : c);
       }
     }
@@ -451,6 +455,7 @@ int csk_ref_fp8kv_decode(const uint8_t* in, int64_t rows, int D, int d_rope, flo
   const int dn = D - d_rope;
   if (D <= 0 || d_rope < 0 || d_rope > D || (d_rope & 1) || dn % 32 || rows < 0) return -1;
   const int ES = csk_ref_fp8kv_entry_bytes(D, d_rope);
+#pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; ++r) {
     const uint8_t* e = in + r * ES;
     float* xr = x + r * D;
