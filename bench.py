@@ -60,7 +60,7 @@ class DecodeWorkload:
     'csa_decode_128k' (CSA only), with host copies for the oracle."""
 
     def __init__(self, name, copies=4, overrides=None, keep_host=True, streams=1, hca_workgroups=64,
-                 csa_workgroups=0, score_dtype=0):
+                 csa_workgroups=0, score_dtype=0, kv_fp8=False):
         import torch
 
         import compressed_sparse_kv_amd as csk
@@ -76,6 +76,12 @@ class DecodeWorkload:
         self.N = d["kv_c"].shape[1]
         self.HI, self.dI, self.k, self.W = d["HI"], d["dI"], d["k"], d["W"]
         self.scale = d["scale"]
+        # KV entries: bf16, or FP8 (E4M3 non-RoPE dims with a power-of-two
+        # scale per 32, the 64 RoPE dims in bf16)
+        self.kv_fp8 = kv_fp8
+        self.kv_out = csk.CSK_FP8KV if kv_fp8 else csk.CSK_BF16
+        self.entry_bytes = csk.fp8kv_entry_bytes(self.D, 64) if kv_fp8 else 2 * self.D
+        self.h8 = None
         if not self.pair:
             # the CSA-only workload appends its newest entry from these sources
             g = synth.rng(1000 + d["B"])
@@ -89,18 +95,20 @@ class DecodeWorkload:
         dev = torch.device("cuda:0")
         self.dev = dev
         T = lambda a: _to_dev(torch, a, dev)
+        # KV caches and windows as the attention reads them
+        TK = (lambda a: self._fp8(T(a))) if kv_fp8 else T
         # per-copy persistent state: caches and windows
-        kv_c0 = T(d["kv_c"])
+        kv_c0 = TK(d["kv_c"])
         kI = T(d["kI"])
         kc0, ks0 = csk.mxfp4_quantize(kI)
         del kI
         self.copies = []
         for c in range(copies):
             st = {"kv_c": kv_c0 if c == 0 else kv_c0.clone(), "kc": kc0 if c == 0 else kc0.clone(),
-                  "ks": ks0 if c == 0 else ks0.clone(), "kv_w": T(d["kv_w"])}
+                  "ks": ks0 if c == 0 else ks0.clone(), "kv_w": TK(d["kv_w"])}
             if self.pair:
-                st["kv_h"] = T(d["kv_h"])
-                st["kv_w_h"] = T(d["kv_w_h"])
+                st["kv_h"] = TK(d["kv_h"])
+                st["kv_w_h"] = TK(d["kv_w_h"])
             self.copies.append(st)
         # per-step inputs (shared by the copies)
         self.x = {k: T(d[k]) for k in ("q", "qI", "w", "q_pos", "w_pos0", "n_entries", "sink",
@@ -150,8 +158,8 @@ class DecodeWorkload:
                             out=st["kc_new"], out_scale=st["ks_new"], dst_bstride=N, S=4, B=B),
                 csk.mxfp4_job(x["qI"], self.qc, self.qs),
                 csk.csa_job(x["src_ca4"], x["src_za4"], x["src_cb4"], x["src_zb4"], x["bias_a"], x["bias_b"],
-                            4, d_rope=64, entry0=N - 1, src_bstride=8, out=st["kv_new"], dst_bstride=N,
-                            S=4, B=B)]
+                            4, d_rope=64, entry0=N - 1, src_bstride=8, out_dtype=self.kv_out, out=st["kv_new"],
+                            dst_bstride=N, S=4, B=B)]
         # the side stream of the HCA branch (default priority), and the
         # workgroup cap of its attention when it runs beside the CSA chain
         self.streams = streams
@@ -202,7 +210,7 @@ class DecodeWorkload:
         """The HCA branch: the newest HCA entry, then dense attention."""
         csk, Nh = self.csk, self.Nh
         csk.hca_compress(x["src_c"], x["src_z"], x["bias_h"], 128, d_rope=64, entry0=Nh - 1,
-                         out=st["kvh_new"], dst_bstride=Nh)
+                         out_dtype=self.kv_out, out=st["kvh_new"], dst_bstride=Nh)
         # beside the CSA chain the dense attention takes at most
         # hca_workgroups workgroups (each holds a whole CU), which leaves the
         # rest of the chip to the chain's kernels
@@ -210,6 +218,20 @@ class DecodeWorkload:
         csk.dense_compressed_attn(x["q_h"], x["q_pos"], st["kv_h"], x["n_entries_h"], 128, st["kv_w_h"],
                                   x["w_pos0"], self.W, x["sink_h"], self.dv, 64, self.scale,
                                   out=self.out_h, lse=self.lse_h, workspace=self.ws_d, max_workgroups=cap)
+
+    def _fp8(self, x):
+        """bf16 entries [B,S,D] (already rotated) as FP8 KV entries, encoded
+        on the GPU by the compression kernel with one token per entry (its
+        softmax weight is exactly 1, zero bias) at RoPE position 0 (the
+        identity rotation): the entries' own values, encoded."""
+        torch, csk = self.torch, self.csk
+        B, S, D = x.shape
+        z = torch.zeros_like(x)
+        bias = torch.zeros((1, D), dtype=torch.float32, device=x.device)
+        pos = torch.zeros((B, S), dtype=torch.int32, device=x.device)
+        e = csk.hca_compress(x, z, bias, 1, d_rope=64, entry_pos=pos, out_dtype=csk.CSK_FP8KV)
+        del x, z
+        return e
 
     def kernels(self):
         names = ["csk_compress_batch", "indexer_scores_fp4", "topk_filter",
@@ -227,12 +249,13 @@ class DecodeWorkload:
         """Bytes the method must move in one launch of `kernel`."""
         B, N, D, dI, HI, k, W, H, dv = (self.B, self.N, self.D, self.dI, self.HI, self.k, self.W,
                                         self.H, self.dv)
+        E = self.entry_bytes
         if kernel == "indexer_scores_fp4":
             return B * N * (dI // 2 + dI // 32) + B * HI * (dI // 2 + dI // 32 + 4)
         if kernel == "attn_bf16_sparse":
-            return B * (k + W) * D * 2 + B * k * 4 + B * H * (D + dv) * 2
+            return B * (k + W) * E + B * k * 4 + B * H * (D + dv) * 2
         if kernel == "attn_bf16_dense":
-            return B * (self.Nh + W) * D * 2 + B * H * (D + dv) * 2
+            return B * (self.Nh + W) * E + B * H * (D + dv) * 2
         return None
 
     def step_bytes(self):
@@ -245,12 +268,45 @@ class DecodeWorkload:
         c = {"workload": self.name, "batch": self.B, "context": int(self.N * 4), "csa_entries": self.N,
              "heads": self.H, "kv_dim": self.D, "value_dim": self.dv, "rope_dims": 64, "indexer_heads": self.HI,
              "indexer_dim": self.dI, "indexer_dtype": "mxfp4", "top_k": self.k, "window": self.W, "sink": True,
-             "state_copies": len(self.copies), "topk_scores": "bf16" if self.score_dtype else "f32"}
+             "state_copies": len(self.copies), "topk_scores": "bf16" if self.score_dtype else "f32",
+             "kv_entries": "fp8_e4m3_scale32+bf16_rope" if self.kv_fp8 else "bf16"}
         if self.pair:
             c["hca_entries"] = self.Nh
         return c
 
     # --------------------------------------------------------- oracle step
+    def oracle_prepare(self, rows):
+        """FP8 KV: the host caches of the batch rows `rows` as the oracle's
+        own encoder writes them (the step's input state, made once, untimed)."""
+        import oracle
+
+        if not self.kv_fp8 or (self.h8 is not None and self.h8["rows"] == list(rows)):
+            return
+        d, sel = self.d, list(rows)
+        self.h8 = {"rows": sel}
+        for k in ("kv_c", "kv_w") + (("kv_h", "kv_w_h") if self.pair else ()):
+            self.h8[k] = oracle.fp8kv_encode(d[k][sel], 64)
+
+    def _oracle_kv(self, name, sel):
+        """A cache of the batch rows `sel` as the oracle's attention reads
+        it: bf16 values, or the FP8 entries decoded."""
+        import oracle
+
+        if not self.kv_fp8:
+            return self.d[name][sel]
+        return oracle.fp8kv_decode(self.h8[name], self.D, 64)
+
+    def _oracle_entry(self, e):
+        """A newest entry (fp64) as the cache stores it, and as the
+        attention reads it."""
+        import oracle
+
+        if not self.kv_fp8:
+            b = oracle.round_bf16(e)
+            return b, b
+        b = oracle.fp8kv_encode(oracle.round_f32(e), 64)
+        return b, oracle.fp8kv_decode(b, self.D, 64)
+
     def oracle_step(self, rows):
         """The same decode step on the CPU oracle for the batch rows `rows`.
         Returns a dict of results; the wall time is the caller's."""
@@ -264,7 +320,8 @@ class DecodeWorkload:
         ca, za, cb, zb = (d[k][sel] for k in ("src_ca", "src_za", "src_cb", "src_zb"))
         pos = np.array([[4 * (N - 2), 4 * (N - 1)]] * len(sel), np.int32)
         e = oracle.csa_compress(ca, za, cb, zb, d["bias_a"], d["bias_b"], 4, d_rope=64, entry_pos=pos)[:, 1]
-        out["kv_new"] = oracle.round_bf16(e)
+        self.oracle_prepare(sel)
+        out["kv_new"], kv_new = self._oracle_entry(e)
         ia, iza, ib, izb = (d[k][sel] for k in ("src_ia", "src_iza", "src_ib", "src_izb"))
         ek = oracle.csa_compress(ia, iza, ib, izb, d["ibias_a"], d["ibias_b"], 4)[:, 1]
         kn_c, kn_s = oracle.mxfp4_encode(oracle.round_f32(ek))
@@ -272,8 +329,8 @@ class DecodeWorkload:
         kc, ks = oracle.mxfp4_encode(d["kI"][sel])
         kc[:, N - 1], ks[:, N - 1] = kn_c, kn_s
         out["kc"], out["ks"] = kc, ks
-        kv_c = d["kv_c"][sel].copy()
-        kv_c[:, N - 1] = out["kv_new"]
+        kv_c = self._oracle_kv("kv_c", sel).copy()
+        kv_c[:, N - 1] = kv_new
         qc, qs = oracle.mxfp4_encode(d["qI"][sel])
         out["qc"], out["qs"] = qc, qs
         npos = d["q_pos"][sel]
@@ -284,7 +341,8 @@ class DecodeWorkload:
         idx, sc = oracle.topk(scores, nvis, self.k)
         out["idx"], out["score"] = idx, sc
         out["scores_full"], out["n_vis"] = scores, nvis
-        o, l = oracle.sparse_attn(d["q"][sel], npos, kv_c, idx[:, None, :], d["kv_w"][sel], d["w_pos0"][sel],
+        o, l = oracle.sparse_attn(d["q"][sel], npos, kv_c, idx[:, None, :], self._oracle_kv("kv_w", sel),
+                                  d["w_pos0"][sel],
                                   self.W, d["sink"], self.dv, 64, d["scale"])
         out["out"], out["lse"] = o, l
         if self.pair:
@@ -292,10 +350,11 @@ class DecodeWorkload:
             c, z = d["src_c"][sel], d["src_z"][sel]
             eh = oracle.hca_compress(c, z, d["bias_h"], 128, d_rope=64,
                                      entry_pos=np.full((len(sel), 1), 128 * (Nh - 1), np.int32))[:, 0]
-            out["kvh_new"] = oracle.round_bf16(eh)
-            kv_h = d["kv_h"][sel].copy()
-            kv_h[:, Nh - 1] = out["kvh_new"]
-            oh, lh = oracle.dense_attn(d["q_h"][sel], npos, kv_h, d["n_entries_h"][sel], 128, d["kv_w_h"][sel],
+            out["kvh_new"], kvh_new = self._oracle_entry(eh)
+            kv_h = self._oracle_kv("kv_h", sel).copy()
+            kv_h[:, Nh - 1] = kvh_new
+            oh, lh = oracle.dense_attn(d["q_h"][sel], npos, kv_h, d["n_entries_h"][sel], 128,
+                                       self._oracle_kv("kv_w_h", sel),
                                        d["w_pos0"][sel], self.W, d["sink_h"], self.dv, 64, d["scale"])
             out["out_h"], out["lse_h"] = oh, lh
         return out
@@ -516,7 +575,8 @@ def run(args):
 
     wl = DecodeWorkload(args.workload, copies=args.copies, streams=args.streams,
                         hca_workgroups=args.hca_workgroups, csa_workgroups=args.csa_workgroups,
-                        score_dtype=csk.CSK_BF16 if args.score_dtype == "bf16" else csk.CSK_F32)
+                        score_dtype=csk.CSK_BF16 if args.score_dtype == "bf16" else csk.CSK_F32,
+                        kv_fp8=args.kv == "fp8")
     K, Wm = args.steps, args.warmup
     # eager warm-up (first calls set kernel attributes outside any capture)
     for i in range(max(Wm, 1)):
@@ -951,6 +1011,7 @@ def cpu_baseline(wl, args):
 
     rows = list(range(min(args.cpu_rows, wl.B)))
     oracle.lib()
+    wl.oracle_prepare(rows)
     t0 = time.perf_counter()
     wl.oracle_step(rows)
     dt = time.perf_counter() - t0
@@ -960,7 +1021,8 @@ def cpu_baseline(wl, args):
     return dict({"value": round(len(rows) / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
                  "sample": f"one full decode step for {len(rows)} of {wl.B} sequences (compression of the newest "
                            f"entries, MXFP4 query encoding, indexer over all {wl.N} entries, top-{wl.k}, sparse "
-                           f"attention" + (", dense HCA attention" if wl.pair else "") + f"); {dt:.1f} s wall; "
+                           f"attention" + (", dense HCA attention" if wl.pair else "") +
+                           (" over FP8 KV caches, decoded" if wl.kv_fp8 else "") + f"); {dt:.1f} s wall; "
                            f"the oracle runs one OpenMP thread per query row"}, **host_cpu())
 
 
@@ -984,6 +1046,8 @@ def main():
                     help="workgroup cap of the CSA sparse attention (0: one per CU)")
     ap.add_argument("--score-dtype", default="f32", choices=["f32", "bf16"],
                     help="decode: indexer scores the top-k compares (bf16: rounded once to bf16)")
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
+                    help="decode: KV entries in bf16, or FP8 (E4M3, scale per 32 dims, RoPE dims bf16)")
     ap.add_argument("--cpu-rows", type=int, default=4, help="decode: sequences the oracle runs")
     ap.add_argument("--cpu-rows-prefill", type=int, default=None,
                     help="prefill: query rows the oracle runs (default 384 for CSA, every row for HCA)")

@@ -240,3 +240,56 @@ def test_csa_prefill_64k_sampled():
     go = host(out)[0, ts]
     report_margin("csa_prefill_64k attention", *check_bf16_attention(go, rout, "csa prefill attention"))
     check_f32(host(lse)[0, ts], rlse, 2e-2, "lse")
+
+
+def _fp8_close(got, want, what):
+    """Two FP8 KV encodings of nearly equal values (the GPU's fp32 entry and
+    the oracle's fp64 one rounded to fp32): decoded, each non-RoPE value is
+    within one E4M3 step of the other's (the step at |v|, or the subnormal
+    step 2^(s-9) of its block scale s), the 64 RoPE values within two bf16
+    ulps."""
+    from util import bf16_ulp
+    D, dr = 576, 64
+    a, b = oracle.fp8kv_decode(got, D, dr), oracle.fp8kv_decode(want, D, dr)
+    s = want[..., D - dr + 2 * dr: D - dr + 2 * dr + (D - dr) // 32].astype(np.int32) - 127
+    sub = np.repeat(np.exp2(s - 9.0), 32, axis=-1)
+    av = np.maximum(np.abs(b[..., :D - dr]).astype(np.float64), 1e-30)
+    step = np.maximum(np.exp2(np.floor(np.log2(av)) - 3), sub)
+    assert np.all(np.abs(a[..., :D - dr] - b[..., :D - dr]) <= step), what
+    rb = b[..., D - dr:]
+    assert np.all(np.abs(a[..., D - dr:] - rb) <= 2 * bf16_ulp(rb) + 1e-5), what
+
+
+def test_decode_1m_pair_fp8kv():
+    # the decode step with FP8 KV caches (E4M3 non-RoPE dims, one
+    # power-of-two scale per 32, RoPE dims bf16): the caches the GPU encodes
+    # are the oracle encoder's bytes; the newest entries agree to one E4M3
+    # step; top-k is unchanged (bit-exact); both attentions match the
+    # oracle's over the decoded caches within the bf16 bars
+    import bench
+
+    wl = bench.DecodeWorkload("decode_1m_pair", copies=1, kv_fp8=True)
+    wl.step(0)
+    torch.cuda.synchronize()
+    rows = list(range(wl.B))
+    ref = wl.oracle_step(rows)
+    st = wl.copies[0]
+    N, Nh = wl.N, wl.Nh
+    # the GPU encodes the caches through the compression kernel with one
+    # token per entry, which turns a -0 source value into +0 (-0 + +0 in its
+    # softmax sum): compared as decoded values, where the two zeros are equal
+    for name, n in (("kv_c", N - 1), ("kv_h", Nh - 1), ("kv_w", None), ("kv_w_h", None)):
+        g = host(st[name])
+        for b in range(wl.B):
+            assert np.array_equal(oracle.fp8kv_decode(g[b, :n], 576, 64),
+                                  oracle.fp8kv_decode(wl.h8[name][b, :n], 576, 64)), (name, b)
+        del g
+    _fp8_close(host(st["kv_c"][:, N - 1]), ref["kv_new"], "newest csa entry")
+    _fp8_close(host(st["kvh_new"][:, 0]), ref["kvh_new"], "newest hca entry")
+    assert np.array_equal(host(wl.idx).reshape(wl.B, -1), ref["idx"])
+    report_margin("decode_1m_pair fp8kv csa attention",
+                  *check_bf16_attention(host(wl.out).reshape(ref["out"].shape), ref["out"], "csa attention"))
+    check_f32(host(wl.lse).reshape(ref["lse"].shape), ref["lse"], 2e-2, "csa lse")
+    report_margin("decode_1m_pair fp8kv hca attention",
+                  *check_bf16_attention(host(wl.out_h).reshape(ref["out_h"].shape), ref["out_h"], "hca attention"))
+    check_f32(host(wl.lse_h).reshape(ref["lse_h"].shape), ref["lse_h"], 2e-2, "hca lse")
