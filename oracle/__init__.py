@@ -55,6 +55,7 @@ def lib():
         L.csk_ref_fp8kv_entry_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
         L.csk_ref_fp8kv_encode.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _u8p]
         L.csk_ref_fp8kv_decode.argtypes = [_u8p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _f32p]
+        L.csk_ref_grouped_out_proj.argtypes = [_f32p, _f32p, _f32p] + [ctypes.c_int] * 6 + [_f32p, _f64p]
         attn_tail = ([_f32p, _i32p, ctypes.c_int, ctypes.c_int, _f32p] + [ctypes.c_int] * 6
                      + [ctypes.c_double, ctypes.c_double, _i32p, ctypes.c_int, _f64p, _f64p])
         L.csk_ref_sparse_attn.argtypes = [_f32p, _i32p, _f32p, ctypes.c_int, _i32p, ctypes.c_int] + attn_tail
@@ -309,3 +310,21 @@ def dense_attn(q, q_pos, kv_c, n_entries, m, kv_w, w_pos0, W, sink, dv, d_rope, 
                                   _p(out, ctypes.c_double), _p(lse, ctypes.c_double))
     _check(rc, "dense_attn")
     return out, lse
+
+
+def grouped_out_proj(o, w1, w2):
+    """Grouped output projection. o [R, H*dv] (bf16 bits or float; heads
+    consecutive); w1 [g, dg, (H/g)*dv]; w2 [d, g*dg]. Returns (y [R, d]
+    float64, u [R, g*dg] float32: the intermediate rounded to bf16)."""
+    w1, w2, of = _f32(w1), _f32(w2), _f32(o)
+    g, dg, K1 = w1.shape
+    d = w2.shape[0]
+    assert of.ndim == 2 and of.shape[1] == g * K1 and w2.shape[1] == g * dg
+    R = of.shape[0]
+    y = np.empty((R, d), np.float64)
+    u = np.empty((R, g * dg), np.float32)
+    # H*dv = g*K1 is all the layout needs: g "heads" of K1 values each
+    _check(lib().csk_ref_grouped_out_proj(_p(of, ctypes.c_float), _p(w1, ctypes.c_float), _p(w2, ctypes.c_float),
+                                          R, g, K1, g, dg, d, _p(u, ctypes.c_float), _p(y, ctypes.c_double)),
+           "grouped_out_proj")
+    return y, u

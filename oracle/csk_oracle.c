@@ -660,3 +660,45 @@ int csk_ref_dense_attn(const float* q, const int32_t* q_pos, const float* kv_c, 
   }
   return err;
 }
+
+/* ------------------------------------------ grouped output projection */
+
+/* [P1] «CSA: сжать в 4 раза и выбрать top-k», step 4: the heads' outputs
+ * are not projected to the hidden size in one matrix; they are split into
+ * g groups, each group is projected to an intermediate width (1024 in the
+ * pages' model), and the groups' intermediates together are projected to
+ * the hidden state. Here: row r's outputs o[r] = [head 0 | head 1 | ...]
+ * (H*dv values); group i holds heads i*H/g .. (i+1)*H/g - 1, i.e. the K1 =
+ * (H/g)*dv values o[r][i*K1 .. (i+1)*K1); u[r][i*dg + n] = sum_k
+ * o[r][i*K1 + k] * w1[i][n][k]; y[r][c] = sum_j u[r][j] * w2[c][j]. Weights
+ * are [out, in] (each output feature's inputs contiguous). Reading: the
+ * intermediate is an activation of a bf16 model, rounded once to bf16
+ * before the second projection; y is returned in double. */
+int csk_ref_grouped_out_proj(const float* o, const float* w1, const float* w2, int R, int H, int dv,
+                             int g, int dg, int d, float* u_out, double* y) {
+  if (R < 0 || H <= 0 || dv <= 0 || g <= 0 || H % g || dg <= 0 || d <= 0) return -1;
+  const int K1 = H / g * dv, K2 = g * dg;
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < R; ++r) {
+    const float* orow = o + (size_t)r * H * dv;
+    float* u = (float*)malloc(sizeof(float) * (size_t)K2);
+    for (int i = 0; i < g; ++i) {
+      for (int n = 0; n < dg; ++n) {
+        const float* wrow = w1 + ((size_t)i * dg + n) * K1;
+        double acc = 0.0;
+        for (int k = 0; k < K1; ++k) acc += (double)orow[(size_t)i * K1 + k] * (double)wrow[k];
+        const uint32_t bits = (uint32_t)round_one_bf16(acc) << 16;
+        memcpy(&u[i * dg + n], &bits, 4);
+      }
+    }
+    for (int c = 0; c < d; ++c) {
+      const float* wrow = w2 + (size_t)c * K2;
+      double acc = 0.0;
+      for (int j = 0; j < K2; ++j) acc += (double)u[j] * (double)wrow[j];
+      y[(size_t)r * d + c] = acc;
+    }
+    if (u_out) memcpy(u_out + (size_t)r * K2, u, sizeof(float) * (size_t)K2);
+    free(u);
+  }
+  return 0;
+}

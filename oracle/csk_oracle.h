@@ -116,6 +116,14 @@ int csk_ref_dense_attn(const float* q, const int32_t* q_pos, const float* kv_c, 
                        int d_rope, double rope_base, double scale, const int32_t* rows,
                        int n_rows, double* out, double* lse);
 
+/* Grouped output projection ([P1] «CSA: сжать в 4 раза и выбрать top-k»,
+ * step 4). o: [R, H*dv] (head h's outputs at h*dv); the g groups hold H/g
+ * consecutive heads each; w1: [g, dg, (H/g)*dv] (group i's projection to
+ * dg intermediate features, [out, in]); w2: [d, g*dg]. u_out: [R, g*dg]
+ * (the intermediate, rounded once to bf16) or NULL; y: [R, d] double. */
+int csk_ref_grouped_out_proj(const float* o, const float* w1, const float* w2, int R, int H, int dv,
+                             int g, int dg, int d, float* u_out, double* y);
+
 /* Number of OpenMP threads the oracle runs with. */
 int csk_ref_num_threads(void);
 
