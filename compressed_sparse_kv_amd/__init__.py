@@ -56,6 +56,9 @@ def lib():
         L.sparse_attn_workspace_size.restype = _sz
         L.dense_compressed_attn_workspace_size.argtypes = [_i] * 10
         L.dense_compressed_attn_workspace_size.restype = _sz
+        L.grouped_out_proj.argtypes = [_vp] * 3 + [_i] * 7 + [_vp, _vp, _sz, _vp]
+        L.grouped_out_proj_workspace_size.argtypes = [_i] * 3
+        L.grouped_out_proj_workspace_size.restype = _sz
         L.csk_kernel_timer_arm.argtypes = [ctypes.c_char_p, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i]
         L.csk_kernel_timer_count.restype = _i
         L.csk_kernel_timer_disarm.restype = None
@@ -322,6 +325,38 @@ def dense_compressed_attn(q, q_pos, kv_c, n_entries, m, kv_w, w_pos0, W, sink, d
                                      _ptr(workspace), workspace.numel(), _stream())
     _check(rc, "dense_compressed_attn")
     return out, lse
+
+
+def grouped_out_proj_workspace_size(R, g, dg):
+    return lib().grouped_out_proj_workspace_size(R, g, dg)
+
+
+def grouped_out_proj(o, w1, w2, y_dtype=None, out=None, workspace=None):
+    """Grouped output projection (see grouped_out_proj in csk.h). o
+    [..., H, dv] or [..., H*dv] bf16 (R = the leading dims' product); w1
+    [g, dg, (H/g)*dv] bf16; w2 [d, g*dg] bf16. Returns (y [..., d] in
+    y_dtype, default bf16; u [R, g*dg] bf16, the intermediate, a view of
+    the workspace)."""
+    g, dg, K1 = w1.shape
+    d = w2.shape[0]
+    HD = g * K1
+    lead = o.shape[:-2] if o.shape[-1] != HD else o.shape[:-1]
+    R = 1
+    for x in lead:
+        R *= int(x)
+    H = g if o.shape[-1] == HD else o.shape[-2]
+    dv = HD // H
+    y_dtype = CSK_BF16 if y_dtype is None else y_dtype
+    if out is None:
+        out = torch.empty(tuple(lead) + (d,), dtype=_torch_dt(y_dtype), device=o.device)
+    nbytes = grouped_out_proj_workspace_size(R, g, dg)
+    if workspace is None:
+        workspace = _ws(nbytes, o.device)
+    rc = lib().grouped_out_proj(_ptr(o), _ptr(w1), _ptr(w2), R, H, dv, g, dg, d, y_dtype, _ptr(out),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
+    _check(rc, "grouped_out_proj")
+    u = workspace[:nbytes].view(torch.bfloat16).view(R, g * dg) if R > 0 else None
+    return out, u
 
 
 class KernelTimer:

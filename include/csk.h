@@ -330,6 +330,32 @@ size_t dense_compressed_attn_workspace_size(int B, int T, int H, int D, int dv, 
                                             int W, int dtype, int max_workgroups);
 
 /*
+ * grouped_out_proj - grouped output projection of the attention heads
+ * ([P1] «CSA: сжать в 4 раза и выбрать top-k», step 4: the heads' outputs
+ * are split into g groups, each group is projected to an intermediate
+ * width, and the groups' intermediates together are projected to the
+ * hidden size, instead of one projection of all heads at once).
+ *   o   : [R,H*dv] bf16, a row's heads consecutive (head h at h*dv) - the
+ *         attention output [B,T,H,dv] with R = B*T.
+ *   w1  : [g,dg,(H/g)*dv] bf16: group i (heads i*H/g .. (i+1)*H/g - 1)
+ *         maps its (H/g)*dv values to dg intermediate features ([out, in]).
+ *   w2  : [d,g*dg] bf16: the g*dg intermediates to the d hidden features.
+ *   y   : [R,d] in y_dtype (CSK_BF16 or CSK_F32).
+ *   workspace: >= grouped_out_proj_workspace_size(R, g, dg) bytes; after
+ *         the call it holds the intermediate u [R,g*dg] in bf16 (each value
+ *         accumulated in fp32 and rounded once, as the second product takes
+ *         it).
+ * Both products accumulate in fp32 on the matrix cores; y is rounded once
+ * to y_dtype. Built for (H/g)*dv and g*dg multiples of 64 and d a multiple
+ * of 8 (else CSK_EUNSUPPORTED); o, w1, w2, y and workspace must be 16-byte
+ * aligned (else CSK_EINVAL). R = 0 is a no-op.
+ */
+int grouped_out_proj(const void* o, const void* w1, const void* w2, int R, int H, int dv, int g,
+                     int dg, int d, int y_dtype, void* y, void* workspace, size_t ws_bytes,
+                     void* stream);
+size_t grouped_out_proj_workspace_size(int R, int g, int dg);
+
+/*
  * csk_kernel_timer_arm - opt-in measurement hook (process-wide, one armed
  * timer at a time). The next n launches of the library kernel named
  * `kernel` ("indexer_scores_fp4", "attn_bf16_sparse", ...) are each

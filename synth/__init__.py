@@ -211,3 +211,14 @@ def make(name, **overrides):
     kw = dict(seed=WORKLOADS[name]["seed"])
     kw.update(overrides)
     return fn(**kw)
+
+
+def out_proj(seed, R, H, dv, g, dg, d):
+    """Grouped output projection inputs: attention outputs o [R, H*dv] bf16
+    N(0,1) (heads consecutive), group weights w1 [g, dg, (H/g)*dv] bf16
+    N(0, 1/((H/g)*dv)), hidden weights w2 [d, g*dg] bf16 N(0, 1/(g*dg))
+    (projection weights N(0, 1/fan_in), so every output is about N(0,1))."""
+    gen = rng(seed)
+    K1 = H // g * dv
+    return dict(o=_bf16_normal(gen, (R, H * dv)), w1=_bf16_normal(gen, (g, dg, K1), 1.0 / K1),
+                w2=_bf16_normal(gen, (d, g * dg), 1.0 / (g * dg)), R=R, H=H, dv=dv, g=g, dg=dg, d=d)

@@ -173,3 +173,24 @@ def test_indexer_rejects_unknown_score_dtype(lib):
     rc = lib.indexer_topk(fake, fake, fake, fake, fake, fake, fake, 1, 1, 64, 128, 4096, 4, 8, 2, 7,
                           fake, fake, fake, ctypes.c_size_t(1 << 30), None)
     assert rc == -2 and b"score_dtype" in lib.csk_last_error()
+
+
+def test_grouped_out_proj_arguments(lib):
+    lib.csk_last_error.restype = ctypes.c_char_p
+    lib.grouped_out_proj_workspace_size.restype = ctypes.c_size_t
+    assert lib.grouped_out_proj_workspace_size(4, 8, 1024) == 4 * 8 * 1024 * 2
+    assert lib.grouped_out_proj_workspace_size(0, 8, 1024) == 0
+    fake = ctypes.c_void_p(4096)
+    sz = ctypes.c_size_t
+
+    def call(R=4, H=64, dv=512, g=8, dg=1024, d=4096, y_dtype=1, ws=sz(1 << 20), o=fake):
+        return lib.grouped_out_proj(o, fake, fake, R, H, dv, g, dg, d, y_dtype, fake, fake, ws, None)
+
+    assert call(g=3) == -1                       # g does not divide H
+    assert call(dv=40) == -2                     # (H/g)*dv = 320 is not a multiple of 64
+    assert call(dg=36) == -2                     # g*dg = 288 likewise
+    assert call(d=100) == -2                     # d not a multiple of 8
+    assert call(y_dtype=2) == -2
+    assert call(ws=sz(100)) == -3 and b"workspace" in lib.csk_last_error()
+    assert call(o=ctypes.c_void_p(4098)) == -1 and b"aligned" in lib.csk_last_error()
+    assert call(R=0, o=None) == 0                # nothing to do
