@@ -56,6 +56,9 @@ def lib():
         L.csk_ref_fp8kv_encode.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _u8p]
         L.csk_ref_fp8kv_decode.argtypes = [_u8p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _f32p]
         L.csk_ref_grouped_out_proj.argtypes = [_f32p, _f32p, _f32p] + [ctypes.c_int] * 6 + [_f32p, _f64p]
+        L.csk_ref_rmsnorm.argtypes = [_f32p, _f32p, ctypes.c_int64, ctypes.c_int, ctypes.c_double, _f64p]
+        L.csk_ref_project_compress.argtypes = ([_f32p] * 5 + [ctypes.c_double] + [ctypes.c_int] * 7
+                                               + [ctypes.c_double, _i32p, _f64p])
         attn_tail = ([_f32p, _i32p, ctypes.c_int, ctypes.c_int, _f32p] + [ctypes.c_int] * 6
                      + [ctypes.c_double, ctypes.c_double, _i32p, ctypes.c_int, _f64p, _f64p])
         L.csk_ref_sparse_attn.argtypes = [_f32p, _i32p, _f32p, ctypes.c_int, _i32p, ctypes.c_int] + attn_tail
@@ -328,3 +331,37 @@ def grouped_out_proj(o, w1, w2):
                                           R, g, K1, g, dg, d, _p(u, ctypes.c_float), _p(y, ctypes.c_double)),
            "grouped_out_proj")
     return y, u
+
+
+RMS_EPS = 1e-6
+
+
+def rmsnorm(x, gamma, eps=RMS_EPS):
+    """RMSNorm over the last dim: x * gamma / sqrt(mean(x^2) + eps), float64."""
+    xf = _f32(x)
+    D = xf.shape[-1]
+    y = np.empty(xf.shape, np.float64)
+    _check(lib().csk_ref_rmsnorm(_p(xf, ctypes.c_float), _p(_f32(gamma), ctypes.c_float), xf.size // D, D,
+                                 float(eps), _p(y, ctypes.c_double)), "rmsnorm")
+    return y
+
+
+def project_compress(x, w, bias_a, bias_b, m, gamma=None, eps=RMS_EPS, d_rope=0, rope_base=10000.0,
+                     entry_pos=None):
+    """Projection then compression. x [B,S,hidden]; w [4,D,hidden] (CSA:
+    W_ca, W_za, W_cb, W_zb) or [2,D,hidden] (HCA: W_c, W_z; bias_b None).
+    Returns [B,S//m,D] float64."""
+    xf, wf = _f32(x), _f32(w)
+    B, S, hidden = xf.shape
+    ns, D, _ = wf.shape
+    csa = 1 if ns == 4 else 0
+    out = np.empty((B, S // m, D), np.float64)
+    ba = _f32(bias_a)
+    bb = _f32(bias_b) if bias_b is not None else ba
+    ep = _i32(entry_pos) if entry_pos is not None else None
+    _check(lib().csk_ref_project_compress(_p(xf, ctypes.c_float), _p(wf, ctypes.c_float), _p(ba, ctypes.c_float),
+                                          _p(bb, ctypes.c_float),
+                                          _p(_f32(gamma), ctypes.c_float) if gamma is not None else None,
+                                          float(eps), csa, B, S, hidden, D, m, d_rope, float(rope_base),
+                                          _p(ep, ctypes.c_int32), _p(out, ctypes.c_double)), "project_compress")
+    return out

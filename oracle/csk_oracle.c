@@ -702,3 +702,94 @@ int csk_ref_grouped_out_proj(const float* o, const float* w1, const float* w2, i
   }
   return 0;
 }
+
+/* ----------------------------------------------------- QK RMSNorm */
+
+/* [P1] «Muon и борьба с нестабильностью»: queries and KV entries can be
+ * normalised directly with RMSNorm; [P4]: QK norms for stability. Reading:
+ * the norm runs over all D values of a vector (RoPE dims included, before
+ * the rotation), y = x * gamma / sqrt(mean(x^2) + eps), gamma a learned
+ * per-dim scale. */
+static void rmsnorm_row(double* v, const float* gamma, int D, double eps) {
+  double ss = 0.0;
+  for (int c = 0; c < D; ++c) ss += v[c] * v[c];
+  const double inv = 1.0 / sqrt(ss / D + eps);
+  for (int c = 0; c < D; ++c) v[c] = v[c] * inv * (double)gamma[c];
+}
+
+int csk_ref_rmsnorm(const float* x, const float* gamma, int64_t rows, int D, double eps, double* y) {
+  if (rows < 0 || D <= 0 || !(eps >= 0.0)) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    double* v = y + r * D;
+    for (int c = 0; c < D; ++c) v[c] = (double)x[r * D + c];
+    rmsnorm_row(v, gamma, D, eps);
+  }
+  return 0;
+}
+
+/* ------------------------------------- projection, then compression */
+
+/* [P1] «CSA…» step 1: the two KV series and the two weight series are
+ * computed from the hidden states; here by learned projections
+ * (series s = X W_s^T, W_s [D, hidden], [out, in]). CSA (csa = 1): w holds
+ * W_ca, W_za, W_cb, W_zb and the entries pool as csk_ref_csa_compress; HCA
+ * (csa = 0): w holds W_c, W_z and the entries pool as
+ * csk_ref_hca_compress. Then, when gamma is given, each entry is
+ * RMS-normalised ([P1] «Muon…»), and its last d_rope dims are rotated at
+ * the entry's position. Everything in double, from the exact products. */
+int csk_ref_project_compress(const float* x, const float* w, const float* bias_a, const float* bias_b,
+                             const float* gamma, double eps, int csa, int B, int S, int hidden, int D,
+                             int m, int d_rope, double rope_base, const int32_t* entry_pos, double* out) {
+  if (check_compress_args(B, S, D, m, d_rope) || hidden <= 0 || !(eps >= 0.0)) return -1;
+  const int NS = csa ? 4 : 2, N = S / m;
+  /* the projected series, [NS][B][S][D] */
+  double* ser = (double*)malloc(sizeof(double) * (size_t)NS * B * S * D);
+  if (!ser) return -1;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int b = 0; b < B; ++b)
+    for (int t = 0; t < S; ++t)
+      for (int s = 0; s < NS; ++s)
+        for (int c = 0; c < D; ++c) {
+          const float* xr = x + ((size_t)b * S + t) * hidden;
+          const float* wr = w + ((size_t)s * D + c) * hidden;
+          double acc = 0.0;
+          for (int k = 0; k < hidden; ++k) acc += (double)xr[k] * (double)wr[k];
+          ser[(((size_t)s * B + b) * S + t) * D + c] = acc;
+        }
+#define SER(s, b, t, c) ser[(((size_t)(s) * B + (b)) * S + (t)) * D + (c)]
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int b = 0; b < B; ++b) {
+    for (int i = 0; i < N; ++i) {
+      double* L = (double*)malloc(sizeof(double) * 2 * (size_t)m);
+      double* V = (double*)malloc(sizeof(double) * 2 * (size_t)m);
+      double* row = out + ((size_t)b * N + i) * D;
+      for (int c = 0; c < D; ++c) {
+        int n = 0;
+        for (int r = 0; r < m; ++r) {
+          const int t = m * i + r;
+          L[n] = SER(1, b, t, c) + (double)bias_a[(size_t)r * D + c];
+          V[n] = SER(0, b, t, c);
+          ++n;
+        }
+        if (csa && i >= 1) {
+          for (int r = 0; r < m; ++r) {
+            const int t = m * (i - 1) + r;
+            L[n] = SER(3, b, t, c) + (double)bias_b[(size_t)r * D + c];
+            V[n] = SER(2, b, t, c);
+            ++n;
+          }
+        }
+        row[c] = softmax_pool(L, V, n);
+      }
+      if (gamma) rmsnorm_row(row, gamma, D, eps);
+      double pos = entry_pos ? (double)entry_pos[(size_t)b * N + i] : (double)m * i;
+      if (d_rope > 0) csk_ref_rope(row, D, d_rope, pos, rope_base);
+      free(L);
+      free(V);
+    }
+  }
+#undef SER
+  free(ser);
+  return 0;
+}

@@ -124,6 +124,22 @@ int csk_ref_dense_attn(const float* q, const int32_t* q_pos, const float* kv_c, 
 int csk_ref_grouped_out_proj(const float* o, const float* w1, const float* w2, int R, int H, int dv,
                              int g, int dg, int d, float* u_out, double* y);
 
+/* RMSNorm of each row of x [rows, D] over all D values:
+ * y = x * gamma / sqrt(mean(x^2) + eps) ([P1] «Muon и борьба с
+ * нестабильностью»: queries and KV entries normalised by RMSNorm; [P4]: QK
+ * norms). y: [rows, D] double. */
+int csk_ref_rmsnorm(const float* x, const float* gamma, int64_t rows, int D, double eps, double* y);
+
+/* Projection then compression ([P1] «CSA…» step 1: the series come from
+ * the hidden states). x: [B,S,hidden]; w: [4,D,hidden] (csa = 1: W_ca,
+ * W_za, W_cb, W_zb) or [2,D,hidden] (csa = 0: W_c, W_z), [out, in]; the
+ * series X W^T pool as csk_ref_csa_compress / csk_ref_hca_compress (bias_b
+ * unused for HCA); gamma [D] or NULL: RMSNorm of each entry before RoPE.
+ * out: [B,S/m,D] double. */
+int csk_ref_project_compress(const float* x, const float* w, const float* bias_a, const float* bias_b,
+                             const float* gamma, double eps, int csa, int B, int S, int hidden, int D,
+                             int m, int d_rope, double rope_base, const int32_t* entry_pos, double* out);
+
 /* Number of OpenMP threads the oracle runs with. */
 int csk_ref_num_threads(void);
 
