@@ -15,7 +15,8 @@
 //     multiplied), four waves of 128x128 each; tiles are handed out
 //     XCD-contiguously so that tiles sharing operand rows run in one L2;
 //   - at most 32 rows (decode): the product streams the weights, so each
-//     workgroup owns 32 output columns, its four waves split K four ways
+//     workgroup owns 32 output columns (16 on 16x16x32 products when there
+//     are at most 16 rows), its four waves split K four ways
 //     and load their fragments straight from memory (many 16-byte loads in
 //     flight per lane), and the four partial tiles are summed in a fixed
 //     order through LDS.
@@ -125,21 +126,33 @@ void gemm_tile_kernel(GemmArgs g) {
     asm volatile("" ::: "memory");
     const uint4* sa = lds[buf][0];
     const uint4* sb = lds[buf][1];
-#pragma unroll
-    for (int ks = 0; ks < TK / 16; ++ks) {
-      v8bf af[4], bfr[4];
+    // the fragments of K-step ks+1 are read while ks's 16 products run
+    v8bf af[2][4], bfr[2][4];
+    auto read_frags = [&](int ks, v8bf (&fa)[4], v8bf (&fb)[4]) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ra = 128 * wm + 32 * i + fr, rb = 128 * wn + 32 * i + fr;
         const int kc = 2 * ks + fh;
-        af[i] = __builtin_bit_cast(v8bf, sa[ra * 8 + (kc ^ (ra & 7))]);
-        bfr[i] = __builtin_bit_cast(v8bf, sb[rb * 8 + (kc ^ (rb & 7))]);
+        fa[i] = __builtin_bit_cast(v8bf, sa[ra * 8 + (kc ^ (ra & 7))]);
+        fb[i] = __builtin_bit_cast(v8bf, sb[rb * 8 + (kc ^ (rb & 7))]);
       }
+    };
+    read_frags(0, af[0], bfr[0]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int ks = 0; ks < TK / 16; ++ks) {
+      // four products, then the next step's reads (hidden by the other twelve)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][0], bfr[ks & 1][j], acc[0][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + 1 < TK / 16) read_frags(ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 1; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // every wave is done with this buffer before the next DMA into it
     asm volatile("" ::: "memory");
@@ -225,10 +238,69 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     }
 }
 
+// At most 16 rows: 16 output columns per workgroup on 16x16x32 products
+// (twice the workgroups of the 32-column form, for the same weight bytes),
+// four lanes reading 64 contiguous bytes of a weight row per K-step.
+constexpr int SK16_UNROLL = 16;
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void gemm_skinny16_kernel(GemmArgs g) {
+  __shared__ float red[3][4][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * 16;
+  const int64_t bt = blockIdx.y;
+  const int kq = g.K / 4;  // this wave's K range, a multiple of 16
+  // fragment rows: A row lane%16 (rows past M read row M-1; not stored),
+  // B row n0 + lane%16; k chunk lane/16 of each 32-deep step
+  const int fr = lane & 15, fq = lane >> 4;
+  const uint16_t* pa = g.A + bt * g.a_bs + (int64_t)min(fr, g.M - 1) * g.lda + wave * kq + 8 * fq;
+  const uint16_t* pb = g.B + bt * g.b_bs + (int64_t)min(n0 + fr, g.N - 1) * g.ldb + wave * kq + 8 * fq;
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  int k = 0;
+  for (; k + 32 * SK16_UNROLL <= kq; k += 32 * SK16_UNROLL) {
+    v8bf af[SK16_UNROLL], bfr[SK16_UNROLL];
+#pragma unroll
+    for (int u = 0; u < SK16_UNROLL; ++u) {
+      bfr[u] = *reinterpret_cast<const v8bf*>(pb + k + 32 * u);
+      af[u] = *reinterpret_cast<const v8bf*>(pa + k + 32 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < SK16_UNROLL; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u], bfr[u], acc, 0, 0, 0);
+  }
+  for (; k < kq; k += 32) {
+    const v8bf bf1 = *reinterpret_cast<const v8bf*>(pb + k);
+    const v8bf af1 = *reinterpret_cast<const v8bf*>(pa + k);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af1, bf1, acc, 0, 0, 0);
+  }
+  if (wave > 0)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[wave - 1][e][lane] = acc[e];
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] = ((acc[e] + red[0][e][lane]) + red[1][e][lane]) + red[2][e][lane];
+  // lane holds column n0 + lane%16, rows 4*(lane/16) + e
+  const int col = n0 + fr;
+  if (col >= g.N) return;
+  char* C = reinterpret_cast<char*>(g.C) + bt * g.c_bs * (g.c_f32 ? 4 : 2);
+  GemmArgs gc = g;
+  gc.C = C;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int row = 4 * fq + e;
+    if (row < g.M) store_c(gc, (int64_t)row * g.ldc + col, acc[e]);
+  }
+}
+
 // Launches C = A B^T for `batches` products. Caller checks: K % 64 == 0,
 // leading dimensions and batch strides multiples of 8 elements, operands
 // 16-byte aligned, M, N >= 1.
 int launch_gemm(const char* name, const GemmArgs& g, int batches, hipStream_t s) {
+  if (g.M <= 16 && (g.K / 4) % 32 == 0)
+    return launch(name, gemm_skinny16_kernel, dim3((unsigned)ceil_div(g.N, 16), (unsigned)batches), dim3(256), 0,
+                  s, g);
   if (g.M <= 32)
     return launch(name, gemm_skinny_kernel, dim3((unsigned)ceil_div(g.N, 32), (unsigned)batches), dim3(256), 0, s,
                   g);
