@@ -59,6 +59,11 @@ def lib():
         L.grouped_out_proj.argtypes = [_vp] * 3 + [_i] * 7 + [_vp, _vp, _sz, _vp]
         L.grouped_out_proj_workspace_size.argtypes = [_i] * 3
         L.grouped_out_proj_workspace_size.restype = _sz
+        L.project_compress.argtypes = ([_i] + [_vp] * 5 + [_f] + [_i] * 6 + [_i64, _i, _f, _vp, _i, _vp, _vp, _i64,
+                                                                       _vp, _sz, _vp])
+        L.project_compress_workspace_size.argtypes = [_i] * 5
+        L.project_compress_workspace_size.restype = _sz
+        L.rmsnorm.argtypes = [_vp, _vp, _i64, _i, _f, _i, _i, _vp, _vp]
         L.csk_kernel_timer_arm.argtypes = [ctypes.c_char_p, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i]
         L.csk_kernel_timer_count.restype = _i
         L.csk_kernel_timer_disarm.restype = None
@@ -357,6 +362,48 @@ def grouped_out_proj(o, w1, w2, y_dtype=None, out=None, workspace=None):
     _check(rc, "grouped_out_proj")
     u = workspace[:nbytes].view(torch.bfloat16).view(R, g * dg) if R > 0 else None
     return out, u
+
+
+RMS_EPS = 1e-6
+
+
+def project_compress_workspace_size(csa, B, S, D, m):
+    return lib().project_compress_workspace_size(csa, B, S, D, m)
+
+
+def project_compress(x, w, bias_a, bias_b, m, gamma=None, eps=RMS_EPS, d_rope=0, rope_base=10000.0,
+                     entry_pos=None, out_dtype=None, entry0=0, src_bstride=0, out=None, out_scale=None,
+                     dst_bstride=0, B=None, S=None, workspace=None):
+    """Projection then compression (see project_compress in csk.h). x
+    [B,S,hidden] bf16; w [4,D,hidden] (CSA) or [2,D,hidden] (HCA) bf16.
+    Returns out ([B,S//m,D] in out_dtype, default bf16) or (codes, scales)
+    for MXFP4."""
+    csa = 1 if w.shape[0] == 4 else 0
+    B = x.shape[0] if B is None else B
+    S = x.shape[1] if S is None else S
+    hidden, D = x.shape[-1], w.shape[1]
+    out_dtype = CSK_BF16 if out_dtype is None else out_dtype
+    out, out_scale = _alloc_compress_out(out, out_scale, B, S // m, D, out_dtype, x.device, d_rope)
+    nbytes = project_compress_workspace_size(csa, B, S, D, m)
+    if workspace is None:
+        workspace = _ws(nbytes, x.device)
+    rc = lib().project_compress(csa, _ptr(x), _ptr(w), _ptr(bias_a), _ptr(bias_b), _ptr(gamma), eps, B, S, hidden,
+                                D, m, entry0, src_bstride, d_rope, rope_base, _ptr(entry_pos), out_dtype, _ptr(out),
+                                _ptr(out_scale), dst_bstride, _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream())
+    _check(rc, "project_compress")
+    return (out, out_scale) if out_dtype == CSK_MXFP4 else out
+
+
+def rmsnorm(x, gamma, eps=RMS_EPS, out_dtype=None, out=None):
+    """RMSNorm over the last dim (see rmsnorm in csk.h)."""
+    D = x.shape[-1]
+    out_dtype = _dt(x) if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty(x.shape, dtype=_torch_dt(out_dtype), device=x.device)
+    rc = lib().rmsnorm(_ptr(x), _ptr(gamma), x.numel() // D, D, eps, _dt(x), out_dtype, _ptr(out), _stream())
+    _check(rc, "rmsnorm")
+    return out
 
 
 class KernelTimer:

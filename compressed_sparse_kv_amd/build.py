@@ -14,7 +14,7 @@ SRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build", "csk")
 LIB = os.path.join(HERE, "libcsk.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["abi.hip", "compress.hip", "indexer.hip", "attention.hip", "gemm.hip"]
+SOURCES = ["abi.hip", "compress.hip", "indexer.hip", "attention.hip", "gemm.hip", "project.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include")]

@@ -42,6 +42,16 @@ int launch(const char* name, Kernel k, dim3 grid, dim3 block, size_t lds, hipStr
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Entries pooled elsewhere (fp32 rows b*N + i of D values, with ncb partial
+// sums of squares per entry): RMSNorm when gamma is given, RoPE of the last
+// d_rope dims at entry_pos[b*N + i] (NULL: m*(entry0 + i)), then the
+// output dtype (CSK_F32, CSK_BF16, CSK_MXFP4 with out_scale, CSK_FP8KV),
+// written to row b*dst_bstride + i (0: N). Defined in compress.hip; the
+// caller has checked the arguments.
+int finalize_entries(const char* name, int B, int N, int D, int m, int entry0, int d_rope, float rope_base,
+                     const int32_t* entry_pos, int out_dtype, void* out, uint8_t* out_scale, int64_t dst_bstride,
+                     const float* pooled, const float* ss, int ncb, const float* gamma, float eps, hipStream_t s);
+
 // ----------------------------------------------------------- device side
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
@@ -233,6 +243,8 @@ struct io<float> {
   __device__ static __forceinline__ float2 load2(const float* p) {
     return *reinterpret_cast<const float2*>(p);
   }
+  __device__ static __forceinline__ float load1(const float* p) { return *p; }
+  __device__ static __forceinline__ void store1(float* p, float v) { *p = v; }
 };
 
 template <>
@@ -241,6 +253,9 @@ struct io<uint16_t> {
     uint32_t v = *reinterpret_cast<const uint32_t*>(p);
     return make_float2(bf16_bits_to_f32(v & 0xffffu), bf16_bits_to_f32(v >> 16));
   }
+  __device__ static __forceinline__ float load1(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+  // round to nearest even
+  __device__ static __forceinline__ void store1(uint16_t* p, float v) { *p = (uint16_t)f32_to_bf16_bits(v); }
 };
 
 }  // namespace csk

@@ -370,6 +370,75 @@ __global__ __launch_bounds__(64) void compress_batch_kernel(BatchArgs args) {
   }
 }
 
+// Entries pooled by another kernel (fp32, row b*N + i, D values) with
+// per-block partial sums of squares (ncb per entry): RMSNorm when gamma is
+// given (the partials summed in ascending block order), then RoPE at the
+// entry's position, then the output rounding or encoding. Same lane layout
+// as compress_kernel: one lane per channel pair, 64 pairs per workgroup.
+struct FinalizeArgs {
+  CompressArgs a;
+  const float* pooled;
+  const float* ss;
+  const float* gamma;
+  int ncb;
+  float eps;
+};
+
+template <int OUT>
+__global__ __launch_bounds__(64) void finalize_kernel(FinalizeArgs f) {
+  const CompressArgs& a = f.a;
+  const int half = a.D / 2;
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= half) return;
+  const int64_t row = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
+  if (row >= (int64_t)a.B * a.N) return;
+  const int b = (int)(row / a.N);
+  const int i = (int)(row - (int64_t)b * a.N);
+  const int ch = 2 * p;
+  const float2 v = *reinterpret_cast<const float2*>(f.pooled + row * a.D + ch);
+  float v0 = v.x, v1 = v.y;
+  if (f.gamma) {
+    float ss = 0.f;
+    for (int cb = 0; cb < f.ncb; ++cb) ss += f.ss[row * f.ncb + cb];
+    const float inv = 1.0f / sqrtf(ss / (float)a.D + f.eps);
+    v0 = v0 * inv * f.gamma[ch];
+    v1 = v1 * inv * f.gamma[ch + 1];
+  }
+  const int rope0 = a.D - a.d_rope;
+  if (ch >= rope0) {
+    const double pos = a.entry_pos ? (double)a.entry_pos[(int64_t)b * a.N + i]
+                                   : (double)a.m * (double)(a.entry0 + i);
+    float c, sn;
+    rope_cs(pos, a.rope.theta[(ch - rope0) / 2], &c, &sn);
+    const float r0 = v0 * c - v1 * sn, r1 = v0 * sn + v1 * c;
+    v0 = r0;
+    v1 = r1;
+  }
+  store_pair<OUT>(a, (int64_t)b * a.dst_bstride + i, p, v0, v1);
+}
+
+int finalize_entries(const char* name, int B, int N, int D, int m, int entry0, int d_rope, float rope_base,
+                     const int32_t* entry_pos, int out_dtype, void* out, uint8_t* out_scale, int64_t dst_bstride,
+                     const float* pooled, const float* ss, int ncb, const float* gamma, float eps, hipStream_t s) {
+  const int64_t rows = (int64_t)B * N;
+  if (rows <= 0) return CSK_OK;
+  CompressArgs a{};
+  a.B = B; a.N = N; a.D = D; a.m = m; a.entry0 = entry0; a.d_rope = d_rope;
+  a.dst_bstride = dst_bstride ? dst_bstride : N;
+  fill_rope_table(&a.rope, d_rope, (double)rope_base);
+  a.entry_pos = entry_pos;
+  a.out = out; a.out_scale = out_scale;
+  FinalizeArgs f{a, pooled, ss, gamma, ncb, eps};
+  const unsigned gy = (unsigned)(rows < 65535 ? rows : 65535);
+  dim3 grid((unsigned)ceil_div(a.D / 2, 64), gy, (unsigned)ceil_div(rows, gy)), block(64);
+  switch (out_dtype) {
+    case CSK_F32: return launch(name, finalize_kernel<OUT_F32>, grid, block, 0, s, f);
+    case CSK_BF16: return launch(name, finalize_kernel<OUT_BF16>, grid, block, 0, s, f);
+    case CSK_FP8KV: return launch(name, finalize_kernel<OUT_FP8KV>, grid, block, 0, s, f);
+    default: return launch(name, finalize_kernel<OUT_MXFP4>, grid, block, 0, s, f);
+  }
+}
+
 template <typename IN, bool CSA>
 static int launch_compress_out(const char* name, const CompressArgs& a, int out_dtype,
                                hipStream_t s) {

@@ -356,6 +356,50 @@ int grouped_out_proj(const void* o, const void* w1, const void* w2, int R, int H
 size_t grouped_out_proj_workspace_size(int R, int g, int dg);
 
 /*
+ * project_compress - the series projected from hidden states and compressed
+ * in one pass ([P1] «CSA: сжать в 4 раза и выбрать top-k», step 1: the KV
+ * series C^a, C^b and the weight series Z^a, Z^b are computed from the
+ * hidden states; «HCA…»: the same pooling over blocks of m' = 128 tokens;
+ * «Muon и борьба с нестабильностью»: KV entries normalised directly by
+ * RMSNorm). The series are products X W^T accumulated in fp32 on the matrix
+ * cores and pooled in registers; they are never written to memory.
+ *   csa     : 1 = CSA (m must be 4; w = [4,D,hidden]: W_ca, W_za, W_cb,
+ *             W_zb), 0 = HCA (m must be 128; w = [2,D,hidden]: W_c, W_z;
+ *             bias_b unused). Weights are [out, in] bf16.
+ *   x       : [B,S,hidden] bf16 hidden states, token t of batch b at
+ *             x + (b*src_bstride + t)*hidden (src_bstride 0 = S). CSA with
+ *             entry0 > 0: the 4 tokens before each batch's first token are
+ *             the previous block (the first entry's b slots) and are read.
+ *   bias_a, bias_b: [m,D] fp32 positional biases of the a / b slots.
+ *   gamma   : [D] fp32 RMSNorm scale, or NULL for no norm. With gamma each
+ *             pooled entry e becomes e * gamma / sqrt(mean(e^2) + eps) over
+ *             all D dims, before its RoPE rotation.
+ *   entry0, d_rope, rope_base, entry_pos, out_dtype, out, out_scale,
+ *   dst_bstride: as csa_compress.
+ *   workspace: >= project_compress_workspace_size(csa, B, S, D, m) bytes
+ *             (the pooled fp32 entries and per-block sums of squares).
+ * Built for hidden % 64 == 0 and D % 32 == 0 (else CSK_EUNSUPPORTED); x, w
+ * and workspace must be 16-byte aligned.
+ */
+int project_compress(int csa, const void* x, const void* w, const float* bias_a, const float* bias_b,
+                     const float* gamma, float eps, int B, int S, int hidden, int D, int m, int entry0,
+                     int64_t src_bstride, int d_rope, float rope_base, const int32_t* entry_pos,
+                     int out_dtype, void* out, uint8_t* out_scale, int64_t dst_bstride, void* workspace,
+                     size_t ws_bytes, void* stream);
+size_t project_compress_workspace_size(int csa, int B, int S, int D, int m);
+
+/*
+ * rmsnorm - RMSNorm of rows of D values (the queries' per-head norm: rows =
+ * B*T*H; [P1] «Muon и борьба с нестабильностью»; [P4]: QK norms):
+ * y = x * gamma / sqrt(mean(x^2) + eps), the sum of squares in fp32.
+ *   x: [rows,D] in in_dtype; gamma: [D] fp32; y: [rows,D] in out_dtype
+ *   (CSK_F32 or CSK_BF16, rounded once). y may equal x (in place, same
+ *   dtype).
+ */
+int rmsnorm(const void* x, const float* gamma, int64_t rows, int D, float eps, int in_dtype,
+            int out_dtype, void* y, void* stream);
+
+/*
  * csk_kernel_timer_arm - opt-in measurement hook (process-wide, one armed
  * timer at a time). The next n launches of the library kernel named
  * `kernel` ("indexer_scores_fp4", "attn_bf16_sparse", ...) are each

@@ -222,3 +222,16 @@ def out_proj(seed, R, H, dv, g, dg, d):
     K1 = H // g * dv
     return dict(o=_bf16_normal(gen, (R, H * dv)), w1=_bf16_normal(gen, (g, dg, K1), 1.0 / K1),
                 w2=_bf16_normal(gen, (d, g * dg), 1.0 / (g * dg)), R=R, H=H, dv=dv, g=g, dg=dg, d=d)
+
+
+def projection(seed, B, S, hidden, D, csa, m):
+    """Projection-then-compression inputs: hidden states x [B,S,hidden] bf16
+    N(0,1); series weights w [4 or 2, D, hidden] bf16 N(0, 1/hidden)
+    (CSA: W_ca, W_za, W_cb, W_zb; HCA: W_c, W_z); positional biases
+    [m, D] N(0, 0.1); RMSNorm scale gamma [D] N(1, 0.01)."""
+    gen = rng(seed)
+    ns = 4 if csa else 2
+    d = dict(x=_bf16_normal(gen, (B, S, hidden)), w=_bf16_normal(gen, (ns, D, hidden), 1.0 / hidden),
+             bias_a=normal(gen, (m, D), 0.1), bias_b=normal(gen, (m, D), 0.1))
+    d["gamma"] = (1.0 + normal(gen, (D,), 0.01)).astype(np.float32)
+    return d

@@ -194,3 +194,30 @@ def test_grouped_out_proj_arguments(lib):
     assert call(ws=sz(100)) == -3 and b"workspace" in lib.csk_last_error()
     assert call(o=ctypes.c_void_p(4098)) == -1 and b"aligned" in lib.csk_last_error()
     assert call(R=0, o=None) == 0                # nothing to do
+
+
+def test_project_compress_and_rmsnorm_arguments(lib):
+    # the binding's argument lists, checked against the library without a
+    # device: every call below fails on its arguments before any launch
+    import compressed_sparse_kv_amd as csk
+    L = csk.lib()
+    assert L.project_compress_workspace_size(1, 1, 65536, 576, 4) == 16384 * 576 * 4 + 16384 * 9 * 4
+    assert L.project_compress_workspace_size(0, 2, 1024, 576, 128) == 16 * 576 * 4 + 16 * 5 * 4
+    fake = ctypes.c_void_p(4096)
+
+    def call(csa=1, m=4, hidden=4096, D=576, S=256, ws=1 << 30, x=fake, out_dtype=1, entry0=0):
+        return L.project_compress(csa, x, fake, fake, fake, None, 1e-6, 1, S, hidden, D, m, entry0, 0, 64, 1e4,
+                                  None, out_dtype, fake, None, 0, fake, ws, None)
+
+    assert call(m=8) == -2 and b"m = 4" in L.csk_last_error()
+    assert call(csa=0, m=4) == -2
+    assert call(hidden=96) == -2
+    assert call(D=48) == -2
+    assert call(out_dtype=7) == -2
+    assert call(out_dtype=2) == -1                   # MXFP4 without out_scale
+    assert call(ws=16) == -3
+    assert call(x=ctypes.c_void_p(4100)) == -1       # misaligned
+    assert call(S=3) == 0                            # no whole block: nothing to do
+    assert L.rmsnorm(fake, fake, 4, 576, ctypes.c_float(1e-6), 1, 5, fake, None) == -2
+    assert L.rmsnorm(None, fake, 4, 576, ctypes.c_float(1e-6), 1, 1, fake, None) == -1
+    assert L.rmsnorm(fake, fake, 0, 576, ctypes.c_float(1e-6), 1, 1, fake, None) == 0
