@@ -833,6 +833,227 @@ def run_prefill(args):
     print(json.dumps(line), flush=True)
 
 
+OUT_PROJ = {  # rows, heads, value dims, groups, intermediate width, hidden
+    "out_proj_prefill_64k": dict(R=65536, H=64, dv=512, g=8, dg=1024, d=4096, seed=11),
+    "out_proj_decode_1m": dict(R=4, H=64, dv=512, g=8, dg=1024, d=4096, seed=12),
+}
+
+
+def run_out_proj(args):
+    """The grouped output projection after attention: the 64 heads' outputs
+    (512 values each) in 8 groups of 8 heads, each group to 1024, then the
+    8192 intermediates to the 4096 hidden features. 'out_proj_prefill_64k':
+    the 65536 rows of the 64K CSA prefill (a matrix-core bound product);
+    'out_proj_decode_1m': the 4 rows of a 1M-context decode step (bound by
+    streaming the 128 MB of weights). Inputs drawn on the device: outputs
+    N(0,1), weights N(0, 1/fan_in), bf16."""
+    import torch
+
+    import compressed_sparse_kv_amd as csk
+
+    c = OUT_PROJ[args.workload]
+    R, H, dv, g, dg, d = c["R"], c["H"], c["dv"], c["g"], c["dg"], c["d"]
+    K1, K2 = H // g * dv, g * dg
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(c["seed"])
+
+    def bf16(*shape, var=1.0):
+        return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * float(np.sqrt(var))).to(
+            torch.bfloat16)
+
+    o = bf16(R, H * dv)
+    w1, w2 = bf16(g, dg, K1, var=1.0 / K1), bf16(d, K2, var=1.0 / K2)
+    y = torch.empty((R, d), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(csk.grouped_out_proj_workspace_size(R, g, dg), dtype=torch.uint8, device=dev)
+    step = lambda: csk.grouped_out_proj(o, w1, w2, out=y, workspace=ws)
+    K, Wm = args.steps, args.warmup
+    for _ in range(max(Wm, 1)):
+        step()
+    torch.cuda.synchronize()
+    prefill = R > 32
+    flops = {"out_proj_groups": 2.0 * R * g * dg * K1, "out_proj_hidden": 2.0 * R * d * K2}
+    nbytes = {"out_proj_groups": 2.0 * (g * dg * K1 + R * H * dv + R * K2),
+              "out_proj_hidden": 2.0 * (d * K2 + R * K2 + R * d)}
+
+    def work(n):
+        if prefill:
+            return "mfma", flops[n], PrefillWorkload.BF16_PEAK_TFLOPS, "TFLOP/s"
+        return "hbm", nbytes[n], HBM_PEAK_GBS, "GB/s"
+
+    per, durs = {}, {}
+    for n in ("out_proj_groups", "out_proj_hidden"):
+        tm = csk.KernelTimer(n, K)
+        for _ in range(K):
+            step()
+        torch.cuda.synchronize()
+        durs[n] = tm.durations_ms()
+        tm.disarm()
+        if len(durs[n]) != K:
+            raise RuntimeError(f"kernel timer recorded {len(durs[n])} of {K} launches of {n}")
+        per[n] = sum(durs[n]) / K
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern = {}
+    for n, ms in per.items():
+        b, wk, pk, un = work(n)
+        a = wk / (ms * 1e-3) / (1e12 if un == "TFLOP/s" else 1e9)
+        kern[n] = dict(avg_launch_us=round(ms * 1e3, 1), bound=b, achieved=round(a, 1), peak=pk, unit=un,
+                       frac=round(a / pk, 4), algorithmic_work=wk)
+    dom = max(per, key=lambda n: per[n])
+    _log("per-kernel: " + ", ".join(f"{n}={v['avg_launch_us']}us {v['frac']:.1%} of {v['bound']}"
+                                    for n, v in kern.items()))
+    _log(f"{K} calls in {elapsed*1e3:.2f} ms -> {elapsed*1e6/K:.1f} us/call")
+    line = {
+        "metric": METRIC, "value": round(R * K / elapsed, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": Wm, "ms_per_step": round(elapsed * 1e3 / K, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "rows": R, "heads": H, "value_dim": dv, "groups": g,
+                   "group_width": dg, "hidden": d, "launch": "eager"},
+        "roofline": dict(kern[dom], kernel=dom, traffic=measured_traffic(dom, args.workload),
+                         timing="HIP events around each launch on its stream, K eager calls"),
+        "kernels": kern,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        n = min(R, 8)
+        ho = o[:n].view(torch.int16).cpu().numpy().view(np.uint16)
+        hw1 = w1.view(torch.int16).cpu().numpy().view(np.uint16)
+        hw2 = w2.view(torch.int16).cpu().numpy().view(np.uint16)
+        oracle.lib()
+        t0 = time.perf_counter()
+        oracle.grouped_out_proj(ho, hw1, hw2)
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = dict({"value": round(n / dt, 3), "unit": "tokens/s",
+                                     "cores": min(oracle.num_threads(), n), "kind": "oracle",
+                                     "sample": f"{n} of the {R} rows ({dt:.1f} s); the oracle runs one thread "
+                                               f"per row"}, **host_cpu())
+    print(json.dumps(line), flush=True)
+
+
+PROJECT = {  # tokens, hidden, series width, RoPE dims, ratio, indexer-key width (CSA)
+    "project_csa_prefill_64k": dict(S=65536, hidden=4096, D=576, d_rope=64, m=4, dI=128, seed=13),
+    "project_hca_prefill_16k": dict(S=16384, hidden=2048, D=128, d_rope=64, m=128, dI=0, seed=14),
+}
+
+
+def run_project(args):
+    """The layer's compression from its hidden states, with the series
+    projections fused into the pooling: 'project_csa_prefill_64k' (65536
+    tokens, hidden 4096: the KV entries 512 + 64 with RMSNorm, bf16, and the
+    indexer keys, 128 wide, MXFP4); 'project_hca_prefill_16k' (16384 tokens,
+    hidden 2048, 128-wide entries with RMSNorm, m' = 128). Bound by the
+    matrix cores: 2 * tokens * hidden * (series widths) flops. Inputs drawn
+    on the device: hidden N(0,1), weights N(0, 1/hidden), biases N(0, 0.1),
+    gamma N(1, 0.01)."""
+    import torch
+
+    import compressed_sparse_kv_amd as csk
+
+    c = PROJECT[args.workload]
+    S, hidden, D, dr, m, dI = c["S"], c["hidden"], c["D"], c["d_rope"], c["m"], c["dI"]
+    csa = m == 4
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(c["seed"])
+
+    def randn(*shape, var=1.0, mean=0.0):
+        return torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * float(np.sqrt(var)) + mean
+
+    ns = 4 if csa else 2
+    x = randn(1, S, hidden).to(torch.bfloat16)
+    w = randn(ns, D, hidden, var=1.0 / hidden).to(torch.bfloat16)
+    ba, bb = randn(m, D, var=0.1), randn(m, D, var=0.1)
+    gamma = randn(D, var=0.01, mean=1.0)
+    N = S // m
+    kv = torch.empty((1, N, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(csk.project_compress_workspace_size(1 if csa else 0, 1, S, D, m), dtype=torch.uint8, device=dev)
+    calls = [lambda: csk.project_compress(x, w, ba, bb if csa else None, m, gamma=gamma, d_rope=dr, out=kv,
+                                          workspace=ws)]
+    flops = {}
+    pool = "csa_project_pool" if csa else "hca_project_pool"
+    fin = "csa_project_finalize" if csa else "hca_project_finalize"
+    if dI:
+        wk = randn(4, dI, hidden, var=1.0 / hidden).to(torch.bfloat16)
+        kba, kbb = randn(m, dI, var=0.1), randn(m, dI, var=0.1)
+        kc = torch.empty((1, N, dI // 2), dtype=torch.uint8, device=dev)
+        ksc = torch.empty((1, N, dI // 32), dtype=torch.uint8, device=dev)
+        wsk = torch.empty(csk.project_compress_workspace_size(1, 1, S, dI, m), dtype=torch.uint8, device=dev)
+        calls.append(lambda: csk.project_compress(x, wk, kba, kbb, m, out_dtype=csk.CSK_MXFP4, out=kc, out_scale=ksc,
+                                                  workspace=wsk))
+    # flops per launch of the pooling kernel, averaged over its launches
+    widths = [ns * D] + ([4 * dI] if dI else [])
+    flops[pool] = 2.0 * S * hidden * sum(widths) / len(widths)
+
+    def step():
+        for f in calls:
+            f()
+
+    K, Wm = args.steps, args.warmup
+    for _ in range(max(Wm, 1)):
+        step()
+    torch.cuda.synchronize()
+    per = {}
+    for n in (pool, fin):
+        tm = csk.KernelTimer(n, K * len(calls))
+        for _ in range(K):
+            step()
+        torch.cuda.synchronize()
+        ds = tm.durations_ms()
+        tm.disarm()
+        if len(ds) != K * len(calls):
+            raise RuntimeError(f"kernel timer recorded {len(ds)} of {K * len(calls)} launches of {n}")
+        per[n] = sum(ds) / len(ds)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern = {}
+    for n, ms in per.items():
+        rec = {"avg_launch_us": round(ms * 1e3, 1), "launches_per_step": len(calls)}
+        if n in flops:
+            a = flops[n] / (ms * 1e-3) / 1e12
+            rec.update(bound="mfma", achieved=round(a, 1), peak=PrefillWorkload.BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                       frac=round(a / PrefillWorkload.BF16_PEAK_TFLOPS, 4), algorithmic_work=flops[n])
+        kern[n] = rec
+    _log("per-kernel: " + ", ".join(f"{n}={v['avg_launch_us']}us" + (f" {v['frac']:.1%} of mfma" if "frac" in v else "")
+                                    for n, v in kern.items()))
+    _log(f"{K} steps in {elapsed*1e3:.2f} ms -> {elapsed*1e3/K:.3f} ms/step")
+    line = {
+        "metric": METRIC, "value": round(S * K / elapsed, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": Wm, "ms_per_step": round(elapsed * 1e3 / K, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" + ("+mxfp4" if dI else ""), "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": S, "hidden": hidden, "kv_dim": D, "rope_dims": dr,
+                   "ratio": m, "indexer_dim": dI, "rmsnorm": True, "launch": "eager"},
+        "roofline": dict(kern[pool], kernel=pool, traffic=measured_traffic(pool, args.workload),
+                         timing="HIP events around each launch on its stream, K eager steps"),
+        "kernels": kern,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        n_tok = 4096 if csa else S  # a few seconds of oracle work
+        hx = x[:, :n_tok].view(torch.int16).cpu().numpy().view(np.uint16)
+        hw = w.view(torch.int16).cpu().numpy().view(np.uint16)
+        oracle.lib()
+        t0 = time.perf_counter()
+        oracle.project_compress(hx, hw, ba.cpu().numpy(), bb.cpu().numpy() if csa else None, m,
+                                gamma=gamma.cpu().numpy(), d_rope=dr)
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = dict({"value": round(n_tok / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
+                                     "kind": "oracle",
+                                     "sample": f"the KV entries of the first {n_tok} tokens ({dt:.1f} s)"},
+                                    **host_cpu())
+    print(json.dumps(line), flush=True)
+
+
 def run_tiny(args):
     """The tiny fp32 CSA prefill (batch 1, seq 256): one whole layer pass -
     compression of the KV and indexer-key series, fp32 indexer scores and
@@ -945,6 +1166,10 @@ KERNEL_SOURCES = {  # sources whose text decides each kernel's code
     "attn_bf16_dense": ["attention.hip", "common.h"],
     "attn_bf16_sparse": ["attention.hip", "common.h"],
     "indexer_scores_fp4": ["indexer.hip", "common.h"],
+    "out_proj_groups": ["gemm.hip", "common.h"],
+    "out_proj_hidden": ["gemm.hip", "common.h"],
+    "csa_project_pool": ["project.hip", "common.h"],
+    "hca_project_pool": ["project.hip", "common.h"],
 }
 
 
@@ -1033,7 +1258,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_1m_pair",
                     choices=["decode_1m_pair", "csa_decode_128k", "hca_prefill_16k", "csa_prefill_64k",
-                             "tiny_csa_prefill"])
+                             "tiny_csa_prefill"] + list(OUT_PROJ) + list(PROJECT))
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--mode", default="graph", choices=["eager", "graph"],
                     help="timed steps as HIP graph replays (default) or as eager launches")
@@ -1064,6 +1289,10 @@ def main():
         return
     if args.workload == "tiny_csa_prefill":
         run_tiny(args)
+    elif args.workload in OUT_PROJ:
+        run_out_proj(args)
+    elif args.workload in PROJECT:
+        run_project(args)
     elif args.workload.endswith("prefill_16k") or args.workload.endswith("prefill_64k"):
         run_prefill(args)
     else:
