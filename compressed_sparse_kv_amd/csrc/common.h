@@ -54,6 +54,15 @@ int finalize_entries(const char* name, int B, int N, int D, int m, int entry0, i
 
 // ----------------------------------------------------------- device side
 
+// 16-byte unit of (row, k chunk kc) in a K slab of 8 chunks per row staged
+// for MFMA fragment reads (32 rows of one chunk per read): the chunk is
+// XOR-swizzled by the row's low three bits and its eighth-row parity, so
+// that any 8 and any 16 consecutive rows of one chunk fall on distinct
+// 16-byte bank groups (128- and 256-byte bank rows alike).
+__host__ __device__ __forceinline__ int slab_unit(int row, int kc) {
+  return row * 8 + (kc ^ (row & 7) ^ ((row >> 3) & 1));
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
   return __uint_as_float(h << 16);
 }

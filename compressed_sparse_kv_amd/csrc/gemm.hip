@@ -50,9 +50,9 @@ constexpr int TM = 256, TN = 256, TK = 64;
 constexpr int TU = TM * TK / 8;  // 16-byte units of one operand slab (2048)
 
 // Slab layout: unit (row, kc) of a 256 x 64 slab (kc = k/8) sits at
-// row*8 + (kc ^ (row & 7)); a DMA instruction fills 64 consecutive units,
-// i.e. eight rows of 128 contiguous bytes each, and a fragment read (32
-// rows, one kc) finds its units on eight distinct bank groups.
+// slab_unit(row, kc); a DMA instruction fills 64 consecutive units, i.e.
+// eight rows of 128 contiguous bytes each, and a fragment read (32 rows,
+// one kc) finds its units on distinct bank groups.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_tile_kernel(GemmArgs g) {
   __shared__ __align__(16) uint4 lds[2][2][TU];  // [buffer][A, B][unit], 128 KB
@@ -77,12 +77,12 @@ void gemm_tile_kernel(GemmArgs g) {
 
   // this lane's DMA sources: instruction i (0..7) of operand X covers
   // units 64*(8*wave + i) + lane: row 8*(8*wave + i) + lane/8, slot lane%8,
-  // k chunk slot ^ (row & 7); rows past the matrix read its last row (their
+  // the k chunk that slab_unit puts in that slot; rows past the matrix read its last row (their
   // products land in output rows or columns that are not stored)
   const int r_base = 64 * wave + (lane >> 3);
   auto src = [&](const uint16_t* X, int64_t ld, int x0, int xmax, int i) {
     const int row = r_base + 8 * i;
-    const int kc = (lane & 7) ^ (row & 7);
+    const int kc = (lane & 7) ^ (row & 7) ^ ((row >> 3) & 1);  // slab_unit's inverse
     return X + (int64_t)min(x0 + row, xmax - 1) * ld + 8 * kc;
   };
   const uint16_t* pa[8];
@@ -133,8 +133,8 @@ void gemm_tile_kernel(GemmArgs g) {
       for (int i = 0; i < 4; ++i) {
         const int ra = 128 * wm + 32 * i + fr, rb = 128 * wn + 32 * i + fr;
         const int kc = 2 * ks + fh;
-        fa[i] = __builtin_bit_cast(v8bf, sa[ra * 8 + (kc ^ (ra & 7))]);
-        fb[i] = __builtin_bit_cast(v8bf, sb[rb * 8 + (kc ^ (rb & 7))]);
+        fa[i] = __builtin_bit_cast(v8bf, sa[slab_unit(ra, kc)]);
+        fb[i] = __builtin_bit_cast(v8bf, sb[slab_unit(rb, kc)]);
       }
     };
     read_frags(0, af[0], bfr[0]);

@@ -109,9 +109,9 @@ void project_compress_kernel(ProjArgs p) {
   }
   __syncthreads();
 
-  // DMA sources. Slab unit (row, kc) at row*8 + (kc ^ (row & 7)); lane l of
+  // DMA sources. Slab unit (row, kc) at slab_unit(row, kc); lane l of
   // instruction i fills unit 64*(8*wave + i) + l: row 64*wave + 8*i + l/8,
-  // k chunk (l%8) ^ (row%8) = (l%8) ^ ((l/8)%8).
+  // k chunk (l%8) ^ (row%8) ^ (row/8 % 2) = (l%8) ^ ((l/8)%8) ^ (i%2).
   const int kc_l = (lane & 7) ^ ((lane >> 3) & 7);
   const int r_base = 64 * wave + (lane >> 3);
   const uint16_t* pa[8];
@@ -119,9 +119,10 @@ void project_compress_kernel(ProjArgs p) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = r_base + 8 * i;
-    pa[i] = X + (int64_t)min(max(T0 + r, lo), p.S - 1) * p.hidden + 8 * kc_l;
+    const int kc = kc_l ^ (i & 1);
+    pa[i] = X + (int64_t)min(max(T0 + r, lo), p.S - 1) * p.hidden + 8 * kc;
     const int s = CSA ? (r >> 6) : (r >> 7), c = CSA ? (r & 63) : (r & 127);
-    pb[i] = p.w + ((int64_t)s * p.D + min(c0 + c, p.D - 1)) * p.hidden + 8 * kc_l;
+    pb[i] = p.w + ((int64_t)s * p.D + min(c0 + c, p.D - 1)) * p.hidden + 8 * kc;
   }
   const uint16_t* px = X + (int64_t)min(max(T0 - 8 + (lane >> 3), lo), p.S - 1) * p.hidden + 8 * kc_l;
   auto issue = [&](int kt, int st) {
@@ -164,18 +165,18 @@ void project_compress_kernel(ProjArgs p) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int ra = 64 * wave + 32 * i + fr;
-        fa[i] = __builtin_bit_cast(v8bf, sl[ra * 8 + (kc ^ (ra & 7))]);
+        fa[i] = __builtin_bit_cast(v8bf, sl[slab_unit(ra, kc)]);
         if (CSA) {
           // token T0 - 4 + ra: slab row ra - 4, or extra row ra + 4
           const int rb = ra - 4;
-          const int u = rb >= 0 ? rb * 8 + (kc ^ (rb & 7)) : 2 * PU + (rb + 8) * 8 + (kc ^ ((rb + 8) & 7));
+          const int u = rb >= 0 ? slab_unit(rb, kc) : 2 * PU + slab_unit(rb + 8, kc);
           fa[2 + i] = __builtin_bit_cast(v8bf, sl[u]);
         }
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int rw = 32 * j + fr;
-        fb[j] = __builtin_bit_cast(v8bf, sl[PU + rw * 8 + (kc ^ (rw & 7))]);
+        fb[j] = __builtin_bit_cast(v8bf, sl[PU + slab_unit(rw, kc)]);
       }
     };
     read_frags(0, af[0], bfr[0]);
