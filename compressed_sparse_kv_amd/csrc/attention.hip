@@ -1110,16 +1110,17 @@ void attn_bf16_row32_kernel(AttnArgs a) {
   constexpr int STU = 64 * ESU;                     // staged tile units
   constexpr int TAIL0 = 64 * CU8;                   // first tail unit of a staged tile
   static_assert(!KV8 || (D == 576 && DV == 512 && CU8 == 32 && ESU == 41), "FP8 KV tiles are built for 512 + 64");
-  // bf16: two tile buffers; KV8: the converted tile (buf0), then two staged
-  // tiles from buf1 on
-  __shared__ __align__(16) uint4 lds_kv[KV8 ? TU + 2 * STU : 2 * TU];
+  // bf16: two tile buffers; KV8: the converted tile (buf0) and the two
+  // staged tiles (buf1). Separate objects: the compiler then knows that a
+  // tile's DMA into one does not write what is read from the other, and
+  // does not wait for the DMA in flight before each LDS read.
+  __shared__ __align__(16) uint4 buf0[TU];
+  __shared__ __align__(16) uint4 buf1[KV8 ? 2 * STU : TU];
   __shared__ __align__(16) uint4 pex_b[KV8 ? 1 : 4 * 2 * 64];  // probabilities, B-operand fragments
   __shared__ int rowtab[KV8 ? 2 * 64 : 1];                     // KV8: the row codes of tiles t, t+1
   __shared__ float mx[4][32];                      // tile maxima per head
   __shared__ float xl[4][32];                      // end-of-row sums per head
   __shared__ float2 rtab[MAX_ROPE_PAIRS];
-  uint4* const buf0 = lds_kv;
-  uint4* const buf1 = lds_kv + TU;
   // staged tile T (KV8)
   auto stg = [&](int T) { return buf1 + STU * (T & 1); };
 
@@ -1550,7 +1551,9 @@ void attn_bf16_row32_kernel(AttnArgs a) {
   // (h%32)*DV/4 + (du ^ h%16), which keeps the scattered writes and the
   // row-wise reads on distinct bank groups.
   constexpr int DU = DV / 4;
-  static_assert(DU % 16 == 0 && (64 * DU) % 512 == 0 && 32 * DV * 4 <= TU * 16, "staging layout");
+  static_assert(DU % 16 == 0 && (64 * DU) % 512 == 0 && 32 * DV * 4 <= TU * 16 &&
+                    32 * DV * 4 <= (KV8 ? 2 * STU : TU) * 16,
+                "staging layout");
   {
     float* st = reinterpret_cast<float*>(hg ? buf1 : buf0);
 #pragma unroll
