@@ -137,14 +137,17 @@ class DecodeWorkload:
         self.out = torch.empty((B, 1, H, dv), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((B, 1, H), dtype=torch.float32, device=dev)
         ws_i = csk.indexer_topk_workspace_size(B, 1, self.HI, self.dI, self.N, k, csk.CSK_MXFP4)
-        ws_s = csk.sparse_attn_workspace_size(B, 1, H, self.D, dv, k, self.W, csk.CSK_BF16)
+        ws_s = csk.sparse_attn_workspace_size(B, 1, H, self.D, dv, k, self.W, csk.CSK_BF16,
+                                              max_workgroups=csa_workgroups)
         self.ws_i = torch.empty(max(ws_i, 1), dtype=torch.uint8, device=dev)
         self.ws_s = torch.empty(max(ws_s, 1), dtype=torch.uint8, device=dev)
         if self.pair:
             self.out_h = torch.empty((B, 1, H, dv), dtype=torch.bfloat16, device=dev)
             self.lse_h = torch.empty((B, 1, H), dtype=torch.float32, device=dev)
-            ws_d = csk.dense_compressed_attn_workspace_size(B, 1, H, self.D, dv, self.Nh, 128, self.W,
-                                                            csk.CSK_BF16)
+            # (the HCA attention runs capped beside the chain, uncapped on one stream)
+            ws_d = max(csk.dense_compressed_attn_workspace_size(B, 1, H, self.D, dv, self.Nh, 128, self.W,
+                                                                csk.CSK_BF16, max_workgroups=cap)
+                       for cap in (0, hca_workgroups))
             self.ws_d = torch.empty(max(ws_d, 1), dtype=torch.uint8, device=dev)
         # the step's three small per-token calls as one batched launch: the
         # newest indexer key (MXFP4), the query encode, and the newest CSA
