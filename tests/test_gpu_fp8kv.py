@@ -137,3 +137,22 @@ def test_fp8kv_unsupported_shape_raises():
     with pytest.raises(csk.CskError):
         csk.sparse_attn(q, dev(np.array([[40]], np.int32)), dev(e), dev(np.zeros((1, 1, 4), np.int32)), None, None, 0,
                         None, DV, DR, 0.04)
+
+
+def test_fp8kv_dense_attention_prefill_rows():
+    # many query rows kept whole (the streamed-row kernel in dense mode over
+    # FP8 entries): causal visibility of 4-token entries, window 32, sink
+    g = synth.rng(840)
+    B, T, N, m, S_w, W = 2, 70, 300, 4, 280, 32
+    e, x = _fp8_cache(g, (B, N))
+    ew, xw = _fp8_cache(g, (B, S_w))
+    q = synth.to_bf16(synth.normal(g, (B, T, H, D)))
+    q_pos = np.sort(g.integers(0, S_w, (B, T)), axis=1).astype(np.int32)
+    w_pos0 = np.zeros(B, np.int32)
+    ne = np.array([N, N - 50], np.int32)
+    sk = synth.normal(g, (H,))
+    out, lse = csk.dense_compressed_attn(dev(q), dev(q_pos), dev(e), dev(ne), m, dev(ew), dev(w_pos0), W, dev(sk),
+                                         DV, DR, 1 / 24)
+    rout, rlse = oracle.dense_attn(q, q_pos, x, ne, m, xw, w_pos0, W, sk, DV, DR, 1 / 24)
+    check_bf16_attention(host(out).reshape(-1, H, DV), rout, "fp8 dense prefill out")
+    check_f32(host(lse).reshape(-1, H), rlse, 2e-2, "fp8 dense prefill lse")
