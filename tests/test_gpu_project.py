@@ -132,3 +132,24 @@ def test_project_compress_errors():
         csk.project_compress(t["x"], t["w"], t["bias_a"], t["bias_b"], 8)     # CSA needs m = 4
     with pytest.raises(csk.CskError):
         csk.project_compress(t["x"][:, :, :32], t["w"][:, :, :32], t["bias_a"], t["bias_b"], 4)  # hidden 32
+
+
+@pytest.mark.parametrize("csa", [True, False])
+def test_strides_and_entry_positions(csa):
+    # batch strides on both sides (sources inside a longer buffer, entries
+    # into a larger cache), explicit entry positions, a ragged tail
+    m = 4 if csa else 128
+    B, S, S_buf, hidden, D = 2, 4 * 67 + 3 if csa else 2 * 128 + 40, 600, 128, 576
+    d, t = _inputs(1800 + csa, B, S_buf, hidden, D, csa, m)
+    N = S // m
+    gen = synth.rng(1810)
+    pos = np.sort(gen.integers(0, 1 << 20, (B, N)), axis=1).astype(np.int32)
+    cache = torch.zeros((B, N + 5, D), dtype=torch.float32, device="cuda")
+    csk.project_compress(t["x"], t["w"], t["bias_a"], t["bias_b"] if csa else None, m, gamma=t["gamma"], d_rope=64,
+                         entry_pos=dev(pos), out_dtype=csk.CSK_F32, src_bstride=S_buf, out=cache, dst_bstride=N + 5,
+                         S=S, B=B)
+    want = oracle.project_compress(d["x"][:, :S], d["w"], d["bias_a"], d["bias_b"] if csa else None, m,
+                                   gamma=d["gamma"], d_rope=64, entry_pos=pos)
+    got = host(cache)
+    check_f32(got[:, :N], want, BAR, "strided fused fp32")
+    assert not got[:, N:].any()
