@@ -53,12 +53,14 @@ constexpr int TU = TM * TK / 8;  // 16-byte units of one operand slab (2048)
 // slab_unit(row, kc); a DMA instruction fills 64 consecutive units, i.e.
 // eight rows of 128 contiguous bytes each, and a fragment read (32 rows,
 // one kc) finds its units on distinct bank groups.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_tile_kernel(GemmArgs g) {
   __shared__ __align__(16) uint4 lds[2][2][TU];  // [buffer][A, B][unit], 128 KB
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  // eight waves, two per SIMD: wave (wr, wc) owns rows 128*wr.. and
+  // columns 64*wc.. of the tile (4 x 2 accumulators of 32 x 32)
+  const int wr = wave & 1, wc = wave >> 1;
   // XCD-contiguous tile order: workgroup w runs on XCD w % 8; XCD x takes
   // a contiguous run of the row-major tile list
   const int tn = (g.N + TN - 1) / TN, tm = (g.M + TM - 1) / TM;
@@ -72,40 +74,41 @@ void gemm_tile_kernel(GemmArgs g) {
 
   // ordinary stores into the slabs first (the DMA builtin is not seen as
   // a writer of them, and without one their reads could be folded away)
-  for (int u = tid; u < 2 * 2 * TU; u += 256) (&lds[0][0][0])[u] = make_uint4(0u, 0u, 0u, 0u);
+  for (int u = tid; u < 2 * 2 * TU; u += 512) (&lds[0][0][0])[u] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
 
-  // this lane's DMA sources: instruction i (0..7) of operand X covers
-  // units 64*(8*wave + i) + lane: row 8*(8*wave + i) + lane/8, slot lane%8,
-  // the k chunk that slab_unit puts in that slot; rows past the matrix read its last row (their
-  // products land in output rows or columns that are not stored)
-  const int r_base = 64 * wave + (lane >> 3);
+  // this lane's DMA sources: instruction i (0..3) of operand X covers
+  // units 64*(4*wave + i) + lane: row 32*wave + 8*i + lane/8, slot lane%8,
+  // the k chunk that slab_unit puts in that slot; rows past the matrix
+  // read its last row (their products land in output rows or columns that
+  // are not stored)
+  const int r_base = 32 * wave + (lane >> 3);
   auto src = [&](const uint16_t* X, int64_t ld, int x0, int xmax, int i) {
     const int row = r_base + 8 * i;
     const int kc = (lane & 7) ^ (row & 7) ^ ((row >> 3) & 1);  // slab_unit's inverse
     return X + (int64_t)min(x0 + row, xmax - 1) * ld + 8 * kc;
   };
-  const uint16_t* pa[8];
-  const uint16_t* pb[8];
+  const uint16_t* pa[4];
+  const uint16_t* pb[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     pa[i] = src(A, g.lda, m0, g.M, i);
     pb[i] = src(B, g.ldb, n0, g.N, i);
   }
   auto issue = [&](int kt, int buf) {
     const int k0 = kt * TK;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_global_load_lds(pa[i] + k0, &lds[buf][0][64 * (8 * wave + i)], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(pb[i] + k0, &lds[buf][1][64 * (8 * wave + i)], 16, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_global_load_lds(pa[i] + k0, &lds[buf][0][64 * (4 * wave + i)], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(pb[i] + k0, &lds[buf][1][64 * (4 * wave + i)], 16, 0, 0);
     }
   };
 
-  v16f acc[4][4];
+  v16f acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
@@ -118,7 +121,7 @@ void gemm_tile_kernel(GemmArgs g) {
     const int buf = kt & 1;
     if (kt + 1 < nk) {
       issue(kt + 1, buf ^ 1);
-      __builtin_amdgcn_s_waitcnt(CSK_G_VMCNT(16));  // slab kt landed (kt+1's 16 in flight)
+      __builtin_amdgcn_s_waitcnt(CSK_G_VMCNT(8));  // slab kt landed (kt+1's 8 in flight)
     } else {
       __builtin_amdgcn_s_waitcnt(CSK_G_VMCNT(0));
     }
@@ -126,23 +129,27 @@ void gemm_tile_kernel(GemmArgs g) {
     asm volatile("" ::: "memory");
     const uint4* sa = lds[buf][0];
     const uint4* sb = lds[buf][1];
-    // the fragments of K-step ks+1 are read while ks's 16 products run
-    v8bf af[2][4], bfr[2][4];
-    auto read_frags = [&](int ks, v8bf (&fa)[4], v8bf (&fb)[4]) {
+    // the fragments of K-step ks+1 are read while ks's 8 products run
+    v8bf af[2][4], bfr[2][2];
+    auto read_frags = [&](int ks, v8bf* fa, v8bf* fb) {
+      const int kc = 2 * ks + fh;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int ra = 128 * wm + 32 * i + fr, rb = 128 * wn + 32 * i + fr;
-        const int kc = 2 * ks + fh;
+        const int ra = 128 * wr + 32 * i + fr;
         fa[i] = __builtin_bit_cast(v8bf, sa[slab_unit(ra, kc)]);
-        fb[i] = __builtin_bit_cast(v8bf, sb[slab_unit(rb, kc)]);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int rb = 64 * wc + 32 * j + fr;
+        fb[j] = __builtin_bit_cast(v8bf, sb[slab_unit(rb, kc)]);
       }
     };
     read_frags(0, af[0], bfr[0]);
 #pragma unroll
     for (int ks = 0; ks < TK / 16; ++ks) {
-      // four products, then the next step's reads (hidden by the other twelve)
+      // two products, then the next step's reads (hidden by the other six)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
         acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][0], bfr[ks & 1][j], acc[0][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       if (ks + 1 < TK / 16) read_frags(ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
@@ -150,7 +157,7 @@ void gemm_tile_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 1; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -161,14 +168,14 @@ void gemm_tile_kernel(GemmArgs g) {
     asm volatile("" ::: "memory");
   }
 
-  // lane holds, per (i, j): column n0 + 128*wn + 32*j + lane%32, rows
-  // m0 + 128*wm + 32*i + 8*q + 4*(lane/32) + e for element 4q + e
+  // lane holds, per (i, j): column n0 + 64*wc + 32*j + lane%32, rows
+  // m0 + 128*wr + 32*i + 8*q + 4*(lane/32) + e for element 4q + e
   char* C = reinterpret_cast<char*>(g.C) + bt * g.c_bs * (g.c_f32 ? 4 : 2);
   GemmArgs gc = g;
   gc.C = C;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int col = n0 + 128 * wn + 32 * j + fr;
+  for (int j = 0; j < 2; ++j) {
+    const int col = n0 + 64 * wc + 32 * j + fr;
     if (col >= g.N) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -176,7 +183,7 @@ void gemm_tile_kernel(GemmArgs g) {
       for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int row = m0 + 128 * wm + 32 * i + 8 * q + 4 * fh + e;
+          const int row = m0 + 128 * wr + 32 * i + 8 * q + 4 * fh + e;
           if (row < g.M) store_c(gc, (int64_t)row * g.ldc + col, acc[i][j][4 * q + e]);
         }
   }
@@ -305,7 +312,7 @@ int launch_gemm(const char* name, const GemmArgs& g, int batches, hipStream_t s)
     return launch(name, gemm_skinny_kernel, dim3((unsigned)ceil_div(g.N, 32), (unsigned)batches), dim3(256), 0, s,
                   g);
   const int64_t tiles = ceil_div(g.M, TM) * ceil_div(g.N, TN);
-  return launch(name, gemm_tile_kernel, dim3((unsigned)tiles, (unsigned)batches), dim3(256), 0, s, g);
+  return launch(name, gemm_tile_kernel, dim3((unsigned)tiles, (unsigned)batches), dim3(512), 0, s, g);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
