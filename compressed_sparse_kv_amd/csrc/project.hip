@@ -14,18 +14,19 @@
 //   - «Muon и борьба с нестабильностью»: queries and KV entries normalised
 //     directly by RMSNorm.
 //
-// Fused kernel: one workgroup computes a 256-token x (channel block) tile
-// of every series with bf16 MFMAs (X W^T, fp32 accumulation), staged by LDS
-// DMA in 64-deep K slabs like the plain matrix product, and pools it in its
-// epilogue, so the series never reach memory:
+// Fused kernel: one workgroup (eight waves of 32 token rows, two per SIMD)
+// computes a 256-token x (channel block) tile of every series with bf16
+// MFMAs (X W^T, fp32 accumulation), staged by LDS DMA in 64-deep K slabs
+// like the plain matrix product, and pools it in its epilogue, so the
+// series never reach memory:
 //   - CSA (m = 4): 64 channels x 4 series. The b series is computed on the
 //     token rows shifted back by 4 (four extra rows staged per slab), so the
 //     a slots (tokens 4j..4j+3) and b slots (4j-4..4j-1) of entry j land in
 //     the same four accumulator rows of the same lane: the 8-slot softmax
 //     runs in registers.
-//   - HCA (m = 128): 128 channels x 2 series; an entry's 128 rows span two
-//     waves: each lane folds its 32 rows, the two half-waves and then the two
-//     waves merge their (max, sum, weighted sum) in a fixed order.
+//   - HCA (m = 128): 128 channels x 2 series; an entry's 128 rows span four
+//     waves: each lane folds its 16 rows, the two half-waves and then the
+//     four waves merge their (max, sum, weighted sum) in a fixed order.
 // The epilogue writes the pooled fp32 entry values and, per entry, the sum
 // of squares of the block's channels; finalize_entries (compress.hip) then
 // applies the RMSNorm (partials summed in ascending block order), RoPE and
@@ -84,12 +85,14 @@ __device__ __forceinline__ Fold merge(Fold a, Fold b) {
 }  // namespace
 
 template <bool CSA>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void project_compress_kernel(ProjArgs p) {
   constexpr int CH = CSA ? 64 : 128;  // channels of a tile
   constexpr int XU = CSA ? PX : 0;
   __shared__ __align__(16) uint4 lds[2][2 * PU + (CSA ? PX : 1)];  // [stage][A | B | A extra]
   const int tid = threadIdx.x, lane = tid & 63;
+  // eight waves, two per SIMD; wave w owns token rows 32w .. 32w+31 of the
+  // tile and every column tile
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ntc = (p.D + CH - 1) / CH;
   const int total = ((p.S + 255) / 256) * ntc;
@@ -103,21 +106,21 @@ void project_compress_kernel(ProjArgs p) {
   // entry) exists in memory only when the call continues a sequence
   const int lo = (CSA && p.entry0 > 0) ? -4 : 0;
 
-  for (int u = tid; u < 2 * (2 * PU + XU); u += 256) {
+  for (int u = tid; u < 2 * (2 * PU + XU); u += 512) {
     const int st = u / (2 * PU + XU), o = u % (2 * PU + XU);
     lds[st][o] = make_uint4(0u, 0u, 0u, 0u);
   }
   __syncthreads();
 
   // DMA sources. Slab unit (row, kc) at slab_unit(row, kc); lane l of
-  // instruction i fills unit 64*(8*wave + i) + l: row 64*wave + 8*i + l/8,
-  // k chunk (l%8) ^ (row%8) ^ (row/8 % 2) = (l%8) ^ ((l/8)%8) ^ (i%2).
+  // instruction i (0..3) fills unit 64*(4*wave + i) + l: row 32*wave + 8*i
+  // + l/8, k chunk (l%8) ^ (row%8) ^ (row/8 % 2) = (l%8) ^ ((l/8)%8) ^ (i%2).
   const int kc_l = (lane & 7) ^ ((lane >> 3) & 7);
-  const int r_base = 64 * wave + (lane >> 3);
-  const uint16_t* pa[8];
-  const uint16_t* pb[8];
+  const int r_base = 32 * wave + (lane >> 3);
+  const uint16_t* pa[4];
+  const uint16_t* pb[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const int r = r_base + 8 * i;
     const int kc = kc_l ^ (i & 1);
     pa[i] = X + (int64_t)min(max(T0 + r, lo), p.S - 1) * p.hidden + 8 * kc;
@@ -128,31 +131,29 @@ void project_compress_kernel(ProjArgs p) {
   auto issue = [&](int kt, int st) {
     const int k0 = kt * PK;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      dma16(pa[i] + k0, &lds[st][64 * (8 * wave + i)]);
-      dma16(pb[i] + k0, &lds[st][PU + 64 * (8 * wave + i)]);
+    for (int i = 0; i < 4; ++i) {
+      dma16(pa[i] + k0, &lds[st][64 * (4 * wave + i)]);
+      dma16(pb[i] + k0, &lds[st][PU + 64 * (4 * wave + i)]);
     }
     if (CSA && wave == 0) dma16(px + k0, &lds[st][2 * PU]);
   };
 
-  v16f acc[2][8];
+  v16f acc[8];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < 8; ++j)
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
 
   const int fr = lane & 31, fh = lane >> 5;
-  constexpr int NA = CSA ? 4 : 2;  // A fragments per K-step (CSA: a rows, then b rows)
+  constexpr int NA = CSA ? 2 : 1;  // A fragments per K-step (CSA: a rows, then b rows)
   const int nk = p.hidden / PK;
   issue(0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
     if (kt + 1 < nk) {
       issue(kt + 1, st ^ 1);
-      if (CSA && wave == 0) __builtin_amdgcn_s_waitcnt(CSK_P_VMCNT(17));
-      else __builtin_amdgcn_s_waitcnt(CSK_P_VMCNT(16));
+      if (CSA && wave == 0) __builtin_amdgcn_s_waitcnt(CSK_P_VMCNT(9));
+      else __builtin_amdgcn_s_waitcnt(CSK_P_VMCNT(8));
     } else {
       __builtin_amdgcn_s_waitcnt(CSK_P_VMCNT(0));
     }
@@ -162,16 +163,13 @@ void project_compress_kernel(ProjArgs p) {
     v8bf af[2][NA], bfr[2][8];
     auto read_frags = [&](int ks, v8bf* fa, v8bf* fb) {
       const int kc = 2 * ks + fh;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int ra = 64 * wave + 32 * i + fr;
-        fa[i] = __builtin_bit_cast(v8bf, sl[slab_unit(ra, kc)]);
-        if (CSA) {
-          // token T0 - 4 + ra: slab row ra - 4, or extra row ra + 4
-          const int rb = ra - 4;
-          const int u = rb >= 0 ? slab_unit(rb, kc) : 2 * PU + slab_unit(rb + 8, kc);
-          fa[2 + i] = __builtin_bit_cast(v8bf, sl[u]);
-        }
+      const int ra = 32 * wave + fr;
+      fa[0] = __builtin_bit_cast(v8bf, sl[slab_unit(ra, kc)]);
+      if (CSA) {
+        // token T0 - 4 + ra: slab row ra - 4, or extra row ra + 4
+        const int rb = ra - 4;
+        const int u = rb >= 0 ? slab_unit(rb, kc) : 2 * PU + slab_unit(rb + 8, kc);
+        fa[1] = __builtin_bit_cast(v8bf, sl[u]);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -183,22 +181,17 @@ void project_compress_kernel(ProjArgs p) {
 #pragma unroll
     for (int ks = 0; ks < PK / 16; ++ks) {
       // CSA: column tiles 0-3 (C^a, Z^a) take the a rows, 4-7 (C^b, Z^b)
-      // the shifted b rows; HCA: every tile takes the block's rows
+      // the shifted b rows; HCA: every tile takes the block's rows. Four
+      // products, then the next step's reads (hidden by the other four).
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][0], bfr[ks & 1][j], acc[0][j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][0], bfr[ks & 1][j], acc[j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       if (ks + 1 < PK / 16) read_frags(ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][1], bfr[ks & 1][j], acc[1][j], 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 4; j < 8; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][CSA ? 2 + i : i], bfr[ks & 1][j],
-                                                              acc[i][j], 0, 0, 0);
+      for (int j = 4; j < 8; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][CSA ? 1 : 0], bfr[ks & 1][j], acc[j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     asm volatile("" ::: "memory");
@@ -207,12 +200,12 @@ void project_compress_kernel(ProjArgs p) {
     asm volatile("" ::: "memory");
   }
 
-  // lane holds, per (i, j): slab column tile j, column lane%32; rows
-  // 64*wave + 32*i + 8*q + 4*fh + e for element 4q + e
+  // lane holds, per column tile j: column lane%32; rows 32*wave + 8*q +
+  // 4*fh + e for element 4q + e
   const int64_t row0 = (int64_t)b * p.N;
   if (CSA) {
-    // entry j = 16*wave + 8*i + 2*q + fh of the tile: a slots at rows
-    // 4j..4j+3 of tiles 0-3, b slots at the same rows of tiles 4-7
+    // entry j = 8*wave + 2*q + fh of the tile: a slots at rows 4j..4j+3 of
+    // tiles 0-3, b slots at the same rows of tiles 4-7
     float ba[2][4], bb[2][4];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
@@ -224,49 +217,47 @@ void project_compress_kernel(ProjArgs p) {
       }
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int q = 0; q < 4; ++q) {
+      const int E = T0 / 4 + 8 * wave + 2 * q + fh;
+      const bool has_b = (p.entry0 + E) > 0;
+      float sq = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int E = T0 / 4 + 16 * wave + 8 * i + 2 * q + fh;
-        const bool has_b = (p.entry0 + E) > 0;
-        float sq = 0.f;
+      for (int ct = 0; ct < 2; ++ct) {
+        const int ch = c0 + 32 * ct + fr;
+        float l[8], v[8];
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const int ch = c0 + 32 * ct + fr;
-          float l[8], v[8];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            l[e] = acc[i][2 + ct][4 * q + e] + ba[ct][e];
-            v[e] = acc[i][ct][4 * q + e];
-            l[4 + e] = has_b ? acc[i][6 + ct][4 * q + e] + bb[ct][e] : -INFINITY;
-            v[4 + e] = acc[i][4 + ct][4 * q + e];
-          }
-          float mx = l[0];
-#pragma unroll
-          for (int e = 1; e < 8; ++e) mx = fmaxf(mx, l[e]);
-          float den = 0.f, num = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float x = l[e] == -INFINITY ? 0.f : expf(l[e] - mx);
-            den += x;
-            num = fmaf(x, v[e], num);
-          }
-          const float pv = num / den;
-          if (ch < p.D) {
-            sq = fmaf(pv, pv, sq);
-            if (E < p.N) p.pooled[(row0 + E) * p.D + ch] = pv;
-          }
+        for (int e = 0; e < 4; ++e) {
+          l[e] = acc[2 + ct][4 * q + e] + ba[ct][e];
+          v[e] = acc[ct][4 * q + e];
+          l[4 + e] = has_b ? acc[6 + ct][4 * q + e] + bb[ct][e] : -INFINITY;
+          v[4 + e] = acc[4 + ct][4 * q + e];
         }
-        // the entry's sum over this block's 64 channels: the 32 lanes of
-        // this half-wave, in a fixed butterfly order
+        float mx = l[0];
 #pragma unroll
-        for (int mk = 1; mk < 32; mk <<= 1) sq += shfl_xor(sq, mk);
-        if (fr == 0 && E < p.N) p.ss[(row0 + E) * p.ncb + tc] = sq;
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, l[e]);
+        float den = 0.f, num = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = l[e] == -INFINITY ? 0.f : expf(l[e] - mx);
+          den += x;
+          num = fmaf(x, v[e], num);
+        }
+        const float pv = num / den;
+        if (ch < p.D) {
+          sq = fmaf(pv, pv, sq);
+          if (E < p.N) p.pooled[(row0 + E) * p.D + ch] = pv;
+        }
       }
+      // the entry's sum over this block's 64 channels: the 32 lanes of
+      // this half-wave, in a fixed butterfly order
+#pragma unroll
+      for (int mk = 1; mk < 32; mk <<= 1) sq += shfl_xor(sq, mk);
+      if (fr == 0 && E < p.N) p.ss[(row0 + E) * p.ncb + tc] = sq;
+    }
   } else {
-    // entry k = wave/2 of the tile (128 rows: waves 2k, 2k+1); this lane's
-    // 32 rows of it: 64*(wave&1) + 32*i + 8*q + 4*fh + e
-    const int k = wave >> 1;
+    // entry k = wave/4 of the tile (128 rows: waves 4k .. 4k+3); this
+    // lane's 16 rows of it: 32*(wave%4) + 8*q + 4*fh + e
+    const int k = wave >> 2, wq = wave & 3;
     const int E = T0 / 128 + k;
     Fold fo[4];
 #pragma unroll
@@ -274,51 +265,49 @@ void project_compress_kernel(ProjArgs p) {
       const int ch = min(c0 + 32 * ct + fr, p.D - 1);
       float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int rr = 64 * (wave & 1) + 32 * i + 8 * q + 4 * fh + e;
-            mx = fmaxf(mx, acc[i][4 + ct][4 * q + e] + p.bias_a[rr * p.D + ch]);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int rr = 32 * wq + 8 * q + 4 * fh + e;
+          mx = fmaxf(mx, acc[4 + ct][4 * q + e] + p.bias_a[rr * p.D + ch]);
+        }
       float den = 0.f, num = 0.f;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int rr = 64 * (wave & 1) + 32 * i + 8 * q + 4 * fh + e;
-            const float x = expf(acc[i][4 + ct][4 * q + e] + p.bias_a[rr * p.D + ch] - mx);
-            den += x;
-            num = fmaf(x, acc[i][ct][4 * q + e], num);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int rr = 32 * wq + 8 * q + 4 * fh + e;
+          const float x = expf(acc[4 + ct][4 * q + e] + p.bias_a[rr * p.D + ch] - mx);
+          den += x;
+          num = fmaf(x, acc[ct][4 * q + e], num);
+        }
       // the two half-waves (rows 4*fh + ...), merged low half first
       const Fold mine{mx, den, num};
       const Fold other{shfl_xor(mx, 32), shfl_xor(den, 32), shfl_xor(num, 32)};
       fo[ct] = fh == 0 ? merge(mine, other) : merge(other, mine);
     }
-    // the two waves of the entry through LDS (the slabs are free), merged
-    // even wave first
+    // the four waves of the entry through LDS (the slabs are free), merged
+    // in wave order
     float* xf = reinterpret_cast<float*>(&lds[0][0]);
-    if (wave & 1)
+    if (wq != 0 && fh == 0)
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
-        const int o = ((k * 4 + ct) * 32 + fr) * 3;
-        if (fh == 0) {
-          xf[o] = fo[ct].mx;
-          xf[o + 1] = fo[ct].den;
-          xf[o + 2] = fo[ct].num;
-        }
+        const int o = (((k * 3 + wq - 1) * 4 + ct) * 32 + fr) * 3;
+        xf[o] = fo[ct].mx;
+        xf[o + 1] = fo[ct].den;
+        xf[o + 2] = fo[ct].num;
       }
     __syncthreads();
-    if ((wave & 1) == 0) {
+    if (wq == 0) {
       float sq = 0.f;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
-        const int o = ((k * 4 + ct) * 32 + fr) * 3;
-        const Fold f = merge(fo[ct], Fold{xf[o], xf[o + 1], xf[o + 2]});
+        Fold f = fo[ct];
+#pragma unroll
+        for (int w2 = 1; w2 < 4; ++w2) {
+          const int o = (((k * 3 + w2 - 1) * 4 + ct) * 32 + fr) * 3;
+          f = merge(f, Fold{xf[o], xf[o + 1], xf[o + 2]});
+        }
         const float pv = f.num / f.den;
         const int ch = c0 + 32 * ct + fr;
         if (ch < p.D) {
@@ -414,8 +403,8 @@ extern "C" int project_compress(int csa, const void* x, const void* w, const flo
   a.src_bstride = src_bstride ? src_bstride : S;
   a.S = S; a.N = N; a.hidden = hidden; a.D = D; a.entry0 = entry0;
   const dim3 grid((unsigned)(ceil_div(S, 256) * a.ncb), (unsigned)B);
-  const int rc = csa ? launch("csa_project_pool", project_compress_kernel<true>, grid, dim3(256), 0, s, a)
-                     : launch("hca_project_pool", project_compress_kernel<false>, grid, dim3(256), 0, s, a);
+  const int rc = csa ? launch("csa_project_pool", project_compress_kernel<true>, grid, dim3(512), 0, s, a)
+                     : launch("hca_project_pool", project_compress_kernel<false>, grid, dim3(512), 0, s, a);
   if (rc != CSK_OK) return rc;
   return finalize_entries(csa ? "csa_project_finalize" : "hca_project_finalize", B, N, D, m, entry0, d_rope,
                           rope_base, entry_pos, out_dtype, out, out_scale, dst_bstride, a.pooled, a.ss, a.ncb,
