@@ -54,7 +54,7 @@ def test_fp32_path_tiny_prefill():
     assert np.all(host(idx)[0, :3] == -1)          # rows 0..2 see no entry
 
 
-@pytest.mark.parametrize("HI,dI", [(64, 128), (32, 128), (16, 256), (8, 64)])
+@pytest.mark.parametrize("HI,dI", [(64, 128), (32, 128), (64, 256), (32, 256), (48, 128), (16, 256), (8, 64)])
 def test_mxfp4_short_rows(HI, dI):
     g = synth.rng(502 + HI + dI)
     B, T, N, m, k = 2, 37, 1000, 4, 64
