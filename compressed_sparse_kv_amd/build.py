@@ -20,10 +20,13 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-I", os.path.join(ROOT, "include")]
 
 
-# Per-source code generation choices. indexer.hip: MFMA results in VGPRs
-# (with the compiler's default the score tiles land in AGPRs, and each of
-# them is copied out before the lane swaps and the head chain).
-EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source code generation choices: MFMA results in VGPRs. indexer.hip:
+# with the compiler's default the score tiles land in AGPRs, and each of
+# them is copied out before the lane swaps and the head chain.
+# attention.hip: with the default the output accumulators sit in AGPRs and
+# are copied to VGPRs and back around every tile step.
+EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src):
