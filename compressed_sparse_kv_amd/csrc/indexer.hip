@@ -47,6 +47,7 @@ constexpr int IDX_TARGET_WGS = 512;   // two resident 4-wave workgroups per CU
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 struct IdxArgs {
   const uint8_t* qc;   // MXFP4 q codes   [R, HI, dI/2]
@@ -75,15 +76,18 @@ __device__ __forceinline__ float topk_score(const IdxArgs& a, float x) {
 // (r is the workgroup's row: uniform.) Both loads are issued before either
 // value is used (the empty asm takes them as scalar operands), so they
 // cost one memory round trip; the arithmetic is branch-free 32-bit.
+__device__ __forceinline__ int visible_count_of(const IdxArgs& a, int p, int ne) {
+  unsigned nv = p < 0 ? 0u : ((unsigned)p + 1u) / (unsigned)a.m;  // p + 1 <= 2^31 fits
+  nv = min(nv, ne < 0 ? 0u : (unsigned)ne);
+  nv = min(nv, (unsigned)a.Nmax);
+  return (int)nv;
+}
 __device__ __forceinline__ int visible_count(const IdxArgs& a, int r) {
   const unsigned b = (unsigned)r / (unsigned)a.T;
   const int p = a.q_pos[r];
   const int ne = a.n_entries[b];
   asm volatile("" ::"s"(p), "s"(ne));
-  unsigned nv = p < 0 ? 0u : ((unsigned)p + 1u) / (unsigned)a.m;  // p + 1 <= 2^31 fits
-  nv = min(nv, ne < 0 ? 0u : (unsigned)ne);
-  nv = min(nv, (unsigned)a.Nmax);
-  return (int)nv;
+  return visible_count_of(a, p, ne);
 }
 
 // order-preserving key: larger score -> larger key; -0 is folded onto +0
@@ -112,8 +116,7 @@ __device__ __forceinline__ void swap16(float& x, float& y) {
 // written for groups of 2^gs_log2 keys (gs <= 64): maxima within aligned
 // lane groups of 2, 4 (quad permutes), 8 (half-row mirror), 16 (row
 // mirror), then across rows (permlane swaps), all VALU steps.
-__device__ __forceinline__ void write_samples(const IdxArgs& a, int r, int base, float v) {
-  const int gs = 1 << a.gs_log2;
+__device__ __forceinline__ float group_max(const IdxArgs& a, float v) {
   const int g = a.gs_log2;
   float mx = v;
   if (g >= 1) mx = fmaxf(mx, CSK_DPP_F(mx, 0xB1));   // quad_perm [1,0,3,2]
@@ -128,10 +131,16 @@ __device__ __forceinline__ void write_samples(const IdxArgs& a, int r, int base,
     const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
     mx = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
   }
+  return mx;
+}
+__device__ __forceinline__ void store_sample(const IdxArgs& a, int r, int base, float mx) {
   const int lane = threadIdx.x & 63;
   const int key = base + lane;
-  if ((lane & (gs - 1)) == 0 && key < a.Nmax)
+  if ((lane & ((1 << a.gs_log2) - 1)) == 0 && key < a.Nmax)
     a.samples[(int64_t)r * a.ng + (key >> a.gs_log2)] = mx;
+}
+__device__ __forceinline__ void write_samples(const IdxArgs& a, int r, int base, float v) {
+  store_sample(a, r, base, group_max(a, v));
 }
 
 // ---------------------------------------------------------------- MFMA path
@@ -289,6 +298,298 @@ __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
     if (base >= nv) break;
     process(buf[it % 3], base);
     if (it + 3 < ITERS) load_keys(buf[it % 3], base + 3 * 256);
+  }
+}
+
+// ------------------------------------------------------ MFMA path, 32 heads
+// The same scores for HI a multiple of 32, on the 32x32 scaled FP4 MFMA
+// (v_mfma_scale_f32_32x32x64_f8f6f4): operand lane l holds row l%32 and the
+// 32 elements of K block l/32 of the 64-wide K-step (16 bytes), with that
+// block's scale byte; result lane l holds column l%32 (the key) and rows
+// 8i + 4*(l/32) + j in element 4i+j. A wave's 64 keys are two key tiles, so
+// one v_permlane32_swap per register pair (half the exchanges of the 16x16
+// form) leaves lane l with every head of key base + l, and half as many
+// MFMA instructions cover the same products. With the four tile exponents
+// of a pair within the fp32 significand every partial sum is exact, so
+// splitting K into 64-wide steps gives the same bits as one 128-wide step.
+//
+// Keys reach LDS by DMA: each wave streams its 64-key groups through NB
+// stages, so that NB groups are in flight and no key occupies a register
+// before its products. The waits are explicit: the stage's DMA count, then
+// the fragment reads in one asm block that waits for them itself (the
+// compiler's own tracking would wait for every DMA in flight). The queries
+// come by DMA as well, and the scores and group maxima stay in registers
+// until the end, so no plain load or store is counted between a stage's DMA
+// and its wait. Used for prefill rows, where the head chain's VALU work
+// bounds the indexer.
+// HT2 = HI/32 head tiles, KB = dI/32 16-byte chunks (and scale bytes) per key.
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+
+__device__ __forceinline__ void idx_dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void idx_dma4(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 4, 0, 0);
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const lds_u32*)(const uint32_t*)p);
+}
+// Four 16-byte and two 4-byte LDS reads (byte addresses), waited for inside
+// the same asm block, so no output register is live while a read is in
+// flight.
+__device__ __forceinline__ void lds_read_4x16_2x4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                                   uint32_t b0, uint32_t b1, v4u& f0, v4u& f1, v4u& f2,
+                                                   v4u& f3, uint32_t& w0, uint32_t& w1) {
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %7\n\t"
+      "ds_read_b128 %2, %8\n\t"
+      "ds_read_b128 %3, %9\n\t"
+      "ds_read_b32 %4, %10\n\t"
+      "ds_read_b32 %5, %11\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f0), "=&v"(f1), "=&v"(f2), "=&v"(f3), "=&v"(w0), "=&v"(w1)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(b0), "v"(b1)
+      : "memory");
+}
+// Two 16-byte and one 4-byte LDS reads, waited for inside the asm block.
+__device__ __forceinline__ void lds_read_2x16_1x4(uint32_t a0, uint32_t a1, uint32_t b0, v4u& f0, v4u& f1,
+                                                   uint32_t& w0) {
+  asm volatile(
+      "ds_read_b128 %0, %3\n\t"
+      "ds_read_b128 %1, %4\n\t"
+      "ds_read_b32 %2, %5\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f0), "=&v"(f1), "=&v"(w0)
+      : "v"(a0), "v"(a1), "v"(b0)
+      : "memory");
+}
+// s_waitcnt immediate: vmcnt(n) only
+#define CSK_IDX_VMCNT(n) ((((n) & 0xF) | ((((n) >> 4) & 0x3) << 14)) | (0x7 << 4) | (0xF << 8))
+
+template <int KB>
+struct IdxStage {
+  uint4 code[4][64 * KB];              // [wave][unit]: 64 keys x KB chunks, swizzled
+  uint32_t scale[4][(KB + 3) / 4][64]; // [wave][dword][key]
+};
+
+template <int HT2, int KB, int ITERS, int NB>
+__global__ __launch_bounds__(256) void idx_fp4_w32_kernel(IdxArgs a) {
+  static_assert(NB >= 2 && NB <= 4, "two to four stages");
+  static_assert(KB == 4 || KB == 8, "dI of 128 or 256");
+  constexpr int KS2 = KB / 2;       // 64-deep K-steps
+  constexpr int SD = (KB + 3) / 4;  // scale dwords per key
+  constexpr int HI = HT2 * 32;
+  constexpr int SWS = KB == 4 ? 2 : 1;  // chunk swizzle: unit KB*k + (c ^ ((k >> SWS) % KB))
+  constexpr int PER = KB + SD;          // DMA instructions per group
+  __shared__ IdxStage<KB> st0, st1, st2, st3;
+  const int r = blockIdx.x;
+  const int b = r / a.T;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // (uniform: scalar branches)
+  const int wg_base = blockIdx.y * (256 * ITERS) + wave * 64;
+  const int rho = lane & 31, hb = lane >> 5;
+  auto stage = [&](int j) -> IdxStage<KB>& {
+    return (j % NB) == 0 ? st0 : ((j % NB) == 1 ? st1 : ((j % NB) == 2 ? st2 : st3));
+  };
+
+  // scalar loads first, before any DMA (once a DMA precedes them in the
+  // program they can no longer be proven unclobbered and become vector
+  // loads, whose wait would cover every DMA issued ahead of them): the
+  // row's position and cache length, and its head weights (scalar
+  // registers for the whole kernel: the head chain's fma takes them as
+  // scalar operands)
+  const int q_pos = a.q_pos[r];
+  const int n_ent = a.n_entries[b];
+  const float* w_row = a.w + (int64_t)r * HI;
+  float wsc[HI];
+#pragma unroll
+  for (int i = 0; i < HI; ++i) wsc[i] = w_row[i];
+
+  // DMA of group j (keys base..base+63, clamped to the cache): instruction
+  // i, lane l fills unit 64i + l = KB*k + p with chunk p ^ swizzle(k) of key
+  // k; the scale dwords go one instruction per dword
+  const uint8_t* kc_b = a.kc + (int64_t)b * a.Nmax * (KB * 16);
+  const uint8_t* ks_b = a.ks + (int64_t)b * a.Nmax * KB;
+  auto issue = [&](int j) {
+    IdxStage<KB>& S = stage(j);
+    const int base = wg_base + 256 * j;
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const int u = 64 * i + lane, k = u / KB, pp = u % KB;
+      const int c = pp ^ ((k >> SWS) % KB);
+      const int key = min(base + k, a.Nmax - 1);
+      idx_dma16(kc_b + (uint32_t)key * (uint32_t)(KB * 16) + 16 * c, &S.code[wave][64 * i]);
+    }
+    const int key = min(base + lane, a.Nmax - 1);
+#pragma unroll
+    for (int d = 0; d < SD; ++d)
+      idx_dma4(ks_b + (uint32_t)key * (uint32_t)KB + 4 * d, &S.scale[wave][d][0]);
+  };
+
+  // The row's queries reach LDS by DMA as well (a plain vector load pending
+  // beside DMA makes every compiler wait a full drain), one copy per
+  // workgroup in the keys' swizzled chunk layout; the waves split the
+  // instructions, wait for their own, and meet at one barrier before any
+  // wave may leave.
+  __shared__ __align__(16) uint4 qlds[HI * KB];
+  __shared__ uint32_t qsl[HI * SD < 64 ? 64 : HI * SD];
+  constexpr int QI = HI * KB / 64;         // 16-byte DMA instructions
+  constexpr int QSI = (HI * SD + 63) / 64; // scale-dword DMA instructions (wave 0)
+  {
+    const uint8_t* q_row = a.qc + (int64_t)r * HI * (KB * 16);
+#pragma unroll
+    for (int i = 0; i < QI; ++i) {
+      if (i % 4 != wave) continue;
+      const int u = 64 * i + lane, h = u / KB, pp = u % KB;
+      const int c = pp ^ ((h >> SWS) % KB);
+      idx_dma16(q_row + h * (KB * 16) + 16 * c, &qlds[64 * i]);
+    }
+    if (wave == 0) {
+      const uint8_t* qs_row = a.qs + (int64_t)r * HI * KB;
+#pragma unroll
+      for (int i = 0; i < QSI; ++i) {
+        const int dw = min(64 * i + lane, HI * SD - 1);
+        idx_dma4(qs_row + 4 * dw, &qsl[64 * i]);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(CSK_IDX_VMCNT(0));
+  // (a bare barrier: the wait above already covers the query DMA)
+  __builtin_amdgcn_s_barrier();
+  // A operands: head 32t + rho in row rho of head tile t (no permutation:
+  // after the swap, register x, tile t, element 4i+j holds head
+  // 32t + 8i + 4x + j, so the chain below visits heads in ascending order)
+  v8i qa[HT2][KS2];
+  int qsc[HT2][KS2];
+#pragma unroll
+  for (int t = 0; t < HT2; ++t) {
+    const int h = 32 * t + rho;
+#pragma unroll
+    for (int s = 0; s < KS2; s += 2) {
+      const int c0 = 2 * s + hb, c1 = 2 * (s + 1) + hb;
+      v4u f0, f1;
+      uint32_t dw;
+      lds_read_2x16_1x4(lds_addr(&qlds[KB * h + (c0 ^ ((h >> SWS) % KB))]),
+                        lds_addr(&qlds[KB * h + (c1 ^ ((h >> SWS) % KB))]), lds_addr(&qsl[h * SD + (c0 >> 2)]),
+                        f0, f1, dw);
+      qa[t][s] = v8i{(int)f0.x, (int)f0.y, (int)f0.z, (int)f0.w, 0, 0, 0, 0};
+      qa[t][s + 1] = v8i{(int)f1.x, (int)f1.y, (int)f1.z, (int)f1.w, 0, 0, 0, 0};
+      qsc[t][s] = (int)((dw >> (8 * (c0 & 3))) & 0xffu);
+      qsc[t][s + 1] = (int)((dw >> (8 * (c1 & 3))) & 0xffu);
+    }
+  }
+
+  const int nv = visible_count_of(a, q_pos, n_ent);
+  if (wg_base >= nv) {
+    __builtin_amdgcn_s_waitcnt(0);  // no DMA outlives the wave
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < NB && j < ITERS; ++j) issue(j);
+  // (nothing that uses the queries moves above the DMA issue: its wait
+  // would cover the DMA too)
+  __builtin_amdgcn_sched_barrier(0);
+
+  float score[ITERS], gmax[ITERS];
+  int done = ITERS;
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int base = wg_base + 256 * it;
+    if (base >= nv) {
+      done = it;
+      break;
+    }
+    // this stage's DMA done: the groups after it stay in flight
+    {
+      const int ahead = NB - 1 < ITERS - 1 - it ? NB - 1 : ITERS - 1 - it;  // groups issued after it
+      if (ahead >= 3) __builtin_amdgcn_s_waitcnt(CSK_IDX_VMCNT(3 * PER));
+      else if (ahead == 2) __builtin_amdgcn_s_waitcnt(CSK_IDX_VMCNT(2 * PER));
+      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(CSK_IDX_VMCNT(PER));
+      else __builtin_amdgcn_s_waitcnt(CSK_IDX_VMCNT(0));
+    }
+    IdxStage<KB>& S = stage(it);
+    // fragments: key tile kt, K-step s -> chunk c = 2s + hb of key 32kt + rho
+    v4u fr[2][KS2];
+    uint32_t scw[2][SD];
+    {
+      auto code_at = [&](int kt, int s) {
+        const int k = 32 * kt + rho, c = 2 * s + hb;
+        return lds_addr(&S.code[wave][KB * k + (c ^ ((k >> SWS) % KB))]);
+      };
+      if constexpr (KB == 4) {
+        lds_read_4x16_2x4(code_at(0, 0), code_at(0, 1), code_at(1, 0), code_at(1, 1),
+                          lds_addr(&S.scale[wave][0][rho]), lds_addr(&S.scale[wave][0][32 + rho]),
+                          fr[0][0], fr[0][1], fr[1][0], fr[1][1], scw[0][0], scw[1][0]);
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+          lds_read_4x16_2x4(code_at(kt, 0), code_at(kt, 1), code_at(kt, 2), code_at(kt, 3),
+                            lds_addr(&S.scale[wave][0][32 * kt + rho]),
+                            lds_addr(&S.scale[wave][SD - 1][32 * kt + rho]),
+                            fr[kt][0], fr[kt][1], fr[kt][2], fr[kt][3], scw[kt][0], scw[kt][SD - 1]);
+      }
+    }
+    // the stage is free again (the reads above have completed): refill it
+    if (it + NB < ITERS) issue(it + NB);
+
+    v16f acc[2][HT2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int t = 0; t < HT2; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[kt][t][e] = 0.f;
+#pragma unroll
+      for (int s = 0; s < KS2; ++s) {
+        const int c = 2 * s + hb;
+        const v8i kbv = v8i{(int)fr[kt][s].x, (int)fr[kt][s].y, (int)fr[kt][s].z, (int)fr[kt][s].w, 0, 0, 0, 0};
+        const int ksc = (int)((scw[kt][s >> 1] >> (8 * (c & 3))) & 0xffu);
+#pragma unroll
+        for (int t = 0; t < HT2; ++t)
+          acc[kt][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              qa[t][s], kbv, acc[kt][t], 4, 4, 0, qsc[t][s], 0, ksc);
+      }
+    }
+
+    // one exchange per register pair: lanes 32-63 of key tile 0 with lanes
+    // 0-31 of key tile 1. Register x then holds the rows 8i + 4x + j of key
+    // base + lane.
+    float d[2][HT2][16];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int t = 0; t < HT2; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) d[kt][t][e] = acc[kt][t][e];
+#pragma unroll
+    for (int t = 0; t < HT2; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) swap32(d[0][t][e], d[1][t][e]);
+
+    // ascending head chain (ReLU as an integer max on the bits)
+    float sum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < HT2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float v = __int_as_float(max(__float_as_int(d[x][t][4 * i + j]), 0));
+            sum = __builtin_fmaf(wsc[32 * t + 8 * i + 4 * x + j], v, sum);
+          }
+    score[it] = topk_score(a, sum);
+    if (a.samples) gmax[it] = group_max(a, base + lane < nv ? score[it] : -INFINITY);
+  }
+
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    if (it >= done) break;
+    const int base = wg_base + 256 * it;
+    if (base + lane < nv) a.scores[(int64_t)r * a.Nmax + base + lane] = score[it];
+    if (a.samples) store_sample(a, r, base, gmax[it]);
   }
 }
 
@@ -939,8 +1240,8 @@ static int indexer_topk_impl(const char* fn, bool noalloc, const void* q, const 
     return fail(CSK_EINVAL, f + ": MXFP4 needs dI % 32 == 0 and both scale arrays");
   if (score_dtype != CSK_F32 && score_dtype != CSK_BF16)
     return fail(CSK_EUNSUPPORTED, f + ": score_dtype must be CSK_F32 or CSK_BF16");
-  if (dtype == CSK_MXFP4 && (reinterpret_cast<uintptr_t>(k_scale) & 3))
-    return fail(CSK_EINVAL, f + ": k_scale must be 4-byte aligned (read as dwords)");
+  if (dtype == CSK_MXFP4 && ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(q_scale)) & 3))
+    return fail(CSK_EINVAL, f + ": k_scale and q_scale must be 4-byte aligned (read as dwords)");
   if ((int64_t)B * T > (1LL << 30) || ceil_div(Nmax, 256 * IDX_MIN_ITERS) > 65535)
     return fail(CSK_EUNSUPPORTED, f + ": B*T or Nmax too large");
   IdxPlan p = plan_indexer(B, T, Nmax, k);
@@ -979,7 +1280,10 @@ static int indexer_topk_impl(const char* fn, bool noalloc, const void* q, const 
   ia.bf16_scores = score_dtype == CSK_BF16;
 
   int rc = CSK_OK;
-  const bool mfma = dtype == CSK_MXFP4 && HI % 16 == 0 && HI <= 64 && dI % 128 == 0 && dI <= 256;
+  // (the MFMA paths read the codes in 16-byte chunks: other alignments take
+  // the VALU path)
+  const bool mfma = dtype == CSK_MXFP4 && HI % 16 == 0 && HI <= 64 && dI % 128 == 0 && dI <= 256 &&
+                    ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kk)) & 15) == 0;
   if (mfma) {
     // 64-key groups per wave: 8 when the grid is short (a few rows over a
     // long cache: it then still has about two workgroups per CU), else 4
@@ -988,13 +1292,26 @@ static int indexer_topk_impl(const char* fn, bool noalloc, const void* q, const 
     ia.iters = iters;
     dim3 grid((unsigned)R, (unsigned)ceil_div(Nmax, 256 * iters)), block(256);
     const int HT = HI / 16, KS = dI / 128;
+    // Prefill rows (several queries per sequence) with 32 or 64 heads: the
+    // 32x32 DMA form (VALU-bound there; it issues fewer VALU instructions
+    // per key). Decode rows, and 16 or 48 heads: the 16x16 form (measured
+    // faster where the key stream dominates).
+    const bool w32 = HI % 32 == 0 && T > 1;
 #define CSK_IDX_CASE(ht, ks)                                                                     \
-  if (HT == ht && KS == ks)                                                                      \
+  if (!w32 && HT == ht && KS == ks)                                                              \
     rc = iters == 8 ? launch("indexer_scores_fp4", idx_fp4_kernel<ht, ks, 8>, grid, block, 0, s, ia) \
                     : launch("indexer_scores_fp4", idx_fp4_kernel<ht, ks, 4>, grid, block, 0, s, ia);
     CSK_IDX_CASE(1, 1) CSK_IDX_CASE(2, 1) CSK_IDX_CASE(3, 1) CSK_IDX_CASE(4, 1)
     CSK_IDX_CASE(1, 2) CSK_IDX_CASE(2, 2) CSK_IDX_CASE(3, 2) CSK_IDX_CASE(4, 2)
 #undef CSK_IDX_CASE
+#define CSK_IDX_W32_CASE(ht2, kb)                                                                  \
+  if (w32 && HI == 32 * ht2 && dI == 32 * kb) {                                                    \
+    constexpr int nb = kb == 4 ? 4 : 2;                                                            \
+    rc = iters == 8 ? launch("indexer_scores_fp4", idx_fp4_w32_kernel<ht2, kb, 8, nb>, grid, block, 0, s, ia) \
+                    : launch("indexer_scores_fp4", idx_fp4_w32_kernel<ht2, kb, 4, nb>, grid, block, 0, s, ia); \
+  }
+    CSK_IDX_W32_CASE(1, 4) CSK_IDX_W32_CASE(2, 4) CSK_IDX_W32_CASE(1, 8) CSK_IDX_W32_CASE(2, 8)
+#undef CSK_IDX_W32_CASE
   } else {
     dim3 grid((unsigned)R, (unsigned)ceil_div(Nmax, 256)), block(256);
     rc = dtype == CSK_MXFP4 ? launch("indexer_scores_valu", idx_valu_kernel<true>, grid, block, 0, s, ia)
