@@ -325,6 +325,60 @@ __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const IN* x, int64_t r
   quant_pair<IN>(x, gid / half, cols, (int)(gid % half), codes, scales);
 }
 
+// Streaming form for whole tensors: sixteen consecutive values per lane (one
+// 64-byte fp32 or 32-byte bf16 load, one 8-byte code store); the two lanes
+// of a 32-value tile (lanes 2i and 2i+1: the element count is a multiple of
+// 32) share the tile maximum through one DPP swap. The encoding is the
+// per-pair one's, value for value. Lanes past the end work on a copy of the
+// last values (their pair partner is past the end too) and store nothing.
+template <typename IN>
+__global__ __launch_bounds__(256) void mxfp4_quant16_kernel(const IN* x, int64_t n16, uint8_t* codes,
+                                                             uint8_t* scales) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t tc = t < n16 ? t : n16 - 1;
+  float v[16];
+  if constexpr (sizeof(IN) == 4) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const f4* src = reinterpret_cast<const f4*>(x) + 4 * tc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f4 f = __builtin_nontemporal_load(src + i);
+      v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+    }
+  } else {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    const u4* src = reinterpret_cast<const u4*>(x) + 2 * tc;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const u4 u = __builtin_nontemporal_load(src + i);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[8 * i + 2 * k] = bf16_bits_to_f32(w[k] & 0xffffu);
+        v[8 * i + 2 * k + 1] = bf16_bits_to_f32(w[k] >> 16);
+      }
+    }
+  }
+  float amax = fabsf(v[0]);
+#pragma unroll
+  for (int i = 1; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, CSK_DPP_F(amax, 0xB1));  // quad_perm [1,0,3,2]: the tile's other lane
+  uint32_t lo = 0u, hi = 0u, sc = 127u;
+  if (amax != 0.0f) {
+    const int s = mx_scale_exp(amax);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      lo |= (e2m1_encode(v[2 * k], s) | (e2m1_encode(v[2 * k + 1], s) << 4)) << (8 * k);
+      hi |= (e2m1_encode(v[8 + 2 * k], s) | (e2m1_encode(v[8 + 2 * k + 1], s) << 4)) << (8 * k);
+    }
+    sc = (uint32_t)(s + 127);
+  }
+  if (t < n16) {
+    *reinterpret_cast<uint2*>(codes + 8 * t) = make_uint2(lo, hi);
+    if ((t & 1) == 0) scales[t >> 1] = (uint8_t)sc;
+  }
+}
+
 // Several independent small compressions and MXFP4 encodes in one launch
 // (a decode step issues a few, each too small to fill the chip, and each
 // launch boundary costs more than its work). The grid is one dimension:
@@ -635,9 +689,19 @@ int mxfp4_quantize(const void* x, int in_dtype, int64_t rows, int cols, uint8_t*
   if (rc != CSK_OK) return rc;
   if (rows == 0) return CSK_OK;
   if (const int dc = csk::check_device("mxfp4_quantize"); dc != CSK_OK) return dc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // aligned tensors: sixteen values per lane
+  if ((reinterpret_cast<uintptr_t>(x) & 15) == 0 && (reinterpret_cast<uintptr_t>(codes) & 7) == 0) {
+    const int64_t n16 = rows * (cols / 16);
+    dim3 grid((unsigned)csk::ceil_div(n16, 256)), block(256);
+    if (in_dtype == CSK_F32)
+      return csk::launch("mxfp4_quantize", csk::mxfp4_quant16_kernel<float>, grid, block, 0, s,
+                         reinterpret_cast<const float*>(x), n16, codes, scales);
+    return csk::launch("mxfp4_quantize", csk::mxfp4_quant16_kernel<uint16_t>, grid, block, 0, s,
+                       reinterpret_cast<const uint16_t*>(x), n16, codes, scales);
+  }
   const int64_t total = rows * (cols / 2);
   dim3 grid((unsigned)csk::ceil_div(total, 256)), block(256);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (in_dtype == CSK_F32)
     return csk::launch("mxfp4_quantize", csk::mxfp4_quant_kernel<float>, grid, block, 0, s,
                        reinterpret_cast<const float*>(x), rows, cols, codes, scales);

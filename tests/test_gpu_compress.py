@@ -48,6 +48,26 @@ def test_mxfp4_quantize_bit_exact(rows, cols, seed):
 
 
 @pytest.mark.parametrize("bf16_in", [False, True])
+def test_mxfp4_quantize_unaligned_input(bf16_in):
+    # an input 4 bytes past a 16-byte boundary takes the per-pair kernel,
+    # an aligned one the sixteen-values-per-lane kernel: both give the
+    # oracle's bytes
+    g = synth.rng(150)
+    rows, cols = 300, 160
+    x = synth.normal(g, (rows, cols))
+    xh = synth.to_bf16(x) if bf16_in else x
+    ref_in = oracle.bf16_to_f32(xh) if bf16_in else x
+    rc, rs = oracle.mxfp4_encode(ref_in)
+    flat = np.concatenate([np.zeros(2 if bf16_in else 1, xh.dtype), xh.reshape(-1)])
+    buf = dev(flat)
+    view = buf[2 if bf16_in else 1:].view(rows, cols)
+    assert view.data_ptr() % 16 != 0
+    for t in (view, dev(xh)):
+        codes, scales = csk.mxfp4_quantize(t)
+        assert np.array_equal(host(codes), rc) and np.array_equal(host(scales), rs)
+
+
+@pytest.mark.parametrize("bf16_in", [False, True])
 @pytest.mark.parametrize("B,S,D,m,d_rope", [(1, 64, 64, 4, 32), (3, 203, 576, 4, 64), (2, 40, 128, 8, 0)])
 def test_csa_compress(bf16_in, B, S, D, m, d_rope):
     g = synth.rng(200 + S + D)
