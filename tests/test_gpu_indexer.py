@@ -81,6 +81,23 @@ def test_mxfp4_long_rows_filtered(N, k):
     _assert_same(gi, gs, ri, rs)
 
 
+@pytest.mark.parametrize("HI,dI", [(64, 128), (32, 256)])
+def test_mxfp4_prefill_rows_filtered(HI, dI):
+    # several queries per sequence over a cache longer than the in-LDS
+    # select (the prefill indexer form with its group maxima), causal
+    # positions from none to every entry visible
+    g = synth.rng(505 + HI + dI)
+    B, T, N, m, k = 2, 5, 40000, 4, 2048
+    qI = synth.normal(g, (B, T, HI, dI))
+    kI = synth.normal(g, (B, N, dI))
+    w = synth.normal(g, (B, T, HI), 1.0 / HI)
+    q_pos = np.array([[2, 4 * k + 5, 4 * 20000 + 1, 4 * 33333 + 3, 4 * N - 1],
+                      [4 * N + 9, 4 * 16384, 4 * 1000, 4 * 39999 + 2, 0]], np.int32)
+    ne = np.array([N, 37001], np.int32)
+    gi, gs, ri, rs = _run_mx(qI, kI, w, q_pos, ne, m, k)
+    _assert_same(gi, gs, ri, rs)
+
+
 @pytest.mark.parametrize("N", [3000, 40000])
 def test_ties_go_to_lower_index(N):
     # w = 0 makes every score +0: the lowest k indices win. Repeated keys
