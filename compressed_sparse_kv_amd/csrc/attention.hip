@@ -2059,6 +2059,10 @@ static int attn_common(const char* fn, bool dense, const void* q, const int32_t*
   clear_error();
   std::string f(fn);
   if (!q || !q_pos || !kv_c || !out) return fail(CSK_EINVAL, f + ": null pointer");
+  // the kernels move q, the caches, the output and the partials in 16-byte pieces
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv_c) | reinterpret_cast<uintptr_t>(kv_w) |
+       reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(workspace)) & 15)
+    return fail(CSK_EINVAL, f + ": q, kv_c, kv_w, out and workspace must be 16-byte aligned");
   if (!dense && !idx) return fail(CSK_EINVAL, f + ": null idx");
   if (dense && !n_entries) return fail(CSK_EINVAL, f + ": null n_entries");
   if (B <= 0 || T <= 0 || H <= 0 || D <= 0 || (D & 1) || dv <= 0 || dv > D || Nmax <= 0)

@@ -14,7 +14,9 @@
  * --------------------------------
  * - Pointers: every tensor pointer is a DEVICE pointer (hipMalloc'd or a
  *   torch CUDA tensor's data_ptr) to a dense row-major array, 4-byte aligned
- *   (16-byte alignment is faster). The caller owns every buffer; the compute
+ *   (16-byte alignment is faster; sparse_attn and dense_compressed_attn
+ *   require it of q, kv_c, kv_w, out and the workspace, CSK_EINVAL
+ *   otherwise). The caller owns every buffer; the compute
  *   calls never allocate or free device memory and keep no pointer or other
  *   state between calls (the one exception is the opt-in measurement hook
  *   csk_kernel_timer_arm, which keeps the caller's event arrays until

@@ -87,6 +87,11 @@ def test_attn_workgroup_cap(lib):
     rc = lib.sparse_attn(fake, fake, fake, 100, fake, 8, None, None, 0, 0, None, 1, 1, 64, 576, 512, 64,
                          10000.0, 0.05, 0, 3, fake, None, 0, None, 0, None)
     assert rc == -2
+    # q, the caches and the output move in 16-byte pieces: a 4-byte-aligned
+    # output is refused before anything runs
+    rc = lib.sparse_attn(fake, fake, fake, 100, fake, 8, None, None, 0, 0, None, 1, 1, 64, 576, 512, 64,
+                         10000.0, 0.05, 1, 1, fake + 4, None, 0, None, 0, None)
+    assert rc == -1 and b"16-byte" in lib.csk_last_error()
 
 
 def test_fp8kv_entry_bytes(lib):
