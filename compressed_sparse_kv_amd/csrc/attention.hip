@@ -756,7 +756,7 @@ void attn_bf16_chunk_kernel(AttnArgs a) {
 // moved only when a tile's maximum passes it by more than 8 (log2 units), so
 // the accumulators are rarely rescaled (probabilities stay below 2^8).
 template <int D, int DV, int HG, int CT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void attn_bf16_qtile_kernel(AttnArgs a) {
   constexpr int NW = 4;
   constexpr int TQ = NW * CT / HG;           // query rows per workgroup
@@ -765,7 +765,7 @@ void attn_bf16_qtile_kernel(AttnArgs a) {
   constexpr int TU = 32 * D / 8;             // 16-byte units per 32-row tile
   constexpr int BLK = D / 16;                // 1 KB DMA blocks per tile
   constexpr int PER = BLK / NW;              // of them per wave
-  constexpr int TILES = 73728 / (64 * D);    // tiles staged at once (72 KB)
+  constexpr int TILES = 49152 / (64 * D);    // tiles staged at once (48 KB: three workgroups per CU)
   constexpr int RP = QTILE_ROPE_PAIRS;
   static_assert(BLK % NW == 0 && TQ * HG == NW * CT && TILES >= 1, "unsupported shape");
   __shared__ __align__(16) uint4 kv[TILES * TU];
