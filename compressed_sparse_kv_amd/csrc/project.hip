@@ -14,19 +14,20 @@
 //   - «Muon и борьба с нестабильностью»: queries and KV entries normalised
 //     directly by RMSNorm.
 //
-// Fused kernel: one workgroup (eight waves of 32 token rows, two per SIMD)
-// computes a 256-token x (channel block) tile of every series with bf16
+// Fused kernel: one workgroup (waves of 32 token rows, two per SIMD)
+// computes a token x 64-channel tile of every series with bf16
 // MFMAs (X W^T, fp32 accumulation), staged by LDS DMA in 64-deep K slabs
 // like the plain matrix product, and pools it in its epilogue, so the
 // series never reach memory:
-//   - CSA (m = 4): 64 channels x 4 series. The b series is computed on the
-//     token rows shifted back by 4 (four extra rows staged per slab), so the
-//     a slots (tokens 4j..4j+3) and b slots (4j-4..4j-1) of entry j land in
-//     the same four accumulator rows of the same lane: the 8-slot softmax
-//     runs in registers.
-//   - HCA (m = 128): 128 channels x 2 series; an entry's 128 rows span four
-//     waves: each lane folds its 16 rows, the two half-waves and then the
-//     four waves merge their (max, sum, weighted sum) in a fixed order.
+//   - CSA (m = 4): 256 tokens (eight waves) x 64 channels x 4 series. The b
+//     series is computed on the token rows shifted back by 4 (four extra
+//     rows staged per slab), so the a slots (tokens 4j..4j+3) and b slots
+//     (4j-4..4j-1) of entry j land in the same four accumulator rows of the
+//     same lane: the 8-slot softmax runs in registers.
+//   - HCA (m = 128): 128 tokens (one entry, four waves) x 64 channels x 2
+//     series, so that 16K tokens make 256 workgroups; each lane folds its
+//     16 rows, the two half-waves and then the four waves merge their (max,
+//     sum, weighted sum) in a fixed order.
 // The epilogue writes the pooled fp32 entry values and, per entry, the sum
 // of squares of the block's channels; finalize_entries (compress.hip) then
 // applies the RMSNorm (partials summed in ascending block order), RoPE and
@@ -52,7 +53,6 @@ struct ProjArgs {
 };
 
 constexpr int PK = 64;            // K slab depth
-constexpr int PU = 256 * PK / 8;  // 16-byte units of a 256-row slab
 constexpr int PX = 64;            // CSA: eight more token rows (T0-8 .. T0-1)
 
 namespace {
@@ -87,27 +87,33 @@ __device__ __forceinline__ Fold merge(Fold a, Fold b) {
 template <bool CSA>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void project_compress_kernel(ProjArgs p) {
-  constexpr int CH = CSA ? 64 : 128;  // channels of a tile
+  constexpr int CH = 64;                // channels of a tile
+  constexpr int NWV = CSA ? 8 : 4;      // waves
+  constexpr int TT = 32 * NWV;          // token rows of a tile
+  constexpr int NCT = CSA ? 8 : 4;      // 32-column tiles: CSA 4 series, HCA 2, of 64 channels
+  constexpr int AU = TT * PK / 8;       // 16-byte units of the A (token) slab
+  constexpr int BU = 32 * NCT * PK / 8; // of the B (weight) slab
   constexpr int XU = CSA ? PX : 0;
-  __shared__ __align__(16) uint4 lds[2][2 * PU + (CSA ? PX : 1)];  // [stage][A | B | A extra]
+  static_assert(AU / 64 / NWV == 4 && BU / 64 / NWV == 4, "four DMA instructions per slab and wave");
+  __shared__ __align__(16) uint4 lds[2][AU + BU + (CSA ? PX : 1)];  // [stage][A | B | A extra]
   const int tid = threadIdx.x, lane = tid & 63;
-  // eight waves, two per SIMD; wave w owns token rows 32w .. 32w+31 of the
-  // tile and every column tile
+  // two waves per SIMD; wave w owns token rows 32w .. 32w+31 of the tile
+  // and every column tile
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ntc = (p.D + CH - 1) / CH;
-  const int total = ((p.S + 255) / 256) * ntc;
+  const int total = ((p.S + TT - 1) / TT) * ntc;
   const int wg = blockIdx.x, xcd = wg & 7, per = total >> 3, rem = total & 7;
   const int L = xcd * per + min(xcd, rem) + (wg >> 3);
   const int tm = L / ntc, tc = L % ntc;
-  const int T0 = 256 * tm, c0 = CH * tc;
+  const int T0 = TT * tm, c0 = CH * tc;
   const int b = blockIdx.y;
   const uint16_t* X = p.x + (int64_t)b * p.src_bstride * p.hidden;
   // lowest readable token row: the previous block (b series of the first
   // entry) exists in memory only when the call continues a sequence
   const int lo = (CSA && p.entry0 > 0) ? -4 : 0;
 
-  for (int u = tid; u < 2 * (2 * PU + XU); u += 512) {
-    const int st = u / (2 * PU + XU), o = u % (2 * PU + XU);
+  for (int u = tid; u < 2 * (AU + BU + XU); u += 64 * NWV) {
+    const int st = u / (AU + BU + XU), o = u % (AU + BU + XU);
     lds[st][o] = make_uint4(0u, 0u, 0u, 0u);
   }
   __syncthreads();
@@ -124,7 +130,7 @@ void project_compress_kernel(ProjArgs p) {
     const int r = r_base + 8 * i;
     const int kc = kc_l ^ (i & 1);
     pa[i] = X + (int64_t)min(max(T0 + r, lo), p.S - 1) * p.hidden + 8 * kc;
-    const int s = CSA ? (r >> 6) : (r >> 7), c = CSA ? (r & 63) : (r & 127);
+    const int s = r >> 6, c = r & 63;  // series, channel of weight row r
     pb[i] = p.w + ((int64_t)s * p.D + min(c0 + c, p.D - 1)) * p.hidden + 8 * kc;
   }
   const uint16_t* px = X + (int64_t)min(max(T0 - 8 + (lane >> 3), lo), p.S - 1) * p.hidden + 8 * kc_l;
@@ -133,14 +139,14 @@ void project_compress_kernel(ProjArgs p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       dma16(pa[i] + k0, &lds[st][64 * (4 * wave + i)]);
-      dma16(pb[i] + k0, &lds[st][PU + 64 * (4 * wave + i)]);
+      dma16(pb[i] + k0, &lds[st][AU + 64 * (4 * wave + i)]);
     }
-    if (CSA && wave == 0) dma16(px + k0, &lds[st][2 * PU]);
+    if (CSA && wave == 0) dma16(px + k0, &lds[st][AU + BU]);
   };
 
-  v16f acc[8];
+  v16f acc[NCT];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+  for (int j = 0; j < NCT; ++j)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
 
@@ -160,7 +166,7 @@ void project_compress_kernel(ProjArgs p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const uint4* sl = lds[st];
-    v8bf af[2][NA], bfr[2][8];
+    v8bf af[2][NA], bfr[2][NCT];
     auto read_frags = [&](int ks, v8bf* fa, v8bf* fb) {
       const int kc = 2 * ks + fh;
       const int ra = 32 * wave + fr;
@@ -168,29 +174,30 @@ void project_compress_kernel(ProjArgs p) {
       if (CSA) {
         // token T0 - 4 + ra: slab row ra - 4, or extra row ra + 4
         const int rb = ra - 4;
-        const int u = rb >= 0 ? slab_unit(rb, kc) : 2 * PU + slab_unit(rb + 8, kc);
+        const int u = rb >= 0 ? slab_unit(rb, kc) : AU + BU + slab_unit(rb + 8, kc);
         fa[1] = __builtin_bit_cast(v8bf, sl[u]);
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < NCT; ++j) {
         const int rw = 32 * j + fr;
-        fb[j] = __builtin_bit_cast(v8bf, sl[PU + slab_unit(rw, kc)]);
+        fb[j] = __builtin_bit_cast(v8bf, sl[AU + slab_unit(rw, kc)]);
       }
     };
     read_frags(0, af[0], bfr[0]);
 #pragma unroll
     for (int ks = 0; ks < PK / 16; ++ks) {
       // CSA: column tiles 0-3 (C^a, Z^a) take the a rows, 4-7 (C^b, Z^b)
-      // the shifted b rows; HCA: every tile takes the block's rows. Four
-      // products, then the next step's reads (hidden by the other four).
+      // the shifted b rows; HCA: every tile (C 0-1, Z 2-3) takes the
+      // block's rows. Half the products, then the next step's reads
+      // (hidden by the other half).
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NCT / 2; ++j)
         acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][0], bfr[ks & 1][j], acc[j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       if (ks + 1 < PK / 16) read_frags(ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 4; j < 8; ++j)
+      for (int j = NCT / 2; j < NCT; ++j)
         acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][CSA ? 1 : 0], bfr[ks & 1][j], acc[j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -255,13 +262,15 @@ void project_compress_kernel(ProjArgs p) {
       if (fr == 0 && E < p.N) p.ss[(row0 + E) * p.ncb + tc] = sq;
     }
   } else {
-    // entry k = wave/4 of the tile (128 rows: waves 4k .. 4k+3); this
-    // lane's 16 rows of it: 32*(wave%4) + 8*q + 4*fh + e
-    const int k = wave >> 2, wq = wave & 3;
-    const int E = T0 / 128 + k;
-    Fold fo[4];
+    // the tile is one entry (128 rows: the four waves); this lane's 16 rows
+    // of it: 32*wave + 8*q + 4*fh + e. Column tiles: C^a 0..CTN-1, Z^a
+    // CTN..2*CTN-1.
+    constexpr int CTN = NCT / 2;  // 32-channel tiles
+    const int k = 0, wq = wave;
+    const int E = T0 / 128;
+    Fold fo[CTN];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
+    for (int ct = 0; ct < CTN; ++ct) {
       const int ch = min(c0 + 32 * ct + fr, p.D - 1);
       float mx = -INFINITY;
 #pragma unroll
@@ -269,7 +278,7 @@ void project_compress_kernel(ProjArgs p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int rr = 32 * wq + 8 * q + 4 * fh + e;
-          mx = fmaxf(mx, acc[4 + ct][4 * q + e] + p.bias_a[rr * p.D + ch]);
+          mx = fmaxf(mx, acc[CTN + ct][4 * q + e] + p.bias_a[rr * p.D + ch]);
         }
       float den = 0.f, num = 0.f;
 #pragma unroll
@@ -277,7 +286,7 @@ void project_compress_kernel(ProjArgs p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int rr = 32 * wq + 8 * q + 4 * fh + e;
-          const float x = expf(acc[4 + ct][4 * q + e] + p.bias_a[rr * p.D + ch] - mx);
+          const float x = expf(acc[CTN + ct][4 * q + e] + p.bias_a[rr * p.D + ch] - mx);
           den += x;
           num = fmaf(x, acc[ct][4 * q + e], num);
         }
@@ -291,8 +300,8 @@ void project_compress_kernel(ProjArgs p) {
     float* xf = reinterpret_cast<float*>(&lds[0][0]);
     if (wq != 0 && fh == 0)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const int o = (((k * 3 + wq - 1) * 4 + ct) * 32 + fr) * 3;
+      for (int ct = 0; ct < CTN; ++ct) {
+        const int o = (((k * 3 + wq - 1) * CTN + ct) * 32 + fr) * 3;
         xf[o] = fo[ct].mx;
         xf[o + 1] = fo[ct].den;
         xf[o + 2] = fo[ct].num;
@@ -301,11 +310,11 @@ void project_compress_kernel(ProjArgs p) {
     if (wq == 0) {
       float sq = 0.f;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
+      for (int ct = 0; ct < CTN; ++ct) {
         Fold f = fo[ct];
 #pragma unroll
         for (int w2 = 1; w2 < 4; ++w2) {
-          const int o = (((k * 3 + w2 - 1) * 4 + ct) * 32 + fr) * 3;
+          const int o = (((k * 3 + w2 - 1) * CTN + ct) * 32 + fr) * 3;
           f = merge(f, Fold{xf[o], xf[o + 1], xf[o + 2]});
         }
         const float pv = f.num / f.den;
@@ -353,7 +362,7 @@ using namespace csk;
 extern "C" size_t project_compress_workspace_size(int csa, int B, int S, int D, int m) {
   if (B <= 0 || S <= 0 || D <= 0 || m <= 0 || S / m == 0) return 0;
   const int64_t n = (int64_t)B * (S / m);
-  const int ncb = (int)ceil_div(D, csa ? 64 : 128);
+  const int ncb = (int)ceil_div(D, 64);
   return (size_t)(ceil_div(n * D * 4, 256) * 256 + n * ncb * 4);
 }
 
@@ -390,7 +399,7 @@ extern "C" int project_compress(int csa, const void* x, const void* w, const flo
     return fail(CSK_EWORKSPACE, f + ": workspace smaller than project_compress_workspace_size()");
   if (const int dc = check_device(f); dc != CSK_OK) return dc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int CH = csa ? 64 : 128;
+  const int CH = 64;  // channels of a tile (both forms)
   ProjArgs a{};
   a.x = reinterpret_cast<const uint16_t*>(x);
   a.w = reinterpret_cast<const uint16_t*>(w);
@@ -402,9 +411,11 @@ extern "C" int project_compress(int csa, const void* x, const void* w, const flo
                                   ceil_div((int64_t)B * N * D * 4, 256) * 256);
   a.src_bstride = src_bstride ? src_bstride : S;
   a.S = S; a.N = N; a.hidden = hidden; a.D = D; a.entry0 = entry0;
-  const dim3 grid((unsigned)(ceil_div(S, 256) * a.ncb), (unsigned)B);
+  // CSA: 256-token tiles, eight waves; HCA: 128-token tiles (one entry),
+  // four waves
+  const dim3 grid((unsigned)(ceil_div(S, csa ? 256 : 128) * a.ncb), (unsigned)B);
   const int rc = csa ? launch("csa_project_pool", project_compress_kernel<true>, grid, dim3(512), 0, s, a)
-                     : launch("hca_project_pool", project_compress_kernel<false>, grid, dim3(512), 0, s, a);
+                     : launch("hca_project_pool", project_compress_kernel<false>, grid, dim3(256), 0, s, a);
   if (rc != CSK_OK) return rc;
   return finalize_entries(csa ? "csa_project_finalize" : "hca_project_finalize", B, N, D, m, entry0, d_rope,
                           rope_base, entry_pos, out_dtype, out, out_scale, dst_bstride, a.pooled, a.ss, a.ncb,

@@ -207,7 +207,7 @@ def test_project_compress_and_rmsnorm_arguments(lib):
     import compressed_sparse_kv_amd as csk
     L = csk.lib()
     assert L.project_compress_workspace_size(1, 1, 65536, 576, 4) == 16384 * 576 * 4 + 16384 * 9 * 4
-    assert L.project_compress_workspace_size(0, 2, 1024, 576, 128) == 16 * 576 * 4 + 16 * 5 * 4
+    assert L.project_compress_workspace_size(0, 2, 1024, 576, 128) == 16 * 576 * 4 + 16 * 9 * 4
     fake = ctypes.c_void_p(4096)
 
     def call(csa=1, m=4, hidden=4096, D=576, S=256, ws=1 << 30, x=fake, out_dtype=1, entry0=0):
