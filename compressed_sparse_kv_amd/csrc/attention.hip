@@ -1923,8 +1923,77 @@ __global__ __launch_bounds__(64 * MERGE8_WAVES) void attn_merge8_kernel(AttnArgs
   if (a.lse && lane == 0) a.lse[(int64_t)r * a.H + h] = lse;
 }
 
+// The same merge for at most NCHM partials and many (row, head) pairs
+// (batched decode rows split over few workgroups): one wave per (row,
+// head), four heads per workgroup. The
+// wave issues every partial's load at once, forms the chunk weights itself
+// and sums the chunks in ascending order; no LDS, no barrier.
+template <typename T, int NCHM>
+__global__ __launch_bounds__(256) void attn_merge_wave_kernel(AttnArgs a) {
+  const int r = blockIdx.x;
+  const int h = 4 * blockIdx.y + (int)(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int nch = a.nch;
+  const int64_t ostride = (int64_t)a.H * a.dv;
+  const uint16_t* pb = reinterpret_cast<const uint16_t*>(a.part_o) + ((int64_t)r * nch * a.H + h) * a.dv;
+  const int d = 8 * lane;
+  const bool dok = d < a.dv;
+  const int dd = dok ? d : 0;
+  uint4 v[NCHM];
+#pragma unroll
+  for (int u = 0; u < NCHM; ++u) {
+    const int c = min(u, nch - 1);  // unconditional: the loads issue together
+    v[u] = *reinterpret_cast<const uint4*>(pb + c * ostride + dd);
+  }
+  const float* ml = a.part_ml + ((int64_t)r * nch * a.H + h) * 2;
+  const float2 mlc = *reinterpret_cast<const float2*>(ml + (int64_t)min(lane, nch - 1) * a.H * 2);
+  const float mc = lane < nch ? mlc.x : -INFINITY;
+  const float m = wave_max(mc);
+  const float w = mc == -INFINITY ? 0.f : exp2f(mc - m);
+  const float l = wave_sum(lane < nch ? w * mlc.y : 0.f);
+  float M, inv_z, lse;
+  finish_row(m, l, a.sink, h, &M, &inv_z, &lse);
+  const float f = (m == -INFINITY) ? 0.f : exp2f(m - M) * inv_z;
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = 0.f;
+#pragma unroll
+  for (int u = 0; u < NCHM; ++u) {
+    const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
+    if (u < nch) {
+      const uint32_t q[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o[2 * i] += bf16_bits_to_f32(q[i] & 0xffffu) * wc;
+        o[2 * i + 1] += bf16_bits_to_f32(q[i] >> 16) * wc;
+      }
+    }
+  }
+  if (dok) {
+    const int64_t orow = ((int64_t)r * a.H + h) * a.dv + d;
+    if (sizeof(T) == 4) {
+      float4* op = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + orow);
+      op[0] = make_float4(o[0] * f, o[1] * f, o[2] * f, o[3] * f);
+      op[1] = make_float4(o[4] * f, o[5] * f, o[6] * f, o[7] * f);
+    } else {
+      uint32_t q[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = f32_to_bf16_bits(o[2 * i] * f) | (f32_to_bf16_bits(o[2 * i + 1] * f) << 16);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + orow) = make_uint4(q[0], q[1], q[2], q[3]);
+    }
+  }
+  if (a.lse && lane == 0) a.lse[(int64_t)r * a.H + h] = lse;
+}
+
 template <typename T>
 static int launch_merge8(const AttnArgs& a, unsigned R, int H, hipStream_t s) {
+  // (a wave per pair: needs enough pairs to spread its loads; few rows keep
+  // eight waves per pair)
+  if (a.nch <= 16 && H % 4 == 0 && (int64_t)R * H >= 1024) {
+    dim3 grid(R, H / 4), block(256);
+    return a.nch <= 8 ? launch("attn_merge", attn_merge_wave_kernel<T, 8>, grid, block, 0, s, a)
+                      : launch("attn_merge", attn_merge_wave_kernel<T, 16>, grid, block, 0, s, a);
+  }
   dim3 grid(R, H), block(64 * MERGE8_WAVES);
   switch ((a.nch + MERGE8_WAVES - 1) / MERGE8_WAVES) {
     case 1: return launch("attn_merge", attn_merge8_kernel<T, 1>, grid, block, 0, s, a);

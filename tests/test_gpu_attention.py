@@ -58,6 +58,14 @@ def test_sparse_prefill_small(bf16):
     _sparse_case(601, B=2, T=19, H=64, D=576, dv=512, N=300, k=40, S_w=300, W=16, bf16=bf16, d_rope=64)
 
 
+@pytest.mark.parametrize("B,k", [(16, 1000), (32, 480)])
+def test_sparse_decode_batched_split(B, k):
+    # batched decode rows split over at most 16 workgroups each (16 and 8
+    # here): the one-wave-per-(row, head) merge of the bf16 partials
+    _sparse_case(630 + B, B=B, T=1, H=64, D=576, dv=512, N=2500, k=k, S_w=128, W=100, bf16=True,
+                 d_rope=64, decode=True)
+
+
 def test_sparse_fp32_tiny_shapes():
     _sparse_case(602, B=1, T=256, H=4, D=64, dv=64, N=64, k=8, S_w=256, W=32, bf16=False, d_rope=32)
 
