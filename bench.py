@@ -378,13 +378,16 @@ class PrefillWorkload:
     BF16_PEAK_TFLOPS = 2500.0
     FP4_PEAK_TFLOPS = 10100.0
 
-    def __init__(self, name, seed):
+    def __init__(self, name, seed, kv_fp8=False):
         import torch
 
         import compressed_sparse_kv_amd as csk
 
         self.torch, self.csk, self.name = torch, csk, name
         self.csa = name == "csa_prefill_64k"
+        if kv_fp8 and not self.csa:
+            raise SystemExit("--kv fp8 is built for the 576-dim CSA entries (csa_prefill_64k, decode workloads)")
+        self.kv_fp8 = kv_fp8
         dev = torch.device("cuda:0")
         g = torch.Generator(device=dev)
         g.manual_seed(seed)
@@ -424,7 +427,19 @@ class PrefillWorkload:
         x["n_entries"] = torch.full((1,), self.N, dtype=torch.int32, device=dev)
         self.x = x
         # outputs and workspaces
-        self.kv = torch.empty((1, self.N, D), dtype=torch.bfloat16, device=dev)
+        self.entry_bytes = csk.fp8kv_entry_bytes(D, 64) if kv_fp8 else 2 * D
+        if kv_fp8:
+            # FP8 KV entries (E4M3 codes, bf16 RoPE dims, block scales): the
+            # compressed cache is written so by the compression call; the
+            # window rows are encoded once here, each token as its own entry
+            self.kv = torch.empty((1, self.N, self.entry_bytes), dtype=torch.uint8, device=dev)
+            z = torch.zeros_like(x["kv_w"])
+            zb = torch.zeros((1, D), dtype=torch.float32, device=dev)
+            p0 = torch.zeros((1, S), dtype=torch.int32, device=dev)
+            x["kv_w8"] = csk.hca_compress(x["kv_w"], z, zb, 1, d_rope=64, entry_pos=p0, out_dtype=csk.CSK_FP8KV)
+            del z
+        else:
+            self.kv = torch.empty((1, self.N, D), dtype=torch.bfloat16, device=dev)
         self.out = torch.empty((1, S, H, dv), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((1, S, H), dtype=torch.float32, device=dev)
         if self.csa:
@@ -453,15 +468,16 @@ class PrefillWorkload:
         csk, x = self.csk, self.x
         if self.csa:
             csk.csa_compress(x["ca"], x["za"], x["cb"], x["zb"], x["bias_a"], x["bias_b"], self.m, d_rope=64,
-                             out=self.kv)
+                             out_dtype=csk.CSK_FP8KV if self.kv_fp8 else csk.CSK_BF16, out=self.kv)
             csk.csa_compress(x["ia"], x["iza"], x["ib"], x["izb"], x["ibias_a"], x["ibias_b"], self.m,
                              out_dtype=csk.CSK_MXFP4, out=self.kc, out_scale=self.ks)
             csk.mxfp4_quantize(x["qI"], self.qc, self.qs)
             csk.indexer_topk(self.qc, x["w"], self.kc, x["q_pos"], x["n_entries"], self.m, self.k,
                              q_scale=self.qs, k_scale=self.ks, idx=self.idx, workspace=self.ws_i,
                              with_score=False)
-            csk.sparse_attn(x["q"], x["q_pos"], self.kv, self.idx, x["kv_w"], x["w_pos0"], self.W, x["sink"],
-                            self.dv, 64, self.scale, out=self.out, lse=self.lse, workspace=self.ws_a)
+            csk.sparse_attn(x["q"], x["q_pos"], self.kv, self.idx, x["kv_w8" if self.kv_fp8 else "kv_w"],
+                            x["w_pos0"], self.W, x["sink"], self.dv, 64, self.scale, out=self.out, lse=self.lse,
+                            workspace=self.ws_a)
         else:
             csk.hca_compress(x["c"], x["z"], x["bias"], self.m, d_rope=64, out=self.kv)
             csk.dense_compressed_attn(x["q"], x["q_pos"], self.kv, x["n_entries"], self.m, x["kv_w"],
@@ -505,8 +521,8 @@ class PrefillWorkload:
     def attention_hbm_bytes(self):
         """Bytes the attention kernel must move: q, out, window KV, the
         compressed cache (once), idx."""
-        S, H, D, dv, N = self.S, self.H, self.D, self.dv, self.N
-        b = S * H * D * 2 + S * H * dv * 2 + S * D * 2 + N * D * 2
+        S, H, D, dv, N, E = self.S, self.H, self.D, self.dv, self.N, self.entry_bytes
+        b = S * H * D * 2 + S * H * dv * 2 + S * E + N * E
         if self.csa:
             b += S * self.k * 4
         return b
@@ -516,7 +532,8 @@ class PrefillWorkload:
              "compression": self.m, "heads": self.H, "kv_dim": self.D, "value_dim": self.dv, "rope_dims": 64,
              "window": self.W, "sink": True}
         if self.csa:
-            c.update(indexer_heads=self.HI, indexer_dim=self.dI, indexer_dtype="mxfp4", top_k=self.k)
+            c.update(indexer_heads=self.HI, indexer_dim=self.dI, indexer_dtype="mxfp4", top_k=self.k,
+                     kv_entries="fp8_e4m3_scale32+bf16_rope" if self.kv_fp8 else "bf16")
         return c
 
     def host(self, t):
@@ -541,7 +558,13 @@ class PrefillWorkload:
             q, qI, w = h(x["q"][:, ts]), h(x["qI"][:, ts]), h(x["w"][:, ts])
             kv_w, q_pos = h(x["kv_w"]), np.arange(S, dtype=np.int32).reshape(1, S)
             t0 = time.perf_counter()
-            kv = oracle.round_bf16(oracle.csa_compress(*srcs, self.m, d_rope=64))
+            if self.kv_fp8:
+                # the entries as FP8 KV stores them, decoded for the attention
+                kv = oracle.fp8kv_decode(oracle.fp8kv_encode(oracle.csa_compress(*srcs, self.m, d_rope=64), 64),
+                                         self.D, 64)
+                kv_w = oracle.fp8kv_decode(oracle.fp8kv_encode(oracle.bf16_to_f32(kv_w), 64), self.D, 64)
+            else:
+                kv = oracle.round_bf16(oracle.csa_compress(*srcs, self.m, d_rope=64))
             kk = oracle.round_f32(oracle.csa_compress(*isrcs, self.m))
             kc, ks = oracle.mxfp4_encode(kk)
             t1 = time.perf_counter()
@@ -732,7 +755,7 @@ def run_prefill(args):
     import compressed_sparse_kv_amd as csk
     import synth
 
-    wl = PrefillWorkload(args.workload, synth.WORKLOADS[args.workload]["seed"])
+    wl = PrefillWorkload(args.workload, synth.WORKLOADS[args.workload]["seed"], kv_fp8=args.kv == "fp8")
     K, Wm = args.steps, args.warmup
     for i in range(max(Wm, 1)):
         wl.step(i)
