@@ -32,6 +32,7 @@
 // per-slice candidate lists in index order, and the same range select
 // finishes.
 #include <algorithm>
+#include <type_traits>
 #include <atomic>
 #include <mutex>
 
@@ -699,21 +700,22 @@ struct SelectState {
 
 constexpr int SEL_SMALL = 64;  // a bin this small is finished by one wave's rank count
 
-struct SelectShared {
-  int hist[SEL_BINS];
+template <int BINS>
+struct SelectSharedT {
+  int hist[BINS];
   int digit, above, binc, nsmall, take;
   uint32_t thr;
   uint32_t kmin[16], kmax[16];
   uint32_t small[SEL_SMALL];
   ScanShared scan;
 };
+using SelectShared = SelectSharedT<SEL_BINS>;
 
 // Index-ordered compaction of the selected elements. Each thread owns a
 // contiguous run of elements; counts of strictly-greater and tied elements
 // are scanned across the block.
-template <int NT, typename Get, typename Emit>
-__device__ void compact_selected(Get get, Emit emit, int n, const SelectState& st,
-                                 SelectShared& sh) {
+template <int NT, typename Get, typename Emit, typename SS>
+__device__ void compact_selected(Get get, Emit emit, int n, const SelectState& st, SS& sh) {
   const int tid = threadIdx.x;
   const int per = (n + NT - 1) / NT;
   const int e0 = tid * per;
@@ -757,6 +759,12 @@ struct TopkShared {
   uint32_t key[TOPK_CAP];
   int eidx[TOPK_CAP];
   int slice_off[1024 + 1];
+};
+// Unfiltered rows (at most TOPK_CAP entries, element index = key index):
+// keys only, and 2048 histogram bins, so that two workgroups fit a CU.
+struct TopkSharedU {
+  SelectSharedT<2048> sel;
+  uint32_t key[TOPK_CAP];
 };
 
 // Threshold from the group maxima: the samples' order-preserving keys are
@@ -824,16 +832,18 @@ __device__ bool find_rank_bin(const int* hist, int want, ScanShared& scan, int* 
 
 // (cleared: the caller has zeroed sh.hist and sh.nsmall, and passed a
 // barrier since, so level 0 skips its own clear.)
-template <int NT, typename Get>
-__device__ SelectState range_select(Get get, int n, int k, uint32_t kmin, uint32_t kmax, SelectShared& sh,
+template <int NT, int BINS, typename Get>
+__device__ SelectState range_select(Get get, int n, int k, uint32_t kmin, uint32_t kmax, SelectSharedT<BINS>& sh,
                                     bool cleared) {
+  static_assert(BINS == 2048 || BINS == 4096, "three levels reach single key values");
+  constexpr int LB = BINS == 4096 ? 12 : 11;  // bits per level
   const int tid = threadIdx.x;
   uint32_t lo = kmin, span = kmax - kmin;  // the current range [lo, lo + span]
   int want = k;                            // rank of the target inside it
   for (int level = 0; level < 3; ++level) {
-    const int sb = span < (uint32_t)SEL_BINS ? 0 : 20 - __clz(span);  // span >> sb < SEL_BINS
+    const int sb = span < (uint32_t)BINS ? 0 : (32 - LB) - __clz(span);  // span >> sb < BINS
     if (level > 0 || !cleared) {
-      for (int i = tid; i < SEL_BINS; i += NT) sh.hist[i] = 0;
+      for (int i = tid; i < BINS; i += NT) sh.hist[i] = 0;
       if (tid == 0) sh.nsmall = 0;
       __syncthreads();
     }
@@ -843,7 +853,7 @@ __device__ SelectState range_select(Get get, int n, int k, uint32_t kmin, uint32
     }
     __syncthreads();
     int d = 0, above = 0;
-    if (find_rank_bin<NT, SEL_BINS / NT>(sh.hist, want, sh.scan, &d, &above)) {
+    if (find_rank_bin<NT, BINS / NT>(sh.hist, want, sh.scan, &d, &above)) {
       sh.digit = d;
       sh.above = above;
       sh.binc = sh.hist[d];
@@ -1014,7 +1024,9 @@ __global__ __launch_bounds__(FUSED_THREADS) void topk_filter_kernel(TopkArgs a) 
 template <bool FILTERED>
 __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  TopkShared& sh = *reinterpret_cast<TopkShared*>(smem);
+  using SH = std::conditional_t<FILTERED, TopkShared, TopkSharedU>;
+  constexpr int BINS = FILTERED ? SEL_BINS : 2048;
+  SH& sh = *reinterpret_cast<SH*>(smem);
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int k = a.k;
@@ -1043,7 +1055,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkArgs a) {
   const int nv = visible_count(a.ia, r);
   int n;
   const int ns = (nv + SLICE - 1) / SLICE;
-  if (!FILTERED) {
+  if constexpr (!FILTERED) {
     n = nv;
   } else {
     // slice offsets: exclusive scan of the per-slice counts (ns <= 1024)
@@ -1063,7 +1075,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkArgs a) {
   // gather elements (in index order) into LDS, or into the spill buffer,
   // with the range of their keys
   uint32_t umin = 0xffffffffu, umax = 0u;
-  if (!FILTERED) {
+  if constexpr (!FILTERED) {
     // (unfiltered rows have at most TOPK_CAP entries: always in LDS)
     for (int e = tid; e < n; e += TOPK_THREADS) {
       const uint32_t u = order_key(srow[e]);
@@ -1110,7 +1122,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkArgs a) {
   }
   // the first level's histogram is cleared here, before the barrier the
   // key range needs anyway
-  for (int i = tid; i < SEL_BINS; i += TOPK_THREADS) sh.sel.hist[i] = 0;
+  for (int i = tid; i < BINS; i += TOPK_THREADS) sh.sel.hist[i] = 0;
   if (tid == 0) sh.sel.nsmall = 0;
   __syncthreads();
 #pragma unroll
@@ -1125,8 +1137,8 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkArgs a) {
     return gkey[e];
   };
   auto index_of = [&](int e) -> int {
-    if (!FILTERED) return e;
-    return in_lds ? sh.eidx[e] : gidx[e];
+    if constexpr (!FILTERED) return e;
+    else return in_lds ? sh.eidx[e] : gidx[e];
   };
   auto emit = [&](int pos, int e) {
     oidx[pos] = index_of(e);
@@ -1329,13 +1341,13 @@ static int indexer_topk_impl(const char* fn, bool noalloc, const void* q, const 
   ta.n_slices = p.n_slices;
   ta.idx = idx;
   ta.out_score = score;
-  const size_t lds = sizeof(TopkShared);
+  const size_t lds = sizeof(TopkShared), lds_u = sizeof(TopkSharedU);
   static std::once_flag attr_once;
   std::call_once(attr_once, [&] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(topk_select_kernel<true>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(topk_select_kernel<false>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_u);
   });
   if (p.filtered) {
     ta.cand_cnt = reinterpret_cast<int*>(ws + p.off_cnt);
@@ -1347,7 +1359,7 @@ static int indexer_topk_impl(const char* fn, bool noalloc, const void* q, const 
     if (rc == CSK_OK)
       rc = launch("topk_select", topk_select_kernel<true>, dim3(R), dim3(TOPK_THREADS), lds, s, ta);
   } else {
-    rc = launch("topk_select", topk_select_kernel<false>, dim3(R), dim3(TOPK_THREADS), lds, s, ta);
+    rc = launch("topk_select", topk_select_kernel<false>, dim3(R), dim3(TOPK_THREADS), lds_u, s, ta);
   }
   return rc;
 }
