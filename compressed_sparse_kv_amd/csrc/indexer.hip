@@ -374,8 +374,10 @@ struct IdxStage {
   uint32_t scale[4][(KB + 3) / 4][64]; // [wave][dword][key]
 };
 
+// (dI = 128: four waves per SIMD, 39 KB of LDS per workgroup with two stages)
 template <int HT2, int KB, int ITERS, int NB>
-__global__ __launch_bounds__(256) void idx_fp4_w32_kernel(IdxArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KB == 4 ? 4 : 2, KB == 4 ? 4 : 2)))
+void idx_fp4_w32_kernel(IdxArgs a) {
   static_assert(NB >= 2 && NB <= 4, "two to four stages");
   static_assert(KB == 4 || KB == 8, "dI of 128 or 256");
   constexpr int KS2 = KB / 2;       // 64-deep K-steps
@@ -1318,7 +1320,7 @@ static int indexer_topk_impl(const char* fn, bool noalloc, const void* q, const 
 #undef CSK_IDX_CASE
 #define CSK_IDX_W32_CASE(ht2, kb)                                                                  \
   if (w32 && HI == 32 * ht2 && dI == 32 * kb) {                                                    \
-    constexpr int nb = kb == 4 ? 4 : 2;                                                            \
+    constexpr int nb = 2;  /* two stages: 39 KB of LDS, four workgroups per CU */                  \
     rc = iters == 8 ? launch("indexer_scores_fp4", idx_fp4_w32_kernel<ht2, kb, 8, nb>, grid, block, 0, s, ia) \
                     : launch("indexer_scores_fp4", idx_fp4_w32_kernel<ht2, kb, 4, nb>, grid, block, 0, s, ia); \
   }
