@@ -586,6 +586,9 @@ void idx_fp4_w32_kernel(IdxArgs a) {
     score[it] = topk_score(a, sum);
     if (a.samples) gmax[it] = group_max(a, base + lane < nv ? score[it] : -INFINITY);
   }
+  // a wave that left early (groups past the visible count) may still have
+  // key DMA in flight: none outlives the wave
+  if (done < ITERS) __builtin_amdgcn_s_waitcnt(CSK_IDX_VMCNT(0));
 
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
