@@ -158,7 +158,7 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 template <int HT, int KS, int ITERS>
 __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
   const int r = blockIdx.x;
-  const int b = r / a.T;
+  const int b = __builtin_amdgcn_readfirstlane(r / a.T);  // (uniform: scalar address bases)
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wg_base = blockIdx.y * (256 * ITERS) + wave * 64;
@@ -206,13 +206,15 @@ __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
     v4u v[4][KS];
     int sc[4][KS];
   };
-  // (the lane's code and scale pointers for key 0 of the batch, formed once;
-  // keys are then a 32-bit offset from them)
-  const uint8_t* kc_lane = a.kc + (int64_t)b * a.Nmax * (a.dI / 2) + kb * 16;
+  // (the row's code and scale bases are uniform, and every key's bytes are
+  // a 32-bit offset from them with compile-time strides (dI = 128*KS), so
+  // each load takes a scalar base and one vector offset: no 64-bit address
+  // or integer multiply per key)
+  const uint8_t* kc_row = a.kc + (int64_t)b * a.Nmax * (64 * KS);
   // (a key's KS*4 scales are KS whole dwords: each lane loads the dword of
   // its K-step and takes byte kb, so a load instruction reads dwords, not
   // single bytes)
-  const uint32_t* ks_row = reinterpret_cast<const uint32_t*>(a.ks + (int64_t)b * a.Nmax * (a.dI / 32));
+  const uint32_t* ks_row = reinterpret_cast<const uint32_t*>(a.ks + (int64_t)b * a.Nmax * (4 * KS));
   auto load_keys = [&](Group& gr, int base) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -220,13 +222,16 @@ __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
       key = key < a.Nmax ? key : a.Nmax - 1;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        gr.v[kt][s] = __builtin_nontemporal_load(
-            reinterpret_cast<const v4u*>(kc_lane + (uint32_t)key * (uint32_t)(a.dI / 2) + s * 64));
-        gr.sc[kt][s] = (int)((ks_row[(uint32_t)key * (uint32_t)KS + s] >> (8 * kb)) & 0xffu);
+        const uint32_t off = (uint32_t)key * (uint32_t)(64 * KS) + (uint32_t)(s * 64 + kb * 16);
+        gr.v[kt][s] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(kc_row + off));
+        const uint32_t so = (uint32_t)key * (uint32_t)(4 * KS) + (uint32_t)(4 * s);
+        gr.sc[kt][s] = (int)((*reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(ks_row) + so) >>
+                              (8 * kb)) & 0xffu);
       }
     }
   };
 
+  float* const score_row = a.scores + (int64_t)r * a.Nmax;
   auto process = [&](const Group& gr, int base) {
     v4f acc[4][HT];
 #pragma unroll
@@ -283,7 +288,7 @@ __global__ __launch_bounds__(256) void idx_fp4_kernel(IdxArgs a) {
 
     score = topk_score(a, score);
     const int key = base + lane;
-    if (key < nv) a.scores[(int64_t)r * a.Nmax + key] = score;
+    if (key < nv) *reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(score_row) + (uint32_t)key * 4u) = score;
     if (a.samples) write_samples(a, r, base, key < nv ? score : -INFINITY);
   };
 
