@@ -154,12 +154,15 @@ def test_dense_prefill_query_tiles(B, T, H, D, N, m, S_w, W):
                 d_rope=min(64, D // 2), decode=False)
 
 
-def test_dense_prefill_unordered_positions():
+@pytest.mark.parametrize("T", [48, 96])
+def test_dense_prefill_unordered_positions(T):
     # query rows at scattered positions: a tile's candidate union spans
-    # several windows and its rows keep different subsets of it
-    g = synth.rng(731)
-    q_pos = np.stack([np.sort(g.permutation(400)[:48]), g.permutation(400)[:48]]).astype(np.int32)
-    _dense_case(732, B=2, T=48, H=16, D=128, dv=128, N=100, m=4, S_w=400, W=24, bf16=True, d_rope=64,
+    # several windows and its rows keep different subsets of it (at 96 rows
+    # a workgroup takes four query groups, and their union exceeds what it
+    # can stage at once)
+    g = synth.rng(731 + T)
+    q_pos = np.stack([np.sort(g.permutation(400)[:T]), g.permutation(400)[:T]]).astype(np.int32)
+    _dense_case(732 + T, B=2, T=T, H=16, D=128, dv=128, N=100, m=4, S_w=400, W=24, bf16=True, d_rope=64,
                 decode=False, q_pos=q_pos)
 
 
