@@ -2066,6 +2066,10 @@ static AttnPlan plan_attn(bool dense, int B, int T, int H, int D, int dv, int Lc
     int64_t nch = max_wg > 0 ? max_wg / (int64_t)R : ceil_div(256, R);
     nch = nch < 1 ? 1 : nch;
     nch = nch < nt ? nch : nt;
+    // the fewest runs that keep the longest one: a row of 34 tiles over 8
+    // workgroups has runs of 5 and 4 tiles, over 7 the same longest run of 5
+    // with an eighth fewer partials to write and merge
+    nch = ceil_div(nt, ceil_div(nt, nch));
     p.row32 = true;
     p.chunk = total;
     p.nch = (int)(nch < 1 ? 1 : nch);
