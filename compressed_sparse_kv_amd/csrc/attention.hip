@@ -1545,45 +1545,45 @@ void attn_bf16_row32_kernel(AttnArgs a) {
       f = z > 0.f ? fo / z : 0.f;
     }
   }
-  // 5. O through LDS (every wave is past its last tile: both buffers are
-  // free), so that each store instruction writes contiguous memory. Head
-  // group hg uses buffer hg; float4 unit du of head h's row sits at
-  // (h%32)*DV/4 + (du ^ h%16), which keeps the scattered writes and the
-  // row-wise reads on distinct bank groups.
+  // 5. O through LDS as bf16 (every wave is past its last tile: both
+  // buffers are free), so that each store instruction writes contiguous
+  // memory. Head group hg uses buffer hg; the 8-byte unit du (value dims
+  // 4du..4du+3) of head h's row sits at (h%32)*DU + 2*((du/2) ^ h%16) +
+  // du%2 (h%8 when a row has 8 pairs), which keeps the scattered writes on distinct bank groups and
+  // leaves each pair of units (16 bytes, one store) adjacent for the
+  // row-wise reads. (Rounded once, as it is stored; the same bits as
+  // rounding after the staging.)
   constexpr int DU = DV / 4;
-  static_assert(DU % 16 == 0 && (64 * DU) % 512 == 0 && 32 * DV * 4 <= TU * 16 &&
-                    32 * DV * 4 <= (KV8 ? 2 * STU : TU) * 16,
+  constexpr int SWM = DU / 2 >= 16 ? 15 : DU / 2 - 1;  // pair swizzle mask (within a row)
+  static_assert((DU / 2) % (SWM + 1) == 0 && (64 * DU) % 512 == 0 && 32 * DV * 2 <= TU * 16 &&
+                    32 * DV * 2 <= (KV8 ? 2 * STU : TU) * 16,
                 "staging layout");
   {
-    float* st = reinterpret_cast<float*>(hg ? buf1 : buf0);
+    uint2* st = reinterpret_cast<uint2*>(hg ? buf1 : buf0);
 #pragma unroll
     for (int u = 0; u < HDT; ++u)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int du = 8 * ch * HDT + 8 * u + 2 * q4 + hio;
-        *reinterpret_cast<float4*>(st + 4 * (c32o * DU + (du ^ (c32o & 15)))) =
-            make_float4(acc[u][4 * q4] * f, acc[u][4 * q4 + 1] * f, acc[u][4 * q4 + 2] * f,
-                        acc[u][4 * q4 + 3] * f);
+        const v2bf p0 = {(__bf16)(acc[u][4 * q4] * f), (__bf16)(acc[u][4 * q4 + 1] * f)};
+        const v2bf p1 = {(__bf16)(acc[u][4 * q4 + 2] * f), (__bf16)(acc[u][4 * q4 + 3] * f)};
+        st[c32o * DU + 2 * ((du >> 1) ^ (c32o & SWM)) + (du & 1)] =
+            make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
       }
   }
   lds_barrier();
   {
-    // eight value dims (two staged units) per lane and store: bf16, 16 bytes
+    // eight value dims (one staged pair of units) per lane and store
     const int ls = fresh_lane() + 64 * wave;
     const int64_t row0 = a.nch > 1 ? ((int64_t)r * a.nch + split) * a.H : (int64_t)r * a.H;
     uint16_t* dst = reinterpret_cast<uint16_t*>(a.nch > 1 ? static_cast<void*>(a.part_o) : a.out);
 #pragma unroll 4
     for (int k = 0; k < 64 * DU / 512; ++k) {
       const int idx = 256 * k + ls;
-      const int h = idx / (DU / 2), du = 2 * (idx % (DU / 2));
-      const float* st = reinterpret_cast<const float*>(h >= 32 ? buf1 : buf0);
-      const float4 v0 = *reinterpret_cast<const float4*>(st + 4 * ((h & 31) * DU + (du ^ (h & 15))));
-      const float4 v1 = *reinterpret_cast<const float4*>(st + 4 * ((h & 31) * DU + ((du + 1) ^ (h & 15))));
-      const v2bf p0 = {(__bf16)v0.x, (__bf16)v0.y}, p1 = {(__bf16)v0.z, (__bf16)v0.w};
-      const v2bf p2 = {(__bf16)v1.x, (__bf16)v1.y}, p3 = {(__bf16)v1.z, (__bf16)v1.w};
-      *reinterpret_cast<uint4*>(dst + (row0 + h) * DV + 4 * du) =
-          make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                     __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+      const int h = idx / (DU / 2), pd = idx % (DU / 2);
+      const uint2* st = reinterpret_cast<const uint2*>(h >= 32 ? buf1 : buf0);
+      const uint4 v = *reinterpret_cast<const uint4*>(st + (h & 31) * DU + 2 * (pd ^ (h & SWM)));
+      *reinterpret_cast<uint4*>(dst + (row0 + h) * DV + 8 * pd) = v;
     }
   }
   if (ch == 0 && hio == 0) {
