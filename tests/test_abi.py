@@ -43,6 +43,28 @@ def test_workspace_sizes(lib):
     assert lib.dense_compressed_attn_workspace_size(4, 1, 64, 576, 512, 8192, 128, 128, 1, 0) > 0
 
 
+def _split_bytes(R, nch, H=64, dv=512):
+    # bf16 partial O per run, then fp32 (m, l) per run, each 256-byte aligned
+    al = lambda x: (x + 255) & ~255
+    return al(R * nch * H * dv * 2) + al(R * nch * H * 2 * 4)
+
+
+def test_attn_split_runs(lib):
+    """A decode row's 64-row tiles go to the fewest runs that keep the longest
+    one, within about one workgroup per CU or the call's cap (the workspace
+    holds one set of partials per run)."""
+    lib.sparse_attn_workspace_size.restype = ctypes.c_size_t
+    lib.dense_compressed_attn_workspace_size.restype = ctypes.c_size_t
+    # 32 rows x (2048 + 128) candidates = 34 tiles: at most 8 runs a row -> 7 runs of <= 5 tiles
+    assert lib.sparse_attn_workspace_size(32, 1, 64, 576, 512, 2048, 128, 1, 0) == _split_bytes(32, 7)
+    # 4 rows: at most 64 runs a row -> one tile each, 34 runs
+    assert lib.sparse_attn_workspace_size(4, 1, 64, 576, 512, 2048, 128, 1, 0) == _split_bytes(4, 34)
+    # 4 rows x (8192 + 128) = 130 tiles capped at 64 workgroups: at most 16 a row -> 15 runs of <= 9
+    assert lib.dense_compressed_attn_workspace_size(4, 1, 64, 576, 512, 8192, 128, 128, 1, 64) == _split_bytes(4, 15)
+    # uncapped: at most 64 a row -> 44 runs of <= 3 tiles
+    assert lib.dense_compressed_attn_workspace_size(4, 1, 64, 576, 512, 8192, 128, 128, 1, 0) == _split_bytes(4, 44)
+
+
 def test_argument_errors_without_device(lib):
     lib.csk_last_error.restype = ctypes.c_char_p
     nul = ctypes.c_void_p(0)
