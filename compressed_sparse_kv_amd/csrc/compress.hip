@@ -400,26 +400,40 @@ struct BatchArgs {
 
 __global__ __launch_bounds__(64) void compress_batch_kernel(BatchArgs args) {
   const int blk = blockIdx.x;
+  // the workgroup's job: first[] is increasing, so z counts the job starts
+  // at or below blk (all of them read at once, not one per step)
   int z = 0;
-  while (z + 1 < args.n && blk >= args.first[z + 1]) ++z;
+#pragma unroll
+  for (int q = 1; q < CSK_MAX_JOBS; ++q) z += (q < args.n && blk >= args.first[q]) ? 1 : 0;
   const BatchJob& j = args.j[z];
-  const int local = blk - args.first[z];
-  const int row = local / j.xblocks;
-  const int p = (local - row * j.xblocks) * 64 + threadIdx.x;
-  if (p >= j.a.D / 2) return;
-  if (j.kind == CSK_JOB_MXFP4) {
+  // (the job's fields read together, before any branch on them: the empty
+  // asm takes them all, so their loads share one wait instead of each
+  // waiting in turn at its first use; the reads below and inside the
+  // pooling find the same values)
+  const int first = args.first[z], xblocks = j.xblocks, D = j.a.D;
+  const int kind = j.kind, in_bf16 = j.in_bf16, out_kind = j.out_kind;
+  asm volatile("" ::"s"(first), "s"(xblocks), "s"(D), "s"(kind), "s"(in_bf16), "s"(out_kind), "s"(j.a.ca),
+               "s"(j.a.za), "s"(j.a.cb), "s"(j.a.zb), "s"(j.a.bias_a), "s"(j.a.bias_b), "s"(j.a.out),
+               "s"(j.a.out_scale), "s"(j.x));
+  asm volatile("" ::"s"(j.a.B), "s"(j.a.N), "s"(j.a.m), "s"(j.a.entry0), "s"(j.a.d_rope), "s"(j.a.src_bstride),
+               "s"(j.a.dst_bstride), "s"(j.a.entry_pos));
+  const int local = blk - first;
+  const int row = local / xblocks;
+  const int p = (local - row * xblocks) * 64 + threadIdx.x;
+  if (p >= D / 2) return;
+  if (kind == CSK_JOB_MXFP4) {
     uint8_t* codes = reinterpret_cast<uint8_t*>(j.a.out);
-    if (j.in_bf16) quant_pair<uint16_t>(reinterpret_cast<const uint16_t*>(j.x), row, j.a.D, p, codes, j.a.out_scale);
-    else quant_pair<float>(reinterpret_cast<const float*>(j.x), row, j.a.D, p, codes, j.a.out_scale);
-  } else if (j.in_bf16) {
-    if (j.out_kind == OUT_BF16) compress_pair<uint16_t, OUT_BF16, true>(j.a, p, row);
-    else if (j.out_kind == OUT_MXFP4) compress_pair<uint16_t, OUT_MXFP4, true>(j.a, p, row);
-    else if (j.out_kind == OUT_FP8KV) compress_pair<uint16_t, OUT_FP8KV, true>(j.a, p, row);
+    if (in_bf16) quant_pair<uint16_t>(reinterpret_cast<const uint16_t*>(j.x), row, D, p, codes, j.a.out_scale);
+    else quant_pair<float>(reinterpret_cast<const float*>(j.x), row, D, p, codes, j.a.out_scale);
+  } else if (in_bf16) {
+    if (out_kind == OUT_BF16) compress_pair<uint16_t, OUT_BF16, true>(j.a, p, row);
+    else if (out_kind == OUT_MXFP4) compress_pair<uint16_t, OUT_MXFP4, true>(j.a, p, row);
+    else if (out_kind == OUT_FP8KV) compress_pair<uint16_t, OUT_FP8KV, true>(j.a, p, row);
     else compress_pair<uint16_t, OUT_F32, true>(j.a, p, row);
   } else {
-    if (j.out_kind == OUT_BF16) compress_pair<float, OUT_BF16, true>(j.a, p, row);
-    else if (j.out_kind == OUT_MXFP4) compress_pair<float, OUT_MXFP4, true>(j.a, p, row);
-    else if (j.out_kind == OUT_FP8KV) compress_pair<float, OUT_FP8KV, true>(j.a, p, row);
+    if (out_kind == OUT_BF16) compress_pair<float, OUT_BF16, true>(j.a, p, row);
+    else if (out_kind == OUT_MXFP4) compress_pair<float, OUT_MXFP4, true>(j.a, p, row);
+    else if (out_kind == OUT_FP8KV) compress_pair<float, OUT_FP8KV, true>(j.a, p, row);
     else compress_pair<float, OUT_F32, true>(j.a, p, row);
   }
 }
