@@ -302,6 +302,9 @@ int indexer_topk_noalloc(const void* q, const uint8_t* q_scale, const float* w, 
  *             > 0 caps that split at max_workgroups workgroups in all (a row
  *             never gets fewer than one), so that a caller running other
  *             work beside the call on another stream can leave CUs to it.
+ *             Within that limit a row's 64-candidate tiles go to the fewest
+ *             workgroups that keep the longest run (34 tiles over at most 8
+ *             workgroups: 7 runs of at most 5).
  *             The split decides the order in which partial results are
  *             combined, so it is part of what the result bits depend on; a
  *             smaller cap never needs a larger workspace.
