@@ -115,10 +115,10 @@ def test_hca_prefill_16k():
     check_f32(host(lse)[0, ts], rlse, 2e-2, "lse")
 
 
-def _decode_parity(name, overrides=None):
+def _decode_parity(name, overrides=None, **kw):
     import bench
 
-    wl = bench.DecodeWorkload(name, copies=1, overrides=overrides)
+    wl = bench.DecodeWorkload(name, copies=1, overrides=overrides, **kw)
     wl.step(0)
     torch.cuda.synchronize()
     rows = list(range(wl.B))
@@ -181,6 +181,32 @@ def test_decode_1m_pair():
         assert torch.equal(wl.idx, eager[0]), rep
         assert torch.equal(wl.out.view(torch.int16), eager[1].view(torch.int16)), rep
         assert torch.equal(wl.out_h.view(torch.int16), eager[2].view(torch.int16)), rep
+
+
+def test_decode_1m_pair_two_streams():
+    # the launch configuration the throughput figure is timed in: the HCA
+    # branch on a side stream with its dense attention capped at 64
+    # workgroups (a different split of each HCA row, so different partial
+    # roundings than the uncapped one-stream step), eager against the
+    # oracle, then as graph replays against the eager step
+    wl = _decode_parity("decode_1m_pair", streams=2, hca_workgroups=64)
+    eager = (wl.idx.clone(), wl.out.clone(), wl.out_h.clone(), wl.lse_h.clone())
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=s):
+        wl.step(0)
+    for rep in range(3):
+        wl.idx.fill_(-7)
+        wl.out.zero_()
+        wl.out_h.zero_()
+        wl.lse_h.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(wl.idx, eager[0]), rep
+        assert torch.equal(wl.out.view(torch.int16), eager[1].view(torch.int16)), rep
+        assert torch.equal(wl.out_h.view(torch.int16), eager[2].view(torch.int16)), rep
+        assert torch.equal(wl.lse_h.view(torch.int32), eager[3].view(torch.int32)), rep
 
 
 def test_csa_prefill_64k_sampled():
