@@ -6,6 +6,8 @@
  *
  * Sources (web pages about the DeepSeek-V4 technical report):
  *   [P1] "Техотчёт DeepSeek-V4 (2026): миллион токенов контекста" (ai.flicky.cc)
+ *   [P2] "Статья DeepSeek V4: Ключевые технические находки официального
+ *        отчёта" (framia.pro)
  *   [P3] aixai.ru blog post on V4's million-token context,
  *        section "Гибридный attention: CSA и HCA"
  *   [P4] "Технический отчёт DeepSeek-V4 — часть 1/2" (aifinder.ae mirror)
