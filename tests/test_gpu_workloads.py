@@ -159,7 +159,24 @@ def _decode_parity(name, overrides=None, **kw):
 
 
 def test_csa_decode_128k():
-    _decode_parity("csa_decode_128k")
+    wl = _decode_parity("csa_decode_128k")
+    # the throughput is timed as graph replays: each replay gives the eager
+    # step's bits
+    eager = (wl.idx.clone(), wl.out.clone(), wl.lse.clone())
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=s):
+        wl.step(0)
+    for rep in range(3):
+        wl.idx.fill_(-7)
+        wl.out.zero_()
+        wl.lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(wl.idx, eager[0]), rep
+        assert torch.equal(wl.out.view(torch.int16), eager[1].view(torch.int16)), rep
+        assert torch.equal(wl.lse.view(torch.int32), eager[2].view(torch.int32)), rep
 
 
 def test_decode_1m_pair():
